@@ -1,0 +1,177 @@
+/*
+ * ramnet.h -- C ABI of the RAM-Net attention core on AMD Instinct MI355X
+ * (gfx950).  Plain pointers and sizes only; no framework types.
+ *
+ * What the calls compute (sources: the paper page "RAM-Net: Linear-Time
+ * Sequence Modeling with Sparsely Addressable State", and the "ramnet-ops
+ * 0.1.0rc0" PyPI project page):
+ *
+ *   state       per (batch b, head h) an array of S slots; slot a holds a
+ *               content row s[a] (d_v floats) and a mass m[a] (paper §3.1;
+ *               ramnet-ops "Quick start": slot (B,H,P^U,C), mass (B,H,P^U)).
+ *   decode      per token, head and side (write side from the key logits,
+ *               read side from the query logits): softmax over the S slots,
+ *               keep the K most probable by (logit descending, slot index
+ *               ascending), weights = their probabilities, optionally
+ *               renormalised to sum 1 (paper §3.2, App. B.2 "Addressing";
+ *               ramnet-ops "Arguments": top_k, top_k_re_norm).
+ *   write (GSU) for each selected write slot a with weight w and the token's
+ *               forgetting modulator gamma (paper §3.4 "Gated Sparse Update"):
+ *                 lambda = sigmoid(logit(1-w) - gamma)
+ *                 m[a]   <- lambda * m[a] + w
+ *                 eta    = w / (m[a] + eps)
+ *                 s[a]   <- (1 - eta) * s[a] + eta * v_t
+ *               every other slot is left bit-for-bit unchanged.
+ *   read        o_t = sum_j r_j * s[a_j] over the selected read slots, with
+ *               the state after token t's writes (paper §3.4 "Read-out").
+ *   order       tokens in time order; slot-parallel execution groups the
+ *               events of each (b, h, slot) and applies them in time order
+ *               (paper §4 "Slot-Parallel Execution"; ramnet-ops "CUDA
+ *               execution", parallel and autoregressive modes).
+ *
+ * Supported: one address digit (U = 1, P = S); CAPE (cape_heads) is not
+ * supported yet and is rejected.
+ *
+ * Layouts (all row-major, contiguous, device memory):
+ *   logits  (B, T, H, S)     io dtype     wlogits: write side, rlogits: read side
+ *   v, o    (B, T, H, d_v)   io dtype
+ *   gamma   (B, T, H)        io dtype
+ *   slot    (B, H, S, d_v)   float32
+ *   mass    (B, H, S)        float32
+ * io dtype is float32 or bfloat16 (RAM_F32 / RAM_BF16); all arithmetic is
+ * float32; bf16 outputs are rounded to nearest even.
+ *
+ * Ownership and streams: the caller allocates every buffer, including the
+ * workspace (size from ram_workspace_size).  The library never allocates or
+ * frees device memory and never blocks the host; all work is enqueued on the
+ * given HIP stream (a hipStream_t passed as void*, NULL = default stream).
+ * Pointers to logits must be 16-byte aligned.
+ *
+ * Errors: every call returns RAM_OK (0) or a negative code; nothing is
+ * enqueued when validation fails.  There is no fallback path.
+ */
+#ifndef RAMNET_H
+#define RAMNET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RAM_OK 0
+#define RAM_EINVAL (-1)       /* bad shape, null pointer, k > S, misalignment  */
+#define RAM_EDTYPE (-2)       /* io_dtype not RAM_F32 / RAM_BF16               */
+#define RAM_ECAPACITY (-3)    /* too many events or tokens, workspace too small */
+#define RAM_EUNSUPPORTED (-4) /* U > 1 or cape_heads > 0                        */
+#define RAM_EHIP (-5)         /* HIP launch or runtime error                    */
+
+#define RAM_F32 0
+#define RAM_BF16 1
+
+/* One problem description, passed to every call. */
+typedef struct ram_problem {
+  int32_t B, H, T;      /* batch, heads, tokens in this call (T = 1 for ram_decode_step) */
+  int32_t U, P;         /* address digits and digit size; S = P^U slots; U must be 1     */
+  int32_t k_w, k_r;     /* top-K of the write and read side: 1 <= k <= min(S, 64)        */
+  int32_t d_v;          /* slot / value width: 1..64, or an even number 66..128          */
+  int32_t io_dtype;     /* RAM_F32 or RAM_BF16 for logits, v, gamma, o and gradients    */
+  float eps;            /* GSU epsilon (finite, >= 0; the paper's default reading 1e-6) */
+  int32_t renorm_w;     /* 1: renormalise the kept write weights to sum 1               */
+  int32_t renorm_r;     /* 1: same for the read side                                    */
+  int32_t cape_heads;   /* heads using CAPE; must be 0                                  */
+  int32_t reserved;     /* must be 0                                                    */
+  int64_t t0;           /* absolute position of token 0 (CAPE only)                     */
+} ram_problem;
+
+/* Byte offsets of the arrays that ram_forward leaves in the workspace for
+ * ram_backward (and for inspection).  N = B*T*H rows, E = N*(k_w+k_r) events. */
+typedef struct ram_ws_layout {
+  size_t idx_w;       /* int32 (N, k_w): selected write slots, sorted by (logit desc, index asc) */
+  size_t w_w;         /* float (N, k_w): their weights                                          */
+  size_t lse_w;       /* float (N): logsumexp of the write logits                                */
+  size_t idx_r;       /* int32 (N, k_r)                                                           */
+  size_t w_r;         /* float (N, k_r)                                                           */
+  size_t lse_r;       /* float (N)                                                                */
+  size_t seg_offset;  /* int32 (B*H*S + 1): first event of segment g = (b*H + h)*S + a          */
+  size_t events;      /* int32 (E): event codes (t << 7) | (side << 6) | j, segment-major,
+                         time order inside a segment, a token's write before its read          */
+  size_t ckpt_s;      /* float (E/32 + 1, d_v): slot content at every 32-aligned event        */
+  size_t ckpt_m;      /* float (E/32 + 1): slot mass at the same points                      */
+  size_t acc;         /* float (N, d_v): accumulator, all zero between calls                   */
+  size_t tile_hist;   /* int32: bucketing scratch                                              */
+  size_t dw;          /* float (N, k_w): backward scratch                                      */
+  size_t dr;          /* float (N, k_r)                                                         */
+  size_t dgam;        /* float (N, k_w)                                                         */
+  size_t fwd_bytes;   /* workspace bytes ram_forward needs                                      */
+  size_t total_bytes; /* workspace bytes ram_forward + ram_backward need                       */
+} ram_ws_layout;
+
+/* Workspace size for a forward (with_backward = 0) or a forward that a
+ * backward will follow (with_backward = 1). */
+int ram_workspace_size(const ram_problem* p, int with_backward, size_t* bytes);
+
+/* Offsets of the saved arrays inside the workspace. */
+int ram_workspace_layout(const ram_problem* p, ram_ws_layout* out);
+
+/* Address decode of one side (paper §3.2 with U = 1): for every row
+ * (b, t, h) of logits (B,T,H,S), writes idx (B,T,H,k) int32 with the K
+ * selected slots in (logit desc, index asc) order, weight (B,T,H,k) float with
+ * their probabilities exp(l - lse) (renormalised if the side's renorm flag is
+ * set) and lse (B,T,H) float.  side: 0 write (k_w, renorm_w), 1 read. */
+int ram_decode(const ram_problem* p, int side, const void* logits, int32_t* idx, float* weight,
+               float* lse, void* stream);
+
+/* Parallel (training / prefill) forward over T tokens: decode both sides,
+ * bucket events into per-slot segments, run the GSU scan per segment and
+ * accumulate the reads into o.  slot0 / mass0: initial state, or both NULL
+ * for empty slots (content 0, mass 0) (ramnet-ops "Arguments": init_ram).
+ * Writes o, slot1, mass1.  slot1 / mass1 may alias slot0 / mass0 (in-place
+ * continuation, ramnet-ops inplace) only when no ram_backward follows.
+ * ws: workspace of at least ram_workspace_size bytes; it keeps what the
+ * backward needs and must stay untouched until then. */
+int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
+                const void* gamma, const float* slot0, const float* mass0, void* o, float* slot1,
+                float* mass1, void* ws, size_t ws_bytes, void* stream);
+
+/* First-order backward (ramnet-ops "Autograd and compile") of the forward
+ * that filled ws (same problem, same inputs, slot0 / mass0 as given to it).
+ * d_o: gradient of o; d_slot1 / d_mass1: gradients of the final state, NULL
+ * for zero.  Writes d_wlogits, d_rlogits (B,T,H,S) io, d_v (B,T,H,d_v) io,
+ * d_gamma (B,T,H) io, and, when non-NULL, d_slot0 (B,H,S,d_v) / d_mass0
+ * (B,H,S) float.  ws must have been sized with with_backward = 1. */
+int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wlogits,
+                 const void* rlogits, const void* v, const void* gamma, const float* slot0,
+                 const float* mass0, const void* d_o, const float* d_slot1, const float* d_mass1,
+                 void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma, float* d_slot0,
+                 float* d_mass0, void* stream);
+
+/* Autoregressive step (ramnet-ops "CUDA execution", autoregressive mode;
+ * paper §4: each new token updates and reads its own K slots): p->T == 1;
+ * decode both sides of the one token per (b, h), apply its k_w writes to
+ * slot / mass in place, then read its k_r slots into o (B,1,H,d_v).  Needs
+ * k_w * d_v <= 8192.  No workspace. */
+int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
+                    const void* gamma, float* slot, float* mass, void* o, void* stream);
+
+/* Text of a status code (static storage). */
+const char* ram_status_string(int status);
+
+/* Optional kernel timing: while enabled, every kernel the library launches
+ * is bracketed by HIP events on its stream.  ram_prof_collect waits for
+ * those events and returns, per kernel name, the launch count and summed
+ * milliseconds since the last enable. */
+typedef struct ram_prof_entry {
+  char name[32];
+  int64_t launches;
+  double total_ms;
+} ram_prof_entry;
+int ram_prof_enable(int on);
+int ram_prof_collect(ram_prof_entry* out, int max_entries, int* n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAMNET_H */

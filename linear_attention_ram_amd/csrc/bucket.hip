@@ -1,0 +1,148 @@
+// Event bucketing (paper §4 "Slot-Parallel Execution": all read and write
+// events are sorted by slot so each slot gets a time-ordered list; ramnet-ops
+// "CUDA execution": events of the same (batch, head, slot) form a segment).
+//
+// A stable counting sort per (b, h), in three kernels:
+//   hist     one block per (b, h, tile of TILE_TOKENS tokens): slot histogram
+//            of the tile's events in LDS;
+//   scan     one block per (b, h): per slot, exclusive prefix of the tile
+//            counts (in place) and, over the slots in blocks of 1024, the
+//            segment offsets.
+//            Every (b, h) holds exactly T*(k_w+k_r) events, so segment
+//            offsets need no scan across (b, h);
+//   scatter  one wave per (b, h, tile): walks the tile's events in order
+//            (t ascending, write side before read side), ranks equal slots
+//            inside each 64-event batch with ballots, and writes the event
+//            codes to their final positions.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ramk {
+
+namespace {
+
+__device__ __forceinline__ int event_slot(const BucketArgs& a, int b, int h, int t, int p) {
+  const int64_t row = ((int64_t)b * a.T + t) * a.H + h;
+  return (p < a.k_w) ? a.idx_w[row * a.k_w + p] : a.idx_r[row * a.k_r + (p - a.k_w)];
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void bucket_hist_kernel(BucketArgs a) {
+  extern __shared__ int hist[];
+  const int tile = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int K = a.k_w + a.k_r;
+  const int t_lo = tile * TILE_TOKENS;
+  const int t_hi = min(a.T, t_lo + TILE_TOKENS);
+  for (int s = threadIdx.x; s < a.S; s += blockDim.x) hist[s] = 0;
+  __syncthreads();
+  const int n = (t_hi - t_lo) * K;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int slot = event_slot(a, b, h, t_lo + e / K, e % K);
+    if ((unsigned)slot < (unsigned)a.S) atomicAdd(&hist[slot], 1);
+  }
+  __syncthreads();
+  int32_t* out = a.tile_hist + ((int64_t)bh * a.ntiles + tile) * a.S;
+  for (int s = threadIdx.x; s < a.S; s += blockDim.x) out[s] = hist[s];
+}
+
+__global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketArgs a) {
+  __shared__ int wave_tot[16];
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int S = a.S;
+  int32_t* th = a.tile_hist + (int64_t)bh * a.ntiles * S;
+  const int64_t base = (int64_t)bh * a.T * (a.k_w + a.k_r);
+  int carry = 0;
+  for (int s0 = 0; s0 < S; s0 += 1024) {
+    const int s = s0 + tid;
+    int cnt = 0;
+    if (s < S) {
+      for (int tile = 0; tile < a.ntiles; ++tile) {
+        const int c = th[(int64_t)tile * S + s];
+        th[(int64_t)tile * S + s] = cnt;
+        cnt += c;
+      }
+    }
+    const int incl = wave_incl_scan(cnt);
+    if (lane_id() == WAVE - 1) wave_tot[tid / WAVE] = incl;
+    __syncthreads();
+    int before = carry;
+    int all = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int wt = wave_tot[w];
+      if (w < tid / WAVE) before += wt;
+      all += wt;
+    }
+    if (s < S) a.seg_offset[(int64_t)bh * S + s] = (int32_t)(base + before + incl - cnt);
+    carry += all;
+    __syncthreads();
+  }
+  if (bh == a.B * a.H - 1 && tid == 0)
+    a.seg_offset[(int64_t)a.B * a.H * S] = (int32_t)((int64_t)a.B * a.H * a.T * (a.k_w + a.k_r));
+}
+
+__global__ __launch_bounds__(64) void bucket_scatter_kernel(BucketArgs a) {
+  extern __shared__ int next[];
+  const int tile = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int lane = lane_id();
+  const int S = a.S;
+  const int32_t* th = a.tile_hist + ((int64_t)bh * a.ntiles + tile) * S;
+  const int32_t* so = a.seg_offset + (int64_t)bh * S;
+  for (int s = lane; s < S; s += WAVE) next[s] = so[s] + th[s];
+  wave_sync();
+  const int K = a.k_w + a.k_r;
+  const int t_lo = tile * TILE_TOKENS;
+  const int t_hi = min(a.T, t_lo + TILE_TOKENS);
+  const int n = (t_hi - t_lo) * K;
+  const uint64_t lt = lanemask_lt();
+  for (int e0 = 0; e0 < n; e0 += WAVE) {
+    const int e = e0 + lane;
+    bool valid = e < n;
+    int slot = 0, code = 0;
+    if (valid) {
+      const int t = t_lo + e / K, p = e % K;
+      slot = event_slot(a, b, h, t, p);
+      code = (t << 7) | ((p < a.k_w ? 0 : 1) << 6) | (p < a.k_w ? p : p - a.k_w);
+      valid = (unsigned)slot < (unsigned)S;   // decoded slots are always < S
+    }
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < a.nbits; ++bit) {
+      const bool one = (slot >> bit) & 1;
+      const uint64_t bal = __ballot(valid && one);
+      peers &= one ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & lt);
+    const int tot = __popcll(peers);
+    const int base = valid ? next[slot] : 0;
+    wave_sync();
+    if (valid && rank == 0) next[slot] = base + tot;
+    wave_sync();
+    if (valid) a.events[base + rank] = code;
+  }
+}
+
+hipError_t launch_bucket(const BucketArgs& a, hipStream_t st, void (*before)(const char*, hipStream_t),
+                         void (*after)(const char*, hipStream_t)) {
+  const int BH = a.B * a.H;
+  if (BH == 0) return hipSuccess;
+  const size_t lds = (size_t)a.S * sizeof(int);
+  if (a.ntiles > 0) {
+    before("bucket_hist", st);
+    hipLaunchKernelGGL(bucket_hist_kernel, dim3(a.ntiles, BH), dim3(256), lds, st, a);
+    after("bucket_hist", st);
+  }
+  before("bucket_scan", st);
+  hipLaunchKernelGGL(bucket_scan_kernel, dim3(BH), dim3(1024), 0, st, a);
+  after("bucket_scan", st);
+  if (a.ntiles > 0) {
+    before("bucket_scatter", st);
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(a.ntiles, BH), dim3(64), lds, st, a);
+    after("bucket_scatter", st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ramk

@@ -1,0 +1,126 @@
+// Device helpers shared by the gfx950 kernels of the RAM-Net attention core.
+// Wave64 throughout: one wavefront = 64 lanes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ramk {
+
+constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// bf16 is carried as its 16-bit pattern.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+template <typename IO> __device__ __forceinline__ IO from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// Round to nearest even; NaN stays NaN (quietened).
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Number of io elements in one 16-byte vector.
+template <typename IO> struct vec16 { static constexpr int E = 16 / (int)sizeof(IO); };
+
+// Unpack a 16-byte vector of io values to float (memory order).
+__device__ __forceinline__ void unpack16(const uint4 q, float (&v)[4]) {
+  v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+  v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+}
+__device__ __forceinline__ void unpack16(const uint4 q, float (&v)[8]) {
+  v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+  v[4] = __uint_as_float(q.z << 16); v[5] = __uint_as_float(q.z & 0xffff0000u);
+  v[6] = __uint_as_float(q.w << 16); v[7] = __uint_as_float(q.w & 0xffff0000u);
+}
+__device__ __forceinline__ uint4 pack16(const float (&v)[4]) {
+  return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                    __float_as_uint(v[3]));
+}
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  return (uint32_t)from_f32<bf16_t>(lo) | ((uint32_t)from_f32<bf16_t>(hi) << 16);
+}
+__device__ __forceinline__ uint4 pack16(const float (&v)[8]) {
+  return make_uint4(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]), pack2bf(v[4], v[5]),
+                    pack2bf(v[6], v[7]));
+}
+
+// 16-byte vector of -inf in the io type (pads a row past its end).
+template <typename IO> __device__ __forceinline__ uint4 neg_inf16();
+template <> __device__ __forceinline__ uint4 neg_inf16<float>() {
+  return make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+}
+template <> __device__ __forceinline__ uint4 neg_inf16<bf16_t>() {
+  return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (WAVE - 1)); }
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  return (1ull << lane_id()) - 1ull;
+}
+
+// Orders LDS traffic between the lanes of one wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, WAVE));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, WAVE);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, WAVE);
+  return x;
+}
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    int y = __shfl_up(x, o, WAVE);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ int readlane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+// Retention lambda = sigmoid(logit(1-w) - g) = (1-w)/((1-w) + w e^g) of the
+// Gated Sparse Update, in the form that stays finite for large |g|: for
+// g >= 0 numerator and denominator are multiplied by e^-g.  w <= 0 gives 1
+// (unaddressed), w >= 1 gives 0.  Optionally d lambda / d w = -e^g / D^2.
+__device__ __forceinline__ float retention(float w, float g, float* dlam_dw) {
+  float c, num, den;
+  if (g >= 0.f) {
+    c = expf(-g);
+    num = (1.f - w) * c;
+    den = num + w;
+  } else {
+    c = expf(g);
+    num = 1.f - w;
+    den = num + w * c;
+  }
+  float lam = (w <= 0.f) ? 1.f : ((w >= 1.f) ? 0.f : num / den);
+  if (dlam_dw) *dlam_dw = -c / (den * den);
+  return lam;
+}
+
+}  // namespace ramk

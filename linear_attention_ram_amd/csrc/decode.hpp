@@ -1,0 +1,210 @@
+// Row decoder of the RAM-Net attention core, shared by the decode kernels and
+// the autoregressive step kernel.  See decode.hip for the algorithm.
+#pragma once
+#include "common.hpp"
+
+namespace ramk {
+
+constexpr int CAND_CAP = 512;   // candidates kept in LDS per row
+constexpr int MAX_K = 64;       // largest top-K per side
+
+// Per-wave LDS work area of the row decoder.
+struct DecodeScratch {
+  float cv[CAND_CAP];
+  int ci[CAND_CAP];
+  float sv[MAX_K];
+  int si[MAX_K];
+  int lanes[WAVE];
+};
+
+struct DecodeFwdArgs {
+  const void* logits[2];   // (N, S) io per side
+  int32_t* idx[2];         // (N, k) per side
+  float* w[2];             // (N, k) per side
+  float* lse[2];           // (N,) per side
+  int k[2];
+  int renorm[2];
+  int64_t N;               // rows per side
+  int S;
+  int nsides;              // 1 or 2 (side 0 = first pointer set)
+  float* zero_rows;        // optional (N, zero_width) float rows to clear
+  int zero_width;
+};
+
+struct DecodeBwdArgs {
+  const void* logits[2];
+  const float* lse[2];
+  const int32_t* idx[2];
+  const float* w[2];
+  const float* g[2];       // gradient of the output weights (N, k)
+  void* dlogits[2];        // (N, S) io
+  int k[2];
+  int renorm[2];
+  int64_t N;
+  int S;
+  int nsides;
+};
+
+hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_decode_bwd(const DecodeBwdArgs& a, bool bf16, hipStream_t st);
+
+namespace {
+
+// (value, index) order of the selection: larger value first, then lower index.
+__device__ __forceinline__ bool before(float v, int i, float v2, int i2) {
+  return (v > v2) || (v == v2 && i < i2);
+}
+
+template <typename IO>
+__device__ __forceinline__ uint4 load_vec(const IO* row, int c, int nvec) {
+  return (c < nvec) ? *reinterpret_cast<const uint4*>(row + (int64_t)c * vec16<IO>::E)
+                    : neg_inf16<IO>();
+}
+
+}  // namespace
+
+// Decodes one row with the calling wave.  Results go to sel_i / sel_w
+// (k entries, LDS or registers visible to the wave after the call) and the
+// returned lse.  scratch: this wave's LDS area.
+template <typename IO>
+__device__ float decode_row_wave(const IO* __restrict__ row, int S, int k, int renorm,
+                                 DecodeScratch& sc, int* sel_i, float* sel_w) {
+  constexpr int E = vec16<IO>::E;
+  constexpr int TILE = 8;                 // 16-byte vectors per lane held at once
+  const int lane = lane_id();
+  const int nvec = S / E;
+
+  // pass 1: online max / sum of exp per lane
+  float m = -INFINITY, s = 0.f;
+  for (int c0 = 0; c0 < nvec; c0 += WAVE * TILE) {
+    uint4 q[TILE];
+#pragma unroll
+    for (int u = 0; u < TILE; ++u) q[u] = load_vec<IO>(row, c0 + u * WAVE + lane, nvec);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < TILE; ++u) {
+      float x[E];
+      unpack16(q[u], x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) tmax = fmaxf(tmax, x[e]);
+    }
+    const float mn = fmaxf(m, tmax);
+    if (mn != -INFINITY) {
+      s *= (m == -INFINITY) ? 0.f : exp2f((m - mn) * LOG2E);
+      const float nml = -mn * LOG2E;
+#pragma unroll
+      for (int u = 0; u < TILE; ++u) {
+        float x[E];
+        unpack16(q[u], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) s += exp2f(fmaf(x[e], LOG2E, nml));
+      }
+      m = mn;
+    }
+  }
+  const float M = wave_max(m);
+  const float part = (m == -INFINITY) ? 0.f : s * exp2f((m - M) * LOG2E);
+  const float lse = M + logf(wave_sum(part));
+
+  // threshold: K-th largest lane maximum (counted with multiplicity)
+  float cur = m, tau = -INFINITY;
+  for (int r = 0; r < k; ++r) {
+    const float mx = wave_max(cur);
+    tau = mx;
+    const uint64_t hit = __ballot(cur == mx);
+    if (lane == (int)__builtin_ctzll(hit)) cur = -INFINITY;
+  }
+
+  // lanes that may hold top-K elements
+  const bool winner = (m >= tau);
+  const uint64_t wmask = __ballot(winner);
+  const int nw = __popcll(wmask);
+  if (winner) sc.lanes[__popcll(wmask & lanemask_lt())] = lane;
+  wave_sync();
+
+  // compact every element >= tau of those lanes into LDS
+  const int per_lane = (nvec + WAVE - 1) / WAVE;
+  const int items = nw * per_lane;
+  int count = 0;
+  bool overflow = false;
+  for (int it0 = 0; it0 < items; it0 += WAVE) {
+    const int it = it0 + lane;
+    float x[E];
+    int base = -1, mine = 0;
+    if (it < items) {
+      const int c = (it % per_lane) * WAVE + sc.lanes[it / per_lane];
+      if (c < nvec) {
+        unpack16(load_vec<IO>(row, c, nvec), x);
+        base = c * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) mine += (x[e] >= tau);
+      }
+    }
+    const int incl = wave_incl_scan(mine);
+    const int total = readlane_i(incl, WAVE - 1);
+    if (count + total > CAND_CAP) { overflow = true; break; }
+    int pos = count + incl - mine;
+    if (base >= 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (x[e] >= tau) { sc.cv[pos] = x[e]; sc.ci[pos] = base + e; ++pos; }
+    }
+    count += total;
+  }
+  wave_sync();
+
+  if (!overflow) {
+    // exact rank of every candidate among the candidates
+    for (int ci = lane; ci < count; ci += WAVE) {
+      const float v = sc.cv[ci];
+      const int id = sc.ci[ci];
+      int rank = 0;
+      for (int o = 0; o < count; ++o) rank += before(sc.cv[o], sc.ci[o], v, id) ? 1 : 0;
+      if (rank < k) { sc.sv[rank] = v; sc.si[rank] = id; }
+    }
+  } else {
+    // fallback: K exact passes, each picks the best element after the
+    // previous pick in (value desc, index asc) order
+    float pv = INFINITY;
+    int pi = -1;
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int c = lane; c < nvec; c += WAVE) {
+        float x[E];
+        unpack16(load_vec<IO>(row, c, nvec), x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int id = c * E + e;
+          if (before(pv, pi, x[e], id) && before(x[e], id, bv, bi)) { bv = x[e]; bi = id; }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, WAVE);
+        const int oi = __shfl_xor(bi, o, WAVE);
+        if (before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (lane == 0) { sc.sv[r] = bv; sc.si[r] = bi; }
+      pv = bv;
+      pi = bi;
+    }
+  }
+  wave_sync();
+
+  // weights
+  float w = 0.f;
+  int id = 0;
+  if (lane < k) {
+    id = sc.si[lane];
+    w = expf(sc.sv[lane] - lse);
+  }
+  if (renorm) {
+    const float tot = wave_sum(lane < k ? w : 0.f);
+    w = w / tot;
+  }
+  if (lane < k) { sel_i[lane] = id; sel_w[lane] = w; }
+  return lse;
+}
+
+}  // namespace ramk

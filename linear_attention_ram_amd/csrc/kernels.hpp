@@ -1,0 +1,92 @@
+// Argument blocks and host launchers of the bucketing, scan and step kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ramk {
+
+constexpr int CHUNK = 32;        // scan chunk: checkpoints at 32-aligned events
+constexpr int TILE_TOKENS = 256; // tokens per bucketing tile
+
+struct BucketArgs {
+  const int32_t* idx_w;   // (N, k_w)
+  const int32_t* idx_r;   // (N, k_r)
+  int B, H, T, S, k_w, k_r;
+  int ntiles;             // ceil(T / TILE_TOKENS)
+  int nbits;              // bits needed for a slot index
+  int32_t* tile_hist;     // (B*H, ntiles, S)
+  int32_t* seg_offset;    // (B*H*S + 1)
+  int32_t* events;        // (E)
+};
+
+struct ScanFwdArgs {
+  int B, H, T, S, d_v, k_w, k_r;
+  float eps;
+  const int32_t* seg_offset;
+  const int32_t* events;
+  const float* w_w;       // (N, k_w)
+  const float* w_r;       // (N, k_r)
+  const void* v;          // (N, d_v) io
+  const void* gamma;      // (N) io
+  const float* slot0;     // (B*H*S, d_v) or null
+  const float* mass0;     // (B*H*S) or null
+  float* slot1;
+  float* mass1;
+  float* acc;             // (N, d_v) read accumulator (zero on entry)
+  float* ckpt_s;          // (E/CHUNK + 1, d_v)
+  float* ckpt_m;          // (E/CHUNK + 1)
+};
+
+struct ScanBwdArgs {
+  int B, H, T, S, d_v, k_w, k_r;
+  float eps;
+  const int32_t* seg_offset;
+  const int32_t* events;
+  const float* w_w;
+  const float* w_r;
+  const void* v;          // io
+  const void* gamma;      // io
+  const void* d_o;        // (N, d_v) io
+  const float* slot0;     // or null
+  const float* mass0;     // or null
+  const float* ckpt_s;
+  const float* ckpt_m;
+  const float* d_slot1;   // or null
+  const float* d_mass1;   // or null
+  float* d_slot0;         // or null
+  float* d_mass0;         // or null
+  float* acc;             // (N, d_v) d_v accumulator (zero on entry)
+  float* dw;              // (N, k_w)
+  float* dr;              // (N, k_r)
+  float* dgam;            // (N, k_w) per-write gamma gradient parts
+};
+
+struct FinalizeArgs {
+  int64_t N;
+  int d_v, k_w;
+  float* acc;             // (N, d_v), cleared after reading
+  void* out;              // (N, d_v) io
+  const float* dgam;      // (N, k_w) or null
+  void* d_gamma;          // (N) io or null
+};
+
+struct StepArgs {
+  int B, H, S, d_v, k_w, k_r, renorm_w, renorm_r;
+  float eps;
+  const void* wl;         // (B*H, S) io
+  const void* rl;
+  const void* v;          // (B*H, d_v) io
+  const void* gamma;      // (B*H) io
+  float* slot;            // (B*H*S, d_v)
+  float* mass;            // (B*H*S)
+  void* o;                // (B*H, d_v) io
+};
+
+hipError_t launch_bucket(const BucketArgs& a, hipStream_t st, void (*before)(const char*, hipStream_t),
+                         void (*after)(const char*, hipStream_t));
+hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t st);
+
+}  // namespace ramk

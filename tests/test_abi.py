@@ -1,0 +1,101 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/ramnet.h declares, and rejects bad problems with the documented
+status codes (host-side validation; nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_ram_amd as ram
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ramnet.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(ram_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    L = ram.lib()
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(ram.EXPORTED)
+
+
+def test_problem_struct_matches_header_size():
+    assert ctypes.sizeof(ram.Problem) == 64
+    assert ctypes.sizeof(ram.WsLayout) == 17 * ctypes.sizeof(ctypes.c_size_t)
+
+
+def status_of(**kw):
+    base = dict(B=2, H=3, T=100, S=64, k_w=4, k_r=2, d_v=16, io="bf16")
+    base.update(kw)
+    p = ram.problem(**base)
+    n = ctypes.c_size_t(0)
+    return ram.lib().ram_workspace_size(ctypes.byref(p), 1, ctypes.byref(n)), p, n.value
+
+
+def test_valid_problem_has_positive_workspace():
+    st, p, n = status_of()
+    assert st == ram.RAM_OK and n > 0
+    L = ram.ram_workspace_layout(p)
+    assert L["fwd_bytes"] <= L["total_bytes"] == n
+    offs = sorted(v for k, v in L.items() if k not in ("fwd_bytes", "total_bytes"))
+    assert all(o % 256 == 0 for o in offs)
+    assert len(set(offs)) == len(offs)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_w=65), ram.RAM_EINVAL),
+    (dict(k_r=0), ram.RAM_EINVAL),
+    (dict(S=8, k_w=9), ram.RAM_EINVAL),
+    (dict(S=4), ram.RAM_EINVAL),              # 4 bf16 logits are not a 16-byte row
+    (dict(d_v=129), ram.RAM_EINVAL),
+    (dict(d_v=65), ram.RAM_EINVAL),
+    (dict(H=0), ram.RAM_EINVAL),
+    (dict(eps=-1.0), ram.RAM_EINVAL),
+    (dict(S=32768), ram.RAM_EUNSUPPORTED),
+    (dict(cape_heads=1), ram.RAM_EUNSUPPORTED),
+    (dict(T=1 << 24), ram.RAM_ECAPACITY),
+    (dict(B=4096, T=8192, H=16, S=64, k_w=8, k_r=8), ram.RAM_ECAPACITY),
+])
+def test_invalid_problems_are_rejected(kw, code):
+    st, _, _ = status_of(**kw)
+    assert st == code, ram.ram_status_string(st)
+
+
+def test_bad_dtype_and_digits():
+    p = ram.problem(1, 1, 4, 64, 2, 2, 16)
+    p.io_dtype = 7
+    n = ctypes.c_size_t(0)
+    assert ram.lib().ram_workspace_size(ctypes.byref(p), 1, ctypes.byref(n)) == ram.RAM_EDTYPE
+    p = ram.problem(1, 1, 4, 64, 2, 2, 16)
+    p.U = 2
+    p.P = 8
+    assert ram.lib().ram_workspace_size(ctypes.byref(p), 1, ctypes.byref(n)) == ram.RAM_EUNSUPPORTED
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert ram.ram_status_string(code)
+    assert ram.ram_status_string(-99) == "unknown status"
+
+
+def test_forward_rejects_small_workspace_before_touching_the_gpu():
+    p = ram.problem(1, 1, 8, 64, 2, 2, 16, io="f32")
+    L = ram.lib()
+    fake = ctypes.c_void_p(16 * 1024)  # never dereferenced: validation fails first
+    st = L.ram_forward(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, fake, fake,
+                       fake, ctypes.c_size_t(16), None)
+    assert st == ram.RAM_ECAPACITY
+    st = L.ram_forward(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, fake, fake,
+                       fake, ctypes.c_size_t(1 << 30), None)
+    assert st == ram.RAM_EINVAL             # slot0 without mass0
+    st = L.ram_decode_step(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None)
+    assert st == ram.RAM_EINVAL             # T != 1

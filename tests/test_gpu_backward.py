@@ -1,0 +1,115 @@
+"""GPU parity of ram_backward against the oracle's reverse token loop:
+gradients of both logit sides, v, gamma and the initial state within the
+tolerance of the io dtype; the decoded-weight gradients (float32 internals)
+within 1e-4."""
+import pytest
+import torch
+
+import linear_attention_ram_amd as ram
+import oracle
+from gpu_util import (TOL, bh_slice, gpu_problem, host, oracle_problem, rel, run_backward,
+                      run_forward, say)
+from linear_attention_ram_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def full_check(cfg, x, p, with_state, with_state_grads, tol):
+    slot0 = x["slot0"] if with_state else None
+    mass0 = x["mass0"] if with_state else None
+    ds1 = x["d_slot1"] if with_state_grads else None
+    dm1 = x["d_mass1"] if with_state_grads else None
+    r = run_forward(p, x, slot0=slot0, mass0=mass0)
+    g = run_backward(p, x, r["ws"], slot0, mass0, ds1, dm1, want_state=True)
+    torch.cuda.synchronize()
+    h = {k: host(v) for k, v in x.items()}
+    say("oracle backward", cfg.name)
+    rg = oracle.backward(oracle_problem(p), h["wl"], h["rl"], h["v"], h["gamma"],
+                         h["slot0"] if with_state else None, h["mass0"] if with_state else None,
+                         h["d_o"], h["d_slot1"] if with_state_grads else None,
+                         h["d_mass1"] if with_state_grads else None)
+    for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma"):
+        err = rel(host(g[name]), rg[name])
+        assert err <= tol, (name, err)
+    views = ram.ws_views(p, r["ws"])
+    # float32 internals computed from the same io values: tighter than the io bar
+    assert rel(views["dw"].cpu().numpy().reshape(rg["dw"].shape), rg["dw"]) <= 1e-4
+    assert rel(views["dr"].cpu().numpy().reshape(rg["dr"].shape), rg["dr"]) <= 1e-4
+    if with_state:
+        assert rel(host(g["d_slot0"]), rg["d_slot0"]) <= tol
+        assert rel(host(g["d_mass0"]), rg["d_mass0"]) <= tol
+    return r, g
+
+
+@pytest.mark.parametrize("with_state,with_state_grads", [(False, False), (True, True),
+                                                         (True, False)])
+def test_tiny_full(with_state, with_state_grads):
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.layer_inputs(cfg, device=DEV, seed=0, with_state=True, with_state_grads=True)
+    full_check(cfg, x, gpu_problem(cfg), with_state, with_state_grads, TOL["f32"])
+
+
+def test_tiny_renormalised():
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.layer_inputs(cfg, device=DEV, seed=4, with_state=True, with_state_grads=True)
+    full_check(cfg, x, gpu_problem(cfg, renorm=(True, True)), True, True, TOL["f32"])
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_340m_full(with_state):
+    cfg = synth.CONFIGS["340m"]
+    x = synth.layer_inputs(cfg, device=DEV, seed=2, with_state=True, with_state_grads=True)
+    full_check(cfg, x, gpu_problem(cfg), with_state, with_state, TOL["bf16"])
+
+
+def test_1_3b_sampled_slices():
+    cfg = synth.CONFIGS["1.3b"]
+    x = synth.layer_inputs(cfg, device=DEV, seed=0)
+    p = gpu_problem(cfg)
+    say("1.3b fwd+bwd on GPU")
+    r = run_forward(p, x)
+    g = run_backward(p, x, r["ws"])
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (6, 9)]:
+        say("1.3b oracle backward slice", b, h)
+        s = bh_slice(x, b, h)
+        op = oracle.problem(1, 1, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, eps=cfg.eps)
+        rg = oracle.backward(op, s["wl"], s["rl"], s["v"], s["gamma"], None, None, s["d_o"])
+        for name, key in (("d_wlogits", "d_wlogits"), ("d_rlogits", "d_rlogits"),
+                          ("d_v", "d_v"), ("d_gamma", "d_gamma")):
+            err = rel(host(g[name][b:b + 1, :, h:h + 1]), rg[key])
+            assert err <= TOL["bf16"], (name, b, h, err)
+
+
+EDGE = [
+    # B, H, T, S, k_w, k_r, d_v, io, renorm, eps
+    (1, 1, 1, 8, 1, 1, 1, "f32", (False, False), 1e-6),
+    (2, 3, 31, 16, 3, 2, 7, "f32", (False, True), 1e-6),
+    (3, 1, 300, 32, 2, 5, 66, "f32", (True, False), 1e-3),
+    (1, 2, 257, 128, 4, 4, 128, "bf16", (False, False), 1e-6),
+    (2, 2, 600, 8, 8, 8, 16, "f32", (False, False), 1e-6),  # long segments: many chunks
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+def test_edge_shapes(case):
+    B, H, T, S, kw, kr, d, io, rn, eps = EDGE[case]
+    cfg = synth.Config("edge", B, H, T, S, kw, kr, d, io)
+    x = synth.layer_inputs(cfg, device=DEV, seed=20 + case, with_state=True, with_state_grads=True)
+    p = ram.problem(B, H, T, S, kw, kr, d, io=io, eps=eps, renorm=rn)
+    full_check(cfg, x, p, case % 2 == 0, case % 2 == 0, TOL[io])
+
+
+def test_backward_twice_gives_the_same_result():
+    # the accumulator is zero again after each call, so a second backward on
+    # the same workspace repeats the first
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.layer_inputs(cfg, device=DEV, seed=9)
+    p = gpu_problem(cfg)
+    r = run_forward(p, x)
+    g1 = run_backward(p, x, r["ws"])
+    g2 = run_backward(p, x, r["ws"])
+    torch.cuda.synchronize()
+    for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma"):
+        assert rel(host(g2[name]), host(g1[name])) <= 1e-6

@@ -1,0 +1,88 @@
+"""GPU parity of the address decoder (ram_decode) against the oracle:
+indices bit-exact, weights and lse within the fp32 tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_ram_amd as ram
+import oracle
+from gpu_util import host, rel, say
+from linear_attention_ram_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def gpu_decode(p, side, logits):
+    k = p.k_w if side == 0 else p.k_r
+    idx = torch.empty((p.B, p.T, p.H, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((p.B, p.T, p.H, k), dtype=torch.float32, device=logits.device)
+    lse = torch.empty((p.B, p.T, p.H), dtype=torch.float32, device=logits.device)
+    ram.ram_decode(p, side, logits, idx, w, lse)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy(), lse.cpu().numpy()
+
+
+def check_rows(p, side, logits_gpu, rows_host, sel):
+    """rows_host: float64 logits (B', T', H', S) of the rows picked by sel."""
+    gi, gw, gl = gpu_decode(p, side, logits_gpu)
+    k = p.k_w if side == 0 else p.k_r
+    B_, T_, H_ = rows_host.shape[:3]
+    op = oracle.problem(B_, H_, T_, p.S, k, k, 1, renorm=(bool(p.renorm_w), bool(p.renorm_r)))
+    oi, ow, ol = oracle.decode(op, side, rows_host)
+    np.testing.assert_array_equal(gi[sel], oi)
+    assert rel(gw[sel], ow) <= 1e-5
+    assert np.max(np.abs(gl[sel] - ol[..., 0])) <= 1e-5 * max(1.0, np.max(np.abs(ol)))
+
+
+@pytest.mark.parametrize("side", [0, 1])
+def test_tiny_full(side):
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.layer_inputs(cfg, device=DEV, seed=0)
+    p = ram.problem(cfg.B, cfg.H, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io="f32")
+    lg = x["wl"] if side == 0 else x["rl"]
+    check_rows(p, side, lg, host(lg), np.s_[:])
+
+
+@pytest.mark.parametrize("S,k,io,renorm", [(1024, 8, "bf16", False), (4096, 8, "bf16", True),
+                                           (16384, 8, "bf16", False), (64, 64, "f32", False),
+                                           (8, 1, "bf16", False), (2048, 33, "f32", True),
+                                           (512, 5, "bf16", False)])
+def test_ties_and_shapes(S, k, io, renorm):
+    # integer-valued logits: heavy ties at the k-th boundary; ragged row count
+    g = torch.Generator(device=DEV).manual_seed(S + k)
+    B, T, H = 1, 37, 3
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    lg = torch.randint(-3, 4, (B, T, H, S), generator=g, device=DEV).to(dt)
+    p = ram.problem(B, H, T, S, k, k, 16, io=io, renorm=renorm)
+    say("ties", S, k, io)
+    check_rows(p, 0, lg, host(lg), np.s_[:])
+
+
+def test_all_equal_rows_take_the_exact_fallback():
+    # every logit equal: more candidates than the LDS list holds
+    B, T, H, S, k = 1, 4, 2, 4096, 8
+    lg = torch.zeros((B, T, H, S), dtype=torch.bfloat16, device=DEV)
+    lg[0, 1, 1, 4000] = 1.0
+    p = ram.problem(B, H, T, S, k, k, 16, io="bf16")
+    check_rows(p, 1, lg, host(lg), np.s_[:])
+
+
+def test_340m_full():
+    cfg = synth.CONFIGS["340m"]
+    x = synth.layer_inputs(cfg, device=DEV, seed=0, with_d_o=False)
+    p = ram.problem(cfg.B, cfg.H, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io=cfg.io)
+    for side, key in ((0, "wl"), (1, "rl")):
+        say("340m side", side)
+        check_rows(p, side, x[key], host(x[key]), np.s_[:])
+
+
+def test_1_3b_sampled_heads():
+    cfg = synth.CONFIGS["1.3b"]
+    x = synth.layer_inputs(cfg, device=DEV, seed=0, with_d_o=False)
+    p = ram.problem(cfg.B, cfg.H, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io=cfg.io)
+    for side, key in ((0, "wl"), (1, "rl")):
+        for b, h in ((0, 0), (5, 11)):
+            say("1.3b side", side, "slice", b, h)
+            rows = host(x[key][b:b + 1, :, h:h + 1])
+            check_rows(p, side, x[key], rows, np.s_[b:b + 1, :, h:h + 1])

@@ -1,0 +1,71 @@
+"""GPU parity of ram_decode_step (one token per (b, h), state updated in
+place) against the oracle's autoregressive step."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_ram_amd as ram
+import oracle
+from gpu_util import TOL, host, rel, say
+from linear_attention_ram_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_steps(cfg, nsteps, seqs, io_tol):
+    slot, mass = synth.decode_state(cfg, device=DEV, seed=0)
+    p = ram.problem(cfg.B, cfg.H, 1, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io=cfg.io, eps=cfg.eps)
+    op = oracle.problem(len(seqs), cfg.H, 1, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, eps=cfg.eps)
+    o_slot = np.ascontiguousarray(host(slot[seqs]))
+    o_mass = np.ascontiguousarray(host(mass[seqs]))
+    o = torch.empty((cfg.B, 1, cfg.H, cfg.d_v), dtype=cfg.dtype, device=DEV)
+    for step in range(nsteps):
+        x = synth.decode_step_inputs(cfg, step, device=DEV, seed=0)
+        ram.ram_decode_step(p, x["wl"], x["rl"], x["v"], x["gamma"], slot, mass, o)
+        torch.cuda.synchronize()
+        h = {k: host(v[seqs]) for k, v in x.items()}
+        ref = oracle.decode_step(op, h["wl"], h["rl"], h["v"], h["gamma"], o_slot, o_mass)
+        err = rel(host(o[seqs]), ref)
+        assert err <= io_tol, (step, err)
+    assert rel(host(slot[seqs]), o_slot) <= io_tol
+    assert rel(host(mass[seqs]), o_mass) <= io_tol
+
+
+def test_small_fp32():
+    cfg = synth.Config("small", 5, 3, 1, 64, 4, 3, 16, "f32")
+    run_steps(cfg, 40, list(range(5)), TOL["f32"])
+
+
+def test_small_bf16_wide():
+    cfg = synth.Config("wide", 3, 2, 1, 1024, 8, 8, 128, "bf16")
+    run_steps(cfg, 30, list(range(3)), TOL["bf16"])
+
+
+def test_decode_config_sampled_sequences():
+    cfg = synth.CONFIGS["decode"]
+    say("decode config: 64 steps, oracle on sequences 0, 100, 255")
+    run_steps(cfg, 64, [0, 100, 255], TOL["bf16"])
+
+
+def test_steps_match_parallel_forward():
+    # T decode steps reproduce one parallel forward over the same T tokens
+    cfg = synth.Config("chain", 2, 2, 48, 32, 3, 2, 16, "f32")
+    x = synth.layer_inputs(cfg, device=DEV, seed=3, with_state=True, with_d_o=False)
+    p = ram.problem(cfg.B, cfg.H, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io="f32")
+    ws = ram.workspace(p, False, DEV)
+    o = torch.empty_like(x["v"])
+    slot1 = torch.empty_like(x["slot0"])
+    mass1 = torch.empty_like(x["mass0"])
+    ram.ram_forward(p, x["wl"], x["rl"], x["v"], x["gamma"], x["slot0"], x["mass0"], o, slot1,
+                    mass1, ws)
+    ps = ram.problem(cfg.B, cfg.H, 1, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io="f32")
+    slot, mass = x["slot0"].clone(), x["mass0"].clone()
+    os_ = torch.empty((cfg.B, 1, cfg.H, cfg.d_v), device=DEV)
+    for t in range(cfg.T):
+        xs = {k: x[k][:, t:t + 1].contiguous() for k in ("wl", "rl", "v", "gamma")}
+        ram.ram_decode_step(ps, xs["wl"], xs["rl"], xs["v"], xs["gamma"], slot, mass, os_)
+        assert rel(host(os_[:, 0]), host(o[:, t])) <= 1e-5
+    torch.cuda.synchronize()
+    assert rel(host(slot), host(slot1)) <= 1e-5
+    assert rel(host(mass), host(mass1)) <= 1e-5
