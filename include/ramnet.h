@@ -39,7 +39,9 @@
  *   slot    (B, H, S, d_v)   float32
  *   mass    (B, H, S)        float32
  * io dtype is float32 or bfloat16 (RAM_F32 / RAM_BF16); all arithmetic is
- * float32; bf16 outputs are rounded to nearest even.
+ * float32 and the state is float32.  o and d_v are sums over the K selected
+ * slots of one token; each of the K terms is rounded to the io dtype before
+ * the float32 sum, which is then rounded (to nearest even) once more.
  *
  * Ownership and streams: the caller allocates every buffer, including the
  * workspace (size from ram_workspace_size).  The library never allocates or
@@ -99,8 +101,10 @@ typedef struct ram_ws_layout {
                          time order inside a segment, a token's write before its read          */
   size_t ckpt_s;      /* float (E/32 + 1, d_v): slot content at every 32-aligned event        */
   size_t ckpt_m;      /* float (E/32 + 1): slot mass at the same points                      */
-  size_t acc;         /* float (N, d_v): accumulator, all zero between calls                   */
+  size_t stash;       /* io (N, max(k_w,k_r), d_v): per-(token, j) read / dv contributions      */
   size_t tile_hist;   /* int32: bucketing scratch                                              */
+  size_t long_list;   /* int32: segments that take the cooperative scan path                   */
+  size_t long_count;  /* int32: their number                                                   */
   size_t dw;          /* float (N, k_w): backward scratch                                      */
   size_t dr;          /* float (N, k_r)                                                         */
   size_t dgam;        /* float (N, k_w)                                                         */

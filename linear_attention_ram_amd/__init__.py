@@ -55,7 +55,8 @@ class Problem(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "idx_w", "w_w", "lse_w", "idx_r", "w_r", "lse_r", "seg_offset", "events", "ckpt_s",
-        "ckpt_m", "acc", "tile_hist", "dw", "dr", "dgam", "fwd_bytes", "total_bytes")]
+        "ckpt_m", "stash", "tile_hist", "long_list", "long_count", "dw", "dr", "dgam",
+        "fwd_bytes", "total_bytes")]
 
 
 class ProfEntry(ctypes.Structure):

@@ -14,6 +14,7 @@ using namespace ramk;
 namespace {
 
 constexpr size_t ALIGN = 256;
+constexpr int LONG_BLOCKS = 512;   // workgroups that walk the list of long segments
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Dims {
@@ -72,8 +73,10 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   L->events = take(sizeof(int32_t) * d.E);
   L->ckpt_s = take(sizeof(float) * d.nck * p->d_v);
   L->ckpt_m = take(sizeof(float) * d.nck);
-  L->acc = take(sizeof(float) * d.N * p->d_v);
+  L->stash = take(d.io_bytes * d.N * (p->k_w > p->k_r ? p->k_w : p->k_r) * p->d_v);
   L->tile_hist = take(sizeof(int32_t) * (size_t)p->B * p->H * d.ntiles * d.S);
+  L->long_list = take(sizeof(int32_t) * (d.E / (LONG_EVENTS + 1) + 1));
+  L->long_count = take(sizeof(int32_t));
   L->fwd_bytes = off;
   L->dw = take(sizeof(float) * d.N * p->k_w);
   L->dr = take(sizeof(float) * d.N * p->k_r);
@@ -219,8 +222,6 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   da.N = d.N;
   da.S = (int)d.S;
   da.nsides = 2;
-  da.zero_rows = (float*)(w + L.acc);
-  da.zero_width = p->d_v;
   prof_before("decode_fwd", s);
   e = launch_decode_fwd(da, bf, s);
   prof_after("decode_fwd", s);
@@ -240,6 +241,8 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   ba.tile_hist = (int32_t*)(w + L.tile_hist);
   ba.seg_offset = (int32_t*)(w + L.seg_offset);
   ba.events = (int32_t*)(w + L.events);
+  ba.long_list = (int32_t*)(w + L.long_list);
+  ba.long_count = (int32_t*)(w + L.long_count);
   e = launch_bucket(ba, s, prof_before, prof_after);
   if (e != hipSuccess) return RAM_EHIP;
 
@@ -252,6 +255,11 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   sa.k_w = p->k_w;
   sa.k_r = p->k_r;
   sa.eps = p->eps;
+  sa.nseg = d.nseg;
+  sa.long_list = ba.long_list;
+  sa.long_count = ba.long_count;
+  sa.use_long = d.ntiles > 0;
+  sa.long_blocks = LONG_BLOCKS;
   sa.seg_offset = ba.seg_offset;
   sa.events = ba.events;
   sa.w_w = da.w[0];
@@ -262,7 +270,7 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   sa.mass0 = mass0;
   sa.slot1 = slot1;
   sa.mass1 = mass1;
-  sa.acc = (float*)(w + L.acc);
+  sa.stash = w + L.stash;
   sa.ckpt_s = (float*)(w + L.ckpt_s);
   sa.ckpt_m = (float*)(w + L.ckpt_m);
   prof_before("scan_fwd", s);
@@ -273,8 +281,8 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   FinalizeArgs fa{};
   fa.N = d.N;
   fa.d_v = p->d_v;
-  fa.k_w = p->k_w;
-  fa.acc = sa.acc;
+  fa.k = p->k_r;
+  fa.stash = sa.stash;
   fa.out = o;
   prof_before("finalize_o", s);
   e = launch_finalize(fa, bf, s);
@@ -315,6 +323,11 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   sb.k_w = p->k_w;
   sb.k_r = p->k_r;
   sb.eps = p->eps;
+  sb.nseg = d.nseg;
+  sb.long_list = (const int32_t*)(w + L.long_list);
+  sb.long_count = (const int32_t*)(w + L.long_count);
+  sb.use_long = d.ntiles > 0;
+  sb.long_blocks = LONG_BLOCKS;
   sb.seg_offset = (const int32_t*)(w + L.seg_offset);
   sb.events = (const int32_t*)(w + L.events);
   sb.w_w = (const float*)(w + L.w_w);
@@ -330,7 +343,7 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   sb.d_mass1 = d_mass1;
   sb.d_slot0 = d_slot0;
   sb.d_mass0 = d_mass0;
-  sb.acc = (float*)(w + L.acc);
+  sb.stash = w + L.stash;
   sb.dw = (float*)(w + L.dw);
   sb.dr = (float*)(w + L.dr);
   sb.dgam = (float*)(w + L.dgam);
@@ -367,8 +380,8 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   FinalizeArgs fa{};
   fa.N = d.N;
   fa.d_v = p->d_v;
-  fa.k_w = p->k_w;
-  fa.acc = sb.acc;
+  fa.k = p->k_w;
+  fa.stash = sb.stash;
   fa.out = d_v;
   fa.dgam = sb.dgam;
   fa.d_gamma = d_gamma;

@@ -7,7 +7,8 @@
 //            of the tile's events in LDS;
 //   scan     one block per (b, h): per slot, exclusive prefix of the tile
 //            counts (in place) and, over the slots in blocks of 1024, the
-//            segment offsets.
+//            segment offsets; segments with more than LONG_EVENTS events
+//            are listed for the cooperative scan path (in any order).
 //            Every (b, h) holds exactly T*(k_w+k_r) events, so segment
 //            offsets need no scan across (b, h);
 //   scatter  one wave per (b, h, tile): walks the tile's events in order
@@ -36,6 +37,7 @@ __global__ __launch_bounds__(256) void bucket_hist_kernel(BucketArgs a) {
   const int t_lo = tile * TILE_TOKENS;
   const int t_hi = min(a.T, t_lo + TILE_TOKENS);
   for (int s = threadIdx.x; s < a.S; s += blockDim.x) hist[s] = 0;
+  if (tile == 0 && bh == 0 && threadIdx.x == 0) *a.long_count = 0;
   __syncthreads();
   const int n = (t_hi - t_lo) * K;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
@@ -75,7 +77,10 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketArgs a) {
       if (w < tid / WAVE) before += wt;
       all += wt;
     }
-    if (s < S) a.seg_offset[(int64_t)bh * S + s] = (int32_t)(base + before + incl - cnt);
+    if (s < S) {
+      a.seg_offset[(int64_t)bh * S + s] = (int32_t)(base + before + incl - cnt);
+      if (cnt > LONG_EVENTS) a.long_list[atomicAdd(a.long_count, 1)] = (int32_t)((int64_t)bh * S + s);
+    }
     carry += all;
     __syncthreads();
   }

@@ -7,6 +7,9 @@ namespace ramk {
 
 constexpr int CHUNK = 32;        // scan chunk: checkpoints at 32-aligned events
 constexpr int TILE_TOKENS = 256; // tokens per bucketing tile
+constexpr int NW = 8;            // waves per scan workgroup
+constexpr int LONG_EVENTS = 128; // segments with more events take the cooperative path
+constexpr int MAX_DV = 128;      // widest slot
 
 struct BucketArgs {
   const int32_t* idx_w;   // (N, k_w)
@@ -17,11 +20,18 @@ struct BucketArgs {
   int32_t* tile_hist;     // (B*H, ntiles, S)
   int32_t* seg_offset;    // (B*H*S + 1)
   int32_t* events;        // (E)
+  int32_t* long_list;     // segments with more than LONG_EVENTS events
+  int32_t* long_count;    // their number
 };
 
 struct ScanFwdArgs {
   int B, H, T, S, d_v, k_w, k_r;
   float eps;
+  int64_t nseg;
+  const int32_t* long_list;
+  const int32_t* long_count;
+  int use_long;           // long_list / long_count are valid
+  int long_blocks;        // workgroups that walk the long list
   const int32_t* seg_offset;
   const int32_t* events;
   const float* w_w;       // (N, k_w)
@@ -32,7 +42,7 @@ struct ScanFwdArgs {
   const float* mass0;     // (B*H*S) or null
   float* slot1;
   float* mass1;
-  float* acc;             // (N, d_v) read accumulator (zero on entry)
+  void* stash;            // (N, k_r, d_v) io: read contributions r*s
   float* ckpt_s;          // (E/CHUNK + 1, d_v)
   float* ckpt_m;          // (E/CHUNK + 1)
 };
@@ -40,6 +50,11 @@ struct ScanFwdArgs {
 struct ScanBwdArgs {
   int B, H, T, S, d_v, k_w, k_r;
   float eps;
+  int64_t nseg;
+  const int32_t* long_list;
+  const int32_t* long_count;
+  int use_long;
+  int long_blocks;
   const int32_t* seg_offset;
   const int32_t* events;
   const float* w_w;
@@ -55,7 +70,7 @@ struct ScanBwdArgs {
   const float* d_mass1;   // or null
   float* d_slot0;         // or null
   float* d_mass0;         // or null
-  float* acc;             // (N, d_v) d_v accumulator (zero on entry)
+  void* stash;            // (N, k_w, d_v) io: dv contributions eta*s_hat
   float* dw;              // (N, k_w)
   float* dr;              // (N, k_r)
   float* dgam;            // (N, k_w) per-write gamma gradient parts
@@ -63,10 +78,10 @@ struct ScanBwdArgs {
 
 struct FinalizeArgs {
   int64_t N;
-  int d_v, k_w;
-  float* acc;             // (N, d_v), cleared after reading
+  int d_v, k;
+  const void* stash;      // (N, k, d_v) io
   void* out;              // (N, d_v) io
-  const float* dgam;      // (N, k_w) or null
+  const float* dgam;      // (N, k) or null
   void* d_gamma;          // (N) io or null
 };
 

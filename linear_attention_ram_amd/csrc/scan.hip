@@ -3,19 +3,24 @@
 // d_v channels in parallel, each slot's events in time order, each read
 // accumulated back to its token).
 //
-// One wavefront owns one segment (b, h, slot): lane l holds channels
-// [l*CPL, l*CPL + CPL) of the slot's content in registers.  Events are taken
-// in chunks of up to CHUNK = 32, aligned to multiples of 32 in the global
-// event list:
-//   * lane i of the wave decodes event i of the chunk and computes its
-//     retention; the mass recurrence m <- lambda*m + w is an affine map, so
-//     the chunk's masses come from one inclusive scan of (lambda, w) pairs
-//     across lanes, then eta_i = w_i / (m_i + eps);
-//   * the v rows of the chunk's writes are loaded together, then the content
-//     chain s <- (1-eta)*s + eta*v runs event by event with the scalars read
-//     from their lanes; a read adds r*s into the token's float accumulator.
-// The state before every 32-aligned event is saved (checkpoint), so the
-// reverse pass can restart any chunk without replaying the whole segment.
+// A segment (b, h, slot) keeps its content in registers: lane l holds channels
+// [l*CPL, l*CPL + CPL).  Events are taken in chunks of up to CHUNK = 32 that
+// are aligned to multiples of 32 in the global event list; the state before
+// every aligned event inside a segment is saved as a checkpoint for the
+// reverse pass.  Inside a chunk:
+//   * lane i decodes event i and its retention; the mass recurrence
+//     m <- lambda*m + w is affine, so one inclusive scan of (lambda, w) pairs
+//     across lanes gives every event's mass, then eta_i = w_i / (m_i + eps);
+//   * the chunk's v rows are loaded together and the content chain
+//     s <- (1-eta)*s + eta*v runs event by event; a read stores its
+//     contribution r*s, in the io dtype, to its own (token, j) row of a stash.
+//     A token-major pass later sums the K rows of each token.  No atomics:
+//     the read-out scatter is plain stores.
+// Short segments (<= LONG_EVENTS events) take one wave each.  Long segments
+// (hot slots) take a workgroup of NW waves that advance NW chunks at a time:
+// each wave forms its chunk's mass map and, once its incoming mass is known,
+// its content map s -> P*s + b (computed from s = 0); the maps are combined
+// through LDS, then each wave replays its chunk from its true start state.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,12 +28,15 @@ namespace ramk {
 
 namespace {
 
-// CPL io values of one row slice, loaded with one instruction.
+// CPL io values of one row slice, loaded or stored with one instruction.
 template <typename IO, int CPL> struct Slice;
 template <> struct Slice<bf16_t, 1> {
   uint16_t r;
   __device__ __forceinline__ void load(const bf16_t* p) { r = *p; }
   __device__ __forceinline__ void get(float (&f)[1]) const { f[0] = to_f32((bf16_t)r); }
+  static __device__ __forceinline__ void store(bf16_t* p, const float (&f)[1]) {
+    *p = from_f32<bf16_t>(f[0]);
+  }
 };
 template <> struct Slice<bf16_t, 2> {
   uint32_t r;
@@ -37,16 +45,23 @@ template <> struct Slice<bf16_t, 2> {
     f[0] = __uint_as_float(r << 16);
     f[1] = __uint_as_float(r & 0xffff0000u);
   }
+  static __device__ __forceinline__ void store(bf16_t* p, const float (&f)[2]) {
+    *reinterpret_cast<uint32_t*>(p) = pack2bf(f[0], f[1]);
+  }
 };
 template <> struct Slice<float, 1> {
   float r;
   __device__ __forceinline__ void load(const float* p) { r = *p; }
   __device__ __forceinline__ void get(float (&f)[1]) const { f[0] = r; }
+  static __device__ __forceinline__ void store(float* p, const float (&f)[1]) { *p = f[0]; }
 };
 template <> struct Slice<float, 2> {
   float2 r;
   __device__ __forceinline__ void load(const float* p) { r = *reinterpret_cast<const float2*>(p); }
   __device__ __forceinline__ void get(float (&f)[2]) const { f[0] = r.x; f[1] = r.y; }
+  static __device__ __forceinline__ void store(float* p, const float (&f)[2]) {
+    *reinterpret_cast<float2*>(p) = make_float2(f[0], f[1]);
+  }
 };
 
 struct EventInfo {
@@ -72,18 +87,53 @@ __device__ __forceinline__ void affine_scan(float& A, float& B) {
   for (int o = 1; o < CHUNK; o <<= 1) {
     const float Ap = __shfl_up(A, o, WAVE);
     const float Bp = __shfl_up(B, o, WAVE);
-    if (lane >= o) {
-      B = fmaf(A, Bp, B);
-      A = A * Ap;
+    const bool take = lane >= o;
+    B = take ? fmaf(A, Bp, B) : B;
+    A = take ? A * Ap : A;
+  }
+}
+
+// Per-event scalars of one chunk: lane i < n holds event cs + i.
+struct ChunkScalars {
+  EventInfo ev;
+  float wt;   // write weight or read weight
+  float lam;  // retention (writes), 1 for reads
+  float dl;   // d lambda / d w (writes)
+};
+
+template <typename IO>
+__device__ __forceinline__ ChunkScalars chunk_scalars(const int32_t* events, const float* w_w,
+                                                      const float* w_r, const IO* gb, int k_w,
+                                                      int k_r, int b, int h, int T, int H, int cs,
+                                                      int n, bool want_dl) {
+  ChunkScalars c{{0, 1, 0}, 0.f, 1.f, 0.f};
+  if (lane_id() < n) {
+    c.ev = decode_event(events[cs + lane_id()], b, h, T, H);
+    if (c.ev.side == 0) {
+      c.wt = w_w[(int64_t)c.ev.row * k_w + c.ev.j];
+      c.lam = retention(c.wt, to_f32(gb[c.ev.row]), want_dl ? &c.dl : nullptr);
+    } else {
+      c.wt = w_r[(int64_t)c.ev.row * k_r + c.ev.j];
     }
   }
+  return c;
+}
+
+// Start of chunk k of the chunk sequence that begins at position p (p is the
+// segment start or a multiple of CHUNK), clamped to end.
+__device__ __forceinline__ int chunk_start(int p, int k, int end) {
+  if (k == 0) return min(p, end);
+  return min(end, (p / CHUNK + k) * CHUNK);
 }
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+
 template <typename IO, int CPL>
-__global__ __launch_bounds__(64) void scan_fwd_kernel(ScanFwdArgs a) {
-  const int64_t g = blockIdx.x;
+__device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
   const int lane = lane_id();
   const int64_t bh = g / a.S;
   const int b = (int)(bh / a.H), h = (int)(bh % a.H);
@@ -92,6 +142,7 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(ScanFwdArgs a) {
   const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
   const IO* vb = reinterpret_cast<const IO*>(a.v);
   const IO* gb = reinterpret_cast<const IO*>(a.gamma);
+  IO* stash = reinterpret_cast<IO*>(a.stash);
 
   float s[CPL];
 #pragma unroll
@@ -109,46 +160,41 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(ScanFwdArgs a) {
       }
       if (lane == 0) a.ckpt_m[p0 / CHUNK] = m;
     }
-    // scalars of event lane
-    EventInfo ev{0, 1, 0};
-    float wt = 0.f, lam = 1.f;
-    if (lane < n) {
-      ev = decode_event(a.events[p0 + lane], b, h, a.T, a.H);
-      if (ev.side == 0) {
-        wt = a.w_w[(int64_t)ev.row * a.k_w + ev.j];
-        lam = retention(wt, to_f32(gb[ev.row]), nullptr);
-      } else {
-        wt = a.w_r[(int64_t)ev.row * a.k_r + ev.j];
-      }
-    }
-    float A = (ev.side == 0) ? lam : 1.f;
-    float Bm = (ev.side == 0) ? wt : 0.f;
+    const ChunkScalars cs = chunk_scalars<IO>(a.events, a.w_w, a.w_r, gb, a.k_w, a.k_r, b, h,
+                                              a.T, a.H, p0, n, false);
+    float A = (cs.ev.side == 0) ? cs.lam : 1.f;
+    float Bm = (cs.ev.side == 0) ? cs.wt : 0.f;
     affine_scan(A, Bm);
     const float mi = fmaf(A, m, Bm);
-    const float eta = (ev.side == 0 && wt > 0.f) ? wt / (mi + a.eps) : 0.f;
+    const float eta = (cs.ev.side == 0 && cs.wt > 0.f) ? cs.wt / (mi + a.eps) : 0.f;
     m = readlane_f(mi, n - 1);
 
     Slice<IO, CPL> raw[CHUNK];
 #pragma unroll
     for (int i = 0; i < CHUNK; ++i) {
       raw[i].r = {};
-      if (i < n && readlane_i(ev.side, i) == 0 && active)
-        raw[i].load(vb + (int64_t)readlane_i(ev.row, i) * a.d_v + c0);
+      if (i < n) {
+        const int si = readlane_i(cs.ev.side, i);
+        const int64_t ri = readlane_i(cs.ev.row, i);
+        if (si == 0 && active) raw[i].load(vb + ri * a.d_v + c0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < CHUNK; ++i) {
       if (i < n) {
-        if (readlane_i(ev.side, i) == 0) {
+        if (readlane_i(cs.ev.side, i) == 0) {
           const float e = readlane_f(eta, i);
           float vv[CPL];
           raw[i].get(vv);
 #pragma unroll
           for (int c = 0; c < CPL; ++c) s[c] = fmaf(1.f - e, s[c], e * vv[c]);
-        } else if (active) {
-          const float r = readlane_f(wt, i);
-          float* dst = a.acc + (int64_t)readlane_i(ev.row, i) * a.d_v + c0;
+        } else {
+          const float r = readlane_f(cs.wt, i);
+          const int64_t slot_row = (int64_t)readlane_i(cs.ev.row, i) * a.k_r + readlane_i(cs.ev.j, i);
+          float contrib[CPL];
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(dst + c, r * s[c]);
+          for (int c = 0; c < CPL; ++c) contrib[c] = r * s[c];
+          if (active) Slice<IO, CPL>::store(stash + slot_row * a.d_v + c0, contrib);
         }
       }
     }
@@ -161,10 +207,159 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(ScanFwdArgs a) {
   if (lane == 0) a.mass1[g] = m;
 }
 
-// Reverse pass, one wave per segment, chunks in reverse order.  Each chunk
-// restarts from its checkpoint (or the initial state), replays its events
-// forward to recover the content before every write and to form the read
-// gradients dr = <dO_t, s>, then walks the events backwards:
+template <typename IO, int CPL>
+__device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
+  __shared__ float mapA[NW], mapB[NW], mapP[NW];
+  __shared__ float mapb[NW][MAX_DV];
+  const int lane = lane_id();
+  const int w = threadIdx.x / WAVE;
+  const int64_t bh = g / a.S;
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const int c0 = lane * CPL;
+  const bool active = c0 < a.d_v;
+  const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
+  const IO* vb = reinterpret_cast<const IO*>(a.v);
+  const IO* gb = reinterpret_cast<const IO*>(a.gamma);
+  IO* stash = reinterpret_cast<IO*>(a.stash);
+
+  float s_carry[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+    s_carry[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
+  float m_carry = a.mass0 ? a.mass0[g] : 0.f;
+
+  for (int p = beg; p < end;) {
+    const int cs = chunk_start(p, w, end);
+    const int n = chunk_start(p, w + 1, end) - cs;
+    const ChunkScalars sc = chunk_scalars<IO>(a.events, a.w_w, a.w_r, gb, a.k_w, a.k_r, b, h,
+                                              a.T, a.H, cs, n, false);
+    float A = (sc.ev.side == 0) ? sc.lam : 1.f;
+    float Bm = (sc.ev.side == 0) ? sc.wt : 0.f;
+    affine_scan(A, Bm);
+    // cross-lane reads stay outside lane-dependent branches
+    const float A_tot = readlane_f(A, max(n, 1) - 1);
+    const float B_tot = readlane_f(Bm, max(n, 1) - 1);
+    if (lane == 0) {
+      mapA[w] = n > 0 ? A_tot : 1.f;
+      mapB[w] = n > 0 ? B_tot : 0.f;
+    }
+    // content loads do not depend on the mass: issue them before the barrier
+    Slice<IO, CPL> raw[CHUNK];
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i) {
+      raw[i].r = {};
+      if (i < n) {
+        const int si = readlane_i(sc.ev.side, i);
+        const int64_t ri = readlane_i(sc.ev.row, i);
+        if (si == 0 && active) raw[i].load(vb + ri * a.d_v + c0);
+      }
+    }
+    __syncthreads();
+    float m_in = m_carry, m_next = m_carry;
+    for (int k = 0; k < NW; ++k) {
+      if (k == w) m_in = m_next;
+      m_next = fmaf(mapA[k], m_next, mapB[k]);
+    }
+    const float mi = fmaf(A, m_in, Bm);
+    const float eta = (sc.ev.side == 0 && sc.wt > 0.f) ? sc.wt / (mi + a.eps) : 0.f;
+    // content map of the chunk from a zero start
+    float sz[CPL], P = 1.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) sz[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i) {
+      if (i < n && readlane_i(sc.ev.side, i) == 0) {
+        const float e = readlane_f(eta, i);
+        float vv[CPL];
+        raw[i].get(vv);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sz[c] = fmaf(1.f - e, sz[c], e * vv[c]);
+        P *= 1.f - e;
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) mapb[w][c0 + c] = sz[c];
+    }
+    if (lane == 0) mapP[w] = P;
+    __syncthreads();
+    float s[CPL], s_next[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) s_next[c] = s_carry[c];
+    for (int k = 0; k < NW; ++k) {
+      const float Pk = mapP[k];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if (k == w) s[c] = s_next[c];
+        s_next[c] = fmaf(Pk, s_next[c], active ? mapb[k][c0 + c] : 0.f);
+      }
+    }
+    if (n > 0 && cs != beg) {
+      float* ck = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) ck[c0 + c] = s[c];
+      }
+      if (lane == 0) a.ckpt_m[cs / CHUNK] = m_in;
+    }
+    // replay from the true start state; reads store their contributions
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i) {
+      if (i < n) {
+        if (readlane_i(sc.ev.side, i) == 0) {
+          const float e = readlane_f(eta, i);
+          float vv[CPL];
+          raw[i].get(vv);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) s[c] = fmaf(1.f - e, s[c], e * vv[c]);
+        } else {
+          const float r = readlane_f(sc.wt, i);
+          const int64_t slot_row = (int64_t)readlane_i(sc.ev.row, i) * a.k_r + readlane_i(sc.ev.j, i);
+          float contrib[CPL];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) contrib[c] = r * s[c];
+          if (active) Slice<IO, CPL>::store(stash + slot_row * a.d_v + c0, contrib);
+        }
+      }
+    }
+    m_carry = m_next;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) s_carry[c] = s_next[c];
+    p = chunk_start(p, NW, end);
+    __syncthreads();
+  }
+  if (w == 0) {
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) a.slot1[g * a.d_v + c0 + c] = s_carry[c];
+    }
+    if (lane == 0) a.mass1[g] = m_carry;
+  }
+}
+
+// Blocks [0, long_blocks) walk the list of long segments; every other block
+// takes NW consecutive segments, one per wave, and skips the long ones.
+template <typename IO, int CPL>
+__global__ __launch_bounds__(NW * WAVE) void scan_fwd_kernel(ScanFwdArgs a) {
+  if ((int)blockIdx.x < a.long_blocks) {
+    const int count = a.use_long ? *a.long_count : 0;
+    for (int i = blockIdx.x; i < count; i += a.long_blocks)
+      scan_fwd_long<IO, CPL>(a, a.long_list[i]);
+    return;
+  }
+  const int64_t g = ((int64_t)blockIdx.x - a.long_blocks) * NW + threadIdx.x / WAVE;
+  if (g >= a.nseg) return;
+  if (a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS) return;
+  scan_fwd_short<IO, CPL>(a, g);
+}
+
+// ---------------------------------------------------------------------------
+// reverse
+// ---------------------------------------------------------------------------
+//
+// Per chunk: restart from its checkpoint (or the initial state), replay the
+// events forward to recover the content before every write and to form the
+// read gradients dr = <dO_t, s>, then walk the events backwards:
 //   read  (weight r):  s_hat += r * dO_t
 //   write (w, gamma):  dv_t += eta * s_hat;  deta = <s_hat, v_t - s_old>;
 //                      s_hat <- (1 - eta) s_hat;
@@ -172,18 +367,178 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(ScanFwdArgs a) {
 //                      dw = deta / (m' + eps) + M + M * m_old * dlambda/dw;
 //                      dgamma part = M * m_old * (-lambda (1 - lambda));
 //                      m_hat <- lambda * M.
+// dv contributions eta * s_hat go, in the io dtype, to the write's (token, j)
+// stash row; a token-major pass sums them.
+
 template <typename IO, int CPL>
-__global__ __launch_bounds__(64) void scan_bwd_kernel(ScanBwdArgs a) {
-  const int64_t g = blockIdx.x;
+struct BwdChunk {
+  ChunkScalars sc;
+  float mi, mo, eta;       // mass after / before the event, step size
+  Slice<IO, CPL> raw[CHUNK];
+  float so[CHUNK][CPL];    // content before each write
+};
+
+// Loads a chunk, replays it forward from (s, m) and writes its dr values.
+template <typename IO, int CPL>
+__device__ __forceinline__ void bwd_replay(const ScanBwdArgs& a, BwdChunk<IO, CPL>& ck, int b,
+                                           int h, int cs, int n, float (&s)[CPL], float m,
+                                           bool active, int c0) {
+  const IO* vb = reinterpret_cast<const IO*>(a.v);
+  const IO* ob = reinterpret_cast<const IO*>(a.d_o);
+  const IO* gb = reinterpret_cast<const IO*>(a.gamma);
+  ck.sc = chunk_scalars<IO>(a.events, a.w_w, a.w_r, gb, a.k_w, a.k_r, b, h, a.T, a.H, cs, n, true);
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < CHUNK; ++i) {
+    ck.raw[i].r = {};
+    if (i < n) {
+      const IO* src = (readlane_i(ck.sc.ev.side, i) == 0) ? vb : ob;
+      const int64_t ri = readlane_i(ck.sc.ev.row, i);
+      if (active) ck.raw[i].load(src + ri * a.d_v + c0);
+    }
+  }
+  float A = (ck.sc.ev.side == 0) ? ck.sc.lam : 1.f;
+  float Bm = (ck.sc.ev.side == 0) ? ck.sc.wt : 0.f;
+  affine_scan(A, Bm);
+  ck.mi = fmaf(A, m, Bm);
+  ck.mo = __shfl_up(ck.mi, 1, WAVE);
+  if (lane == 0) ck.mo = m;
+  ck.eta = (ck.sc.ev.side == 0 && ck.sc.wt > 0.f) ? ck.sc.wt / (ck.mi + a.eps) : 0.f;
+#pragma unroll
+  for (int i = 0; i < CHUNK; ++i) {
+    if (i < n) {
+      float x[CPL];
+      ck.raw[i].get(x);
+      if (readlane_i(ck.sc.ev.side, i) == 0) {
+        const float e = readlane_f(ck.eta, i);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          ck.so[i][c] = s[c];
+          s[c] = fmaf(1.f - e, s[c], e * x[c]);
+        }
+      } else {
+        float d = 0.f;
+        if (active) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) d = fmaf(x[c], s[c], d);
+        }
+        d = wave_sum(d);
+        const int64_t dri = (int64_t)readlane_i(ck.sc.ev.row, i) * a.k_r + readlane_i(ck.sc.ev.j, i);
+        if (lane == 0) a.dr[dri] = d;
+      }
+    }
+  }
+}
+
+// Reverse walk of a loaded chunk from the adjoints (sh, mh) after its last
+// event; leaves the adjoints before its first event in (sh, mh).
+template <typename IO, int CPL>
+__device__ __forceinline__ void bwd_walk(const ScanBwdArgs& a, const BwdChunk<IO, CPL>& ck, int n,
+                                         float (&sh)[CPL], float& mh, bool active, int c0) {
+  IO* stash = reinterpret_cast<IO*>(a.stash);
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = CHUNK - 1; i >= 0; --i) {
+    if (i < n) {
+      float x[CPL];
+      ck.raw[i].get(x);
+      const int ri = readlane_i(ck.sc.ev.row, i);
+      if (readlane_i(ck.sc.ev.side, i) == 1) {
+        const float r = readlane_f(ck.sc.wt, i);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sh[c] = fmaf(r, x[c], sh[c]);
+      } else {
+        const float e = readlane_f(ck.eta, i);
+        const int64_t srow = (int64_t)ri * a.k_w + readlane_i(ck.sc.ev.j, i);
+        float d = 0.f;
+        if (active) {
+          float contrib[CPL];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            contrib[c] = e * sh[c];
+            d = fmaf(sh[c], x[c] - ck.so[i][c], d);
+          }
+          Slice<IO, CPL>::store(stash + srow * a.d_v + c0, contrib);
+        }
+        d = wave_sum(d);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sh[c] = (1.f - e) * sh[c];
+        const float w = readlane_f(ck.sc.wt, i);
+        const float mnew = readlane_f(ck.mi, i);
+        const float mold = readlane_f(ck.mo, i);
+        const float li = readlane_f(ck.sc.lam, i);
+        const float dli = readlane_f(ck.sc.dl, i);
+        const float den = mnew + a.eps;
+        const float M = (w > 0.f) ? mh - d * w / (den * den) : mh;
+        const float dwi = ((w > 0.f) ? d / den : 0.f) + M + M * mold * dli;
+        const float dgi = M * mold * (-li * (1.f - li));
+        mh = li * M;
+        if (lane == 0) {
+          a.dw[srow] = dwi;
+          a.dgam[srow] = dgi;
+        }
+      }
+    }
+  }
+}
+
+// The chunk's adjoint map, from a symbolic zero at its end:
+//   s_hat_in = Q * s_hat_out + q
+//   m_hat_in = L * m_hat_out + <s_hat_out, U> + K
+template <typename IO, int CPL>
+__device__ __forceinline__ void bwd_map(const ScanBwdArgs& a, const BwdChunk<IO, CPL>& ck, int n,
+                                        float& Q, float (&q)[CPL], float& L, float (&U)[CPL],
+                                        float& K, bool active) {
+  Q = 1.f;
+  L = 1.f;
+  K = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) { q[c] = 0.f; U[c] = 0.f; }
+#pragma unroll
+  for (int i = CHUNK - 1; i >= 0; --i) {
+    if (i < n) {
+      float x[CPL];
+      ck.raw[i].get(x);
+      if (readlane_i(ck.sc.ev.side, i) == 1) {
+        const float r = readlane_f(ck.sc.wt, i);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) q[c] = fmaf(r, x[c], q[c]);
+      } else {
+        const float e = readlane_f(ck.eta, i);
+        const float w = readlane_f(ck.sc.wt, i);
+        const float mnew = readlane_f(ck.mi, i);
+        const float li = readlane_f(ck.sc.lam, i);
+        const float den = mnew + a.eps;
+        const float gq = (w > 0.f) ? w / (den * den) : 0.f;
+        float u[CPL];
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          u[c] = active ? x[c] - ck.so[i][c] : 0.f;
+          d = fmaf(q[c], u[c], d);
+        }
+        d = wave_sum(d);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          U[c] = li * (U[c] - gq * Q * u[c]);
+          q[c] = (1.f - e) * q[c];
+        }
+        K = li * (K - gq * d);
+        L = li * L;
+        Q = (1.f - e) * Q;
+      }
+    }
+  }
+}
+
+template <typename IO, int CPL>
+__device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
   const int lane = lane_id();
   const int64_t bh = g / a.S;
   const int b = (int)(bh / a.H), h = (int)(bh % a.H);
   const int c0 = lane * CPL;
   const bool active = c0 < a.d_v;
   const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
-  const IO* vb = reinterpret_cast<const IO*>(a.v);
-  const IO* ob = reinterpret_cast<const IO*>(a.d_o);
-  const IO* gb = reinterpret_cast<const IO*>(a.gamma);
 
   float sh[CPL];
 #pragma unroll
@@ -191,6 +546,7 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(ScanBwdArgs a) {
   float mh = a.d_mass1 ? a.d_mass1[g] : 0.f;
 
   if (beg < end) {
+    BwdChunk<IO, CPL> ck;
     int cs = max(beg, ((end - 1) / CHUNK) * CHUNK);
     while (true) {
       const int ce = min(end, (cs / CHUNK + 1) * CHUNK);
@@ -202,110 +558,13 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(ScanBwdArgs a) {
         for (int c = 0; c < CPL; ++c) s[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
         m = a.mass0 ? a.mass0[g] : 0.f;
       } else {
-        const float* ck = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
+        const float* cp = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) s[c] = active ? ck[c0 + c] : 0.f;
+        for (int c = 0; c < CPL; ++c) s[c] = active ? cp[c0 + c] : 0.f;
         m = a.ckpt_m[cs / CHUNK];
       }
-      EventInfo ev{0, 1, 0};
-      float wt = 0.f, lam = 1.f, dl = 0.f;
-      if (lane < n) {
-        ev = decode_event(a.events[cs + lane], b, h, a.T, a.H);
-        if (ev.side == 0) {
-          wt = a.w_w[(int64_t)ev.row * a.k_w + ev.j];
-          lam = retention(wt, to_f32(gb[ev.row]), &dl);
-        } else {
-          wt = a.w_r[(int64_t)ev.row * a.k_r + ev.j];
-        }
-      }
-      float A = (ev.side == 0) ? lam : 1.f;
-      float Bm = (ev.side == 0) ? wt : 0.f;
-      affine_scan(A, Bm);
-      const float mi = fmaf(A, m, Bm);                     // mass after event
-      float mo = __shfl_up(mi, 1, WAVE);                   // mass before event
-      if (lane == 0) mo = m;
-      const float eta = (ev.side == 0 && wt > 0.f) ? wt / (mi + a.eps) : 0.f;
-
-      Slice<IO, CPL> raw[CHUNK];
-#pragma unroll
-      for (int i = 0; i < CHUNK; ++i) {
-        raw[i].r = {};
-        if (i < n && active) {
-          const IO* src = (readlane_i(ev.side, i) == 0) ? vb : ob;
-          raw[i].load(src + (int64_t)readlane_i(ev.row, i) * a.d_v + c0);
-        }
-      }
-      // forward replay
-      float so[CHUNK][CPL];
-#pragma unroll
-      for (int i = 0; i < CHUNK; ++i) {
-        if (i < n) {
-          float x[CPL];
-          raw[i].get(x);
-          if (readlane_i(ev.side, i) == 0) {
-            const float e = readlane_f(eta, i);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-              so[i][c] = s[c];
-              s[c] = fmaf(1.f - e, s[c], e * x[c]);
-            }
-          } else {
-            float d = 0.f;
-            if (active) {
-#pragma unroll
-              for (int c = 0; c < CPL; ++c) d = fmaf(x[c], s[c], d);
-            }
-            d = wave_sum(d);
-            if (lane == 0) {
-              const int ri = readlane_i(ev.row, i);
-              a.dr[(int64_t)ri * a.k_r + readlane_i(ev.j, i)] = d;
-            }
-          }
-        }
-      }
-      // reverse walk
-#pragma unroll
-      for (int i = CHUNK - 1; i >= 0; --i) {
-        if (i < n) {
-          float x[CPL];
-          raw[i].get(x);
-          const int ri = readlane_i(ev.row, i);
-          if (readlane_i(ev.side, i) == 1) {
-            const float r = readlane_f(wt, i);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) sh[c] = fmaf(r, x[c], sh[c]);
-          } else {
-            const float e = readlane_f(eta, i);
-            float d = 0.f;
-            if (active) {
-              float* dst = a.acc + (int64_t)ri * a.d_v + c0;
-#pragma unroll
-              for (int c = 0; c < CPL; ++c) {
-                unsafeAtomicAdd(dst + c, e * sh[c]);
-                d = fmaf(sh[c], x[c] - so[i][c], d);
-              }
-            }
-            d = wave_sum(d);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) sh[c] = (1.f - e) * sh[c];
-            const float w = readlane_f(wt, i);
-            const float mnew = readlane_f(mi, i);
-            const float mold = readlane_f(mo, i);
-            const float li = readlane_f(lam, i);
-            const float dli = readlane_f(dl, i);
-            const float den = mnew + a.eps;
-            const float M = (w > 0.f) ? mh - d * w / (den * den) : mh;
-            const float dwi = ((w > 0.f) ? d / den : 0.f) + M + M * mold * dli;
-            const float dgi = M * mold * (-li * (1.f - li));
-            mh = li * M;
-            if (lane == 0) {
-              const int64_t o = (int64_t)ri * a.k_w + readlane_i(ev.j, i);
-              a.dw[o] = dwi;
-              a.dgam[o] = dgi;
-            }
-          }
-        }
-      }
+      bwd_replay<IO, CPL>(a, ck, b, h, cs, n, s, m, active, c0);
+      bwd_walk<IO, CPL>(a, ck, n, sh, mh, active, c0);
       if (cs == beg) break;
       cs = max(beg, cs - CHUNK);
     }
@@ -317,31 +576,146 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(ScanBwdArgs a) {
   if (a.d_mass0 && lane == 0) a.d_mass0[g] = mh;
 }
 
-// acc -> io output (cleared afterwards, so the accumulator is zero between
-// calls); optionally d_gamma[row] = sum_j dgam[row, j].
-template <typename IO>
-__global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
-  IO* out = reinterpret_cast<IO*>(a.out);
-  const int64_t total = a.N * a.d_v;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    out[i] = from_f32<IO>(a.acc[i]);
-    a.acc[i] = 0.f;
-  }
-  if (a.dgam) {
-    IO* dg = reinterpret_cast<IO*>(a.d_gamma);
-    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < a.N; r += stride) {
-      float sum = 0.f;
-      for (int j = 0; j < a.k_w; ++j) sum += a.dgam[r * a.k_w + j];
-      dg[r] = from_f32<IO>(sum);
+template <typename IO, int CPL>
+__device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
+  __shared__ float mQ[NW], mL[NW], mK[NW];
+  __shared__ float mq[NW][MAX_DV], mU[NW][MAX_DV];
+  __shared__ float carry_s[MAX_DV];
+  __shared__ float carry_m;
+  const int lane = lane_id();
+  const int w = threadIdx.x / WAVE;
+  const int64_t bh = g / a.S;
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const int c0 = lane * CPL;
+  const bool active = c0 < a.d_v;
+  const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
+  // chunk k starts at beg (k = 0) or at (beg/CHUNK + k)*CHUNK
+  const int nchunks = (end - 1) / CHUNK - beg / CHUNK + 1;
+
+  float sh_carry[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+    sh_carry[c] = (active && a.d_slot1) ? a.d_slot1[g * a.d_v + c0 + c] : 0.f;
+  float mh_carry = a.d_mass1 ? a.d_mass1[g] : 0.f;
+
+  BwdChunk<IO, CPL> ck;
+  for (int u0 = ((nchunks - 1) / NW) * NW; u0 >= 0; u0 -= NW) {
+    const int k = u0 + w;
+    int cs = end, n = 0;
+    if (k < nchunks) {
+      cs = chunk_start(beg, k, end);
+      n = chunk_start(beg, k + 1, end) - cs;
     }
+    float s[CPL];
+    float m = 0.f;
+    if (n > 0) {
+      if (cs == beg) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) s[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
+        m = a.mass0 ? a.mass0[g] : 0.f;
+      } else {
+        const float* cp = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) s[c] = active ? cp[c0 + c] : 0.f;
+        m = a.ckpt_m[cs / CHUNK];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) s[c] = 0.f;
+    }
+    bwd_replay<IO, CPL>(a, ck, b, h, cs, n, s, m, active, c0);
+    float Q, q[CPL], L, U[CPL], K;
+    bwd_map<IO, CPL>(a, ck, n, Q, q, L, U, K, active);
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) { mq[w][c0 + c] = q[c]; mU[w][c0 + c] = U[c]; }
+    }
+    if (lane == 0) { mQ[w] = Q; mL[w] = L; mK[w] = K; }
+    __syncthreads();
+    // adjoints after this wave's chunk: fold the maps of the later chunks
+    float sh[CPL];
+    float mh = mh_carry;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) sh[c] = sh_carry[c];
+    for (int kk = NW - 1; kk > w; --kk) {
+      float d = 0.f;
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) d = fmaf(sh[c], mU[kk][c0 + c], d);
+      }
+      d = wave_sum(d);
+      mh = fmaf(mL[kk], mh, d + mK[kk]);
+      const float Qk = mQ[kk];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) sh[c] = fmaf(Qk, sh[c], active ? mq[kk][c0 + c] : 0.f);
+    }
+    bwd_walk<IO, CPL>(a, ck, n, sh, mh, active, c0);
+    if (w == 0) {
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) carry_s[c0 + c] = sh[c];
+      }
+      if (lane == 0) carry_m = mh;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) sh_carry[c] = active ? carry_s[c0 + c] : 0.f;
+    mh_carry = carry_m;
+    __syncthreads();
+  }
+  if (w == 0) {
+    if (a.d_slot0 && active) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) a.d_slot0[g * a.d_v + c0 + c] = sh_carry[c];
+    }
+    if (a.d_mass0 && lane == 0) a.d_mass0[g] = mh_carry;
   }
 }
 
+template <typename IO, int CPL>
+__global__ __launch_bounds__(NW * WAVE) void scan_bwd_kernel(ScanBwdArgs a) {
+  if ((int)blockIdx.x < a.long_blocks) {
+    const int count = a.use_long ? *a.long_count : 0;
+    for (int i = blockIdx.x; i < count; i += a.long_blocks)
+      scan_bwd_long<IO, CPL>(a, a.long_list[i]);
+    return;
+  }
+  const int64_t g = ((int64_t)blockIdx.x - a.long_blocks) * NW + threadIdx.x / WAVE;
+  if (g >= a.nseg) return;
+  if (a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS) return;
+  scan_bwd_short<IO, CPL>(a, g);
+}
+
+// ---------------------------------------------------------------------------
+// token-major sums of the stash rows
+// ---------------------------------------------------------------------------
+
+// out[row] = sum_j stash[row, j] (float accumulation, j ascending), one wave
+// per row; optionally d_gamma[row] = sum_j dgam[row, j].
+template <typename IO>
+__global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
+  const int lane = lane_id();
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / WAVE;
+  if (row >= a.N) return;
+  const IO* st = reinterpret_cast<const IO*>(a.stash) + row * a.k * a.d_v;
+  IO* out = reinterpret_cast<IO*>(a.out) + row * a.d_v;
+  for (int c = lane; c < a.d_v; c += WAVE) {
+    float acc = 0.f;
+    for (int j = 0; j < a.k; ++j) acc += to_f32(st[j * a.d_v + c]);
+    out[c] = from_f32<IO>(acc);
+  }
+  if (a.dgam && lane == 0) {
+    float sum = 0.f;
+    for (int j = 0; j < a.k; ++j) sum += a.dgam[row * a.k + j];
+    reinterpret_cast<IO*>(a.d_gamma)[row] = from_f32<IO>(sum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st) {
-  const int64_t nseg = (int64_t)a.B * a.H * a.S;
-  if (nseg == 0) return hipSuccess;
-  const dim3 grid((unsigned)nseg), block(64);
+  if (a.nseg == 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.long_blocks + (a.nseg + NW - 1) / NW)), block(NW * WAVE);
   if (bf16) {
     if (a.d_v > 64) hipLaunchKernelGGL((scan_fwd_kernel<bf16_t, 2>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((scan_fwd_kernel<bf16_t, 1>), grid, block, 0, st, a);
@@ -353,9 +727,8 @@ hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st) {
 }
 
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st) {
-  const int64_t nseg = (int64_t)a.B * a.H * a.S;
-  if (nseg == 0) return hipSuccess;
-  const dim3 grid((unsigned)nseg), block(64);
+  if (a.nseg == 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.long_blocks + (a.nseg + NW - 1) / NW)), block(NW * WAVE);
   if (bf16) {
     if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_kernel<bf16_t, 2>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((scan_bwd_kernel<bf16_t, 1>), grid, block, 0, st, a);
@@ -367,12 +740,10 @@ hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st) {
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st) {
-  const int64_t total = a.N * a.d_v;
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  if (bf16) hipLaunchKernelGGL(finalize_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(finalize_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (a.N == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
+  if (bf16) hipLaunchKernelGGL(finalize_kernel<bf16_t>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(finalize_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

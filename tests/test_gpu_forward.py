@@ -141,6 +141,8 @@ EDGE = [
     (3, 1, 300, 32, 2, 5, 66, "f32", (False, True), 1e-3),
     (1, 2, 257, 128, 4, 4, 128, "bf16", (False, False), 1e-6),
     (2, 2, 600, 8, 8, 8, 16, "bf16", (True, True), 0.0),   # 8 slots, every token writes all
+    (1, 2, 2000, 16, 4, 4, 16, "f32", (False, False), 1e-6),  # ~1000-event segments
+    (1, 1, 3000, 8, 3, 2, 128, "f32", (False, False), 1e-6),  # long segments, wide slots
 ]
 
 
