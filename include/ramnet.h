@@ -99,8 +99,8 @@ typedef struct ram_ws_layout {
   size_t seg_offset;  /* int32 (B*H*S + 1): first event of segment g = (b*H + h)*S + a          */
   size_t events;      /* int32 (E): event codes (t << 7) | (side << 6) | j, segment-major,
                          time order inside a segment, a token's write before its read          */
-  size_t ckpt_s;      /* float (E/32 + 1, d_v): slot content at every 32-aligned event        */
-  size_t ckpt_m;      /* float (E/32 + 1): slot mass at the same points                      */
+  size_t ckpt_s;      /* float (E/16 + 1, d_v): slot content at every 16-aligned event        */
+  size_t ckpt_m;      /* float (E/16 + 1): slot mass at the same points                      */
   size_t stash;       /* io (N, max(k_w,k_r), d_v): per-(token, j) read / dv contributions      */
   size_t tile_hist;   /* int32: bucketing scratch                                              */
   size_t long_list;   /* int32: segments that take the cooperative scan path                   */

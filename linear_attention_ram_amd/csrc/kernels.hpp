@@ -5,9 +5,10 @@
 
 namespace ramk {
 
-constexpr int CHUNK = 32;        // scan chunk: checkpoints at 32-aligned events
+constexpr int CHUNK = 16;        // scan chunk: checkpoints at 16-aligned events
 constexpr int TILE_TOKENS = 256; // tokens per bucketing tile
-constexpr int NW = 8;            // waves per scan workgroup
+constexpr int NW = 16;           // waves per forward scan workgroup
+constexpr int NWB = 8;           // waves per reverse long-segment workgroup
 constexpr int LONG_EVENTS = 128; // segments with more events take the cooperative path
 constexpr int MAX_DV = 128;      // widest slot
 

@@ -4,8 +4,8 @@
 // accumulated back to its token).
 //
 // A segment (b, h, slot) keeps its content in registers: lane l holds channels
-// [l*CPL, l*CPL + CPL).  Events are taken in chunks of up to CHUNK = 32 that
-// are aligned to multiples of 32 in the global event list; the state before
+// [l*CPL, l*CPL + CPL).  Events are taken in chunks of up to CHUNK = 16 that
+// are aligned to multiples of 16 in the global event list; the state before
 // every aligned event inside a segment is saved as a checkpoint for the
 // reverse pass.  Inside a chunk:
 //   * lane i decodes event i and its retention; the mass recurrence
@@ -358,17 +358,20 @@ __global__ __launch_bounds__(NW * WAVE) void scan_fwd_kernel(ScanFwdArgs a) {
 // ---------------------------------------------------------------------------
 //
 // Per chunk: restart from its checkpoint (or the initial state), replay the
-// events forward to recover the content before every write and to form the
-// read gradients dr = <dO_t, s>, then walk the events backwards:
-//   read  (weight r):  s_hat += r * dO_t
-//   write (w, gamma):  dv_t += eta * s_hat;  deta = <s_hat, v_t - s_old>;
-//                      s_hat <- (1 - eta) s_hat;
-//                      M = m_hat - deta * w / (m' + eps)^2;
-//                      dw = deta / (m' + eps) + M + M * m_old * dlambda/dw;
-//                      dgamma part = M * m_old * (-lambda (1 - lambda));
-//                      m_hat <- lambda * M.
-// dv contributions eta * s_hat go, in the io dtype, to the write's (token, j)
-// stash row; a token-major pass sums them.
+// events forward to recover the content before every write, then walk the
+// events backwards with the content adjoint s_hat:
+//   read  (weight r):  s_hat += r * dO_t;               dr   = <dO_t, s>
+//   write (w, gamma):  dv_t += eta * s_hat (io stash);  deta = <s_hat, v_t - s_old>;
+//                      s_hat <- (1 - eta) s_hat
+// The inner products are accumulated lane-locally for all events of the
+// chunk and summed in one batched transpose-reduction.  The mass adjoint
+// then follows m_hat_before = lambda * (m_hat_after - g * deta), with
+// g = w / (m' + eps)^2, which is affine in m_hat: an inclusive suffix scan
+// across lanes gives it for every event at once, and each lane forms
+//   M = m_hat_after - g * deta
+//   dw = deta / (m' + eps) + M + M * m_old * dlambda/dw
+//   dgamma part = M * m_old * (-lambda (1 - lambda))
+// for its own event and stores it.
 
 template <typename IO, int CPL>
 struct BwdChunk {
@@ -378,16 +381,62 @@ struct BwdChunk {
   float so[CHUNK][CPL];    // content before each write
 };
 
-// Loads a chunk, replays it forward from (s, m) and writes its dr values.
+// Sums x[i] over the 64 lanes for every i < CHUNK; lane i < CHUNK receives
+// the total of index i.  Each halving step exchanges the half of the values
+// a lane does not keep, so 16 sums cost 17 shuffles.
+__device__ __forceinline__ float batched_sum(const float (&x)[CHUNK]) {
+  static_assert(CHUNK == 16, "batched_sum is written for 16 values");
+  const int lane = lane_id();
+  float y8[8], y4[4], y2[2];
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float send = b5 ? x[i] : x[i + 8];
+    y8[i] = (b5 ? x[i + 8] : x[i]) + __shfl_xor(send, 32, WAVE);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float send = b4 ? y8[i] : y8[i + 4];
+    y4[i] = (b4 ? y8[i + 4] : y8[i]) + __shfl_xor(send, 16, WAVE);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float send = b3 ? y4[i] : y4[i + 2];
+    y2[i] = (b3 ? y4[i + 2] : y4[i]) + __shfl_xor(send, 8, WAVE);
+  }
+  float y = (b2 ? y2[1] : y2[0]) + __shfl_xor(b2 ? y2[0] : y2[1], 4, WAVE);
+  y += __shfl_xor(y, 2, WAVE);
+  y += __shfl_xor(y, 1, WAVE);
+  // lane l now holds the total of index l >> 2
+  return __shfl(y, (lane & (CHUNK - 1)) * 4, WAVE);
+}
+
+// Inclusive suffix scan across lanes of affine maps x -> A*x + B, later lanes
+// applied first (lane i ends with F_i o F_{i+1} o ...).  Lanes past the chunk
+// carry the identity.
+__device__ __forceinline__ void affine_suffix_scan(float& A, float& B) {
+#pragma unroll
+  for (int o = 1; o < CHUNK; o <<= 1) {
+    const float An = __shfl_down(A, o, WAVE);
+    const float Bn = __shfl_down(B, o, WAVE);
+    const bool take = lane_id() + o < WAVE;
+    B = take ? fmaf(A, Bn, B) : B;
+    A = take ? A * An : A;
+  }
+}
+
+// Loads a chunk and replays it forward from (s, m): fills the chunk's
+// scalars, rows and pre-write contents, and part[i] = <dO_i, s> (lane-local
+// partial) for the reads.  s ends as the content after the chunk.
 template <typename IO, int CPL>
-__device__ __forceinline__ void bwd_replay(const ScanBwdArgs& a, BwdChunk<IO, CPL>& ck, int b,
-                                           int h, int cs, int n, float (&s)[CPL], float m,
-                                           bool active, int c0) {
+__device__ __forceinline__ void bwd_load_replay(const ScanBwdArgs& a, BwdChunk<IO, CPL>& ck,
+                                                int b, int h, int cs, int n, float (&s)[CPL],
+                                                float m, bool active, int c0,
+                                                float (&part)[CHUNK]) {
   const IO* vb = reinterpret_cast<const IO*>(a.v);
   const IO* ob = reinterpret_cast<const IO*>(a.d_o);
   const IO* gb = reinterpret_cast<const IO*>(a.gamma);
   ck.sc = chunk_scalars<IO>(a.events, a.w_w, a.w_r, gb, a.k_w, a.k_r, b, h, a.T, a.H, cs, n, true);
-  const int lane = lane_id();
 #pragma unroll
   for (int i = 0; i < CHUNK; ++i) {
     ck.raw[i].r = {};
@@ -401,11 +450,12 @@ __device__ __forceinline__ void bwd_replay(const ScanBwdArgs& a, BwdChunk<IO, CP
   float Bm = (ck.sc.ev.side == 0) ? ck.sc.wt : 0.f;
   affine_scan(A, Bm);
   ck.mi = fmaf(A, m, Bm);
-  ck.mo = __shfl_up(ck.mi, 1, WAVE);
-  if (lane == 0) ck.mo = m;
+  const float up = __shfl_up(ck.mi, 1, WAVE);
+  ck.mo = (lane_id() == 0) ? m : up;
   ck.eta = (ck.sc.ev.side == 0 && ck.sc.wt > 0.f) ? ck.sc.wt / (ck.mi + a.eps) : 0.f;
 #pragma unroll
   for (int i = 0; i < CHUNK; ++i) {
+    part[i] = 0.f;
     if (i < n) {
       float x[CPL];
       ck.raw[i].get(x);
@@ -416,118 +466,96 @@ __device__ __forceinline__ void bwd_replay(const ScanBwdArgs& a, BwdChunk<IO, CP
           ck.so[i][c] = s[c];
           s[c] = fmaf(1.f - e, s[c], e * x[c]);
         }
-      } else {
-        float d = 0.f;
-        if (active) {
+      } else if (active) {
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) d = fmaf(x[c], s[c], d);
-        }
-        d = wave_sum(d);
-        const int64_t dri = (int64_t)readlane_i(ck.sc.ev.row, i) * a.k_r + readlane_i(ck.sc.ev.j, i);
-        if (lane == 0) a.dr[dri] = d;
+        for (int c = 0; c < CPL; ++c) part[i] = fmaf(x[c], s[c], part[i]);
       }
     }
   }
 }
 
-// Reverse walk of a loaded chunk from the adjoints (sh, mh) after its last
-// event; leaves the adjoints before its first event in (sh, mh).
+// Reverse walk of the content adjoint from sh (after the chunk) to sh (before
+// it): stores the dv contributions and puts <s_hat_after, v - s_old> partials
+// of the writes into part[i].
 template <typename IO, int CPL>
-__device__ __forceinline__ void bwd_walk(const ScanBwdArgs& a, const BwdChunk<IO, CPL>& ck, int n,
-                                         float (&sh)[CPL], float& mh, bool active, int c0) {
+__device__ __forceinline__ void bwd_walk_content(const ScanBwdArgs& a, const BwdChunk<IO, CPL>& ck,
+                                                 int n, float (&sh)[CPL], bool active, int c0,
+                                                 float (&part)[CHUNK]) {
   IO* stash = reinterpret_cast<IO*>(a.stash);
-  const int lane = lane_id();
 #pragma unroll
   for (int i = CHUNK - 1; i >= 0; --i) {
     if (i < n) {
       float x[CPL];
       ck.raw[i].get(x);
-      const int ri = readlane_i(ck.sc.ev.row, i);
+      const float r_or_w = readlane_f(ck.sc.wt, i);
       if (readlane_i(ck.sc.ev.side, i) == 1) {
-        const float r = readlane_f(ck.sc.wt, i);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) sh[c] = fmaf(r, x[c], sh[c]);
+        for (int c = 0; c < CPL; ++c) sh[c] = fmaf(r_or_w, x[c], sh[c]);
       } else {
         const float e = readlane_f(ck.eta, i);
-        const int64_t srow = (int64_t)ri * a.k_w + readlane_i(ck.sc.ev.j, i);
+        const int64_t srow = (int64_t)readlane_i(ck.sc.ev.row, i) * a.k_w + readlane_i(ck.sc.ev.j, i);
+        float contrib[CPL];
         float d = 0.f;
-        if (active) {
-          float contrib[CPL];
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            contrib[c] = e * sh[c];
-            d = fmaf(sh[c], x[c] - ck.so[i][c], d);
-          }
-          Slice<IO, CPL>::store(stash + srow * a.d_v + c0, contrib);
+        for (int c = 0; c < CPL; ++c) {
+          contrib[c] = e * sh[c];
+          d = fmaf(sh[c], x[c] - ck.so[i][c], d);
+          sh[c] = (1.f - e) * sh[c];
         }
-        d = wave_sum(d);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) sh[c] = (1.f - e) * sh[c];
-        const float w = readlane_f(ck.sc.wt, i);
-        const float mnew = readlane_f(ck.mi, i);
-        const float mold = readlane_f(ck.mo, i);
-        const float li = readlane_f(ck.sc.lam, i);
-        const float dli = readlane_f(ck.sc.dl, i);
-        const float den = mnew + a.eps;
-        const float M = (w > 0.f) ? mh - d * w / (den * den) : mh;
-        const float dwi = ((w > 0.f) ? d / den : 0.f) + M + M * mold * dli;
-        const float dgi = M * mold * (-li * (1.f - li));
-        mh = li * M;
-        if (lane == 0) {
-          a.dw[srow] = dwi;
-          a.dgam[srow] = dgi;
+        if (active) {
+          Slice<IO, CPL>::store(stash + srow * a.d_v + c0, contrib);
+          part[i] = d;
         }
       }
     }
   }
 }
 
-// The chunk's adjoint map, from a symbolic zero at its end:
-//   s_hat_in = Q * s_hat_out + q
-//   m_hat_in = L * m_hat_out + <s_hat_out, U> + K
+// Lane-parallel scalar part of a chunk's reverse step.  red (lane i) holds
+// dr_i for a read and deta_i for a write.  Stores dr, dw and the gamma parts;
+// mh goes from the mass adjoint after the chunk to the one before it.
 template <typename IO, int CPL>
-__device__ __forceinline__ void bwd_map(const ScanBwdArgs& a, const BwdChunk<IO, CPL>& ck, int n,
-                                        float& Q, float (&q)[CPL], float& L, float (&U)[CPL],
-                                        float& K, bool active) {
-  Q = 1.f;
-  L = 1.f;
-  K = 0.f;
+__device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const BwdChunk<IO, CPL>& ck,
+                                            int n, float red, float& mh) {
+  const int lane = lane_id();
+  const bool ev = lane < n;
+  const bool wr = ev && ck.sc.ev.side == 0;
+  const float den = ck.mi + a.eps;
+  const float g = (wr && ck.sc.wt > 0.f) ? ck.sc.wt / (den * den) : 0.f;
+  const float deta = wr ? red : 0.f;
+  float A = wr ? ck.sc.lam : 1.f;
+  float B = wr ? -ck.sc.lam * g * deta : 0.f;
+  affine_suffix_scan(A, B);
+  const float before = fmaf(A, mh, B);
+  const float after_n = __shfl_down(before, 1, WAVE);
+  const float after = (lane == WAVE - 1) ? mh : after_n;
+  if (wr) {
+    const float M = after - g * deta;
+    const float dwi = ((ck.sc.wt > 0.f) ? deta / den : 0.f) + M + M * ck.mo * ck.sc.dl;
+    const float dgi = M * ck.mo * (-ck.sc.lam * (1.f - ck.sc.lam));
+    const int64_t o = (int64_t)ck.sc.ev.row * a.k_w + ck.sc.ev.j;
+    a.dw[o] = dwi;
+    a.dgam[o] = dgi;
+  } else if (ev) {
+    a.dr[(int64_t)ck.sc.ev.row * a.k_r + ck.sc.ev.j] = red;
+  }
+  mh = readlane_f(before, 0);
+}
+
+// State at the start of chunk cs of segment g: the initial state for the
+// segment's first chunk, else the checkpoint the forward saved.
+template <int CPL>
+__device__ __forceinline__ void chunk_state(const ScanBwdArgs& a, int64_t g, int beg, int cs,
+                                            bool active, int c0, float (&s)[CPL], float& m) {
+  if (cs == beg) {
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) { q[c] = 0.f; U[c] = 0.f; }
+    for (int c = 0; c < CPL; ++c) s[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
+    m = a.mass0 ? a.mass0[g] : 0.f;
+  } else {
+    const float* cp = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
 #pragma unroll
-  for (int i = CHUNK - 1; i >= 0; --i) {
-    if (i < n) {
-      float x[CPL];
-      ck.raw[i].get(x);
-      if (readlane_i(ck.sc.ev.side, i) == 1) {
-        const float r = readlane_f(ck.sc.wt, i);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) q[c] = fmaf(r, x[c], q[c]);
-      } else {
-        const float e = readlane_f(ck.eta, i);
-        const float w = readlane_f(ck.sc.wt, i);
-        const float mnew = readlane_f(ck.mi, i);
-        const float li = readlane_f(ck.sc.lam, i);
-        const float den = mnew + a.eps;
-        const float gq = (w > 0.f) ? w / (den * den) : 0.f;
-        float u[CPL];
-        float d = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          u[c] = active ? x[c] - ck.so[i][c] : 0.f;
-          d = fmaf(q[c], u[c], d);
-        }
-        d = wave_sum(d);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          U[c] = li * (U[c] - gq * Q * u[c]);
-          q[c] = (1.f - e) * q[c];
-        }
-        K = li * (K - gq * d);
-        L = li * L;
-        Q = (1.f - e) * Q;
-      }
-    }
+    for (int c = 0; c < CPL; ++c) s[c] = active ? cp[c0 + c] : 0.f;
+    m = a.ckpt_m[cs / CHUNK];
   }
 }
 
@@ -547,24 +575,15 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
 
   if (beg < end) {
     BwdChunk<IO, CPL> ck;
+    float part[CHUNK];
     int cs = max(beg, ((end - 1) / CHUNK) * CHUNK);
     while (true) {
-      const int ce = min(end, (cs / CHUNK + 1) * CHUNK);
-      const int n = ce - cs;
-      float s[CPL];
-      float m;
-      if (cs == beg) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) s[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
-        m = a.mass0 ? a.mass0[g] : 0.f;
-      } else {
-        const float* cp = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) s[c] = active ? cp[c0 + c] : 0.f;
-        m = a.ckpt_m[cs / CHUNK];
-      }
-      bwd_replay<IO, CPL>(a, ck, b, h, cs, n, s, m, active, c0);
-      bwd_walk<IO, CPL>(a, ck, n, sh, mh, active, c0);
+      const int n = min(end, (cs / CHUNK + 1) * CHUNK) - cs;
+      float s[CPL], m;
+      chunk_state<CPL>(a, g, beg, cs, active, c0, s, m);
+      bwd_load_replay<IO, CPL>(a, ck, b, h, cs, n, s, m, active, c0, part);
+      bwd_walk_content<IO, CPL>(a, ck, n, sh, active, c0, part);
+      bwd_scalars<IO, CPL>(a, ck, n, batched_sum(part), mh);
       if (cs == beg) break;
       cs = max(beg, cs - CHUNK);
     }
@@ -576,8 +595,18 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
   if (a.d_mass0 && lane == 0) a.d_mass0[g] = mh;
 }
 
+// Long segments: a workgroup of NWB waves takes NWB consecutive chunks at a
+// time, from the end of the segment.  Each wave replays its chunk from its
+// checkpoint and forms the chunk's adjoint map from a symbolic zero at its end
+//   s_hat_in = Q * s_hat_out + q
+//   m_hat_in = L * m_hat_out + <s_hat_out, U> + K
+// (Q = prod (1-eta), L = prod lambda over the writes; U and K collect the
+// mass terms), the maps of the later chunks are folded to give each wave its
+// true adjoints after its chunk, and each wave then runs the exact reverse
+// step.  Wave 0's result is the carry into the previous NW chunks.
 template <typename IO, int CPL>
 __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
+  constexpr int NW = NWB;
   __shared__ float mQ[NW], mL[NW], mK[NW];
   __shared__ float mq[NW][MAX_DV], mU[NW][MAX_DV];
   __shared__ float carry_s[MAX_DV];
@@ -589,7 +618,6 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
   const int c0 = lane * CPL;
   const bool active = c0 < a.d_v;
   const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
-  // chunk k starts at beg (k = 0) or at (beg/CHUNK + k)*CHUNK
   const int nchunks = (end - 1) / CHUNK - beg / CHUNK + 1;
 
   float sh_carry[CPL];
@@ -599,6 +627,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
   float mh_carry = a.d_mass1 ? a.d_mass1[g] : 0.f;
 
   BwdChunk<IO, CPL> ck;
+  float part[CHUNK];
   for (int u0 = ((nchunks - 1) / NW) * NW; u0 >= 0; u0 -= NW) {
     const int k = u0 + w;
     int cs = end, n = 0;
@@ -606,31 +635,58 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
       cs = chunk_start(beg, k, end);
       n = chunk_start(beg, k + 1, end) - cs;
     }
-    float s[CPL];
-    float m = 0.f;
-    if (n > 0) {
-      if (cs == beg) {
+    float s[CPL], m = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) s[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
-        m = a.mass0 ? a.mass0[g] : 0.f;
-      } else {
-        const float* cp = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
+    for (int c = 0; c < CPL; ++c) s[c] = 0.f;
+    if (n > 0) chunk_state<CPL>(a, g, beg, cs, active, c0, s, m);
+    bwd_load_replay<IO, CPL>(a, ck, b, h, cs, n, s, m, active, c0, part);
+    // adjoint map of the chunk (reverse walk from zero); write partials
+    // <q_after_i, u_i> join the read partials in part[]
+    float Lp = (lane < n && ck.sc.ev.side == 0) ? ck.sc.lam : 1.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) s[c] = active ? cp[c0 + c] : 0.f;
-        m = a.ckpt_m[cs / CHUNK];
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) s[c] = 0.f;
+    for (int o = 1; o < CHUNK; o <<= 1) {                   // prefix products of lambda
+      const float up = __shfl_up(Lp, o, WAVE);
+      Lp = (lane >= o) ? Lp * up : Lp;
     }
-    bwd_replay<IO, CPL>(a, ck, b, h, cs, n, s, m, active, c0);
-    float Q, q[CPL], L, U[CPL], K;
-    bwd_map<IO, CPL>(a, ck, n, Q, q, L, U, K, active);
+    const float den = ck.mi + a.eps;
+    const float gq = (ck.sc.ev.side == 0 && ck.sc.wt > 0.f) ? ck.sc.wt / (den * den) : 0.f;
+    float Q = 1.f, q[CPL], U[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) { q[c] = 0.f; U[c] = 0.f; }
+#pragma unroll
+    for (int i = CHUNK - 1; i >= 0; --i) {
+      if (i < n) {
+        float x[CPL];
+        ck.raw[i].get(x);
+        const float r_or_w = readlane_f(ck.sc.wt, i);
+        if (readlane_i(ck.sc.ev.side, i) == 1) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) q[c] = fmaf(r_or_w, x[c], q[c]);
+        } else {
+          const float e = readlane_f(ck.eta, i);
+          const float coef = -readlane_f(Lp, i) * readlane_f(gq, i) * Q;
+          float d = 0.f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const float u = active ? x[c] - ck.so[i][c] : 0.f;
+            d = fmaf(q[c], u, d);
+            U[c] = fmaf(coef, u, U[c]);
+            q[c] = (1.f - e) * q[c];
+          }
+          part[i] = active ? d : 0.f;
+          Q *= 1.f - e;
+        }
+      }
+    }
+    const float red1 = batched_sum(part);     // dr (reads), <q_after, u> (writes)
+    const bool wr = lane < n && ck.sc.ev.side == 0;
+    const float K = wave_sum(wr ? -Lp * gq * red1 : 0.f);
+    const float L = readlane_f(Lp, max(n, 1) - 1);
     if (active) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) { mq[w][c0 + c] = q[c]; mU[w][c0 + c] = U[c]; }
     }
-    if (lane == 0) { mQ[w] = Q; mL[w] = L; mK[w] = K; }
+    if (lane == 0) { mQ[w] = Q; mL[w] = (n > 0) ? L : 1.f; mK[w] = K; }
     __syncthreads();
     // adjoints after this wave's chunk: fold the maps of the later chunks
     float sh[CPL];
@@ -649,7 +705,16 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) sh[c] = fmaf(Qk, sh[c], active ? mq[kk][c0 + c] : 0.f);
     }
-    bwd_walk<IO, CPL>(a, ck, n, sh, mh, active, c0);
+    // exact reverse step of this wave's chunk
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i) part[i] = 0.f;
+    bwd_walk_content<IO, CPL>(a, ck, n, sh, active, c0, part);
+    const float red2 = batched_sum(part);     // deta (writes)
+    {
+      // bwd_scalars stores dr for reads too; keep the values from red1 there
+      const bool rd = lane < n && ck.sc.ev.side == 1;
+      bwd_scalars<IO, CPL>(a, ck, n, rd ? red1 : red2, mh);
+    }
     if (w == 0) {
       if (active) {
 #pragma unroll
@@ -672,15 +737,17 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
   }
 }
 
+// Long segments: NWB waves per workgroup, the workgroups walk the long list.
 template <typename IO, int CPL>
-__global__ __launch_bounds__(NW * WAVE) void scan_bwd_kernel(ScanBwdArgs a) {
-  if ((int)blockIdx.x < a.long_blocks) {
-    const int count = a.use_long ? *a.long_count : 0;
-    for (int i = blockIdx.x; i < count; i += a.long_blocks)
-      scan_bwd_long<IO, CPL>(a, a.long_list[i]);
-    return;
-  }
-  const int64_t g = ((int64_t)blockIdx.x - a.long_blocks) * NW + threadIdx.x / WAVE;
+__global__ __launch_bounds__(NWB * WAVE) void scan_bwd_long_kernel(ScanBwdArgs a) {
+  const int count = a.use_long ? *a.long_count : 0;
+  for (int i = blockIdx.x; i < count; i += gridDim.x) scan_bwd_long<IO, CPL>(a, a.long_list[i]);
+}
+
+// Short segments: one wave each, four per workgroup.
+template <typename IO, int CPL>
+__global__ __launch_bounds__(4 * WAVE) void scan_bwd_short_kernel(ScanBwdArgs a) {
+  const int64_t g = (int64_t)blockIdx.x * 4 + threadIdx.x / WAVE;
   if (g >= a.nseg) return;
   if (a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS) return;
   scan_bwd_short<IO, CPL>(a, g);
@@ -690,24 +757,42 @@ __global__ __launch_bounds__(NW * WAVE) void scan_bwd_kernel(ScanBwdArgs a) {
 // token-major sums of the stash rows
 // ---------------------------------------------------------------------------
 
-// out[row] = sum_j stash[row, j] (float accumulation, j ascending), one wave
-// per row; optionally d_gamma[row] = sum_j dgam[row, j].
+// out[row] = sum_j stash[row, j] (float accumulation, j ascending).  With
+// d_v a multiple of one 16-byte vector, a thread sums one vector column.
 template <typename IO>
 __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
-  const int lane = lane_id();
-  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / WAVE;
-  if (row >= a.N) return;
-  const IO* st = reinterpret_cast<const IO*>(a.stash) + row * a.k * a.d_v;
-  IO* out = reinterpret_cast<IO*>(a.out) + row * a.d_v;
-  for (int c = lane; c < a.d_v; c += WAVE) {
+  constexpr int E = vec16<IO>::E;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const IO* st = reinterpret_cast<const IO*>(a.stash);
+  IO* out = reinterpret_cast<IO*>(a.out);
+  if (a.d_v % E == 0) {
+    const int vpr = a.d_v / E;
+    if (tid < a.N * vpr) {
+      const int64_t row = tid / vpr;
+      const int vcol = (int)(tid % vpr);
+      float acc[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = 0.f;
+      const IO* base = st + row * a.k * a.d_v + vcol * E;
+      for (int j = 0; j < a.k; ++j) {
+        float x[E];
+        unpack16(*reinterpret_cast<const uint4*>(base + (int64_t)j * a.d_v), x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += x[e];
+      }
+      *reinterpret_cast<uint4*>(out + row * a.d_v + vcol * E) = pack16(acc);
+    }
+  } else if (tid < a.N * a.d_v) {
+    const int64_t row = tid / a.d_v;
+    const int c = (int)(tid % a.d_v);
     float acc = 0.f;
-    for (int j = 0; j < a.k; ++j) acc += to_f32(st[j * a.d_v + c]);
-    out[c] = from_f32<IO>(acc);
+    for (int j = 0; j < a.k; ++j) acc += to_f32(st[(row * a.k + j) * a.d_v + c]);
+    out[row * a.d_v + c] = from_f32<IO>(acc);
   }
-  if (a.dgam && lane == 0) {
+  if (a.dgam && tid < a.N) {
     float sum = 0.f;
-    for (int j = 0; j < a.k; ++j) sum += a.dgam[row * a.k + j];
-    reinterpret_cast<IO*>(a.d_gamma)[row] = from_f32<IO>(sum);
+    for (int j = 0; j < a.k; ++j) sum += a.dgam[tid * a.k + j];
+    reinterpret_cast<IO*>(a.d_gamma)[tid] = from_f32<IO>(sum);
   }
 }
 
@@ -728,20 +813,33 @@ hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st) {
 
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st) {
   if (a.nseg == 0) return hipSuccess;
-  const dim3 grid((unsigned)(a.long_blocks + (a.nseg + NW - 1) / NW)), block(NW * WAVE);
+  const dim3 lgrid((unsigned)a.long_blocks), lblock(NWB * WAVE);
+  const dim3 sgrid((unsigned)((a.nseg + 3) / 4)), sblock(4 * WAVE);
+  if (a.use_long) {
+    if (bf16) {
+      if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_long_kernel<bf16_t, 2>), lgrid, lblock, 0, st, a);
+      else hipLaunchKernelGGL((scan_bwd_long_kernel<bf16_t, 1>), lgrid, lblock, 0, st, a);
+    } else {
+      if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_long_kernel<float, 2>), lgrid, lblock, 0, st, a);
+      else hipLaunchKernelGGL((scan_bwd_long_kernel<float, 1>), lgrid, lblock, 0, st, a);
+    }
+  }
   if (bf16) {
-    if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_kernel<bf16_t, 2>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scan_bwd_kernel<bf16_t, 1>), grid, block, 0, st, a);
+    if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_short_kernel<bf16_t, 2>), sgrid, sblock, 0, st, a);
+    else hipLaunchKernelGGL((scan_bwd_short_kernel<bf16_t, 1>), sgrid, sblock, 0, st, a);
   } else {
-    if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_kernel<float, 2>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scan_bwd_kernel<float, 1>), grid, block, 0, st, a);
+    if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_short_kernel<float, 2>), sgrid, sblock, 0, st, a);
+    else hipLaunchKernelGGL((scan_bwd_short_kernel<float, 1>), sgrid, sblock, 0, st, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
+  const int E = bf16 ? 8 : 4;
+  int64_t threads = (a.d_v % E == 0) ? a.N * (a.d_v / E) : a.N * a.d_v;
+  if (threads < a.N) threads = a.N;
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   if (bf16) hipLaunchKernelGGL(finalize_kernel<bf16_t>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(finalize_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
