@@ -97,8 +97,9 @@ typedef struct ram_ws_layout {
   size_t w_r;         /* float (N, k_r)                                                           */
   size_t lse_r;       /* float (N)                                                                */
   size_t seg_offset;  /* int32 (B*H*S + 1): first event of segment g = (b*H + h)*S + a          */
-  size_t events;      /* int32 (E): event codes (t << 7) | (side << 6) | j, segment-major,
-                         time order inside a segment, a token's write before its read          */
+  size_t events;      /* (E) 16-byte records {int32 code, float weight, float lambda, float
+                         d lambda/d w}; code = (t << 7) | (side << 6) | j; segment-major, time
+                         order inside a segment, a token's write before its read            */
   size_t ckpt_s;      /* float (E/16 + 1, d_v): slot content at every 16-aligned event        */
   size_t ckpt_m;      /* float (E/16 + 1): slot mass at the same points                      */
   size_t stash;       /* io (N, max(k_w,k_r), d_v): per-(token, j) read / dv contributions      */

@@ -173,7 +173,8 @@ def ws_views(p: Problem, ws: torch.Tensor) -> dict:
         "w_r": view(L["w_r"], N * p.k_r, torch.float32),
         "lse_r": view(L["lse_r"], N, torch.float32),
         "seg_offset": view(L["seg_offset"], p.B * p.H * S + 1, torch.int32),
-        "events": view(L["events"], E, torch.int32),
+        "events": view(L["events"], 4 * E, torch.int32).view(E, 4)[:, 0],
+        "event_w": view(L["events"], 4 * E, torch.float32).view(E, 4)[:, 1],
         "dw": view(L["dw"], N * p.k_w, torch.float32),
         "dr": view(L["dr"], N * p.k_r, torch.float32),
     }

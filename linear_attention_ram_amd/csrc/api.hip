@@ -70,7 +70,7 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   L->w_r = take(sizeof(float) * d.N * p->k_r);
   L->lse_r = take(sizeof(float) * d.N);
   L->seg_offset = take(sizeof(int32_t) * (d.nseg + 1));
-  L->events = take(sizeof(int32_t) * d.E);
+  L->events = take(sizeof(EventRec) * d.E);
   L->ckpt_s = take(sizeof(float) * d.nck * p->d_v);
   L->ckpt_m = take(sizeof(float) * d.nck);
   L->stash = take(d.io_bytes * d.N * (p->k_w > p->k_r ? p->k_w : p->k_r) * p->d_v);
@@ -230,6 +230,9 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   BucketArgs ba{};
   ba.idx_w = da.idx[0];
   ba.idx_r = da.idx[1];
+  ba.w_w = da.w[0];
+  ba.w_r = da.w[1];
+  ba.gamma = gamma;
   ba.B = p->B;
   ba.H = p->H;
   ba.T = p->T;
@@ -240,10 +243,10 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   ba.nbits = d.nbits;
   ba.tile_hist = (int32_t*)(w + L.tile_hist);
   ba.seg_offset = (int32_t*)(w + L.seg_offset);
-  ba.events = (int32_t*)(w + L.events);
+  ba.events = (EventRec*)(w + L.events);
   ba.long_list = (int32_t*)(w + L.long_list);
   ba.long_count = (int32_t*)(w + L.long_count);
-  e = launch_bucket(ba, s, prof_before, prof_after);
+  e = launch_bucket(ba, bf, s, prof_before, prof_after);
   if (e != hipSuccess) return RAM_EHIP;
 
   ScanFwdArgs sa{};
@@ -262,10 +265,7 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   sa.long_blocks = LONG_BLOCKS;
   sa.seg_offset = ba.seg_offset;
   sa.events = ba.events;
-  sa.w_w = da.w[0];
-  sa.w_r = da.w[1];
   sa.v = v;
-  sa.gamma = gamma;
   sa.slot0 = slot0;
   sa.mass0 = mass0;
   sa.slot1 = slot1;
@@ -329,11 +329,8 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   sb.use_long = d.ntiles > 0;
   sb.long_blocks = LONG_BLOCKS;
   sb.seg_offset = (const int32_t*)(w + L.seg_offset);
-  sb.events = (const int32_t*)(w + L.events);
-  sb.w_w = (const float*)(w + L.w_w);
-  sb.w_r = (const float*)(w + L.w_r);
+  sb.events = (const EventRec*)(w + L.events);
   sb.v = v;
-  sb.gamma = gamma;
   sb.d_o = d_o;
   sb.slot0 = slot0;
   sb.mass0 = mass0;
@@ -359,8 +356,8 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   db.lse[1] = (const float*)(w + L.lse_r);
   db.idx[0] = (const int32_t*)(w + L.idx_w);
   db.idx[1] = (const int32_t*)(w + L.idx_r);
-  db.w[0] = sb.w_w;
-  db.w[1] = sb.w_r;
+  db.w[0] = (const float*)(w + L.w_w);
+  db.w[1] = (const float*)(w + L.w_r);
   db.g[0] = sb.dw;
   db.g[1] = sb.dr;
   db.dlogits[0] = d_wlogits;

@@ -13,8 +13,10 @@
 //            offsets need no scan across (b, h);
 //   scatter  one wave per (b, h, tile): walks the tile's events in order
 //            (t ascending, write side before read side), ranks equal slots
-//            inside each 64-event batch with ballots, and writes the event
-//            codes to their final positions.
+//            inside each 64-event batch with ballots, and writes each event
+//            as a 16-byte record (code, weight, retention lambda and
+//            d lambda / d w of a write) to its final position, so the scans
+//            read their events with one coalesced load and gather nothing.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketArgs a) {
     a.seg_offset[(int64_t)a.B * a.H * S] = (int32_t)((int64_t)a.B * a.H * a.T * (a.k_w + a.k_r));
 }
 
+template <typename IO>
 __global__ __launch_bounds__(64) void bucket_scatter_kernel(BucketArgs a) {
   extern __shared__ int next[];
   const int tile = blockIdx.x, bh = blockIdx.y;
@@ -96,6 +99,7 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(BucketArgs a) {
   const int S = a.S;
   const int32_t* th = a.tile_hist + ((int64_t)bh * a.ntiles + tile) * S;
   const int32_t* so = a.seg_offset + (int64_t)bh * S;
+  const IO* gam = reinterpret_cast<const IO*>(a.gamma);
   for (int s = lane; s < S; s += WAVE) next[s] = so[s] + th[s];
   wave_sync();
   const int K = a.k_w + a.k_r;
@@ -106,11 +110,21 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(BucketArgs a) {
   for (int e0 = 0; e0 < n; e0 += WAVE) {
     const int e = e0 + lane;
     bool valid = e < n;
-    int slot = 0, code = 0;
+    int slot = 0;
+    EventRec rec{0, 0.f, 1.f, 0.f};
     if (valid) {
       const int t = t_lo + e / K, p = e % K;
-      slot = event_slot(a, b, h, t, p);
-      code = (t << 7) | ((p < a.k_w ? 0 : 1) << 6) | (p < a.k_w ? p : p - a.k_w);
+      const int64_t row = ((int64_t)b * a.T + t) * a.H + h;
+      if (p < a.k_w) {
+        slot = a.idx_w[row * a.k_w + p];
+        rec.code = (t << 7) | p;
+        rec.w = a.w_w[row * a.k_w + p];
+        rec.lam = retention(rec.w, to_f32(gam[row]), &rec.dlam);
+      } else {
+        slot = a.idx_r[row * a.k_r + (p - a.k_w)];
+        rec.code = (t << 7) | (1 << 6) | (p - a.k_w);
+        rec.w = a.w_r[row * a.k_r + (p - a.k_w)];
+      }
       valid = (unsigned)slot < (unsigned)S;   // decoded slots are always < S
     }
     uint64_t peers = __ballot(valid);
@@ -125,11 +139,12 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(BucketArgs a) {
     wave_sync();
     if (valid && rank == 0) next[slot] = base + tot;
     wave_sync();
-    if (valid) a.events[base + rank] = code;
+    if (valid) a.events[base + rank] = rec;
   }
 }
 
-hipError_t launch_bucket(const BucketArgs& a, hipStream_t st, void (*before)(const char*, hipStream_t),
+hipError_t launch_bucket(const BucketArgs& a, bool bf16, hipStream_t st,
+                         void (*before)(const char*, hipStream_t),
                          void (*after)(const char*, hipStream_t)) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
@@ -144,7 +159,8 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t st, void (*before)(con
   after("bucket_scan", st);
   if (a.ntiles > 0) {
     before("bucket_scatter", st);
-    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(a.ntiles, BH), dim3(64), lds, st, a);
+    if (bf16) hipLaunchKernelGGL(bucket_scatter_kernel<bf16_t>, dim3(a.ntiles, BH), dim3(64), lds, st, a);
+    else hipLaunchKernelGGL(bucket_scatter_kernel<float>, dim3(a.ntiles, BH), dim3(64), lds, st, a);
     after("bucket_scatter", st);
   }
   return hipGetLastError();

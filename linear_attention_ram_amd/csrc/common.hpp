@@ -72,15 +72,60 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, WAVE));
-  return x;
+// Cross-lane moves without LDS: DPP within rows of 16 lanes and the gfx950
+// permlane swaps across rows.  All callers run with every lane active.
+//   quad_perm [1,0,3,2] = lane ^ 1      quad_perm [2,3,0,1] = lane ^ 2
+//   row_half_mirror: lane i <-> 7 - i in groups of 8
+//   row_mirror:      lane i <-> 15 - i in rows of 16
+//   row_ror:8 = lane ^ 8;  row_shl:k: lane i reads i + k;  row_shr:k: i - k
+//   permlane16_swap(A, B): even row r gets {A_r, A_r+1}, odd row gets
+//   {B_r-1, B_r};  permlane32_swap(A, B): lane l < 32 gets {A_l, A_l+32},
+//   lane l >= 32 gets {B_l-32, B_l}.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+constexpr int DPP_ROR8 = 0x128, DPP_SHL1 = 0x101, DPP_SHL4 = 0x104, DPP_SHR1 = 0x111;
+constexpr int DPP_SHR4 = 0x114;
+template <int K> struct DppShr;
+template <> struct DppShr<1> { static constexpr int v = 0x111; };
+template <> struct DppShr<2> { static constexpr int v = 0x112; };
+template <> struct DppShr<4> { static constexpr int v = 0x114; };
+template <> struct DppShr<8> { static constexpr int v = 0x118; };
+template <int K> struct DppShl;
+template <> struct DppShl<1> { static constexpr int v = 0x101; };
+template <> struct DppShl<2> { static constexpr int v = 0x102; };
+template <> struct DppShl<4> { static constexpr int v = 0x104; };
+template <> struct DppShl<8> { static constexpr int v = 0x108; };
+
+// Sum of a and the value of the lane that differs in bit 4 (or bit 5).
+__device__ __forceinline__ float xor16_pair(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_pair(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, WAVE);
-  return x;
+  x += dpp<DPP_XOR1>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_HALF_MIRROR>(x);
+  x += dpp<DPP_MIRROR>(x);
+  x = xor16_pair(x, x);
+  return xor32_pair(x, x);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<DPP_XOR1>(x));
+  x = fmaxf(x, dpp<DPP_XOR2>(x));
+  x = fmaxf(x, dpp<DPP_HALF_MIRROR>(x));
+  x = fmaxf(x, dpp<DPP_MIRROR>(x));
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll

@@ -12,15 +12,26 @@ constexpr int NWB = 8;           // waves per reverse long-segment workgroup
 constexpr int LONG_EVENTS = 128; // segments with more events take the cooperative path
 constexpr int MAX_DV = 128;      // widest slot
 
+// One event of the segment lists: 16 bytes, read with one vector load.
+struct EventRec {
+  int32_t code;           // (t << 7) | (side << 6) | j
+  float w;                // write weight or read weight
+  float lam;              // retention of a write (1 for a read)
+  float dlam;             // d lambda / d w of a write (0 for a read)
+};
+
 struct BucketArgs {
   const int32_t* idx_w;   // (N, k_w)
   const int32_t* idx_r;   // (N, k_r)
+  const float* w_w;       // (N, k_w)
+  const float* w_r;       // (N, k_r)
+  const void* gamma;      // (N) io
   int B, H, T, S, k_w, k_r;
   int ntiles;             // ceil(T / TILE_TOKENS)
   int nbits;              // bits needed for a slot index
   int32_t* tile_hist;     // (B*H, ntiles, S)
   int32_t* seg_offset;    // (B*H*S + 1)
-  int32_t* events;        // (E)
+  EventRec* events;       // (E)
   int32_t* long_list;     // segments with more than LONG_EVENTS events
   int32_t* long_count;    // their number
 };
@@ -34,11 +45,8 @@ struct ScanFwdArgs {
   int use_long;           // long_list / long_count are valid
   int long_blocks;        // workgroups that walk the long list
   const int32_t* seg_offset;
-  const int32_t* events;
-  const float* w_w;       // (N, k_w)
-  const float* w_r;       // (N, k_r)
+  const EventRec* events;
   const void* v;          // (N, d_v) io
-  const void* gamma;      // (N) io
   const float* slot0;     // (B*H*S, d_v) or null
   const float* mass0;     // (B*H*S) or null
   float* slot1;
@@ -57,11 +65,8 @@ struct ScanBwdArgs {
   int use_long;
   int long_blocks;
   const int32_t* seg_offset;
-  const int32_t* events;
-  const float* w_w;
-  const float* w_r;
+  const EventRec* events;
   const void* v;          // io
-  const void* gamma;      // io
   const void* d_o;        // (N, d_v) io
   const float* slot0;     // or null
   const float* mass0;     // or null
@@ -98,7 +103,8 @@ struct StepArgs {
   void* o;                // (B*H, d_v) io
 };
 
-hipError_t launch_bucket(const BucketArgs& a, hipStream_t st, void (*before)(const char*, hipStream_t),
+hipError_t launch_bucket(const BucketArgs& a, bool bf16, hipStream_t st,
+                         void (*before)(const char*, hipStream_t),
                          void (*after)(const char*, hipStream_t));
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st);

@@ -8,7 +8,7 @@
 // are aligned to multiples of 16 in the global event list; the state before
 // every aligned event inside a segment is saved as a checkpoint for the
 // reverse pass.  Inside a chunk:
-//   * lane i decodes event i and its retention; the mass recurrence
+//   * lane i loads event record i (code, weight, retention); the mass recurrence
 //     m <- lambda*m + w is affine, so one inclusive scan of (lambda, w) pairs
 //     across lanes gives every event's mass, then eta_i = w_i / (m_i + eps);
 //   * the chunk's v rows are loaded together and the content chain
@@ -79,18 +79,23 @@ __device__ __forceinline__ EventInfo decode_event(int code, int b, int h, int T,
   return e;
 }
 
-// Inclusive scan across lanes of affine maps x -> A*x + B (earlier lanes
-// applied first).  Lanes past the chunk carry the identity.
+// Inclusive scan across the CHUNK = 16 lanes of each row of affine maps
+// x -> A*x + B (earlier lanes applied first), with DPP row shifts.  Lanes
+// past the chunk carry the identity.
+template <int O>
+__device__ __forceinline__ void affine_step(float& A, float& B) {
+  const float Ap = dpp<DppShr<O>::v>(A);
+  const float Bp = dpp<DppShr<O>::v>(B);
+  const bool take = (lane_id() & (CHUNK - 1)) >= O;
+  B = take ? fmaf(A, Bp, B) : B;
+  A = take ? A * Ap : A;
+}
 __device__ __forceinline__ void affine_scan(float& A, float& B) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < CHUNK; o <<= 1) {
-    const float Ap = __shfl_up(A, o, WAVE);
-    const float Bp = __shfl_up(B, o, WAVE);
-    const bool take = lane >= o;
-    B = take ? fmaf(A, Bp, B) : B;
-    A = take ? A * Ap : A;
-  }
+  static_assert(CHUNK == 16, "scans are written for rows of 16 lanes");
+  affine_step<1>(A, B);
+  affine_step<2>(A, B);
+  affine_step<4>(A, B);
+  affine_step<8>(A, B);
 }
 
 // Per-event scalars of one chunk: lane i < n holds event cs + i.
@@ -98,24 +103,22 @@ struct ChunkScalars {
   EventInfo ev;
   float wt;   // write weight or read weight
   float lam;  // retention (writes), 1 for reads
-  float dl;   // d lambda / d w (writes)
+  float dl;   // d lambda / d w (writes), 0 for reads
 };
 
-template <typename IO>
-__device__ __forceinline__ ChunkScalars chunk_scalars(const int32_t* events, const float* w_w,
-                                                      const float* w_r, const IO* gb, int k_w,
-                                                      int k_r, int b, int h, int T, int H, int cs,
-                                                      int n, bool want_dl) {
-  ChunkScalars c{{0, 1, 0}, 0.f, 1.f, 0.f};
-  if (lane_id() < n) {
-    c.ev = decode_event(events[cs + lane_id()], b, h, T, H);
-    if (c.ev.side == 0) {
-      c.wt = w_w[(int64_t)c.ev.row * k_w + c.ev.j];
-      c.lam = retention(c.wt, to_f32(gb[c.ev.row]), want_dl ? &c.dl : nullptr);
-    } else {
-      c.wt = w_r[(int64_t)c.ev.row * k_r + c.ev.j];
-    }
-  }
+// Event record cs + lane for lanes < n (one 16-byte load; issued early so
+// the next chunk's records arrive while the current chunk computes).
+__device__ __forceinline__ float4 load_rec(const EventRec* events, int cs, int n) {
+  return (lane_id() < n) ? *reinterpret_cast<const float4*>(events + cs + lane_id())
+                         : make_float4(__int_as_float(1 << 6), 0.f, 1.f, 0.f);
+}
+
+__device__ __forceinline__ ChunkScalars chunk_scalars(float4 r, int b, int h, int T, int H) {
+  ChunkScalars c;
+  c.ev = decode_event(__float_as_int(r.x), b, h, T, H);
+  c.wt = r.y;
+  c.lam = r.z;
+  c.dl = r.w;
   return c;
 }
 
@@ -141,7 +144,6 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
   const bool active = c0 < a.d_v;
   const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
   const IO* vb = reinterpret_cast<const IO*>(a.v);
-  const IO* gb = reinterpret_cast<const IO*>(a.gamma);
   IO* stash = reinterpret_cast<IO*>(a.stash);
 
   float s[CPL];
@@ -149,6 +151,7 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
   for (int c = 0; c < CPL; ++c) s[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
   float m = a.mass0 ? a.mass0[g] : 0.f;
 
+  float4 rec = load_rec(a.events, beg, min(end, (beg / CHUNK + 1) * CHUNK) - beg);
   for (int p0 = beg; p0 < end;) {
     const int p1 = min(end, (p0 / CHUNK + 1) * CHUNK);
     const int n = p1 - p0;
@@ -160,8 +163,7 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
       }
       if (lane == 0) a.ckpt_m[p0 / CHUNK] = m;
     }
-    const ChunkScalars cs = chunk_scalars<IO>(a.events, a.w_w, a.w_r, gb, a.k_w, a.k_r, b, h,
-                                              a.T, a.H, p0, n, false);
+    const ChunkScalars cs = chunk_scalars(rec, b, h, a.T, a.H);
     float A = (cs.ev.side == 0) ? cs.lam : 1.f;
     float Bm = (cs.ev.side == 0) ? cs.wt : 0.f;
     affine_scan(A, Bm);
@@ -179,6 +181,7 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
         if (si == 0 && active) raw[i].load(vb + ri * a.d_v + c0);
       }
     }
+    rec = load_rec(a.events, p1, min(end, (p1 / CHUNK + 1) * CHUNK) - p1);   // next chunk
 #pragma unroll
     for (int i = 0; i < CHUNK; ++i) {
       if (i < n) {
@@ -219,7 +222,6 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
   const bool active = c0 < a.d_v;
   const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
   const IO* vb = reinterpret_cast<const IO*>(a.v);
-  const IO* gb = reinterpret_cast<const IO*>(a.gamma);
   IO* stash = reinterpret_cast<IO*>(a.stash);
 
   float s_carry[CPL];
@@ -228,11 +230,13 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
     s_carry[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
   float m_carry = a.mass0 ? a.mass0[g] : 0.f;
 
+  float4 rec = load_rec(a.events, chunk_start(beg, w, end),
+                        chunk_start(beg, w + 1, end) - chunk_start(beg, w, end));
   for (int p = beg; p < end;) {
     const int cs = chunk_start(p, w, end);
     const int n = chunk_start(p, w + 1, end) - cs;
-    const ChunkScalars sc = chunk_scalars<IO>(a.events, a.w_w, a.w_r, gb, a.k_w, a.k_r, b, h,
-                                              a.T, a.H, cs, n, false);
+    const int pn = chunk_start(p, NW, end);
+    const ChunkScalars sc = chunk_scalars(rec, b, h, a.T, a.H);
     float A = (sc.ev.side == 0) ? sc.lam : 1.f;
     float Bm = (sc.ev.side == 0) ? sc.wt : 0.f;
     affine_scan(A, Bm);
@@ -254,6 +258,9 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
         if (si == 0 && active) raw[i].load(vb + ri * a.d_v + c0);
       }
     }
+    if (pn < end)   // next super-chunk's records for this wave
+      rec = load_rec(a.events, chunk_start(pn, w, end),
+                     chunk_start(pn, w + 1, end) - chunk_start(pn, w, end));
     __syncthreads();
     float m_in = m_carry, m_next = m_carry;
     for (int k = 0; k < NW; ++k) {
@@ -325,7 +332,7 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
     m_carry = m_next;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) s_carry[c] = s_next[c];
-    p = chunk_start(p, NW, end);
+    p = pn;
     __syncthreads();
   }
   if (w == 0) {
@@ -382,47 +389,51 @@ struct BwdChunk {
 };
 
 // Sums x[i] over the 64 lanes for every i < CHUNK; lane i < CHUNK receives
-// the total of index i.  Each halving step exchanges the half of the values
-// a lane does not keep, so 16 sums cost 17 shuffles.
+// the total of index i.  Each halving step exchanges the half of the values a
+// lane does not keep (permlane swaps across rows, DPP inside rows), so 16
+// sums cost 15 cross-lane moves plus one final gather.
 __device__ __forceinline__ float batched_sum(const float (&x)[CHUNK]) {
   static_assert(CHUNK == 16, "batched_sum is written for 16 values");
   const int lane = lane_id();
   float y8[8], y4[4], y2[2];
-  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float send = b5 ? x[i] : x[i + 8];
-    y8[i] = (b5 ? x[i + 8] : x[i]) + __shfl_xor(send, 32, WAVE);
-  }
+  for (int i = 0; i < 8; ++i) y8[i] = xor32_pair(x[i], x[i + 8]);   // index i + 8*b5
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float send = b4 ? y8[i] : y8[i + 4];
-    y4[i] = (b4 ? y8[i + 4] : y8[i]) + __shfl_xor(send, 16, WAVE);
-  }
+  for (int i = 0; i < 4; ++i) y4[i] = xor16_pair(y8[i], y8[i + 4]); // + 4*b4
+  const bool b3 = lane & 8, b2 = lane & 4;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const float send = b3 ? y4[i] : y4[i + 2];
-    y2[i] = (b3 ? y4[i + 2] : y4[i]) + __shfl_xor(send, 8, WAVE);
+    y2[i] = (b3 ? y4[i + 2] : y4[i]) + dpp<DPP_ROR8>(send);           // + 2*b3
   }
-  float y = (b2 ? y2[1] : y2[0]) + __shfl_xor(b2 ? y2[0] : y2[1], 4, WAVE);
-  y += __shfl_xor(y, 2, WAVE);
-  y += __shfl_xor(y, 1, WAVE);
+  // row_half_mirror pairs lane i with 7 - i, whose bit 2 is the opposite one.
+  // (Each cross-lane move is evaluated unconditionally: a DPP move inside one
+  // arm of a ?: would run with the other lanes inactive and read zeros.)
+  const float send = b2 ? y2[0] : y2[1];
+  const float recv = dpp<DPP_HALF_MIRROR>(send);
+  float y = (b2 ? y2[1] : y2[0]) + recv;                              // + b2
+  y += dpp<DPP_XOR2>(y);
+  y += dpp<DPP_XOR1>(y);
   // lane l now holds the total of index l >> 2
   return __shfl(y, (lane & (CHUNK - 1)) * 4, WAVE);
 }
 
-// Inclusive suffix scan across lanes of affine maps x -> A*x + B, later lanes
-// applied first (lane i ends with F_i o F_{i+1} o ...).  Lanes past the chunk
-// carry the identity.
+// Inclusive suffix scan across the 16 lanes of each row of affine maps
+// x -> A*x + B, later lanes applied first (lane i ends with F_i o F_i+1 o
+// ...).  Lanes past the chunk carry the identity.
+template <int O>
+__device__ __forceinline__ void affine_suffix_step(float& A, float& B) {
+  const float An = dpp<DppShl<O>::v>(A);
+  const float Bn = dpp<DppShl<O>::v>(B);
+  const bool take = (lane_id() & (CHUNK - 1)) + O < CHUNK;
+  B = take ? fmaf(A, Bn, B) : B;
+  A = take ? A * An : A;
+}
 __device__ __forceinline__ void affine_suffix_scan(float& A, float& B) {
-#pragma unroll
-  for (int o = 1; o < CHUNK; o <<= 1) {
-    const float An = __shfl_down(A, o, WAVE);
-    const float Bn = __shfl_down(B, o, WAVE);
-    const bool take = lane_id() + o < WAVE;
-    B = take ? fmaf(A, Bn, B) : B;
-    A = take ? A * An : A;
-  }
+  affine_suffix_step<1>(A, B);
+  affine_suffix_step<2>(A, B);
+  affine_suffix_step<4>(A, B);
+  affine_suffix_step<8>(A, B);
 }
 
 // Loads a chunk and replays it forward from (s, m): fills the chunk's
@@ -430,13 +441,12 @@ __device__ __forceinline__ void affine_suffix_scan(float& A, float& B) {
 // partial) for the reads.  s ends as the content after the chunk.
 template <typename IO, int CPL>
 __device__ __forceinline__ void bwd_load_replay(const ScanBwdArgs& a, BwdChunk<IO, CPL>& ck,
-                                                int b, int h, int cs, int n, float (&s)[CPL],
+                                                int b, int h, float4 rec, int n, float (&s)[CPL],
                                                 float m, bool active, int c0,
                                                 float (&part)[CHUNK]) {
   const IO* vb = reinterpret_cast<const IO*>(a.v);
   const IO* ob = reinterpret_cast<const IO*>(a.d_o);
-  const IO* gb = reinterpret_cast<const IO*>(a.gamma);
-  ck.sc = chunk_scalars<IO>(a.events, a.w_w, a.w_r, gb, a.k_w, a.k_r, b, h, a.T, a.H, cs, n, true);
+  ck.sc = chunk_scalars(rec, b, h, a.T, a.H);
 #pragma unroll
   for (int i = 0; i < CHUNK; ++i) {
     ck.raw[i].r = {};
@@ -450,8 +460,8 @@ __device__ __forceinline__ void bwd_load_replay(const ScanBwdArgs& a, BwdChunk<I
   float Bm = (ck.sc.ev.side == 0) ? ck.sc.wt : 0.f;
   affine_scan(A, Bm);
   ck.mi = fmaf(A, m, Bm);
-  const float up = __shfl_up(ck.mi, 1, WAVE);
-  ck.mo = (lane_id() == 0) ? m : up;
+  const float up = dpp<DPP_SHR1>(ck.mi);
+  ck.mo = ((lane_id() & (CHUNK - 1)) == 0) ? m : up;
   ck.eta = (ck.sc.ev.side == 0 && ck.sc.wt > 0.f) ? ck.sc.wt / (ck.mi + a.eps) : 0.f;
 #pragma unroll
   for (int i = 0; i < CHUNK; ++i) {
@@ -527,8 +537,8 @@ __device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const BwdChunk
   float B = wr ? -ck.sc.lam * g * deta : 0.f;
   affine_suffix_scan(A, B);
   const float before = fmaf(A, mh, B);
-  const float after_n = __shfl_down(before, 1, WAVE);
-  const float after = (lane == WAVE - 1) ? mh : after_n;
+  const float after_n = dpp<DPP_SHL1>(before);
+  const float after = ((lane & (CHUNK - 1)) == CHUNK - 1) ? mh : after_n;
   if (wr) {
     const float M = after - g * deta;
     const float dwi = ((ck.sc.wt > 0.f) ? deta / den : 0.f) + M + M * ck.mo * ck.sc.dl;
@@ -577,15 +587,19 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
     BwdChunk<IO, CPL> ck;
     float part[CHUNK];
     int cs = max(beg, ((end - 1) / CHUNK) * CHUNK);
+    float4 rec = load_rec(a.events, cs, end - cs);
     while (true) {
       const int n = min(end, (cs / CHUNK + 1) * CHUNK) - cs;
+      const int cp = max(beg, cs - CHUNK);
       float s[CPL], m;
       chunk_state<CPL>(a, g, beg, cs, active, c0, s, m);
-      bwd_load_replay<IO, CPL>(a, ck, b, h, cs, n, s, m, active, c0, part);
+      const float4 rec_cur = rec;
+      if (cs != beg) rec = load_rec(a.events, cp, cs - cp);   // previous chunk
+      bwd_load_replay<IO, CPL>(a, ck, b, h, rec_cur, n, s, m, active, c0, part);
       bwd_walk_content<IO, CPL>(a, ck, n, sh, active, c0, part);
       bwd_scalars<IO, CPL>(a, ck, n, batched_sum(part), mh);
       if (cs == beg) break;
-      cs = max(beg, cs - CHUNK);
+      cs = cp;
     }
   }
   if (a.d_slot0 && active) {
@@ -628,25 +642,40 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
 
   BwdChunk<IO, CPL> ck;
   float part[CHUNK];
-  for (int u0 = ((nchunks - 1) / NW) * NW; u0 >= 0; u0 -= NW) {
-    const int k = u0 + w;
-    int cs = end, n = 0;
+  auto chunk_of = [&](int k, int& cs, int& n) {
+    cs = end;
+    n = 0;
     if (k < nchunks) {
       cs = chunk_start(beg, k, end);
       n = chunk_start(beg, k + 1, end) - cs;
     }
+  };
+  float4 rec;
+  {
+    int cs0, n0;
+    chunk_of(((nchunks - 1) / NW) * NW + w, cs0, n0);
+    rec = load_rec(a.events, cs0, n0);
+  }
+  for (int u0 = ((nchunks - 1) / NW) * NW; u0 >= 0; u0 -= NW) {
+    int cs, n;
+    chunk_of(u0 + w, cs, n);
     float s[CPL], m = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) s[c] = 0.f;
     if (n > 0) chunk_state<CPL>(a, g, beg, cs, active, c0, s, m);
-    bwd_load_replay<IO, CPL>(a, ck, b, h, cs, n, s, m, active, c0, part);
+    const float4 rec_cur = rec;
+    if (u0 >= NW) {   // this wave's chunk of the previous super-chunk
+      int csp, np;
+      chunk_of(u0 - NW + w, csp, np);
+      rec = load_rec(a.events, csp, np);
+    }
+    bwd_load_replay<IO, CPL>(a, ck, b, h, rec_cur, n, s, m, active, c0, part);
     // adjoint map of the chunk (reverse walk from zero); write partials
     // <q_after_i, u_i> join the read partials in part[]
     float Lp = (lane < n && ck.sc.ev.side == 0) ? ck.sc.lam : 1.f;
-#pragma unroll
-    for (int o = 1; o < CHUNK; o <<= 1) {                   // prefix products of lambda
-      const float up = __shfl_up(Lp, o, WAVE);
-      Lp = (lane >= o) ? Lp * up : Lp;
+    {                                                        // prefix products of lambda
+      float dummy = 0.f;
+      affine_scan(Lp, dummy);
     }
     const float den = ck.mi + a.eps;
     const float gq = (ck.sc.ev.side == 0 && ck.sc.wt > 0.f) ? ck.sc.wt / (den * den) : 0.f;
