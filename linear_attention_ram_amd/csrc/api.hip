@@ -14,7 +14,6 @@ using namespace ramk;
 namespace {
 
 constexpr size_t ALIGN = 256;
-constexpr int LONG_BLOCKS = 512;   // workgroups that walk the list of long segments
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Dims {
@@ -45,6 +44,11 @@ int check_problem(const ram_problem* p, Dims* d) {
   const int64_t nseg = (int64_t)p->B * p->H * S;
   if (E >= ((int64_t)1 << 31) || nseg >= ((int64_t)1 << 31) || N * p->d_v >= ((int64_t)1 << 40))
     return RAM_ECAPACITY;
+  // the scans address one batch's rows of v, dO and the stash through
+  // buffer resources of at most MAX_BUF_BYTES
+  const int64_t kmax = p->k_w > p->k_r ? p->k_w : p->k_r;
+  if ((int64_t)p->T * p->H * kmax * p->d_v * (int64_t)io > (int64_t)MAX_BUF_BYTES)
+    return RAM_ECAPACITY;
   if (d) {
     d->S = S;
     d->N = N;
@@ -58,6 +62,13 @@ int check_problem(const ram_problem* p, Dims* d) {
     d->io_bytes = io;
   }
   return RAM_OK;
+}
+
+// Entries per length class of the long-segment list: every long segment has
+// more than LONG_EVENTS events.
+int long_cap(const Dims& d) {
+  const int64_t c = d.E / (LONG_EVENTS + 1) + 1;
+  return (int)(c < d.nseg ? c : d.nseg);
 }
 
 void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
@@ -75,8 +86,8 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   L->ckpt_m = take(sizeof(float) * d.nck);
   L->stash = take(d.io_bytes * d.N * (p->k_w > p->k_r ? p->k_w : p->k_r) * p->d_v);
   L->tile_hist = take(sizeof(int32_t) * (size_t)p->B * p->H * d.ntiles * d.S);
-  L->long_list = take(sizeof(int32_t) * (d.E / (LONG_EVENTS + 1) + 1));
-  L->long_count = take(sizeof(int32_t));
+  L->long_list = take(sizeof(int32_t) * NBIN * long_cap(d));
+  L->long_count = take(sizeof(int32_t) * NBIN);
   L->fwd_bytes = off;
   L->dw = take(sizeof(float) * d.N * p->k_w);
   L->dr = take(sizeof(float) * d.N * p->k_r);
@@ -246,6 +257,7 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   ba.events = (EventRec*)(w + L.events);
   ba.long_list = (int32_t*)(w + L.long_list);
   ba.long_count = (int32_t*)(w + L.long_count);
+  ba.long_cap = long_cap(d);
   e = launch_bucket(ba, bf, s, prof_before, prof_after);
   if (e != hipSuccess) return RAM_EHIP;
 
@@ -261,8 +273,8 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   sa.nseg = d.nseg;
   sa.long_list = ba.long_list;
   sa.long_count = ba.long_count;
+  sa.long_cap = ba.long_cap;
   sa.use_long = d.ntiles > 0;
-  sa.long_blocks = LONG_BLOCKS;
   sa.seg_offset = ba.seg_offset;
   sa.events = ba.events;
   sa.v = v;
@@ -326,8 +338,8 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   sb.nseg = d.nseg;
   sb.long_list = (const int32_t*)(w + L.long_list);
   sb.long_count = (const int32_t*)(w + L.long_count);
+  sb.long_cap = long_cap(d);
   sb.use_long = d.ntiles > 0;
-  sb.long_blocks = LONG_BLOCKS;
   sb.seg_offset = (const int32_t*)(w + L.seg_offset);
   sb.events = (const EventRec*)(w + L.events);
   sb.v = v;

@@ -8,7 +8,8 @@
 //   scan     one block per (b, h): per slot, exclusive prefix of the tile
 //            counts (in place) and, over the slots in blocks of 1024, the
 //            segment offsets; segments with more than LONG_EVENTS events
-//            are listed for the cooperative scan path (in any order).
+//            are listed for the cooperative scan path, in NBIN classes of
+//            doubling length (any order inside a class).
 //            Every (b, h) holds exactly T*(k_w+k_r) events, so segment
 //            offsets need no scan across (b, h);
 //   scatter  one wave per (b, h, tile): walks the tile's events in order
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(256) void bucket_hist_kernel(BucketArgs a) {
   const int t_lo = tile * TILE_TOKENS;
   const int t_hi = min(a.T, t_lo + TILE_TOKENS);
   for (int s = threadIdx.x; s < a.S; s += blockDim.x) hist[s] = 0;
-  if (tile == 0 && bh == 0 && threadIdx.x == 0) *a.long_count = 0;
+  if (tile == 0 && bh == 0 && threadIdx.x < NBIN) a.long_count[threadIdx.x] = 0;
   __syncthreads();
   const int n = (t_hi - t_lo) * K;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
@@ -81,7 +82,12 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketArgs a) {
     }
     if (s < S) {
       a.seg_offset[(int64_t)bh * S + s] = (int32_t)(base + before + incl - cnt);
-      if (cnt > LONG_EVENTS) a.long_list[atomicAdd(a.long_count, 1)] = (int32_t)((int64_t)bh * S + s);
+      if (cnt > LONG_EVENTS) {
+        const int q = cnt / (LONG_EVENTS + 1);            // >= 1
+        const int cls = min(NBIN - 1, 31 - __clz(q));
+        a.long_list[(int64_t)cls * a.long_cap + atomicAdd(&a.long_count[cls], 1)] =
+            (int32_t)((int64_t)bh * S + s);
+      }
     }
     carry += all;
     __syncthreads();

@@ -85,6 +85,13 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
+// Same move, but a lane whose source lane lies outside its row keeps `old`
+// (row shifts: the lanes at the row's edge).
+template <int CTRL>
+__device__ __forceinline__ float dpp_or(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL,
+                                                    0xF, 0xF, false));
+}
 constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
 constexpr int DPP_ROR8 = 0x128, DPP_SHL1 = 0x101, DPP_SHL4 = 0x104, DPP_SHR1 = 0x111;
 constexpr int DPP_SHR4 = 0x114;

@@ -7,10 +7,13 @@ namespace ramk {
 
 constexpr int CHUNK = 16;        // scan chunk: checkpoints at 16-aligned events
 constexpr int TILE_TOKENS = 256; // tokens per bucketing tile
-constexpr int NW = 16;           // waves per forward scan workgroup
-constexpr int NWB = 8;           // waves per reverse long-segment workgroup
+constexpr int NWL = 8;           // waves per scan workgroup (one long segment, or NWL short ones)
 constexpr int LONG_EVENTS = 128; // segments with more events take the cooperative path
+constexpr int NBIN = 8;          // length classes of the long-segment list: class c holds
+                                 // segments of [129 * 2^c, 129 * 2^(c+1)) events (the last
+                                 // class is open-ended); scans take the longest first
 constexpr int MAX_DV = 128;      // widest slot
+constexpr uint32_t MAX_BUF_BYTES = 0x7FE00000u;  // one batch's v, dO or stash rows (scans)
 
 // One event of the segment lists: 16 bytes, read with one vector load.
 struct EventRec {
@@ -32,18 +35,19 @@ struct BucketArgs {
   int32_t* tile_hist;     // (B*H, ntiles, S)
   int32_t* seg_offset;    // (B*H*S + 1)
   EventRec* events;       // (E)
-  int32_t* long_list;     // segments with more than LONG_EVENTS events
-  int32_t* long_count;    // their number
+  int32_t* long_list;     // (NBIN, long_cap): segments with more than LONG_EVENTS events
+  int32_t* long_count;    // (NBIN): entries per class
+  int long_cap;
 };
 
 struct ScanFwdArgs {
   int B, H, T, S, d_v, k_w, k_r;
   float eps;
   int64_t nseg;
-  const int32_t* long_list;
-  const int32_t* long_count;
+  const int32_t* long_list;   // (NBIN, long_cap)
+  const int32_t* long_count;  // (NBIN)
+  int long_cap;
   int use_long;           // long_list / long_count are valid
-  int long_blocks;        // workgroups that walk the long list
   const int32_t* seg_offset;
   const EventRec* events;
   const void* v;          // (N, d_v) io
@@ -62,8 +66,8 @@ struct ScanBwdArgs {
   int64_t nseg;
   const int32_t* long_list;
   const int32_t* long_count;
+  int long_cap;
   int use_long;
-  int long_blocks;
   const int32_t* seg_offset;
   const EventRec* events;
   const void* v;          // io

@@ -7,20 +7,38 @@
 // [l*CPL, l*CPL + CPL).  Events are taken in chunks of up to CHUNK = 16 that
 // are aligned to multiples of 16 in the global event list; the state before
 // every aligned event inside a segment is saved as a checkpoint for the
-// reverse pass.  Inside a chunk:
-//   * lane i loads event record i (code, weight, retention); the mass recurrence
-//     m <- lambda*m + w is affine, so one inclusive scan of (lambda, w) pairs
-//     across lanes gives every event's mass, then eta_i = w_i / (m_i + eps);
-//   * the chunk's v rows are loaded together and the content chain
-//     s <- (1-eta)*s + eta*v runs event by event; a read stores its
-//     contribution r*s, in the io dtype, to its own (token, j) row of a stash.
-//     A token-major pass later sums the K rows of each token.  No atomics:
-//     the read-out scatter is plain stores.
+// reverse pass.
+//
+// Lane layout of a chunk.  Lane l also holds the scalars of event (l & 15):
+// the four 16-lane rows of the wave carry identical copies, so the DPP
+// row_newbcast:i move hands every lane the scalars of event i without a trip
+// through a scalar register, and every per-row DPP scan or reduction sees all
+// 16 events.  Lanes past the chunk's end hold a read of weight 0.
+//
+// Branch-free event loops.  Every event runs the same straight-line code:
+// a write has step size eta and read weight 0, a read the reverse, and the
+// row loads and stores go through buffer resources whose range check turns
+// an offset of OOB into a load of zero or a dropped store.  Reads therefore
+// load nothing, writes store nothing in the forward, and padded events do
+// neither.
+//
+// Inside a chunk:
+//   * the mass recurrence m <- lambda*m + w is affine, so one inclusive scan
+//     of (lambda, w) pairs across each row gives every event's mass, then
+//     eta_i = w_i / (m_i + eps);
+//   * the content chain s <- (1-eta)*s + eta*v runs event by event (eta = 1
+//     replaces the content exactly); a read
+//     stores its contribution r*s, in the io dtype, to its own (token, j) row
+//     of a stash.  A token-major pass later sums the K rows of each token.
+//     No atomics: the read-out scatter is plain stores.
 // Short segments (<= LONG_EVENTS events) take one wave each.  Long segments
-// (hot slots) take a workgroup of NW waves that advance NW chunks at a time:
-// each wave forms its chunk's mass map and, once its incoming mass is known,
-// its content map s -> P*s + b (computed from s = 0); the maps are combined
-// through LDS, then each wave replays its chunk from its true start state.
+// (hot slots) take a workgroup of NWL waves that advance NWL chunks at a
+// time: each wave forms its chunk's mass map and, once its incoming mass is
+// known, its content map s -> P*s + b (computed from s = 0); the maps are
+// combined through LDS, then each wave replays its chunk from its true start
+// state.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,67 +46,182 @@ namespace ramk {
 
 namespace {
 
-// CPL io values of one row slice, loaded or stored with one instruction.
-template <typename IO, int CPL> struct Slice;
-template <> struct Slice<bf16_t, 1> {
-  uint16_t r;
-  __device__ __forceinline__ void load(const bf16_t* p) { r = *p; }
-  __device__ __forceinline__ void get(float (&f)[1]) const { f[0] = to_f32((bf16_t)r); }
-  static __device__ __forceinline__ void store(bf16_t* p, const float (&f)[1]) {
-    *p = from_f32<bf16_t>(f[0]);
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Byte offsets that fall outside every buffer (load 0, drop the store).  An
+// access offset is event offset + lane offset; buffers hold at most
+// MAX_BUF_BYTES (checked on the host), and the two sentinels are chosen so
+// that no sum wraps around 2^32:
+//   OOB (event): + a lane offset < 2^20 stays in [OOB, 2^31)
+//   OOB_LANE:    + an event offset < 2^31 stays in [2^31, 2^32)
+constexpr uint32_t OOB = 0x7FF00000u;
+constexpr uint32_t OOB_LANE = 0x80000000u;
+static_assert(OOB >= MAX_BUF_BYTES, "event sentinel inside a buffer");
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Raw buffer of `bytes` bytes (<= MAX_BUF_BYTES) at base.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Index of the wave in its workgroup, as a value the compiler knows to be
+// uniform (buffer resources built from it stay in scalar registers).
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE));
+}
+
+// Value of event I of the lane's row (DPP row_newbcast:I).
+template <int I>
+__device__ __forceinline__ float bc(float x) { return dpp<0x150 + I>(x); }
+template <int I>
+__device__ __forceinline__ uint32_t bcu(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x150 + I, 0xF, 0xF, true);
+}
+
+// Compile-time loops over the events of a chunk.
+template <int I, int N, typename F>
+__device__ __forceinline__ void for_up(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    for_up<I + 1, N>(f);
+  }
+}
+template <int I, typename F>
+__device__ __forceinline__ void for_down(F&& f) {   // I-1, I-2, ..., 0
+  if constexpr (I > 0) {
+    f(std::integral_constant<int, I - 1>());
+    for_down<I - 1>(f);
+  }
+}
+
+// CPL io values of one row slice at a byte offset of a buffer.
+template <typename IO, int CPL> struct Lanes;
+template <> struct Lanes<bf16_t, 1> {
+  typedef uint32_t Raw;
+  static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+  static __device__ __forceinline__ void get(Raw x, float (&f)[1]) { f[0] = __uint_as_float(x << 16); }
+  static __device__ __forceinline__ Raw merge(Raw a, Raw b) { return a | b; }
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[1]) {
+    const f32x2_t x = {f[0], 0.f};
+    const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)u, r, off, 0, 0);
   }
 };
-template <> struct Slice<bf16_t, 2> {
-  uint32_t r;
-  __device__ __forceinline__ void load(const bf16_t* p) { r = *reinterpret_cast<const uint32_t*>(p); }
-  __device__ __forceinline__ void get(float (&f)[2]) const {
-    f[0] = __uint_as_float(r << 16);
-    f[1] = __uint_as_float(r & 0xffff0000u);
+template <> struct Lanes<bf16_t, 2> {
+  typedef uint32_t Raw;
+  static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
-  static __device__ __forceinline__ void store(bf16_t* p, const float (&f)[2]) {
-    *reinterpret_cast<uint32_t*>(p) = pack2bf(f[0], f[1]);
+  static __device__ __forceinline__ void get(Raw x, float (&f)[2]) {
+    f[0] = __uint_as_float(x << 16);
+    f[1] = __uint_as_float(x & 0xffff0000u);
+  }
+  static __device__ __forceinline__ Raw merge(Raw a, Raw b) { return a | b; }
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[2]) {
+    const f32x2_t x = {f[0], f[1]};
+    __builtin_amdgcn_raw_buffer_store_b32(
+        __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t)), r, off, 0, 0);
   }
 };
-template <> struct Slice<float, 1> {
-  float r;
-  __device__ __forceinline__ void load(const float* p) { r = *p; }
-  __device__ __forceinline__ void get(float (&f)[1]) const { f[0] = r; }
-  static __device__ __forceinline__ void store(float* p, const float (&f)[1]) { *p = f[0]; }
+template <> struct Lanes<float, 1> {
+  typedef uint32_t Raw;
+  static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  static __device__ __forceinline__ void get(Raw x, float (&f)[1]) { f[0] = __uint_as_float(x); }
+  static __device__ __forceinline__ Raw merge(Raw a, Raw b) { return a | b; }
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[1]) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f[0]), r, off, 0, 0);
+  }
 };
-template <> struct Slice<float, 2> {
-  float2 r;
-  __device__ __forceinline__ void load(const float* p) { r = *reinterpret_cast<const float2*>(p); }
-  __device__ __forceinline__ void get(float (&f)[2]) const { f[0] = r.x; f[1] = r.y; }
-  static __device__ __forceinline__ void store(float* p, const float (&f)[2]) {
-    *reinterpret_cast<float2*>(p) = make_float2(f[0], f[1]);
+template <> struct Lanes<float, 2> {
+  typedef uint2 Raw;
+  static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v[0], v[1]);
+  }
+  static __device__ __forceinline__ void get(Raw x, float (&f)[2]) {
+    f[0] = __uint_as_float(x.x);
+    f[1] = __uint_as_float(x.y);
+  }
+  static __device__ __forceinline__ Raw merge(Raw a, Raw b) { return make_uint2(a.x | b.x, a.y | b.y); }
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[2]) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = {__float_as_uint(f[0]), __float_as_uint(f[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
   }
 };
 
-struct EventInfo {
-  int row;    // token row (b*T + t)*H + h
-  int side;   // 0 write, 1 read
-  int j;      // rank inside the side's top-K
+// Where a segment's lanes read and write: buffers of its batch b, the lane's
+// byte offset inside a row (OOB for lanes past d_v) and the row pitch.
+template <typename IO, int CPL>
+struct SegCtx {
+  int b, h;
+  int c0;             // first channel of the lane
+  bool active;        // c0 < d_v
+  uint32_t lb;        // c0 * sizeof(IO), or OOB_LANE
+  uint32_t pitch;     // d_v * sizeof(IO)
+  int64_t row0;       // first token row of batch b: b * T * H
 };
 
-__device__ __forceinline__ EventInfo decode_event(int code, int b, int h, int T, int H) {
-  EventInfo e;
-  const int t = code >> 7;
+template <typename IO, int CPL>
+__device__ __forceinline__ SegCtx<IO, CPL> seg_ctx(int64_t g, int S, int H, int T, int d_v) {
+  SegCtx<IO, CPL> c;
+  const int64_t bh = g / S;
+  c.b = (int)(bh / H);
+  c.h = (int)(bh % H);
+  c.c0 = lane_id() * CPL;
+  c.active = c.c0 < d_v;
+  c.lb = c.active ? (uint32_t)(c.c0 * sizeof(IO)) : OOB_LANE;
+  c.pitch = (uint32_t)(d_v * sizeof(IO));
+  c.row0 = (int64_t)c.b * T * H;
+  return c;
+}
+
+// Scalars of event (lane & 15) of a chunk.
+struct Ev {
+  bool valid;   // the chunk has this event
+  int side;     // 0 write, 1 read (padding: read of weight 0)
+  int rb;       // token row inside the batch: t*H + h
+  int j;        // rank inside the side's top-K
+  float wt;     // write weight or read weight
+  float lam;    // retention (writes), 1 for reads
+  float dl;     // d lambda / d w (writes), 0 for reads
+};
+
+// Record of event cs + (lane & 15) for (lane & 15) < n; issued early so the
+// next chunk's records arrive while the current chunk computes.
+__device__ __forceinline__ float4 load_rec(const EventRec* events, int cs, int n) {
+  const int i = lane_id() & (CHUNK - 1);
+  return (i < n) ? *reinterpret_cast<const float4*>(events + cs + i)
+                 : make_float4(__int_as_float(1 << 6), 0.f, 1.f, 0.f);
+}
+
+__device__ __forceinline__ Ev decode_rec(float4 r, int n, int h, int H) {
+  Ev e;
+  const int code = __float_as_int(r.x);
+  e.valid = (lane_id() & (CHUNK - 1)) < n;
   e.side = (code >> 6) & 1;
   e.j = code & 63;
-  e.row = (int)(((int64_t)b * T + t) * H + h);
+  e.rb = (code >> 7) * H + h;
+  e.wt = r.y;
+  e.lam = r.z;
+  e.dl = r.w;
   return e;
 }
 
-// Inclusive scan across the CHUNK = 16 lanes of each row of affine maps
-// x -> A*x + B (earlier lanes applied first), with DPP row shifts.  Lanes
-// past the chunk carry the identity.
+// Inclusive scan across the 16 lanes of each row of affine maps x -> A*x + B
+// (earlier lanes applied first), with DPP row shifts; the first O lanes of a
+// row receive the identity map (A, B finite).
 template <int O>
 __device__ __forceinline__ void affine_step(float& A, float& B) {
-  const float Ap = dpp<DppShr<O>::v>(A);
-  const float Bp = dpp<DppShr<O>::v>(B);
-  const bool take = (lane_id() & (CHUNK - 1)) >= O;
-  B = take ? fmaf(A, Bp, B) : B;
-  A = take ? A * Ap : A;
+  const float Ap = dpp_or<DppShr<O>::v>(1.f, A);
+  const float Bp = dpp_or<DppShr<O>::v>(0.f, B);
+  B = fmaf(A, Bp, B);
+  A = A * Ap;
 }
 __device__ __forceinline__ void affine_scan(float& A, float& B) {
   static_assert(CHUNK == 16, "scans are written for rows of 16 lanes");
@@ -98,298 +231,38 @@ __device__ __forceinline__ void affine_scan(float& A, float& B) {
   affine_step<8>(A, B);
 }
 
-// Per-event scalars of one chunk: lane i < n holds event cs + i.
-struct ChunkScalars {
-  EventInfo ev;
-  float wt;   // write weight or read weight
-  float lam;  // retention (writes), 1 for reads
-  float dl;   // d lambda / d w (writes), 0 for reads
-};
-
-// Event record cs + lane for lanes < n (one 16-byte load; issued early so
-// the next chunk's records arrive while the current chunk computes).
-__device__ __forceinline__ float4 load_rec(const EventRec* events, int cs, int n) {
-  return (lane_id() < n) ? *reinterpret_cast<const float4*>(events + cs + lane_id())
-                         : make_float4(__int_as_float(1 << 6), 0.f, 1.f, 0.f);
+// Inclusive suffix scan of the same maps, later lanes applied first (lane i
+// ends with F_i o F_i+1 o ... o F_15).
+template <int O>
+__device__ __forceinline__ void affine_suffix_step(float& A, float& B) {
+  const float An = dpp_or<DppShl<O>::v>(1.f, A);
+  const float Bn = dpp_or<DppShl<O>::v>(0.f, B);
+  B = fmaf(A, Bn, B);
+  A = A * An;
+}
+__device__ __forceinline__ void affine_suffix_scan(float& A, float& B) {
+  affine_suffix_step<1>(A, B);
+  affine_suffix_step<2>(A, B);
+  affine_suffix_step<4>(A, B);
+  affine_suffix_step<8>(A, B);
 }
 
-__device__ __forceinline__ ChunkScalars chunk_scalars(float4 r, int b, int h, int T, int H) {
-  ChunkScalars c;
-  c.ev = decode_event(__float_as_int(r.x), b, h, T, H);
-  c.wt = r.y;
-  c.lam = r.z;
-  c.dl = r.w;
-  return c;
+// Product of x over the 16 lanes of each row (every lane gets it).
+__device__ __forceinline__ float row_prod(float x) {
+  x *= dpp<DPP_XOR1>(x);
+  x *= dpp<DPP_XOR2>(x);
+  x *= dpp<DPP_HALF_MIRROR>(x);
+  return x * dpp<DPP_MIRROR>(x);
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<DPP_XOR1>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_HALF_MIRROR>(x);
+  return x + dpp<DPP_MIRROR>(x);
 }
 
-// Start of chunk k of the chunk sequence that begins at position p (p is the
-// segment start or a multiple of CHUNK), clamped to end.
-__device__ __forceinline__ int chunk_start(int p, int k, int end) {
-  if (k == 0) return min(p, end);
-  return min(end, (p / CHUNK + k) * CHUNK);
-}
-
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// forward
-// ---------------------------------------------------------------------------
-
-template <typename IO, int CPL>
-__device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
-  const int lane = lane_id();
-  const int64_t bh = g / a.S;
-  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-  const int c0 = lane * CPL;
-  const bool active = c0 < a.d_v;
-  const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
-  const IO* vb = reinterpret_cast<const IO*>(a.v);
-  IO* stash = reinterpret_cast<IO*>(a.stash);
-
-  float s[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) s[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
-  float m = a.mass0 ? a.mass0[g] : 0.f;
-
-  float4 rec = load_rec(a.events, beg, min(end, (beg / CHUNK + 1) * CHUNK) - beg);
-  for (int p0 = beg; p0 < end;) {
-    const int p1 = min(end, (p0 / CHUNK + 1) * CHUNK);
-    const int n = p1 - p0;
-    if (p0 != beg) {
-      float* ck = a.ckpt_s + (int64_t)(p0 / CHUNK) * a.d_v;
-      if (active) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) ck[c0 + c] = s[c];
-      }
-      if (lane == 0) a.ckpt_m[p0 / CHUNK] = m;
-    }
-    const ChunkScalars cs = chunk_scalars(rec, b, h, a.T, a.H);
-    float A = (cs.ev.side == 0) ? cs.lam : 1.f;
-    float Bm = (cs.ev.side == 0) ? cs.wt : 0.f;
-    affine_scan(A, Bm);
-    const float mi = fmaf(A, m, Bm);
-    const float eta = (cs.ev.side == 0 && cs.wt > 0.f) ? cs.wt / (mi + a.eps) : 0.f;
-    m = readlane_f(mi, n - 1);
-
-    Slice<IO, CPL> raw[CHUNK];
-#pragma unroll
-    for (int i = 0; i < CHUNK; ++i) {
-      raw[i].r = {};
-      if (i < n) {
-        const int si = readlane_i(cs.ev.side, i);
-        const int64_t ri = readlane_i(cs.ev.row, i);
-        if (si == 0 && active) raw[i].load(vb + ri * a.d_v + c0);
-      }
-    }
-    rec = load_rec(a.events, p1, min(end, (p1 / CHUNK + 1) * CHUNK) - p1);   // next chunk
-#pragma unroll
-    for (int i = 0; i < CHUNK; ++i) {
-      if (i < n) {
-        if (readlane_i(cs.ev.side, i) == 0) {
-          const float e = readlane_f(eta, i);
-          float vv[CPL];
-          raw[i].get(vv);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) s[c] = fmaf(1.f - e, s[c], e * vv[c]);
-        } else {
-          const float r = readlane_f(cs.wt, i);
-          const int64_t slot_row = (int64_t)readlane_i(cs.ev.row, i) * a.k_r + readlane_i(cs.ev.j, i);
-          float contrib[CPL];
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) contrib[c] = r * s[c];
-          if (active) Slice<IO, CPL>::store(stash + slot_row * a.d_v + c0, contrib);
-        }
-      }
-    }
-    p0 = p1;
-  }
-  if (active) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) a.slot1[g * a.d_v + c0 + c] = s[c];
-  }
-  if (lane == 0) a.mass1[g] = m;
-}
-
-template <typename IO, int CPL>
-__device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
-  __shared__ float mapA[NW], mapB[NW], mapP[NW];
-  __shared__ float mapb[NW][MAX_DV];
-  const int lane = lane_id();
-  const int w = threadIdx.x / WAVE;
-  const int64_t bh = g / a.S;
-  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-  const int c0 = lane * CPL;
-  const bool active = c0 < a.d_v;
-  const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
-  const IO* vb = reinterpret_cast<const IO*>(a.v);
-  IO* stash = reinterpret_cast<IO*>(a.stash);
-
-  float s_carry[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c)
-    s_carry[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
-  float m_carry = a.mass0 ? a.mass0[g] : 0.f;
-
-  float4 rec = load_rec(a.events, chunk_start(beg, w, end),
-                        chunk_start(beg, w + 1, end) - chunk_start(beg, w, end));
-  for (int p = beg; p < end;) {
-    const int cs = chunk_start(p, w, end);
-    const int n = chunk_start(p, w + 1, end) - cs;
-    const int pn = chunk_start(p, NW, end);
-    const ChunkScalars sc = chunk_scalars(rec, b, h, a.T, a.H);
-    float A = (sc.ev.side == 0) ? sc.lam : 1.f;
-    float Bm = (sc.ev.side == 0) ? sc.wt : 0.f;
-    affine_scan(A, Bm);
-    // cross-lane reads stay outside lane-dependent branches
-    const float A_tot = readlane_f(A, max(n, 1) - 1);
-    const float B_tot = readlane_f(Bm, max(n, 1) - 1);
-    if (lane == 0) {
-      mapA[w] = n > 0 ? A_tot : 1.f;
-      mapB[w] = n > 0 ? B_tot : 0.f;
-    }
-    // content loads do not depend on the mass: issue them before the barrier
-    Slice<IO, CPL> raw[CHUNK];
-#pragma unroll
-    for (int i = 0; i < CHUNK; ++i) {
-      raw[i].r = {};
-      if (i < n) {
-        const int si = readlane_i(sc.ev.side, i);
-        const int64_t ri = readlane_i(sc.ev.row, i);
-        if (si == 0 && active) raw[i].load(vb + ri * a.d_v + c0);
-      }
-    }
-    if (pn < end)   // next super-chunk's records for this wave
-      rec = load_rec(a.events, chunk_start(pn, w, end),
-                     chunk_start(pn, w + 1, end) - chunk_start(pn, w, end));
-    __syncthreads();
-    float m_in = m_carry, m_next = m_carry;
-    for (int k = 0; k < NW; ++k) {
-      if (k == w) m_in = m_next;
-      m_next = fmaf(mapA[k], m_next, mapB[k]);
-    }
-    const float mi = fmaf(A, m_in, Bm);
-    const float eta = (sc.ev.side == 0 && sc.wt > 0.f) ? sc.wt / (mi + a.eps) : 0.f;
-    // content map of the chunk from a zero start
-    float sz[CPL], P = 1.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) sz[c] = 0.f;
-#pragma unroll
-    for (int i = 0; i < CHUNK; ++i) {
-      if (i < n && readlane_i(sc.ev.side, i) == 0) {
-        const float e = readlane_f(eta, i);
-        float vv[CPL];
-        raw[i].get(vv);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) sz[c] = fmaf(1.f - e, sz[c], e * vv[c]);
-        P *= 1.f - e;
-      }
-    }
-    if (active) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) mapb[w][c0 + c] = sz[c];
-    }
-    if (lane == 0) mapP[w] = P;
-    __syncthreads();
-    float s[CPL], s_next[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) s_next[c] = s_carry[c];
-    for (int k = 0; k < NW; ++k) {
-      const float Pk = mapP[k];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        if (k == w) s[c] = s_next[c];
-        s_next[c] = fmaf(Pk, s_next[c], active ? mapb[k][c0 + c] : 0.f);
-      }
-    }
-    if (n > 0 && cs != beg) {
-      float* ck = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
-      if (active) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) ck[c0 + c] = s[c];
-      }
-      if (lane == 0) a.ckpt_m[cs / CHUNK] = m_in;
-    }
-    // replay from the true start state; reads store their contributions
-#pragma unroll
-    for (int i = 0; i < CHUNK; ++i) {
-      if (i < n) {
-        if (readlane_i(sc.ev.side, i) == 0) {
-          const float e = readlane_f(eta, i);
-          float vv[CPL];
-          raw[i].get(vv);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) s[c] = fmaf(1.f - e, s[c], e * vv[c]);
-        } else {
-          const float r = readlane_f(sc.wt, i);
-          const int64_t slot_row = (int64_t)readlane_i(sc.ev.row, i) * a.k_r + readlane_i(sc.ev.j, i);
-          float contrib[CPL];
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) contrib[c] = r * s[c];
-          if (active) Slice<IO, CPL>::store(stash + slot_row * a.d_v + c0, contrib);
-        }
-      }
-    }
-    m_carry = m_next;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) s_carry[c] = s_next[c];
-    p = pn;
-    __syncthreads();
-  }
-  if (w == 0) {
-    if (active) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) a.slot1[g * a.d_v + c0 + c] = s_carry[c];
-    }
-    if (lane == 0) a.mass1[g] = m_carry;
-  }
-}
-
-// Blocks [0, long_blocks) walk the list of long segments; every other block
-// takes NW consecutive segments, one per wave, and skips the long ones.
-template <typename IO, int CPL>
-__global__ __launch_bounds__(NW * WAVE) void scan_fwd_kernel(ScanFwdArgs a) {
-  if ((int)blockIdx.x < a.long_blocks) {
-    const int count = a.use_long ? *a.long_count : 0;
-    for (int i = blockIdx.x; i < count; i += a.long_blocks)
-      scan_fwd_long<IO, CPL>(a, a.long_list[i]);
-    return;
-  }
-  const int64_t g = ((int64_t)blockIdx.x - a.long_blocks) * NW + threadIdx.x / WAVE;
-  if (g >= a.nseg) return;
-  if (a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS) return;
-  scan_fwd_short<IO, CPL>(a, g);
-}
-
-// ---------------------------------------------------------------------------
-// reverse
-// ---------------------------------------------------------------------------
-//
-// Per chunk: restart from its checkpoint (or the initial state), replay the
-// events forward to recover the content before every write, then walk the
-// events backwards with the content adjoint s_hat:
-//   read  (weight r):  s_hat += r * dO_t;               dr   = <dO_t, s>
-//   write (w, gamma):  dv_t += eta * s_hat (io stash);  deta = <s_hat, v_t - s_old>;
-//                      s_hat <- (1 - eta) s_hat
-// The inner products are accumulated lane-locally for all events of the
-// chunk and summed in one batched transpose-reduction.  The mass adjoint
-// then follows m_hat_before = lambda * (m_hat_after - g * deta), with
-// g = w / (m' + eps)^2, which is affine in m_hat: an inclusive suffix scan
-// across lanes gives it for every event at once, and each lane forms
-//   M = m_hat_after - g * deta
-//   dw = deta / (m' + eps) + M + M * m_old * dlambda/dw
-//   dgamma part = M * m_old * (-lambda (1 - lambda))
-// for its own event and stores it.
-
-template <typename IO, int CPL>
-struct BwdChunk {
-  ChunkScalars sc;
-  float mi, mo, eta;       // mass after / before the event, step size
-  Slice<IO, CPL> raw[CHUNK];
-  float so[CHUNK][CPL];    // content before each write
-};
-
-// Sums x[i] over the 64 lanes for every i < CHUNK; lane i < CHUNK receives
-// the total of index i.  Each halving step exchanges the half of the values a
+// Sums x[i] over the 64 lanes for every i < CHUNK; lane l receives the total
+// of index l & 15.  Each halving step exchanges the half of the values a
 // lane does not keep (permlane swaps across rows, DPP inside rows), so 16
 // sums cost 15 cross-lane moves plus one final gather.
 __device__ __forceinline__ float batched_sum(const float (&x)[CHUNK]) {
@@ -414,234 +287,522 @@ __device__ __forceinline__ float batched_sum(const float (&x)[CHUNK]) {
   float y = (b2 ? y2[1] : y2[0]) + recv;                              // + b2
   y += dpp<DPP_XOR2>(y);
   y += dpp<DPP_XOR1>(y);
-  // lane l now holds the total of index l >> 2
+  // lane l (of each row) now holds the total of index (l & 15) >> 2
   return __shfl(y, (lane & (CHUNK - 1)) * 4, WAVE);
 }
 
-// Inclusive suffix scan across the 16 lanes of each row of affine maps
-// x -> A*x + B, later lanes applied first (lane i ends with F_i o F_i+1 o
-// ...).  Lanes past the chunk carry the identity.
-template <int O>
-__device__ __forceinline__ void affine_suffix_step(float& A, float& B) {
-  const float An = dpp<DppShl<O>::v>(A);
-  const float Bn = dpp<DppShl<O>::v>(B);
-  const bool take = (lane_id() & (CHUNK - 1)) + O < CHUNK;
-  B = take ? fmaf(A, Bn, B) : B;
-  A = take ? A * An : A;
-}
-__device__ __forceinline__ void affine_suffix_scan(float& A, float& B) {
-  affine_suffix_step<1>(A, B);
-  affine_suffix_step<2>(A, B);
-  affine_suffix_step<4>(A, B);
-  affine_suffix_step<8>(A, B);
+// Start of chunk k of the chunk sequence that begins at position p (p is the
+// segment start or a multiple of CHUNK), clamped to end.
+__device__ __forceinline__ int chunk_start(int p, int k, int end) {
+  if (k == 0) return min(p, end);
+  return min(end, (p / CHUNK + k) * CHUNK);
 }
 
-// Loads a chunk and replays it forward from (s, m): fills the chunk's
-// scalars, rows and pre-write contents, and part[i] = <dO_i, s> (lane-local
-// partial) for the reads.  s ends as the content after the chunk.
-template <typename IO, int CPL>
-__device__ __forceinline__ void bwd_load_replay(const ScanBwdArgs& a, BwdChunk<IO, CPL>& ck,
-                                                int b, int h, float4 rec, int n, float (&s)[CPL],
-                                                float m, bool active, int c0,
-                                                float (&part)[CHUNK]) {
-  const IO* vb = reinterpret_cast<const IO*>(a.v);
-  const IO* ob = reinterpret_cast<const IO*>(a.d_o);
-  ck.sc = chunk_scalars(rec, b, h, a.T, a.H);
-#pragma unroll
-  for (int i = 0; i < CHUNK; ++i) {
-    ck.raw[i].r = {};
-    if (i < n) {
-      const IO* src = (readlane_i(ck.sc.ev.side, i) == 0) ? vb : ob;
-      const int64_t ri = readlane_i(ck.sc.ev.row, i);
-      if (active) ck.raw[i].load(src + ri * a.d_v + c0);
-    }
+// Entry i of the long-segment list, longest class first.
+__device__ __forceinline__ int64_t long_entry(const int32_t* list, const int32_t* count, int cap,
+                                              int i) {
+  for (int c = NBIN - 1; c >= 0; --c) {
+    const int n = count[c];
+    if (i < n) return list[(int64_t)c * cap + i];
+    i -= n;
   }
-  float A = (ck.sc.ev.side == 0) ? ck.sc.lam : 1.f;
-  float Bm = (ck.sc.ev.side == 0) ? ck.sc.wt : 0.f;
-  affine_scan(A, Bm);
-  ck.mi = fmaf(A, m, Bm);
-  const float up = dpp<DPP_SHR1>(ck.mi);
-  ck.mo = ((lane_id() & (CHUNK - 1)) == 0) ? m : up;
-  ck.eta = (ck.sc.ev.side == 0 && ck.sc.wt > 0.f) ? ck.sc.wt / (ck.mi + a.eps) : 0.f;
+  return -1;
+}
+__device__ __forceinline__ int long_total(const int32_t* count) {
+  int n = 0;
 #pragma unroll
-  for (int i = 0; i < CHUNK; ++i) {
-    part[i] = 0.f;
-    if (i < n) {
-      float x[CPL];
-      ck.raw[i].get(x);
-      if (readlane_i(ck.sc.ev.side, i) == 0) {
-        const float e = readlane_f(ck.eta, i);
+  for (int c = 0; c < NBIN; ++c) n += count[c];
+  return n;
+}
+
+// Per-event mass of a chunk from the incoming mass m: mi after the event,
+// mo before it, and the write step size eta (0 for reads and padding).
+struct Mass {
+  float A, B;     // inclusive affine prefix of the chunk's mass maps
+  float mi, mo, eta;
+  float keep;     // 1 - eta
+};
+__device__ __forceinline__ Mass mass_prefix(const Ev& ev) {
+  Mass M;
+  M.A = (ev.side == 0) ? ev.lam : 1.f;
+  M.B = (ev.side == 0) ? ev.wt : 0.f;
+  affine_scan(M.A, M.B);
+  return M;
+}
+__device__ __forceinline__ void mass_apply(Mass& M, const Ev& ev, float m, float eps) {
+  M.mi = fmaf(M.A, m, M.B);
+  M.mo = dpp_or<DPP_SHR1>(m, M.mi);   // lane 0 of a row: the incoming mass
+  M.eta = (ev.side == 0 && ev.wt > 0.f) ? ev.wt / (M.mi + eps) : 0.f;
+  M.keep = 1.f - M.eta;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+
+template <typename IO, int CPL>
+__device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
+  using LN = Lanes<IO, CPL>;
+  const SegCtx<IO, CPL> c = seg_ctx<IO, CPL>(g, a.S, a.H, a.T, a.d_v);
+  const int lane = lane_id();
+  const uint32_t nrow = (uint32_t)a.T * a.H;
+  const rsrc_t rv = make_rsrc(reinterpret_cast<const IO*>(a.v) + c.row0 * a.d_v, nrow * c.pitch);
+  const rsrc_t rs = make_rsrc(reinterpret_cast<IO*>(a.stash) + c.row0 * a.k_r * a.d_v,
+                              nrow * a.k_r * c.pitch);
+  const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
+
+  float s[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          ck.so[i][c] = s[c];
-          s[c] = fmaf(1.f - e, s[c], e * x[c]);
-        }
-      } else if (active) {
+  for (int k = 0; k < CPL; ++k) s[k] = (c.active && a.slot0) ? a.slot0[g * a.d_v + c.c0 + k] : 0.f;
+  float m = a.mass0 ? a.mass0[g] : 0.f;
+
+  float4 rec = load_rec(a.events, beg, min(end, (beg / CHUNK + 1) * CHUNK) - beg);
+  for (int p0 = beg; p0 < end;) {
+    const int p1 = min(end, (p0 / CHUNK + 1) * CHUNK);
+    const int n = p1 - p0;
+    if (p0 != beg) {
+      float* ck = a.ckpt_s + (int64_t)(p0 / CHUNK) * a.d_v;
+      if (c.active) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) part[i] = fmaf(x[c], s[c], part[i]);
+        for (int k = 0; k < CPL; ++k) ck[c.c0 + k] = s[k];
+      }
+      if (lane == 0) a.ckpt_m[p0 / CHUNK] = m;
+    }
+    const Ev ev = decode_rec(rec, n, c.h, a.H);
+    Mass M = mass_prefix(ev);
+    mass_apply(M, ev, m, a.eps);
+    m = readlane_f(M.mi, n - 1);
+    const float rr = (ev.side == 1) ? ev.wt : 0.f;
+    const uint32_t xo = (ev.valid && ev.side == 0) ? (uint32_t)ev.rb * c.pitch : OOB;
+    const uint32_t so = (ev.valid && ev.side == 1) ? ((uint32_t)ev.rb * a.k_r + ev.j) * c.pitch : OOB;
+    rec = load_rec(a.events, p1, min(end, (p1 / CHUNK + 1) * CHUNK) - p1);   // next chunk
+
+    typename LN::Raw x[CHUNK];
+    for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo) + c.lb); });
+    for_up<0, CHUNK>([&](auto I) {
+      float xf[CPL], ctr[CPL];
+      LN::get(x[I], xf);
+      const float e = bc<I>(M.eta), om = bc<I>(M.keep), r = bc<I>(rr);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        s[k] = fmaf(om, s[k], e * xf[k]);
+        ctr[k] = r * s[k];
+      }
+      LN::store(rs, bcu<I>(so) + c.lb, ctr);
+    });
+    p0 = p1;
+  }
+  if (c.active) {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) a.slot1[g * a.d_v + c.c0 + k] = s[k];
+  }
+  if (lane == 0) a.mass1[g] = m;
+}
+
+template <typename IO, int CPL>
+__device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
+  constexpr int NW = NWL;
+  using LN = Lanes<IO, CPL>;
+  __shared__ float mapA[NW], mapB[NW], mapP[NW];
+  __shared__ float mapb[NW][MAX_DV];
+  const SegCtx<IO, CPL> c = seg_ctx<IO, CPL>(g, a.S, a.H, a.T, a.d_v);
+  const int lane = lane_id();
+  const int w = wave_index();
+  const uint32_t nrow = (uint32_t)a.T * a.H;
+  const rsrc_t rv = make_rsrc(reinterpret_cast<const IO*>(a.v) + c.row0 * a.d_v, nrow * c.pitch);
+  const rsrc_t rs = make_rsrc(reinterpret_cast<IO*>(a.stash) + c.row0 * a.k_r * a.d_v,
+                              nrow * a.k_r * c.pitch);
+  const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
+
+  float s_carry[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k)
+    s_carry[k] = (c.active && a.slot0) ? a.slot0[g * a.d_v + c.c0 + k] : 0.f;
+  float m_carry = a.mass0 ? a.mass0[g] : 0.f;
+
+  float4 rec = load_rec(a.events, chunk_start(beg, w, end),
+                        chunk_start(beg, w + 1, end) - chunk_start(beg, w, end));
+  for (int p = beg; p < end;) {
+    const int cs = chunk_start(p, w, end);
+    const int n = chunk_start(p, w + 1, end) - cs;
+    const int pn = chunk_start(p, NW, end);
+    const Ev ev = decode_rec(rec, n, c.h, a.H);
+    Mass M = mass_prefix(ev);
+    // padded lanes carry the identity, so lane 15 holds the chunk's map
+    const float A_tot = bc<15>(M.A), B_tot = bc<15>(M.B);
+    if (lane == 0) {
+      mapA[w] = A_tot;
+      mapB[w] = B_tot;
+    }
+    const float rr = (ev.side == 1) ? ev.wt : 0.f;
+    const uint32_t xo = (ev.valid && ev.side == 0) ? (uint32_t)ev.rb * c.pitch : OOB;
+    const uint32_t so = (ev.valid && ev.side == 1) ? ((uint32_t)ev.rb * a.k_r + ev.j) * c.pitch : OOB;
+    // content loads do not depend on the mass: issue them before the barrier
+    typename LN::Raw x[CHUNK];
+    for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo) + c.lb); });
+    if (pn < end)   // next super-chunk's records for this wave
+      rec = load_rec(a.events, chunk_start(pn, w, end),
+                     chunk_start(pn, w + 1, end) - chunk_start(pn, w, end));
+    __syncthreads();
+    float m_in = m_carry, m_next = m_carry;
+    for (int k = 0; k < NW; ++k) {
+      if (k == w) m_in = m_next;
+      m_next = fmaf(mapA[k], m_next, mapB[k]);
+    }
+    mass_apply(M, ev, m_in, a.eps);
+    // content map of the chunk from a zero start: s -> P*s + sz
+    float sz[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) sz[k] = 0.f;
+    for_up<0, CHUNK>([&](auto I) {
+      float xf[CPL];
+      LN::get(x[I], xf);
+      const float e = bc<I>(M.eta), om = bc<I>(M.keep);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) sz[k] = fmaf(om, sz[k], e * xf[k]);
+    });
+    const float P = row_prod(M.keep);
+    if (c.active) {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) mapb[w][c.c0 + k] = sz[k];
+    }
+    if (lane == 0) mapP[w] = P;
+    __syncthreads();
+    float s[CPL], s_next[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) s_next[k] = s_carry[k];
+    for (int kk = 0; kk < NW; ++kk) {
+      const float Pk = mapP[kk];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        if (kk == w) s[k] = s_next[k];
+        s_next[k] = fmaf(Pk, s_next[k], c.active ? mapb[kk][c.c0 + k] : 0.f);
       }
     }
+    if (n > 0 && cs != beg) {
+      float* ck = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
+      if (c.active) {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) ck[c.c0 + k] = s[k];
+      }
+      if (lane == 0) a.ckpt_m[cs / CHUNK] = m_in;
+    }
+    // replay from the true start state; reads store their contributions
+    for_up<0, CHUNK>([&](auto I) {
+      float xf[CPL], ctr[CPL];
+      LN::get(x[I], xf);
+      const float e = bc<I>(M.eta), om = bc<I>(M.keep), r = bc<I>(rr);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        s[k] = fmaf(om, s[k], e * xf[k]);
+        ctr[k] = r * s[k];
+      }
+      LN::store(rs, bcu<I>(so) + c.lb, ctr);
+    });
+    m_carry = m_next;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) s_carry[k] = s_next[k];
+    p = pn;
+    __syncthreads();
   }
+  if (w == 0) {
+    if (c.active) {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) a.slot1[g * a.d_v + c.c0 + k] = s_carry[k];
+    }
+    if (lane == 0) a.mass1[g] = m_carry;
+  }
+}
+
+// A grid of resident workgroups.  Each first takes groups of NWL consecutive
+// segments, one per wave, skipping the long ones; then the workgroups walk
+// the list of long segments, longest class first, one segment at a time.
+template <typename IO, int CPL>
+__global__ __launch_bounds__(NWL * WAVE, 4) void scan_fwd_kernel(ScanFwdArgs a) {
+  const int64_t ngroups = (a.nseg + NWL - 1) / NWL;
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int64_t g = grp * NWL + wave_index();
+    if (g < a.nseg && !(a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS))
+      scan_fwd_short<IO, CPL>(a, g);
+  }
+  const int count = a.use_long ? long_total(a.long_count) : 0;
+  for (int i = blockIdx.x; i < count; i += gridDim.x)
+    scan_fwd_long<IO, CPL>(a, long_entry(a.long_list, a.long_count, a.long_cap, i));
+}
+
+// ---------------------------------------------------------------------------
+// reverse
+// ---------------------------------------------------------------------------
+//
+// Per chunk: restart from its checkpoint (or the initial state), replay the
+// events forward to recover the content before every write, then walk the
+// events backwards with the content adjoint s_hat:
+//   read  (weight r):  s_hat += r * dO_t;               dr   = <dO_t, s>
+//   write (w, gamma):  dv_t += eta * s_hat (io stash);  deta = <s_hat, v_t - s_old>;
+//                      s_hat <- (1 - eta) s_hat
+// The inner products are accumulated lane-locally for all events of the
+// chunk and summed in batched transpose-reductions.  The mass adjoint then
+// follows m_hat_before = lambda * (m_hat_after - g * deta), with
+// g = w / (m' + eps)^2, which is affine in m_hat: an inclusive suffix scan
+// across lanes gives it for every event at once, and each lane forms
+//   M = m_hat_after - g * deta
+//   dw = deta / (m' + eps) + M + M * m_old * dlambda/dw
+//   dgamma part = M * m_old * (-lambda (1 - lambda))
+// for its own event and stores it.
+
+// One chunk of the reverse pass: scalars, the event rows x (v for a write,
+// dO for a read) and the content before each event, kept in registers or
+// (SO_LDS, where registers are short) in this wave's block of LDS.
+template <typename IO, int CPL, bool SO_LDS>
+struct BwdChunk {
+  Ev ev;
+  Mass M;
+  float rr;                        // read weight, 0 for writes and padding
+  uint32_t sw;                     // stash offset of a write's dv row, else OOB
+  typename Lanes<IO, CPL>::Raw x[CHUNK];
+  float so_reg[SO_LDS ? 1 : CHUNK][CPL];
+  float* so_lds;                   // [CHUNK][MAX_DV] floats at the lane's channel c0
+
+  template <int I>
+  __device__ __forceinline__ void put_so(const float (&s)[CPL]) {
+    if constexpr (SO_LDS) {
+      if constexpr (CPL == 2) *reinterpret_cast<float2*>(so_lds + I * MAX_DV) = make_float2(s[0], s[1]);
+      else so_lds[I * MAX_DV] = s[0];
+    } else {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) so_reg[I][k] = s[k];
+    }
+  }
+  template <int I>
+  __device__ __forceinline__ void get_so(float (&o)[CPL]) const {
+    if constexpr (SO_LDS) {
+      if constexpr (CPL == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(so_lds + I * MAX_DV);
+        o[0] = t.x;
+        o[1] = t.y;
+      } else {
+        o[0] = so_lds[I * MAX_DV];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) o[k] = so_reg[I][k];
+    }
+  }
+};
+
+// Per-wave LDS blocks [NWL][CHUNK][MAX_DV] for the pre-write contents, shared
+// by the short and the long path of the reverse kernel.
+__device__ __forceinline__ float* so_area() {
+  __shared__ float so_lds[NWL * CHUNK * MAX_DV];
+  return so_lds;
+}
+
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ void bwd_setup(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                          rsrc_t rv, rsrc_t ro, BwdChunk<IO, CPL, SO>& ck, float4 rec,
+                                          int n, float m) {
+  using LN = Lanes<IO, CPL>;
+  ck.ev = decode_rec(rec, n, c.h, a.H);
+  const Ev& ev = ck.ev;
+  ck.M = mass_prefix(ev);
+  mass_apply(ck.M, ev, m, a.eps);
+  ck.rr = (ev.side == 1) ? ev.wt : 0.f;
+  const uint32_t roff = (uint32_t)ev.rb * c.pitch;
+  const uint32_t xv = (ev.valid && ev.side == 0) ? roff : OOB;
+  const uint32_t xd = (ev.valid && ev.side == 1) ? roff : OOB;
+  ck.sw = (ev.valid && ev.side == 0) ? ((uint32_t)ev.rb * a.k_w + ev.j) * c.pitch : OOB;
+  // one of the two loads is out of range and gives 0
+  for_up<0, CHUNK>([&](auto I) {
+    ck.x[I] = LN::merge(LN::load(rv, bcu<I>(xv) + c.lb), LN::load(ro, bcu<I>(xd) + c.lb));
+  });
+}
+
+// Forward replay of a chunk from s: keeps the content before each event and
+// pr[i] = <x_i, s_i> (lane-local), which for a read is its dr partial.
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ void bwd_replay(BwdChunk<IO, CPL, SO>& ck, float (&s)[CPL],
+                                           float (&pr)[CHUNK]) {
+  using LN = Lanes<IO, CPL>;
+  for_up<0, CHUNK>([&](auto I) {
+    float xf[CPL];
+    LN::get(ck.x[I], xf);
+    const float e = bc<I>(ck.M.eta), om = bc<I>(ck.M.keep);
+    float d = 0.f;
+    ck.template put_so<I>(s);
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      s[k] = fmaf(om, s[k], e * xf[k]);
+      d = fmaf(xf[k], s[k], d);
+    }
+    pr[I] = d;
+  });
 }
 
 // Reverse walk of the content adjoint from sh (after the chunk) to sh (before
-// it): stores the dv contributions and puts <s_hat_after, v - s_old> partials
-// of the writes into part[i].
-template <typename IO, int CPL>
-__device__ __forceinline__ void bwd_walk_content(const ScanBwdArgs& a, const BwdChunk<IO, CPL>& ck,
-                                                 int n, float (&sh)[CPL], bool active, int c0,
-                                                 float (&part)[CHUNK]) {
-  IO* stash = reinterpret_cast<IO*>(a.stash);
+// it): stores the dv contributions e * s_hat and leaves the lane-local
+// partials <s_hat_after, x - s_old> (the deta of a write) in pw.
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ void bwd_walk(const BwdChunk<IO, CPL, SO>& ck, const SegCtx<IO, CPL>& c,
+                                         rsrc_t rs, float (&sh)[CPL], float (&pw)[CHUNK]) {
+  using LN = Lanes<IO, CPL>;
+  for_down<CHUNK>([&](auto I) {
+    float xf[CPL], ctr[CPL], so[CPL];
+    LN::get(ck.x[I], xf);
+    ck.template get_so<I>(so);
+    const float e = bc<I>(ck.M.eta), r = bc<I>(ck.rr);
+    float d = 0.f;
 #pragma unroll
-  for (int i = CHUNK - 1; i >= 0; --i) {
-    if (i < n) {
-      float x[CPL];
-      ck.raw[i].get(x);
-      const float r_or_w = readlane_f(ck.sc.wt, i);
-      if (readlane_i(ck.sc.ev.side, i) == 1) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) sh[c] = fmaf(r_or_w, x[c], sh[c]);
-      } else {
-        const float e = readlane_f(ck.eta, i);
-        const int64_t srow = (int64_t)readlane_i(ck.sc.ev.row, i) * a.k_w + readlane_i(ck.sc.ev.j, i);
-        float contrib[CPL];
-        float d = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          contrib[c] = e * sh[c];
-          d = fmaf(sh[c], x[c] - ck.so[i][c], d);
-          sh[c] = (1.f - e) * sh[c];
-        }
-        if (active) {
-          Slice<IO, CPL>::store(stash + srow * a.d_v + c0, contrib);
-          part[i] = d;
-        }
-      }
+    for (int k = 0; k < CPL; ++k) {
+      ctr[k] = e * sh[k];
+      d = fmaf(sh[k], xf[k] - so[k], d);
+      sh[k] = fmaf(r, xf[k], fmaf(-e, sh[k], sh[k]));
     }
-  }
+    LN::store(rs, bcu<I>(ck.sw) + c.lb, ctr);
+    pw[I] = d;
+  });
 }
 
 // Lane-parallel scalar part of a chunk's reverse step.  red (lane i) holds
 // dr_i for a read and deta_i for a write.  Stores dr, dw and the gamma parts;
 // mh goes from the mass adjoint after the chunk to the one before it.
-template <typename IO, int CPL>
-__device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const BwdChunk<IO, CPL>& ck,
-                                            int n, float red, float& mh) {
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                            const BwdChunk<IO, CPL, SO>& ck, float red, float& mh) {
   const int lane = lane_id();
-  const bool ev = lane < n;
-  const bool wr = ev && ck.sc.ev.side == 0;
-  const float den = ck.mi + a.eps;
-  const float g = (wr && ck.sc.wt > 0.f) ? ck.sc.wt / (den * den) : 0.f;
+  const Ev& ev = ck.ev;
+  const bool wr = ev.valid && ev.side == 0;
+  const float den = ck.M.mi + a.eps;
+  const float g = (wr && ev.wt > 0.f) ? ev.wt / (den * den) : 0.f;
   const float deta = wr ? red : 0.f;
-  float A = wr ? ck.sc.lam : 1.f;
-  float B = wr ? -ck.sc.lam * g * deta : 0.f;
+  float A = wr ? ev.lam : 1.f;
+  float B = wr ? -ev.lam * g * deta : 0.f;
   affine_suffix_scan(A, B);
   const float before = fmaf(A, mh, B);
-  const float after_n = dpp<DPP_SHL1>(before);
-  const float after = ((lane & (CHUNK - 1)) == CHUNK - 1) ? mh : after_n;
-  if (wr) {
-    const float M = after - g * deta;
-    const float dwi = ((ck.sc.wt > 0.f) ? deta / den : 0.f) + M + M * ck.mo * ck.sc.dl;
-    const float dgi = M * ck.mo * (-ck.sc.lam * (1.f - ck.sc.lam));
-    const int64_t o = (int64_t)ck.sc.ev.row * a.k_w + ck.sc.ev.j;
-    a.dw[o] = dwi;
-    a.dgam[o] = dgi;
-  } else if (ev) {
-    a.dr[(int64_t)ck.sc.ev.row * a.k_r + ck.sc.ev.j] = red;
+  const float after = dpp_or<DPP_SHL1>(mh, before);   // lane 15: the chunk's m_hat
+  const int64_t row = c.row0 + ev.rb;
+  if (lane < CHUNK) {
+    if (wr) {
+      const float M = after - g * deta;
+      const float dwi = ((ev.wt > 0.f) ? deta / den : 0.f) + M + M * ck.M.mo * ev.dl;
+      const float dgi = M * ck.M.mo * (-ev.lam * (1.f - ev.lam));
+      const int64_t o = row * a.k_w + ev.j;
+      a.dw[o] = dwi;
+      a.dgam[o] = dgi;
+    } else if (ev.valid) {
+      a.dr[row * a.k_r + ev.j] = red;
+    }
   }
   mh = readlane_f(before, 0);
 }
 
 // State at the start of chunk cs of segment g: the initial state for the
 // segment's first chunk, else the checkpoint the forward saved.
-template <int CPL>
-__device__ __forceinline__ void chunk_state(const ScanBwdArgs& a, int64_t g, int beg, int cs,
-                                            bool active, int c0, float (&s)[CPL], float& m) {
+template <typename IO, int CPL>
+__device__ __forceinline__ void chunk_state(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                            int64_t g, int beg, int cs, float (&s)[CPL],
+                                            float& m) {
   if (cs == beg) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) s[c] = (active && a.slot0) ? a.slot0[g * a.d_v + c0 + c] : 0.f;
+    for (int k = 0; k < CPL; ++k) s[k] = (c.active && a.slot0) ? a.slot0[g * a.d_v + c.c0 + k] : 0.f;
     m = a.mass0 ? a.mass0[g] : 0.f;
   } else {
     const float* cp = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) s[c] = active ? cp[c0 + c] : 0.f;
+    for (int k = 0; k < CPL; ++k) s[k] = c.active ? cp[c.c0 + k] : 0.f;
     m = a.ckpt_m[cs / CHUNK];
   }
 }
 
 template <typename IO, int CPL>
 __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
+  const SegCtx<IO, CPL> c = seg_ctx<IO, CPL>(g, a.S, a.H, a.T, a.d_v);
   const int lane = lane_id();
-  const int64_t bh = g / a.S;
-  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-  const int c0 = lane * CPL;
-  const bool active = c0 < a.d_v;
+  const uint32_t nrow = (uint32_t)a.T * a.H;
+  const rsrc_t rv = make_rsrc(reinterpret_cast<const IO*>(a.v) + c.row0 * a.d_v, nrow * c.pitch);
+  const rsrc_t ro = make_rsrc(reinterpret_cast<const IO*>(a.d_o) + c.row0 * a.d_v, nrow * c.pitch);
+  const rsrc_t rs = make_rsrc(reinterpret_cast<IO*>(a.stash) + c.row0 * a.k_w * a.d_v,
+                              nrow * a.k_w * c.pitch);
   const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
 
   float sh[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) sh[c] = (active && a.d_slot1) ? a.d_slot1[g * a.d_v + c0 + c] : 0.f;
+  for (int k = 0; k < CPL; ++k)
+    sh[k] = (c.active && a.d_slot1) ? a.d_slot1[g * a.d_v + c.c0 + k] : 0.f;
   float mh = a.d_mass1 ? a.d_mass1[g] : 0.f;
 
   if (beg < end) {
-    BwdChunk<IO, CPL> ck;
-    float part[CHUNK];
+    BwdChunk<IO, CPL, true> ck;
+    ck.so_lds = so_area() + wave_index() * (CHUNK * MAX_DV) + c.c0;
+    float pr[CHUNK], pw[CHUNK];
     int cs = max(beg, ((end - 1) / CHUNK) * CHUNK);
     float4 rec = load_rec(a.events, cs, end - cs);
     while (true) {
       const int n = min(end, (cs / CHUNK + 1) * CHUNK) - cs;
       const int cp = max(beg, cs - CHUNK);
       float s[CPL], m;
-      chunk_state<CPL>(a, g, beg, cs, active, c0, s, m);
+      chunk_state<IO, CPL>(a, c, g, beg, cs, s, m);
       const float4 rec_cur = rec;
       if (cs != beg) rec = load_rec(a.events, cp, cs - cp);   // previous chunk
-      bwd_load_replay<IO, CPL>(a, ck, b, h, rec_cur, n, s, m, active, c0, part);
-      bwd_walk_content<IO, CPL>(a, ck, n, sh, active, c0, part);
-      bwd_scalars<IO, CPL>(a, ck, n, batched_sum(part), mh);
+      bwd_setup(a, c, rv, ro, ck, rec_cur, n, m);
+      bwd_replay(ck, s, pr);
+      const float red_r = batched_sum(pr);
+      bwd_walk(ck, c, rs, sh, pw);
+      const float red_w = batched_sum(pw);
+      bwd_scalars(a, c, ck, ck.ev.side == 1 ? red_r : red_w, mh);
       if (cs == beg) break;
       cs = cp;
     }
   }
-  if (a.d_slot0 && active) {
+  if (a.d_slot0 && c.active) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) a.d_slot0[g * a.d_v + c0 + c] = sh[c];
+    for (int k = 0; k < CPL; ++k) a.d_slot0[g * a.d_v + c.c0 + k] = sh[k];
   }
   if (a.d_mass0 && lane == 0) a.d_mass0[g] = mh;
 }
 
-// Long segments: a workgroup of NWB waves takes NWB consecutive chunks at a
+// Long segments: a workgroup of NWL waves takes NWL consecutive chunks at a
 // time, from the end of the segment.  Each wave replays its chunk from its
-// checkpoint and forms the chunk's adjoint map from a symbolic zero at its end
+// checkpoint and forms the chunk's adjoint map from a symbolic zero at its
+// end
 //   s_hat_in = Q * s_hat_out + q
 //   m_hat_in = L * m_hat_out + <s_hat_out, U> + K
 // (Q = prod (1-eta), L = prod lambda over the writes; U and K collect the
-// mass terms), the maps of the later chunks are folded to give each wave its
-// true adjoints after its chunk, and each wave then runs the exact reverse
-// step.  Wave 0's result is the carry into the previous NW chunks.
+// mass terms).  Folding the content maps of the later chunks gives each wave
+// its true s_hat after its chunk; each wave then contributes
+// <s_hat_out, U> of its own map, which makes the mass maps scalar, and the
+// folded mass maps give each wave its true m_hat.  Each wave then runs the
+// exact reverse step; wave 0's result is the carry into the previous NWL
+// chunks.
 template <typename IO, int CPL>
 __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
-  constexpr int NW = NWB;
-  __shared__ float mQ[NW], mL[NW], mK[NW];
-  __shared__ float mq[NW][MAX_DV], mU[NW][MAX_DV];
+  constexpr int NW = NWL;
+  using LN = Lanes<IO, CPL>;
+  __shared__ float mQ[NW], mL[NW], mK[NW], mD[NW];
+  __shared__ float mq[NW][MAX_DV];
   __shared__ float carry_s[MAX_DV];
   __shared__ float carry_m;
+  const SegCtx<IO, CPL> c = seg_ctx<IO, CPL>(g, a.S, a.H, a.T, a.d_v);
   const int lane = lane_id();
-  const int w = threadIdx.x / WAVE;
-  const int64_t bh = g / a.S;
-  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-  const int c0 = lane * CPL;
-  const bool active = c0 < a.d_v;
+  const int w = wave_index();
+  const uint32_t nrow = (uint32_t)a.T * a.H;
+  const rsrc_t rv = make_rsrc(reinterpret_cast<const IO*>(a.v) + c.row0 * a.d_v, nrow * c.pitch);
+  const rsrc_t ro = make_rsrc(reinterpret_cast<const IO*>(a.d_o) + c.row0 * a.d_v, nrow * c.pitch);
+  const rsrc_t rs = make_rsrc(reinterpret_cast<IO*>(a.stash) + c.row0 * a.k_w * a.d_v,
+                              nrow * a.k_w * c.pitch);
   const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
   const int nchunks = (end - 1) / CHUNK - beg / CHUNK + 1;
 
   float sh_carry[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c)
-    sh_carry[c] = (active && a.d_slot1) ? a.d_slot1[g * a.d_v + c0 + c] : 0.f;
+  for (int k = 0; k < CPL; ++k)
+    sh_carry[k] = (c.active && a.d_slot1) ? a.d_slot1[g * a.d_v + c.c0 + k] : 0.f;
   float mh_carry = a.d_mass1 ? a.d_mass1[g] : 0.f;
 
-  BwdChunk<IO, CPL> ck;
-  float part[CHUNK];
+  BwdChunk<IO, CPL, true> ck;
+  ck.so_lds = so_area() + w * (CHUNK * MAX_DV) + c.c0;
+  float pr[CHUNK], pw[CHUNK];
   auto chunk_of = [&](int k, int& cs, int& n) {
     cs = end;
     n = 0;
@@ -661,125 +822,118 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
     chunk_of(u0 + w, cs, n);
     float s[CPL], m = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) s[c] = 0.f;
-    if (n > 0) chunk_state<CPL>(a, g, beg, cs, active, c0, s, m);
+    for (int k = 0; k < CPL; ++k) s[k] = 0.f;
+    if (n > 0) chunk_state<IO, CPL>(a, c, g, beg, cs, s, m);
     const float4 rec_cur = rec;
     if (u0 >= NW) {   // this wave's chunk of the previous super-chunk
       int csp, np;
       chunk_of(u0 - NW + w, csp, np);
       rec = load_rec(a.events, csp, np);
     }
-    bwd_load_replay<IO, CPL>(a, ck, b, h, rec_cur, n, s, m, active, c0, part);
-    // adjoint map of the chunk (reverse walk from zero); write partials
-    // <q_after_i, u_i> join the read partials in part[]
-    float Lp = (lane < n && ck.sc.ev.side == 0) ? ck.sc.lam : 1.f;
-    {                                                        // prefix products of lambda
+    bwd_setup(a, c, rv, ro, ck, rec_cur, n, m);
+    bwd_replay(ck, s, pr);
+    const float red_r = batched_sum(pr);   // dr of the reads
+    const Ev& ev = ck.ev;
+    // adjoint map of the chunk: a reverse walk from zero.  coef_i is the
+    // factor of u_i = x_i - s_old_i in U: -(prefix product of lambda) *
+    // g_i * (product of (1 - eta) over the later events).
+    const bool wr = ev.valid && ev.side == 0;
+    float Lp = wr ? ev.lam : 1.f;
+    {
       float dummy = 0.f;
       affine_scan(Lp, dummy);
     }
-    const float den = ck.mi + a.eps;
-    const float gq = (ck.sc.ev.side == 0 && ck.sc.wt > 0.f) ? ck.sc.wt / (den * den) : 0.f;
-    float Q = 1.f, q[CPL], U[CPL];
+    float Qs = ck.M.keep, dz = 0.f;
+    affine_suffix_scan(Qs, dz);
+    const float Qx = dpp_or<DPP_SHL1>(1.f, Qs);
+    const float den = ck.M.mi + a.eps;
+    const float gq = (wr && ev.wt > 0.f) ? ev.wt / (den * den) : 0.f;
+    const float coef = -Lp * gq * Qx;
+    float q[CPL], U[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) { q[c] = 0.f; U[c] = 0.f; }
-#pragma unroll
-    for (int i = CHUNK - 1; i >= 0; --i) {
-      if (i < n) {
-        float x[CPL];
-        ck.raw[i].get(x);
-        const float r_or_w = readlane_f(ck.sc.wt, i);
-        if (readlane_i(ck.sc.ev.side, i) == 1) {
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) q[c] = fmaf(r_or_w, x[c], q[c]);
-        } else {
-          const float e = readlane_f(ck.eta, i);
-          const float coef = -readlane_f(Lp, i) * readlane_f(gq, i) * Q;
-          float d = 0.f;
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            const float u = active ? x[c] - ck.so[i][c] : 0.f;
-            d = fmaf(q[c], u, d);
-            U[c] = fmaf(coef, u, U[c]);
-            q[c] = (1.f - e) * q[c];
-          }
-          part[i] = active ? d : 0.f;
-          Q *= 1.f - e;
-        }
-      }
-    }
-    const float red1 = batched_sum(part);     // dr (reads), <q_after, u> (writes)
-    const bool wr = lane < n && ck.sc.ev.side == 0;
-    const float K = wave_sum(wr ? -Lp * gq * red1 : 0.f);
-    const float L = readlane_f(Lp, max(n, 1) - 1);
-    if (active) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) { mq[w][c0 + c] = q[c]; mU[w][c0 + c] = U[c]; }
-    }
-    if (lane == 0) { mQ[w] = Q; mL[w] = (n > 0) ? L : 1.f; mK[w] = K; }
-    __syncthreads();
-    // adjoints after this wave's chunk: fold the maps of the later chunks
-    float sh[CPL];
-    float mh = mh_carry;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) sh[c] = sh_carry[c];
-    for (int kk = NW - 1; kk > w; --kk) {
+    for (int k = 0; k < CPL; ++k) { q[k] = 0.f; U[k] = 0.f; }
+    for_down<CHUNK>([&](auto I) {
+      float xf[CPL], so[CPL];
+      LN::get(ck.x[I], xf);
+      ck.template get_so<I>(so);
+      const float e = bc<I>(ck.M.eta), r = bc<I>(ck.rr), cf = bc<I>(coef);
       float d = 0.f;
-      if (active) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) d = fmaf(sh[c], mU[kk][c0 + c], d);
+      for (int k = 0; k < CPL; ++k) {
+        const float u = xf[k] - so[k];
+        d = fmaf(q[k], u, d);
+        U[k] = fmaf(cf, u, U[k]);
+        q[k] = fmaf(r, xf[k], fmaf(-e, q[k], q[k]));
       }
-      d = wave_sum(d);
-      mh = fmaf(mL[kk], mh, d + mK[kk]);
+      pw[I] = d;
+    });
+    const float red1 = batched_sum(pw);    // <q_after, u> of the writes
+    const float K = row_sum(wr ? -Lp * gq * red1 : 0.f);
+    const float L = bc<15>(Lp);
+    const float Q = bc<0>(Qs);
+    if (c.active) {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) mq[w][c.c0 + k] = q[k];
+    }
+    if (lane == 0) { mQ[w] = Q; mL[w] = L; mK[w] = K; }
+    __syncthreads();
+    // content adjoint after this wave's chunk: fold the later content maps
+    float sh[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) sh[k] = sh_carry[k];
+    for (int kk = NW - 1; kk > w; --kk) {
       const float Qk = mQ[kk];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) sh[c] = fmaf(Qk, sh[c], active ? mq[kk][c0 + c] : 0.f);
+      for (int k = 0; k < CPL; ++k) sh[k] = fmaf(Qk, sh[k], c.active ? mq[kk][c.c0 + k] : 0.f);
     }
-    // exact reverse step of this wave's chunk
-#pragma unroll
-    for (int i = 0; i < CHUNK; ++i) part[i] = 0.f;
-    bwd_walk_content<IO, CPL>(a, ck, n, sh, active, c0, part);
-    const float red2 = batched_sum(part);     // deta (writes)
     {
-      // bwd_scalars stores dr for reads too; keep the values from red1 there
-      const bool rd = lane < n && ck.sc.ev.side == 1;
-      bwd_scalars<IO, CPL>(a, ck, n, rd ? red1 : red2, mh);
-    }
-    if (w == 0) {
-      if (active) {
+      float d = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) carry_s[c0 + c] = sh[c];
+      for (int k = 0; k < CPL; ++k) d = fmaf(sh[k], U[k], d);
+      d = wave_sum(d);
+      if (lane == 0) mD[w] = d;
+    }
+    __syncthreads();
+    float mh = mh_carry;
+    for (int kk = NW - 1; kk > w; --kk) mh = fmaf(mL[kk], mh, mD[kk] + mK[kk]);
+    // exact reverse step of this wave's chunk
+    bwd_walk(ck, c, rs, sh, pw);
+    const float red2 = batched_sum(pw);     // deta of the writes
+    bwd_scalars(a, c, ck, ev.side == 1 ? red_r : red2, mh);
+    if (w == 0) {
+      if (c.active) {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) carry_s[c.c0 + k] = sh[k];
       }
       if (lane == 0) carry_m = mh;
     }
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) sh_carry[c] = active ? carry_s[c0 + c] : 0.f;
+    for (int k = 0; k < CPL; ++k) sh_carry[k] = c.active ? carry_s[c.c0 + k] : 0.f;
     mh_carry = carry_m;
     __syncthreads();
   }
   if (w == 0) {
-    if (a.d_slot0 && active) {
+    if (a.d_slot0 && c.active) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) a.d_slot0[g * a.d_v + c0 + c] = sh_carry[c];
+      for (int k = 0; k < CPL; ++k) a.d_slot0[g * a.d_v + c.c0 + k] = sh_carry[k];
     }
     if (a.d_mass0 && lane == 0) a.d_mass0[g] = mh_carry;
   }
 }
 
-// Long segments: NWB waves per workgroup, the workgroups walk the long list.
+// Same schedule as the forward: short segments first, then the long list.
 template <typename IO, int CPL>
-__global__ __launch_bounds__(NWB * WAVE) void scan_bwd_long_kernel(ScanBwdArgs a) {
-  const int count = a.use_long ? *a.long_count : 0;
-  for (int i = blockIdx.x; i < count; i += gridDim.x) scan_bwd_long<IO, CPL>(a, a.long_list[i]);
-}
-
-// Short segments: one wave each, four per workgroup.
-template <typename IO, int CPL>
-__global__ __launch_bounds__(4 * WAVE) void scan_bwd_short_kernel(ScanBwdArgs a) {
-  const int64_t g = (int64_t)blockIdx.x * 4 + threadIdx.x / WAVE;
-  if (g >= a.nseg) return;
-  if (a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS) return;
-  scan_bwd_short<IO, CPL>(a, g);
+__global__ __launch_bounds__(NWL * WAVE, 2) void scan_bwd_kernel(ScanBwdArgs a) {
+  const int64_t ngroups = (a.nseg + NWL - 1) / NWL;
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int64_t g = grp * NWL + wave_index();
+    if (g < a.nseg && !(a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS))
+      scan_bwd_short<IO, CPL>(a, g);
+  }
+  const int count = a.use_long ? long_total(a.long_count) : 0;
+  for (int i = blockIdx.x; i < count; i += gridDim.x)
+    scan_bwd_long<IO, CPL>(a, long_entry(a.long_list, a.long_count, a.long_cap, i));
 }
 
 // ---------------------------------------------------------------------------
@@ -827,40 +981,47 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
 
 // ---------------------------------------------------------------------------
 
+namespace {
+// Grid of the scan kernels: the workgroups that fit on the device at once
+// (a grid-stride schedule needs no more), and no more than there are
+// segment groups and long segments to take.
+template <typename Args>
+hipError_t launch_scan(void (*kern)(Args), const Args& a, hipStream_t st) {
+  static int resident = 0;   // per kernel instantiation
+  if (resident == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NWL * WAVE, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+      return hipErrorInvalidDeviceFunction;
+    resident = cus * per_cu;
+  }
+  const int64_t work = (a.nseg + NWL - 1) / NWL + (a.use_long ? a.long_cap * (int64_t)NBIN : 0);
+  const unsigned grid = (unsigned)(work < resident ? work : resident);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NWL * WAVE), 0, st, a);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st) {
   if (a.nseg == 0) return hipSuccess;
-  const dim3 grid((unsigned)(a.long_blocks + (a.nseg + NW - 1) / NW)), block(NW * WAVE);
   if (bf16) {
-    if (a.d_v > 64) hipLaunchKernelGGL((scan_fwd_kernel<bf16_t, 2>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scan_fwd_kernel<bf16_t, 1>), grid, block, 0, st, a);
-  } else {
-    if (a.d_v > 64) hipLaunchKernelGGL((scan_fwd_kernel<float, 2>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scan_fwd_kernel<float, 1>), grid, block, 0, st, a);
+    if (a.d_v > 64) return launch_scan(scan_fwd_kernel<bf16_t, 2>, a, st);
+    return launch_scan(scan_fwd_kernel<bf16_t, 1>, a, st);
   }
-  return hipGetLastError();
+  if (a.d_v > 64) return launch_scan(scan_fwd_kernel<float, 2>, a, st);
+  return launch_scan(scan_fwd_kernel<float, 1>, a, st);
 }
 
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st) {
   if (a.nseg == 0) return hipSuccess;
-  const dim3 lgrid((unsigned)a.long_blocks), lblock(NWB * WAVE);
-  const dim3 sgrid((unsigned)((a.nseg + 3) / 4)), sblock(4 * WAVE);
-  if (a.use_long) {
-    if (bf16) {
-      if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_long_kernel<bf16_t, 2>), lgrid, lblock, 0, st, a);
-      else hipLaunchKernelGGL((scan_bwd_long_kernel<bf16_t, 1>), lgrid, lblock, 0, st, a);
-    } else {
-      if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_long_kernel<float, 2>), lgrid, lblock, 0, st, a);
-      else hipLaunchKernelGGL((scan_bwd_long_kernel<float, 1>), lgrid, lblock, 0, st, a);
-    }
-  }
   if (bf16) {
-    if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_short_kernel<bf16_t, 2>), sgrid, sblock, 0, st, a);
-    else hipLaunchKernelGGL((scan_bwd_short_kernel<bf16_t, 1>), sgrid, sblock, 0, st, a);
-  } else {
-    if (a.d_v > 64) hipLaunchKernelGGL((scan_bwd_short_kernel<float, 2>), sgrid, sblock, 0, st, a);
-    else hipLaunchKernelGGL((scan_bwd_short_kernel<float, 1>), sgrid, sblock, 0, st, a);
+    if (a.d_v > 64) return launch_scan(scan_bwd_kernel<bf16_t, 2>, a, st);
+    return launch_scan(scan_bwd_kernel<bf16_t, 1>, a, st);
   }
-  return hipGetLastError();
+  if (a.d_v > 64) return launch_scan(scan_bwd_kernel<float, 2>, a, st);
+  return launch_scan(scan_bwd_kernel<float, 1>, a, st);
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st) {
