@@ -30,7 +30,9 @@
  *               execution", parallel and autoregressive modes).
  *
  * Supported: one address digit (U = 1, P = S); CAPE (cape_heads) is not
- * supported yet and is rejected.
+ * supported yet and is rejected.  One batch's rows of v (and of the read-out
+ * and gradient staging, T*H*max(k_w, k_r)*d_v io values) must fit in
+ * 0x7FE00000 bytes, else RAM_ECAPACITY (split T over calls).
  *
  * Layouts (all row-major, contiguous, device memory):
  *   logits  (B, T, H, S)     io dtype     wlogits: write side, rlogits: read side
@@ -45,8 +47,11 @@
  *
  * Ownership and streams: the caller allocates every buffer, including the
  * workspace (size from ram_workspace_size).  The library never allocates or
- * frees device memory and never blocks the host; all work is enqueued on the
- * given HIP stream (a hipStream_t passed as void*, NULL = default stream).
+ * frees device memory and never blocks the host.  All work is ordered on the
+ * given HIP stream (a hipStream_t passed as void*, NULL = default stream):
+ * parts of a call may run on a library-owned stream of the same device,
+ * which first waits for the work already on the given stream and which the
+ * given stream then waits for (event fork and join; capturable in a graph).
  * Pointers to logits must be 16-byte aligned.
  *
  * Errors: every call returns RAM_OK (0) or a negative code; nothing is

@@ -141,6 +141,43 @@ void prof_after(const char*, hipStream_t st) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RAM_OK : RAM_EHIP; }
 
+// ---- a second stream per device ---------------------------------------------
+// Independent kernels of one call (the short- and the long-segment scans) run
+// on the caller's stream and on a library stream at the same time.  The
+// library stream waits for everything enqueued on the caller's stream before
+// the call (fork event), and the caller's stream waits for the library
+// stream's part (join event), so the call stays ordered on the caller's
+// stream.  Default priority; non-blocking with respect to the null stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex side_mu;
+std::vector<SideStream> side_streams;
+
+// Runs launch(main, side) between a fork and a join.  Holds side_mu so the
+// pair of events is not shared by two calls at once.
+template <typename F>
+hipError_t forked(hipStream_t st, F&& launch) {
+  std::lock_guard<std::mutex> lk(side_mu);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((int)side_streams.size() <= dev) side_streams.resize(dev + 1);
+  SideStream& ss = side_streams[dev];
+  if (!ss.s) {
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  if ((e = hipEventRecord(ss.fork, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(ss.s, ss.fork, 0)) != hipSuccess) return e;
+  const hipError_t le = launch(st, ss.s);
+  if ((e = hipEventRecord(ss.join, ss.s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(st, ss.join, 0)) != hipSuccess) return e;
+  return le;
+}
+
 }  // namespace
 
 extern "C" {
@@ -286,7 +323,7 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   sa.ckpt_s = (float*)(w + L.ckpt_s);
   sa.ckpt_m = (float*)(w + L.ckpt_m);
   prof_before("scan_fwd", s);
-  e = launch_scan_fwd(sa, bf, s);
+  e = forked(s, [&](hipStream_t m, hipStream_t x) { return launch_scan_fwd(sa, bf, m, x); });
   prof_after("scan_fwd", s);
   if (e != hipSuccess) return RAM_EHIP;
 
@@ -357,7 +394,7 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   sb.dr = (float*)(w + L.dr);
   sb.dgam = (float*)(w + L.dgam);
   prof_before("scan_bwd", s);
-  e = launch_scan_bwd(sb, bf, s);
+  e = forked(s, [&](hipStream_t m, hipStream_t x) { return launch_scan_bwd(sb, bf, m, x); });
   prof_after("scan_bwd", s);
   if (e != hipSuccess) return RAM_EHIP;
 

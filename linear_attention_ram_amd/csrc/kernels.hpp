@@ -7,7 +7,8 @@ namespace ramk {
 
 constexpr int CHUNK = 16;        // scan chunk: checkpoints at 16-aligned events
 constexpr int TILE_TOKENS = 256; // tokens per bucketing tile
-constexpr int NWL = 8;           // waves per scan workgroup (one long segment, or NWL short ones)
+constexpr int NWL = 8;           // waves per long-segment scan workgroup
+constexpr int SHORT_WAVES = 4;   // waves (one short segment each) per short-segment workgroup
 constexpr int LONG_EVENTS = 128; // segments with more events take the cooperative path
 constexpr int NBIN = 8;          // length classes of the long-segment list: class c holds
                                  // segments of [129 * 2^c, 129 * 2^(c+1)) events (the last
@@ -110,8 +111,10 @@ struct StepArgs {
 hipError_t launch_bucket(const BucketArgs& a, bool bf16, hipStream_t st,
                          void (*before)(const char*, hipStream_t),
                          void (*after)(const char*, hipStream_t));
-hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st);
-hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st);
+// Short-segment kernel on `side`, long-segment kernel on `st`; the caller
+// makes both streams wait for the inputs and joins them afterwards.
+hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st, hipStream_t side);
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st, hipStream_t side);
 hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t st);
 

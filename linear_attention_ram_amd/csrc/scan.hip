@@ -95,6 +95,15 @@ __device__ __forceinline__ void for_down(F&& f) {   // I-1, I-2, ..., 0
   }
 }
 
+// Scheduling fence every SCHED_EVENTS events of a chunk loop: keeps the
+// compiler from hoisting the loads and broadcasts of all 16 events at once,
+// which would cost more registers than the latency it hides.
+constexpr int SCHED_EVENTS = 4;
+template <int I>
+__device__ __forceinline__ void sched_fence() {
+  if constexpr (I % SCHED_EVENTS == SCHED_EVENTS - 1) __builtin_amdgcn_sched_barrier(0);
+}
+
 // CPL io values of one row slice at a byte offset of a buffer.
 template <typename IO, int CPL> struct Lanes;
 template <> struct Lanes<bf16_t, 1> {
@@ -516,18 +525,21 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
   }
 }
 
-// A grid of resident workgroups.  Each first takes groups of NWL consecutive
-// segments, one per wave, skipping the long ones; then the workgroups walk
-// the list of long segments, longest class first, one segment at a time.
+// Short segments: one wave each, SHORT_WAVES waves per workgroup, one
+// workgroup per SHORT_WAVES consecutive segments (long ones are skipped).
 template <typename IO, int CPL>
-__global__ __launch_bounds__(NWL * WAVE, 4) void scan_fwd_kernel(ScanFwdArgs a) {
-  const int64_t ngroups = (a.nseg + NWL - 1) / NWL;
-  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
-    const int64_t g = grp * NWL + wave_index();
-    if (g < a.nseg && !(a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS))
-      scan_fwd_short<IO, CPL>(a, g);
-  }
-  const int count = a.use_long ? long_total(a.long_count) : 0;
+__global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_fwd_short_kernel(ScanFwdArgs a) {
+  const int64_t g = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
+  if (g >= a.nseg) return;
+  if (a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS) return;
+  scan_fwd_short<IO, CPL>(a, g);
+}
+
+// Long segments: a resident grid of NWL-wave workgroups walks the list,
+// longest class first.
+template <typename IO, int CPL>
+__global__ __launch_bounds__(NWL * WAVE) void scan_fwd_long_kernel(ScanFwdArgs a) {
+  const int count = long_total(a.long_count);
   for (int i = blockIdx.x; i < count; i += gridDim.x)
     scan_fwd_long<IO, CPL>(a, long_entry(a.long_list, a.long_count, a.long_cap, i));
 }
@@ -592,13 +604,6 @@ struct BwdChunk {
   }
 };
 
-// Per-wave LDS blocks [NWL][CHUNK][MAX_DV] for the pre-write contents, shared
-// by the short and the long path of the reverse kernel.
-__device__ __forceinline__ float* so_area() {
-  __shared__ float so_lds[NWL * CHUNK * MAX_DV];
-  return so_lds;
-}
-
 template <typename IO, int CPL, bool SO>
 __device__ __forceinline__ void bwd_setup(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
                                           rsrc_t rv, rsrc_t ro, BwdChunk<IO, CPL, SO>& ck, float4 rec,
@@ -637,6 +642,7 @@ __device__ __forceinline__ void bwd_replay(BwdChunk<IO, CPL, SO>& ck, float (&s)
       d = fmaf(xf[k], s[k], d);
     }
     pr[I] = d;
+    sched_fence<I>();
   });
 }
 
@@ -661,6 +667,7 @@ __device__ __forceinline__ void bwd_walk(const BwdChunk<IO, CPL, SO>& ck, const 
     }
     LN::store(rs, bcu<I>(ck.sw) + c.lb, ctr);
     pw[I] = d;
+    sched_fence<I>();
   });
 }
 
@@ -733,8 +740,7 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
   float mh = a.d_mass1 ? a.d_mass1[g] : 0.f;
 
   if (beg < end) {
-    BwdChunk<IO, CPL, true> ck;
-    ck.so_lds = so_area() + wave_index() * (CHUNK * MAX_DV) + c.c0;
+    BwdChunk<IO, CPL, false> ck;
     float pr[CHUNK], pw[CHUNK];
     int cs = max(beg, ((end - 1) / CHUNK) * CHUNK);
     float4 rec = load_rec(a.events, cs, end - cs);
@@ -800,8 +806,9 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
     sh_carry[k] = (c.active && a.d_slot1) ? a.d_slot1[g * a.d_v + c.c0 + k] : 0.f;
   float mh_carry = a.d_mass1 ? a.d_mass1[g] : 0.f;
 
+  __shared__ float so_lds[NW][CHUNK][MAX_DV];   // pre-write contents, per wave
   BwdChunk<IO, CPL, true> ck;
-  ck.so_lds = so_area() + w * (CHUNK * MAX_DV) + c.c0;
+  ck.so_lds = &so_lds[w][0][0] + c.c0;
   float pr[CHUNK], pw[CHUNK];
   auto chunk_of = [&](int k, int& cs, int& n) {
     cs = end;
@@ -866,6 +873,8 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
         q[k] = fmaf(r, xf[k], fmaf(-e, q[k], q[k]));
       }
       pw[I] = d;
+      sched_fence<I>();
+    sched_fence<I>();
     });
     const float red1 = batched_sum(pw);    // <q_after, u> of the writes
     const float K = row_sum(wr ? -Lp * gq * red1 : 0.f);
@@ -922,16 +931,18 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
   }
 }
 
-// Same schedule as the forward: short segments first, then the long list.
+// Same split as the forward.
 template <typename IO, int CPL>
-__global__ __launch_bounds__(NWL * WAVE, 2) void scan_bwd_kernel(ScanBwdArgs a) {
-  const int64_t ngroups = (a.nseg + NWL - 1) / NWL;
-  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
-    const int64_t g = grp * NWL + wave_index();
-    if (g < a.nseg && !(a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS))
-      scan_bwd_short<IO, CPL>(a, g);
-  }
-  const int count = a.use_long ? long_total(a.long_count) : 0;
+__global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_bwd_short_kernel(ScanBwdArgs a) {
+  const int64_t g = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
+  if (g >= a.nseg) return;
+  if (a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS) return;
+  scan_bwd_short<IO, CPL>(a, g);
+}
+
+template <typename IO, int CPL>
+__global__ __launch_bounds__(NWL * WAVE) void scan_bwd_long_kernel(ScanBwdArgs a) {
+  const int count = long_total(a.long_count);
   for (int i = blockIdx.x; i < count; i += gridDim.x)
     scan_bwd_long<IO, CPL>(a, long_entry(a.long_list, a.long_count, a.long_cap, i));
 }
@@ -982,46 +993,60 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
 // ---------------------------------------------------------------------------
 
 namespace {
-// Grid of the scan kernels: the workgroups that fit on the device at once
-// (a grid-stride schedule needs no more), and no more than there are
-// segment groups and long segments to take.
+// Workgroups of a kernel that fit on the device at once.
 template <typename Args>
-hipError_t launch_scan(void (*kern)(Args), const Args& a, hipStream_t st) {
-  static int resident = 0;   // per kernel instantiation
-  if (resident == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NWL * WAVE, 0) != hipSuccess ||
-        cus <= 0 || per_cu <= 0)
-      return hipErrorInvalidDeviceFunction;
-    resident = cus * per_cu;
+int resident_blocks(void (*kern)(Args), int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess)
+    return 0;
+  return cus > 0 && per_cu > 0 ? cus * per_cu : 0;
+}
+
+// Short kernel on `side`, long kernel on `st` (the caller orders the two
+// streams).  The long grid is the resident workgroup count, capped by the
+// list capacity: a grid-stride walk needs no more.
+template <typename Args>
+hipError_t launch_pair(void (*shortk)(Args), void (*longk)(Args), int& resident, const Args& a,
+                       hipStream_t st, hipStream_t side) {
+  const unsigned sgrid = (unsigned)((a.nseg + SHORT_WAVES - 1) / SHORT_WAVES);
+  hipLaunchKernelGGL(shortk, dim3(sgrid), dim3(SHORT_WAVES * WAVE), 0, side, a);
+  if (a.use_long) {
+    if (resident == 0) resident = resident_blocks(longk, NWL * WAVE);
+    if (resident == 0) return hipErrorInvalidDeviceFunction;
+    const int64_t cap = (int64_t)a.long_cap * NBIN;
+    const unsigned lgrid = (unsigned)(cap < resident ? cap : resident);
+    hipLaunchKernelGGL(longk, dim3(lgrid), dim3(NWL * WAVE), 0, st, a);
   }
-  const int64_t work = (a.nseg + NWL - 1) / NWL + (a.use_long ? a.long_cap * (int64_t)NBIN : 0);
-  const unsigned grid = (unsigned)(work < resident ? work : resident);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NWL * WAVE), 0, st, a);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st) {
+hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st, hipStream_t side) {
   if (a.nseg == 0) return hipSuccess;
+  static int res[4] = {0, 0, 0, 0};
   if (bf16) {
-    if (a.d_v > 64) return launch_scan(scan_fwd_kernel<bf16_t, 2>, a, st);
-    return launch_scan(scan_fwd_kernel<bf16_t, 1>, a, st);
+    if (a.d_v > 64)
+      return launch_pair(scan_fwd_short_kernel<bf16_t, 2>, scan_fwd_long_kernel<bf16_t, 2>, res[0], a, st, side);
+    return launch_pair(scan_fwd_short_kernel<bf16_t, 1>, scan_fwd_long_kernel<bf16_t, 1>, res[1], a, st, side);
   }
-  if (a.d_v > 64) return launch_scan(scan_fwd_kernel<float, 2>, a, st);
-  return launch_scan(scan_fwd_kernel<float, 1>, a, st);
+  if (a.d_v > 64)
+    return launch_pair(scan_fwd_short_kernel<float, 2>, scan_fwd_long_kernel<float, 2>, res[2], a, st, side);
+  return launch_pair(scan_fwd_short_kernel<float, 1>, scan_fwd_long_kernel<float, 1>, res[3], a, st, side);
 }
 
-hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st) {
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st, hipStream_t side) {
   if (a.nseg == 0) return hipSuccess;
+  static int res[4] = {0, 0, 0, 0};
   if (bf16) {
-    if (a.d_v > 64) return launch_scan(scan_bwd_kernel<bf16_t, 2>, a, st);
-    return launch_scan(scan_bwd_kernel<bf16_t, 1>, a, st);
+    if (a.d_v > 64)
+      return launch_pair(scan_bwd_short_kernel<bf16_t, 2>, scan_bwd_long_kernel<bf16_t, 2>, res[0], a, st, side);
+    return launch_pair(scan_bwd_short_kernel<bf16_t, 1>, scan_bwd_long_kernel<bf16_t, 1>, res[1], a, st, side);
   }
-  if (a.d_v > 64) return launch_scan(scan_bwd_kernel<float, 2>, a, st);
-  return launch_scan(scan_bwd_kernel<float, 1>, a, st);
+  if (a.d_v > 64)
+    return launch_pair(scan_bwd_short_kernel<float, 2>, scan_bwd_long_kernel<float, 2>, res[2], a, st, side);
+  return launch_pair(scan_bwd_short_kernel<float, 1>, scan_bwd_long_kernel<float, 1>, res[3], a, st, side);
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st) {

@@ -64,6 +64,9 @@ def test_valid_problem_has_positive_workspace():
     (dict(cape_heads=1), ram.RAM_EUNSUPPORTED),
     (dict(T=1 << 24), ram.RAM_ECAPACITY),
     (dict(B=4096, T=8192, H=16, S=64, k_w=8, k_r=8), ram.RAM_ECAPACITY),
+    # one batch's staging rows (T*H*k*d_v bf16) above the scans' buffer limit
+    (dict(B=1, T=70000, H=16, S=64, k_w=8, k_r=8, d_v=128), ram.RAM_ECAPACITY),
+    (dict(B=1, T=65000, H=16, S=64, k_w=8, k_r=8, d_v=128), ram.RAM_OK),
 ])
 def test_invalid_problems_are_rejected(kw, code):
     st, _, _ = status_of(**kw)
