@@ -46,9 +46,31 @@ __device__ __forceinline__ uint4 pack16(const float (&v)[4]) {
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
   return (uint32_t)from_f32<bf16_t>(lo) | ((uint32_t)from_f32<bf16_t>(hi) << 16);
 }
+// Two floats to packed bf16 with the gfx950 conversion (round to nearest
+// even, like from_f32; a NaN stays a NaN).
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2bf(float lo, float hi) {
+  const f32x2_hw x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_hw));
+}
 __device__ __forceinline__ uint4 pack16(const float (&v)[8]) {
-  return make_uint4(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]), pack2bf(v[4], v[5]),
-                    pack2bf(v[6], v[7]));
+  return make_uint4(cvt2bf(v[0], v[1]), cvt2bf(v[2], v[3]), cvt2bf(v[4], v[5]),
+                    cvt2bf(v[6], v[7]));
+}
+
+// Streaming 16-byte load / store (nontemporal hint: the line is not kept in
+// the caches for reuse).  Rows that are read or written exactly once go
+// through these; on gfx950 they reach a markedly higher share of HBM
+// bandwidth than plain accesses.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  const u32x4_nt t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void st_nt16(void* p, uint4 v) {
+  const u32x4_nt t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4_nt*>(p));
 }
 
 // 16-byte vector of -inf in the io type (pads a row past its end).
@@ -59,6 +81,11 @@ template <> __device__ __forceinline__ uint4 neg_inf16<float>() {
 template <> __device__ __forceinline__ uint4 neg_inf16<bf16_t>() {
   return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
 }
+
+// 2^x with the hardware instruction alone: results below 2^-126 flush to 0
+// (exp2f adds a range reduction to keep them), which only drops softmax
+// terms more than 87 nats below the row maximum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (WAVE - 1)); }
 __device__ __forceinline__ uint64_t lanemask_lt() {

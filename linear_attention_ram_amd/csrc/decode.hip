@@ -20,8 +20,9 @@
 
 namespace ramk {
 
-// One wave per row; rows of side 0 first, then side 1.
-template <typename IO>
+// One wave per row; rows of side 0 first, then side 1.  NV > 0: rows of at
+// most NV * 64 vectors, held in registers; NV = 0: any length, streamed.
+template <typename IO, int NV>
 __global__ __launch_bounds__(256) void decode_fwd_kernel(DecodeFwdArgs a) {
   __shared__ DecodeScratch scratch[4];
   __shared__ int s_idx[4][MAX_K];
@@ -34,7 +35,11 @@ __global__ __launch_bounds__(256) void decode_fwd_kernel(DecodeFwdArgs a) {
   const int64_t row = grow - (int64_t)side * a.N;
   const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
   const int k = a.k[side];
-  const float lse = decode_row_wave<IO>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
+  float lse;
+  if constexpr (NV > 0)
+    lse = decode_row_resident<IO, NV>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
+  else
+    lse = decode_row_wave<IO>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
   wave_sync();
   if (lane < k) {
     a.idx[side][row * k + lane] = s_idx[wv][lane];
@@ -50,25 +55,31 @@ __global__ __launch_bounds__(256) void decode_fwd_kernel(DecodeFwdArgs a) {
 // Decode backward (one wave per row): with g_j the gradient of the j-th
 // output weight, gw_j = g_j w_j (renormalised: gw_j = (g_j - sum_i g_i w_i) w_j),
 // dl_i = [i = a_j] gw_j - p_i sum_j gw_j, p = softmax(l) = exp(l - lse).
+// The row streams through in tiles of TILE 16-byte vectors per lane (all
+// loads of a tile in flight before the first store).  Lane j < k gathers its
+// selected logit and forms the full value of entry a_j; the lane that owns
+// that entry's vector puts it into the vector before the vector is stored
+// (scattered 2-byte stores after the stream cost more than the stream's
+// own writes would suggest).
 template <typename IO>
 __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
   constexpr int E = vec16<IO>::E;
-  const int wv = threadIdx.x >> 6;
+  constexpr int TILE = 8;
   const int lane = lane_id();
-  const int64_t grow = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t grow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (grow >= (int64_t)a.nsides * a.N) return;
-  (void)wv;
   const int side = (int)(grow / a.N);
   const int64_t row = grow - (int64_t)side * a.N;
   const int k = a.k[side];
-  const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
-  IO* dst = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)a.S;
-  float gw = 0.f, wj = 0.f, gj = 0.f;
+  const IO* __restrict__ src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
+  IO* __restrict__ dst = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)a.S;
+  float gw = 0.f, wj = 0.f, gj = 0.f, lj = 0.f;
   int aj = 0;
   if (lane < k) {
     gj = a.g[side][row * k + lane];
     wj = a.w[side][row * k + lane];
     aj = a.idx[side][row * k + lane];
+    lj = to_f32(src[aj]);
   }
   if (a.renorm[side]) {
     const float dot = wave_sum(gj * wj);
@@ -79,22 +90,35 @@ __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
   const float tot = wave_sum(gw);
   const float nl = -a.lse[side][row] * LOG2E;
   const float ntot = -tot;
+  const float fix = gw + ntot * fast_exp2(fmaf(lj, LOG2E, nl));
+  const int fix_row = (lane < k) ? aj / (E * WAVE) : -1;   // vector row of the wave holding a_j
   const int nvec = a.S / E;
-  for (int c = lane; c < nvec; c += WAVE) {
-    float x[E];
-    unpack16(*reinterpret_cast<const uint4*>(src + (int64_t)c * E), x);
+  for (int c0 = 0; c0 < nvec; c0 += WAVE * TILE) {
+    uint4 q[TILE];
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = ntot * exp2f(fmaf(x[e], LOG2E, nl));
-    *reinterpret_cast<uint4*>(dst + (int64_t)c * E) = pack16(x);
-  }
-  // the selected entries get their extra term; each is rewritten by the lane
-  // that wrote its vector above, so program order keeps the later store
-  for (int j = 0; j < k; ++j) {
-    const int id = readlane_i(aj, j);
-    const float g = readlane_f(gw, j);
-    if (lane == (id / E) % WAVE) {
-      const float p = exp2f(fmaf(to_f32(src[id]), LOG2E, nl));
-      dst[id] = from_f32<IO>(g + ntot * p);
+    for (int u = 0; u < TILE; ++u) {
+      const int c = c0 + u * WAVE + lane;
+      if (c < nvec) q[u] = ld_nt16(src + (int64_t)c * E);
+    }
+#pragma unroll
+    for (int u = 0; u < TILE; ++u) {
+      const int c = c0 + u * WAVE + lane;
+      float x[E];
+      unpack16(q[u], x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = ntot * fast_exp2(fmaf(x[e], LOG2E, nl));
+      // selected entries inside this vector row of the wave (usually none)
+      uint64_t fixes = __ballot(fix_row == c0 / WAVE + u);
+      while (fixes) {
+        const int j = (int)__builtin_ctzll(fixes);
+        fixes &= fixes - 1;
+        const int id = readlane_i(aj, j);
+        const float v = readlane_f(fix, j);
+        const bool mine = lane == (id / E) % WAVE;
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = (mine && id % E == e) ? v : x[e];
+      }
+      if (c < nvec) st_nt16(dst + (int64_t)c * E, pack16(x));
     }
   }
 }
@@ -103,8 +127,20 @@ hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st) 
   const int64_t rows = (int64_t)a.nsides * a.N;
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-  if (bf16) hipLaunchKernelGGL(decode_fwd_kernel<bf16_t>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(decode_fwd_kernel<float>, grid, block, 0, st, a);
+  const int nvec = a.S / (bf16 ? 8 : 4);
+  if (bf16) {
+    if (nvec <= 64) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 1>), grid, block, 0, st, a);
+    else if (nvec <= 128) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 2>), grid, block, 0, st, a);
+    else if (nvec <= 256) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 4>), grid, block, 0, st, a);
+    else if (nvec <= 512) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 8>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 0>), grid, block, 0, st, a);
+  } else {
+    if (nvec <= 64) hipLaunchKernelGGL((decode_fwd_kernel<float, 1>), grid, block, 0, st, a);
+    else if (nvec <= 128) hipLaunchKernelGGL((decode_fwd_kernel<float, 2>), grid, block, 0, st, a);
+    else if (nvec <= 256) hipLaunchKernelGGL((decode_fwd_kernel<float, 4>), grid, block, 0, st, a);
+    else if (nvec <= 512) hipLaunchKernelGGL((decode_fwd_kernel<float, 8>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_fwd_kernel<float, 0>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -5,13 +5,17 @@
 
 namespace ramk {
 
-constexpr int CAND_CAP = 512;   // candidates kept in LDS per row
+constexpr int CAND_CAP = 256;   // candidates kept in LDS per row
 constexpr int MAX_K = 64;       // largest top-K per side
 
 // Per-wave LDS work area of the row decoder.
+constexpr int STAGE_CAP = 64;   // 16-byte vectors staged per row by the resident decoder
+
 struct DecodeScratch {
   float cv[CAND_CAP];
   int ci[CAND_CAP];
+  uint4 stage[STAGE_CAP];
+  int stage_c[STAGE_CAP];
   float sv[MAX_K];
   int si[MAX_K];
   int lanes[WAVE];
@@ -60,8 +64,186 @@ __device__ __forceinline__ uint4 load_vec(const IO* row, int c, int nvec) {
   return (c < nvec) ? *reinterpret_cast<const uint4*>(row + (int64_t)c * vec16<IO>::E)
                     : neg_inf16<IO>();
 }
+// Same for a row that is read exactly once.
+template <typename IO>
+__device__ __forceinline__ uint4 load_vec_nt(const IO* row, int c, int nvec) {
+  return (c < nvec) ? ld_nt16(row + (int64_t)c * vec16<IO>::E) : neg_inf16<IO>();
+}
+
+// Makes the compiler forget what it knows about q (emits no code), so values
+// unpacked from q earlier are not kept alive for reuse after this point.
+template <int NV>
+__device__ __forceinline__ void hide_regs(uint4 (&q)[NV]) {
+#pragma unroll
+  for (int u = 0; u < NV; ++u) asm volatile("" : "+v"(q[u].x), "+v"(q[u].y), "+v"(q[u].z), "+v"(q[u].w));
+}
+
+// tau = K-th largest lane value m (counted with multiplicity).  Every top-K
+// element of the row is >= tau, and lies in a lane whose maximum is >= tau.
+__device__ __forceinline__ float kth_lane_max(float m, int k) {
+  const int lane = lane_id();
+  float cur = m, tau = -INFINITY;
+  for (int r = 0; r < k; ++r) {
+    const float mx = wave_max(cur);
+    tau = mx;
+    const uint64_t hit = __ballot(cur == mx);
+    if (lane == (int)__builtin_ctzll(hit)) cur = -INFINITY;
+  }
+  return tau;
+}
+
+// Exact rank of every one of the `count` candidates in sc among the
+// candidates; the K best go to sc.sv / sc.si in order.
+__device__ __forceinline__ void rank_candidates(DecodeScratch& sc, int count, int k) {
+  for (int ci = lane_id(); ci < count; ci += WAVE) {
+    const float v = sc.cv[ci];
+    const int id = sc.ci[ci];
+    int rank = 0;
+    for (int o = 0; o < count; ++o) rank += before(sc.cv[o], sc.ci[o], v, id) ? 1 : 0;
+    if (rank < k) { sc.sv[rank] = v; sc.si[rank] = id; }
+  }
+}
+
+// Rows with more than CAND_CAP candidates (massive ties): K exact passes
+// over the row in memory, each taking the best element after the previous
+// pick in (value desc, index asc) order, to sc.sv / sc.si.  Kept out of line
+// so its registers do not count against the common path.
+template <typename IO>
+__device__ __noinline__ void exact_k_passes(const IO* __restrict__ row, int nvec, int k,
+                                            DecodeScratch& sc) {
+  constexpr int E = vec16<IO>::E;
+  const int lane = lane_id();
+  float pv = INFINITY;
+  int pi = -1;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int c = lane; c < nvec; c += WAVE) {
+      float x[E];
+      unpack16(load_vec<IO>(row, c, nvec), x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int id = c * E + e;
+        if (before(pv, pi, x[e], id) && before(x[e], id, bv, bi)) { bv = x[e]; bi = id; }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, WAVE);
+      const int oi = __shfl_xor(bi, o, WAVE);
+      if (before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) { sc.sv[r] = bv; sc.si[r] = bi; }
+    pv = bv;
+    pi = bi;
+  }
+}
+
+// Weights exp(l - lse) of the K selected entries (optionally renormalised)
+// to sel_i / sel_w, lanes < k.
+__device__ __forceinline__ void finish_weights(const DecodeScratch& sc, int k, float lse,
+                                               int renorm, int* sel_i, float* sel_w) {
+  const int lane = lane_id();
+  float w = 0.f;
+  int id = 0;
+  if (lane < k) {
+    id = sc.si[lane];
+    w = expf(sc.sv[lane] - lse);
+  }
+  if (renorm) {
+    const float tot = wave_sum(lane < k ? w : 0.f);
+    w = w / tot;
+  }
+  if (lane < k) { sel_i[lane] = id; sel_w[lane] = w; }
+}
 
 }  // namespace
+
+// Decodes one row of at most NV * 64 16-byte vectors with the calling wave,
+// holding the whole row in registers (lane l: vectors l, l + 64, ...):
+// one read of the row from memory, then every pass works on registers.
+template <typename IO, int NV>
+__device__ float decode_row_resident(const IO* __restrict__ row, int S, int k, int renorm,
+                                     DecodeScratch& sc, int* sel_i, float* sel_w) {
+  constexpr int E = vec16<IO>::E;
+  const int lane = lane_id();
+  const int nvec = S / E;
+  uint4 q[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) q[u] = load_vec_nt<IO>(row, u * WAVE + lane, nvec);
+  float vm[NV];            // maximum of each of the lane's vectors
+  float m = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    float x[E];
+    unpack16(q[u], x);
+    vm[u] = x[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) vm[u] = fmaxf(vm[u], x[e]);
+    m = fmaxf(m, vm[u]);
+  }
+  const float M = wave_max(m);
+  // each pass unpacks the packed row again instead of keeping the floats
+  hide_regs(q);
+  float s = 0.f;
+  if (M != -INFINITY) {
+    const float nm = -M * LOG2E;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      float x[E];
+      unpack16(q[u], x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s += fast_exp2(fmaf(x[e], LOG2E, nm));
+    }
+  }
+  const float lse = M + logf(wave_sum(s));
+  const float tau = kth_lane_max(m, k);
+
+  // stage the vectors whose maximum reaches tau (they hold every top-K
+  // element), then compact their elements >= tau into the candidate list
+  const uint64_t lt = lanemask_lt();
+  int nq = 0;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int c = u * WAVE + lane;
+    const bool qual = c < nvec && vm[u] >= tau;
+    const uint64_t bal = __ballot(qual);
+    const int pos = nq + __popcll(bal & lt);
+    if (qual && pos < STAGE_CAP) {
+      sc.stage[pos] = q[u];
+      sc.stage_c[pos] = c;
+    }
+    nq += __popcll(bal);
+  }
+  wave_sync();
+  int count = 0;
+  bool overflow = nq > STAGE_CAP;
+  if (!overflow) {
+    float x[E];
+    int base = 0, mine = 0;
+    if (lane < nq) {
+      unpack16(sc.stage[lane], x);
+      base = sc.stage_c[lane] * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) mine += (x[e] >= tau) ? 1 : 0;
+    }
+    const int incl = wave_incl_scan(mine);
+    count = readlane_i(incl, WAVE - 1);
+    overflow = count > CAND_CAP;
+    if (!overflow && lane < nq) {
+      int pos = incl - mine;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (x[e] >= tau) { sc.cv[pos] = x[e]; sc.ci[pos] = base + e; ++pos; }
+    }
+  }
+  wave_sync();
+  if (!overflow) rank_candidates(sc, count, k);
+  else exact_k_passes<IO>(row, nvec, k, sc);
+  wave_sync();
+  finish_weights(sc, k, lse, renorm, sel_i, sel_w);
+  return lse;
+}
 
 // Decodes one row with the calling wave.  Results go to sel_i / sel_w
 // (k entries, LDS or registers visible to the wave after the call) and the
@@ -90,30 +272,23 @@ __device__ float decode_row_wave(const IO* __restrict__ row, int S, int k, int r
     }
     const float mn = fmaxf(m, tmax);
     if (mn != -INFINITY) {
-      s *= (m == -INFINITY) ? 0.f : exp2f((m - mn) * LOG2E);
+      s *= (m == -INFINITY) ? 0.f : fast_exp2((m - mn) * LOG2E);
       const float nml = -mn * LOG2E;
 #pragma unroll
       for (int u = 0; u < TILE; ++u) {
         float x[E];
         unpack16(q[u], x);
 #pragma unroll
-        for (int e = 0; e < E; ++e) s += exp2f(fmaf(x[e], LOG2E, nml));
+        for (int e = 0; e < E; ++e) s += fast_exp2(fmaf(x[e], LOG2E, nml));
       }
       m = mn;
     }
   }
   const float M = wave_max(m);
-  const float part = (m == -INFINITY) ? 0.f : s * exp2f((m - M) * LOG2E);
+  const float part = (m == -INFINITY) ? 0.f : s * fast_exp2((m - M) * LOG2E);
   const float lse = M + logf(wave_sum(part));
 
-  // threshold: K-th largest lane maximum (counted with multiplicity)
-  float cur = m, tau = -INFINITY;
-  for (int r = 0; r < k; ++r) {
-    const float mx = wave_max(cur);
-    tau = mx;
-    const uint64_t hit = __ballot(cur == mx);
-    if (lane == (int)__builtin_ctzll(hit)) cur = -INFINITY;
-  }
+  const float tau = kth_lane_max(m, k);
 
   // lanes that may hold top-K elements
   const bool winner = (m >= tau);
@@ -154,56 +329,12 @@ __device__ float decode_row_wave(const IO* __restrict__ row, int S, int k, int r
   wave_sync();
 
   if (!overflow) {
-    // exact rank of every candidate among the candidates
-    for (int ci = lane; ci < count; ci += WAVE) {
-      const float v = sc.cv[ci];
-      const int id = sc.ci[ci];
-      int rank = 0;
-      for (int o = 0; o < count; ++o) rank += before(sc.cv[o], sc.ci[o], v, id) ? 1 : 0;
-      if (rank < k) { sc.sv[rank] = v; sc.si[rank] = id; }
-    }
+    rank_candidates(sc, count, k);
   } else {
-    // fallback: K exact passes, each picks the best element after the
-    // previous pick in (value desc, index asc) order
-    float pv = INFINITY;
-    int pi = -1;
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int c = lane; c < nvec; c += WAVE) {
-        float x[E];
-        unpack16(load_vec<IO>(row, c, nvec), x);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int id = c * E + e;
-          if (before(pv, pi, x[e], id) && before(x[e], id, bv, bi)) { bv = x[e]; bi = id; }
-        }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, WAVE);
-        const int oi = __shfl_xor(bi, o, WAVE);
-        if (before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if (lane == 0) { sc.sv[r] = bv; sc.si[r] = bi; }
-      pv = bv;
-      pi = bi;
-    }
+    exact_k_passes<IO>(row, nvec, k, sc);
   }
   wave_sync();
-
-  // weights
-  float w = 0.f;
-  int id = 0;
-  if (lane < k) {
-    id = sc.si[lane];
-    w = expf(sc.sv[lane] - lse);
-  }
-  if (renorm) {
-    const float tot = wave_sum(lane < k ? w : 0.f);
-    w = w / tot;
-  }
-  if (lane < k) { sel_i[lane] = id; sel_w[lane] = w; }
+  finish_weights(sc, k, lse, renorm, sel_i, sel_w);
   return lse;
 }
 

@@ -970,11 +970,11 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
       const IO* base = st + row * a.k * a.d_v + vcol * E;
       for (int j = 0; j < a.k; ++j) {
         float x[E];
-        unpack16(*reinterpret_cast<const uint4*>(base + (int64_t)j * a.d_v), x);
+        unpack16(ld_nt16(base + (int64_t)j * a.d_v), x);
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] += x[e];
       }
-      *reinterpret_cast<uint4*>(out + row * a.d_v + vcol * E) = pack16(acc);
+      st_nt16(out + row * a.d_v + vcol * E, pack16(acc));
     }
   } else if (tid < a.N * a.d_v) {
     const int64_t row = tid / a.d_v;
