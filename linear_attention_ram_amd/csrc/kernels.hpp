@@ -7,7 +7,7 @@ namespace ramk {
 
 constexpr int CHUNK = 16;        // scan chunk: checkpoints at 16-aligned events
 constexpr int TILE_TOKENS = 256; // tokens per bucketing tile
-constexpr int NWL = 8;           // waves per long-segment scan workgroup
+constexpr int NWL = 4;           // waves per long-segment scan workgroup
 constexpr int SHORT_WAVES = 4;   // waves (one short segment each) per short-segment workgroup
 constexpr int LONG_EVENTS = 128; // segments with more events take the cooperative path
 constexpr int NBIN = 8;          // length classes of the long-segment list: class c holds
