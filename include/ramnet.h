@@ -49,9 +49,12 @@
  * workspace (size from ram_workspace_size).  The library never allocates or
  * frees device memory and never blocks the host.  All work is ordered on the
  * given HIP stream (a hipStream_t passed as void*, NULL = default stream):
- * parts of a call may run on a library-owned stream of the same device,
- * which first waits for the work already on the given stream and which the
+ * parts of a call run on two library-owned streams of the same device,
+ * which first wait for the work already on the given stream and which the
  * given stream then waits for (event fork and join; capturable in a graph).
+ * ram_forward and ram_backward cut a call into up to four pieces of whole
+ * batches so that one piece's scans overlap the next piece's decode; calls
+ * from several host threads are serialised inside the library.
  * Pointers to logits must be 16-byte aligned.
  *
  * Errors: every call returns RAM_OK (0) or a negative code; nothing is

@@ -1,5 +1,6 @@
 // C ABI of the RAM-Net attention core: validation, workspace layout and the
 // launch sequence of each entry point.  See include/ramnet.h for the contract.
+#include <algorithm>
 #include <mutex>
 #include <string.h>
 #include <string>
@@ -64,11 +65,36 @@ int check_problem(const ram_problem* p, Dims* d) {
   return RAM_OK;
 }
 
-// Entries per length class of the long-segment list: every long segment has
-// more than LONG_EVENTS events.
-int long_cap(const Dims& d) {
-  const int64_t c = d.E / (LONG_EVENTS + 1) + 1;
-  return (int)(c < d.nseg ? c : d.nseg);
+// A call can be cut into pieces of whole batches that go through the path
+// one after the other, so that one piece's bucketing and scans
+// (latency-bound) run while the next piece's address decode
+// (bandwidth-bound) streams.  With the present kernels one piece is fastest
+// (measured at the 1.3B shape: 2 and 4 pieces lose 0.4 and 1.0 ms): the
+// longest segment of a piece is as long as that of the whole call, so the
+// pieces' scans do not shrink, and the decode starves their small
+// workgroups of the device.
+constexpr int MAX_PIECES = 1;
+struct Pieces {
+  int n;
+  int b0[MAX_PIECES + 1];   // piece q holds batches [b0[q], b0[q + 1])
+};
+Pieces make_pieces(int B) {
+  Pieces P;
+  P.n = B < MAX_PIECES ? B : MAX_PIECES;
+  for (int q = 0; q <= P.n; ++q) P.b0[q] = (int)((int64_t)B * q / P.n);
+  return P;
+}
+
+// Entries per length class of one piece's long-segment list: every long
+// segment has more than LONG_EVENTS events.
+int long_cap(const ram_problem* p, const Dims& d) {
+  const Pieces P = make_pieces(p->B);
+  int nb = 0;
+  for (int q = 0; q < P.n; ++q) nb = std::max(nb, P.b0[q + 1] - P.b0[q]);
+  const int64_t E = (int64_t)nb * p->H * p->T * (p->k_w + p->k_r);
+  const int64_t nseg = (int64_t)nb * p->H * d.S;
+  const int64_t c = E / (LONG_EVENTS + 1) + 1;
+  return (int)(c < nseg ? c : nseg);
 }
 
 void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
@@ -86,8 +112,9 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   L->ckpt_m = take(sizeof(float) * d.nck);
   L->stash = take(d.io_bytes * d.N * (p->k_w > p->k_r ? p->k_w : p->k_r) * p->d_v);
   L->tile_hist = take(sizeof(int32_t) * (size_t)p->B * p->H * d.ntiles * d.S);
-  L->long_list = take(sizeof(int32_t) * NBIN * long_cap(d));
-  L->long_count = take(sizeof(int32_t) * NBIN);
+  const int pieces = make_pieces(p->B).n;
+  L->long_list = take(sizeof(int32_t) * pieces * NBIN * long_cap(p, d));
+  L->long_count = take(sizeof(int32_t) * pieces * NBIN);
   L->fwd_bytes = off;
   L->dw = take(sizeof(float) * d.N * p->k_w);
   L->dr = take(sizeof(float) * d.N * p->k_r);
@@ -141,41 +168,57 @@ void prof_after(const char*, hipStream_t st) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RAM_OK : RAM_EHIP; }
 
-// ---- a second stream per device ---------------------------------------------
-// Independent kernels of one call (the short- and the long-segment scans) run
-// on the caller's stream and on a library stream at the same time.  The
-// library stream waits for everything enqueued on the caller's stream before
-// the call (fork event), and the caller's stream waits for the library
-// stream's part (join event), so the call stays ordered on the caller's
-// stream.  Default priority; non-blocking with respect to the null stream.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+// ---- library streams ---------------------------------------------------------
+// The kernels of a call run on the caller's stream and on two library
+// streams of the same device (default priority, non-blocking with respect to
+// the null stream).  Every dependency goes through an event: the library
+// streams first wait for everything already on the caller's stream (fork),
+// and the caller's stream ends waiting for the library streams' work
+// (join), so the call as a whole is ordered on the caller's stream.
+constexpr int EV_POOL = 8 * MAX_PIECES + 8;
+struct Sched {
+  hipStream_t side[2] = {nullptr, nullptr};
+  hipEvent_t ev[EV_POOL] = {};
+  int used = 0;
+  hipError_t err = hipSuccess;
+  // `waiter` waits for all work enqueued on `signaler` so far.
+  void dep(hipStream_t waiter, hipStream_t signaler) {
+    if (err != hipSuccess || waiter == signaler) return;
+    if (used == EV_POOL) { err = hipErrorOutOfMemory; return; }
+    hipEvent_t e = ev[used++];
+    err = hipEventRecord(e, signaler);
+    if (err == hipSuccess) err = hipStreamWaitEvent(waiter, e, 0);
+  }
 };
-std::mutex side_mu;
-std::vector<SideStream> side_streams;
+std::mutex sched_mu;   // held for a whole call: one call uses the event pool at a time
+std::vector<Sched> scheds;
 
-// Runs launch(main, side) between a fork and a join.  Holds side_mu so the
-// pair of events is not shared by two calls at once.
-template <typename F>
-hipError_t forked(hipStream_t st, F&& launch) {
-  std::lock_guard<std::mutex> lk(side_mu);
+hipError_t get_sched(Sched** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if ((int)side_streams.size() <= dev) side_streams.resize(dev + 1);
-  SideStream& ss = side_streams[dev];
-  if (!ss.s) {
-    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+  if ((int)scheds.size() <= dev) scheds.resize(dev + 1);
+  Sched& S = scheds[dev];
+  if (!S.ev[0]) {
+    for (auto& ev : S.ev)
+      if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
   }
-  if ((e = hipEventRecord(ss.fork, st)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(ss.s, ss.fork, 0)) != hipSuccess) return e;
-  const hipError_t le = launch(st, ss.s);
-  if ((e = hipEventRecord(ss.join, ss.s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(st, ss.join, 0)) != hipSuccess) return e;
-  return le;
+  // streams are created on first use only: each one takes a hardware queue,
+  // and a stream that shares its queue with the caller's serialises with it
+  const int nside = MAX_PIECES > 1 ? 2 : 1;
+  for (int i = 0; i < nside; ++i)
+    if (!S.side[i] && (e = hipStreamCreateWithFlags(&S.side[i], hipStreamNonBlocking)) != hipSuccess)
+      return e;
+  S.used = 0;
+  S.err = hipSuccess;
+  *out = &S;
+  return hipSuccess;
+}
+
+// Byte offset helper: p advanced by n elements of `bytes` bytes.
+template <typename T>
+T* adv(T* q, int64_t n, size_t bytes) {
+  return q ? (T*)((const char*)q + n * (int64_t)bytes) : nullptr;
 }
 
 }  // namespace
@@ -252,91 +295,118 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   char* w = (char*)ws;
   hipStream_t s = (hipStream_t)stream;
   const bool bf = p->io_dtype == RAM_BF16;
+  const size_t io = d.io_bytes;
+  const int64_t TH = (int64_t)p->T * p->H, HS = (int64_t)p->H * d.S;
+  const int K = p->k_w + p->k_r, kmax = std::max(p->k_w, p->k_r);
+  const int cap = long_cap(p, d);
+  const Pieces P = make_pieces(p->B);
+
+  std::lock_guard<std::mutex> lk(sched_mu);
+  Sched* S = nullptr;
+  if (get_sched(&S) != hipSuccess) return RAM_EHIP;
+  // one piece: the serial part stays on the caller's stream (fewer
+  // cross-stream waits); only the short-segment scans run beside it
+  hipStream_t a = P.n > 1 ? S->side[1] : s, b = S->side[0];
+  S->dep(a, s);
   hipError_t e = hipSuccess;
+  for (int q = 0; q < P.n && e == hipSuccess && S->err == hipSuccess; ++q) {
+    const int b0 = P.b0[q], nb = P.b0[q + 1] - P.b0[q];
+    const int64_t r0 = (int64_t)b0 * TH, rows = (int64_t)nb * TH;   // token rows of the piece
 
-  DecodeFwdArgs da{};
-  da.logits[0] = wlogits;
-  da.logits[1] = rlogits;
-  da.idx[0] = (int32_t*)(w + L.idx_w);
-  da.idx[1] = (int32_t*)(w + L.idx_r);
-  da.w[0] = (float*)(w + L.w_w);
-  da.w[1] = (float*)(w + L.w_r);
-  da.lse[0] = (float*)(w + L.lse_w);
-  da.lse[1] = (float*)(w + L.lse_r);
-  da.k[0] = p->k_w;
-  da.k[1] = p->k_r;
-  da.renorm[0] = p->renorm_w;
-  da.renorm[1] = p->renorm_r;
-  da.N = d.N;
-  da.S = (int)d.S;
-  da.nsides = 2;
-  prof_before("decode_fwd", s);
-  e = launch_decode_fwd(da, bf, s);
-  prof_after("decode_fwd", s);
-  if (e != hipSuccess) return RAM_EHIP;
+    DecodeFwdArgs da{};
+    da.logits[0] = adv(wlogits, r0 * d.S, io);
+    da.logits[1] = adv(rlogits, r0 * d.S, io);
+    da.idx[0] = (int32_t*)(w + L.idx_w) + r0 * p->k_w;
+    da.idx[1] = (int32_t*)(w + L.idx_r) + r0 * p->k_r;
+    da.w[0] = (float*)(w + L.w_w) + r0 * p->k_w;
+    da.w[1] = (float*)(w + L.w_r) + r0 * p->k_r;
+    da.lse[0] = (float*)(w + L.lse_w) + r0;
+    da.lse[1] = (float*)(w + L.lse_r) + r0;
+    da.k[0] = p->k_w;
+    da.k[1] = p->k_r;
+    da.renorm[0] = p->renorm_w;
+    da.renorm[1] = p->renorm_r;
+    da.N = rows;
+    da.S = (int)d.S;
+    da.nsides = 2;
+    prof_before("decode_fwd", s);
+    e = launch_decode_fwd(da, bf, s);
+    prof_after("decode_fwd", s);
+    if (e != hipSuccess) break;
+    S->dep(a, s);
 
-  BucketArgs ba{};
-  ba.idx_w = da.idx[0];
-  ba.idx_r = da.idx[1];
-  ba.w_w = da.w[0];
-  ba.w_r = da.w[1];
-  ba.gamma = gamma;
-  ba.B = p->B;
-  ba.H = p->H;
-  ba.T = p->T;
-  ba.S = (int)d.S;
-  ba.k_w = p->k_w;
-  ba.k_r = p->k_r;
-  ba.ntiles = d.ntiles;
-  ba.nbits = d.nbits;
-  ba.tile_hist = (int32_t*)(w + L.tile_hist);
-  ba.seg_offset = (int32_t*)(w + L.seg_offset);
-  ba.events = (EventRec*)(w + L.events);
-  ba.long_list = (int32_t*)(w + L.long_list);
-  ba.long_count = (int32_t*)(w + L.long_count);
-  ba.long_cap = long_cap(d);
-  e = launch_bucket(ba, bf, s, prof_before, prof_after);
-  if (e != hipSuccess) return RAM_EHIP;
+    BucketArgs ba{};
+    ba.idx_w = da.idx[0];
+    ba.idx_r = da.idx[1];
+    ba.w_w = da.w[0];
+    ba.w_r = da.w[1];
+    ba.gamma = adv(gamma, r0, io);
+    ba.B = nb;
+    ba.H = p->H;
+    ba.T = p->T;
+    ba.S = (int)d.S;
+    ba.k_w = p->k_w;
+    ba.k_r = p->k_r;
+    ba.ntiles = d.ntiles;
+    ba.nbits = d.nbits;
+    ba.tile_hist = (int32_t*)(w + L.tile_hist) + (int64_t)b0 * p->H * d.ntiles * d.S;
+    ba.seg_offset = (int32_t*)(w + L.seg_offset) + (int64_t)b0 * HS;
+    ba.ev_base = r0 * K;
+    ba.events = (EventRec*)(w + L.events);
+    ba.long_list = (int32_t*)(w + L.long_list) + (int64_t)q * NBIN * cap;
+    ba.long_count = (int32_t*)(w + L.long_count) + q * NBIN;
+    ba.long_cap = cap;
+    e = launch_bucket(ba, bf, a, prof_before, prof_after);
+    if (e != hipSuccess) break;
 
-  ScanFwdArgs sa{};
-  sa.B = p->B;
-  sa.H = p->H;
-  sa.T = p->T;
-  sa.S = (int)d.S;
-  sa.d_v = p->d_v;
-  sa.k_w = p->k_w;
-  sa.k_r = p->k_r;
-  sa.eps = p->eps;
-  sa.nseg = d.nseg;
-  sa.long_list = ba.long_list;
-  sa.long_count = ba.long_count;
-  sa.long_cap = ba.long_cap;
-  sa.use_long = d.ntiles > 0;
-  sa.seg_offset = ba.seg_offset;
-  sa.events = ba.events;
-  sa.v = v;
-  sa.slot0 = slot0;
-  sa.mass0 = mass0;
-  sa.slot1 = slot1;
-  sa.mass1 = mass1;
-  sa.stash = w + L.stash;
-  sa.ckpt_s = (float*)(w + L.ckpt_s);
-  sa.ckpt_m = (float*)(w + L.ckpt_m);
-  prof_before("scan_fwd", s);
-  e = forked(s, [&](hipStream_t m, hipStream_t x) { return launch_scan_fwd(sa, bf, m, x); });
-  prof_after("scan_fwd", s);
-  if (e != hipSuccess) return RAM_EHIP;
+    ScanFwdArgs sa{};
+    sa.B = nb;
+    sa.H = p->H;
+    sa.T = p->T;
+    sa.S = (int)d.S;
+    sa.d_v = p->d_v;
+    sa.k_w = p->k_w;
+    sa.k_r = p->k_r;
+    sa.eps = p->eps;
+    sa.nseg = (int64_t)nb * HS;
+    sa.long_list = ba.long_list;
+    sa.long_count = ba.long_count;
+    sa.long_cap = cap;
+    sa.use_long = d.ntiles > 0;
+    sa.seg_offset = ba.seg_offset;
+    sa.events = ba.events;
+    sa.v = adv(v, r0 * p->d_v, io);
+    sa.slot0 = adv(slot0, (int64_t)b0 * HS * p->d_v, sizeof(float));
+    sa.mass0 = adv(mass0, (int64_t)b0 * HS, sizeof(float));
+    sa.slot1 = adv(slot1, (int64_t)b0 * HS * p->d_v, sizeof(float));
+    sa.mass1 = adv(mass1, (int64_t)b0 * HS, sizeof(float));
+    sa.stash = w + L.stash + r0 * kmax * p->d_v * (int64_t)io;
+    sa.ckpt_s = (float*)(w + L.ckpt_s);
+    sa.ckpt_m = (float*)(w + L.ckpt_m);
+    // The short-segment stream forks off just before the launch and joins
+    // right after it; the timing events bracket the fork and the join (an
+    // event recorded between the launch and the join slows the scans down).
+    prof_before("scan_fwd", a);
+    S->dep(b, a);
+    e = launch_scan_fwd(sa, bf, a, b);
+    S->dep(a, b);
+    prof_after("scan_fwd", a);
+    if (e != hipSuccess) break;
 
-  FinalizeArgs fa{};
-  fa.N = d.N;
-  fa.d_v = p->d_v;
-  fa.k = p->k_r;
-  fa.stash = sa.stash;
-  fa.out = o;
-  prof_before("finalize_o", s);
-  e = launch_finalize(fa, bf, s);
-  prof_after("finalize_o", s);
-  return hip_status(e);
+    FinalizeArgs fa{};
+    fa.N = rows;
+    fa.d_v = p->d_v;
+    fa.k = p->k_r;
+    fa.stash = sa.stash;
+    fa.out = adv(o, r0 * p->d_v, io);
+    prof_before("finalize_o", a);
+    e = launch_finalize(fa, bf, a);
+    prof_after("finalize_o", a);
+  }
+  S->dep(s, a);
+  S->dep(s, b);
+  if (e != hipSuccess || S->err != hipSuccess) return RAM_EHIP;
+  return RAM_OK;
 }
 
 int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wlogits,
@@ -361,80 +431,104 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   char* w = (char*)ws;
   hipStream_t s = (hipStream_t)stream;
   const bool bf = p->io_dtype == RAM_BF16;
-  hipError_t e;
+  const size_t io = d.io_bytes;
+  const int64_t TH = (int64_t)p->T * p->H, HS = (int64_t)p->H * d.S;
+  const int kmax = std::max(p->k_w, p->k_r);
+  const int cap = long_cap(p, d);
+  const Pieces P = make_pieces(p->B);
+  (void)gamma;   // the event records carry lambda and d lambda / d w
 
-  ScanBwdArgs sb{};
-  sb.B = p->B;
-  sb.H = p->H;
-  sb.T = p->T;
-  sb.S = (int)d.S;
-  sb.d_v = p->d_v;
-  sb.k_w = p->k_w;
-  sb.k_r = p->k_r;
-  sb.eps = p->eps;
-  sb.nseg = d.nseg;
-  sb.long_list = (const int32_t*)(w + L.long_list);
-  sb.long_count = (const int32_t*)(w + L.long_count);
-  sb.long_cap = long_cap(d);
-  sb.use_long = d.ntiles > 0;
-  sb.seg_offset = (const int32_t*)(w + L.seg_offset);
-  sb.events = (const EventRec*)(w + L.events);
-  sb.v = v;
-  sb.d_o = d_o;
-  sb.slot0 = slot0;
-  sb.mass0 = mass0;
-  sb.ckpt_s = (const float*)(w + L.ckpt_s);
-  sb.ckpt_m = (const float*)(w + L.ckpt_m);
-  sb.d_slot1 = d_slot1;
-  sb.d_mass1 = d_mass1;
-  sb.d_slot0 = d_slot0;
-  sb.d_mass0 = d_mass0;
-  sb.stash = w + L.stash;
-  sb.dw = (float*)(w + L.dw);
-  sb.dr = (float*)(w + L.dr);
-  sb.dgam = (float*)(w + L.dgam);
-  prof_before("scan_bwd", s);
-  e = forked(s, [&](hipStream_t m, hipStream_t x) { return launch_scan_bwd(sb, bf, m, x); });
-  prof_after("scan_bwd", s);
-  if (e != hipSuccess) return RAM_EHIP;
+  std::lock_guard<std::mutex> lk(sched_mu);
+  Sched* S = nullptr;
+  if (get_sched(&S) != hipSuccess) return RAM_EHIP;
+  // one piece: the serial part stays on the caller's stream (fewer
+  // cross-stream waits); only the short-segment scans run beside it
+  hipStream_t a = P.n > 1 ? S->side[1] : s, b = S->side[0];
+  S->dep(a, s);
+  hipError_t e = hipSuccess;
+  for (int q = 0; q < P.n && e == hipSuccess && S->err == hipSuccess; ++q) {
+    const int b0 = P.b0[q], nb = P.b0[q + 1] - P.b0[q];
+    const int64_t r0 = (int64_t)b0 * TH, rows = (int64_t)nb * TH;
 
-  DecodeBwdArgs db{};
-  db.logits[0] = wlogits;
-  db.logits[1] = rlogits;
-  db.lse[0] = (const float*)(w + L.lse_w);
-  db.lse[1] = (const float*)(w + L.lse_r);
-  db.idx[0] = (const int32_t*)(w + L.idx_w);
-  db.idx[1] = (const int32_t*)(w + L.idx_r);
-  db.w[0] = (const float*)(w + L.w_w);
-  db.w[1] = (const float*)(w + L.w_r);
-  db.g[0] = sb.dw;
-  db.g[1] = sb.dr;
-  db.dlogits[0] = d_wlogits;
-  db.dlogits[1] = d_rlogits;
-  db.k[0] = p->k_w;
-  db.k[1] = p->k_r;
-  db.renorm[0] = p->renorm_w;
-  db.renorm[1] = p->renorm_r;
-  db.N = d.N;
-  db.S = (int)d.S;
-  db.nsides = 2;
-  prof_before("decode_bwd", s);
-  e = launch_decode_bwd(db, bf, s);
-  prof_after("decode_bwd", s);
-  if (e != hipSuccess) return RAM_EHIP;
+    ScanBwdArgs sb{};
+    sb.B = nb;
+    sb.H = p->H;
+    sb.T = p->T;
+    sb.S = (int)d.S;
+    sb.d_v = p->d_v;
+    sb.k_w = p->k_w;
+    sb.k_r = p->k_r;
+    sb.eps = p->eps;
+    sb.nseg = (int64_t)nb * HS;
+    sb.long_list = (const int32_t*)(w + L.long_list) + (int64_t)q * NBIN * cap;
+    sb.long_count = (const int32_t*)(w + L.long_count) + q * NBIN;
+    sb.long_cap = cap;
+    sb.use_long = d.ntiles > 0;
+    sb.seg_offset = (const int32_t*)(w + L.seg_offset) + (int64_t)b0 * HS;
+    sb.events = (const EventRec*)(w + L.events);
+    sb.v = adv(v, r0 * p->d_v, io);
+    sb.d_o = adv(d_o, r0 * p->d_v, io);
+    sb.slot0 = adv(slot0, (int64_t)b0 * HS * p->d_v, sizeof(float));
+    sb.mass0 = adv(mass0, (int64_t)b0 * HS, sizeof(float));
+    sb.ckpt_s = (const float*)(w + L.ckpt_s);
+    sb.ckpt_m = (const float*)(w + L.ckpt_m);
+    sb.d_slot1 = adv(d_slot1, (int64_t)b0 * HS * p->d_v, sizeof(float));
+    sb.d_mass1 = adv(d_mass1, (int64_t)b0 * HS, sizeof(float));
+    sb.d_slot0 = adv(d_slot0, (int64_t)b0 * HS * p->d_v, sizeof(float));
+    sb.d_mass0 = adv(d_mass0, (int64_t)b0 * HS, sizeof(float));
+    sb.stash = w + L.stash + r0 * kmax * p->d_v * (int64_t)io;
+    sb.dw = (float*)(w + L.dw) + r0 * p->k_w;
+    sb.dr = (float*)(w + L.dr) + r0 * p->k_r;
+    sb.dgam = (float*)(w + L.dgam) + r0 * p->k_w;
+    prof_before("scan_bwd", a);
+    S->dep(b, a);
+    e = launch_scan_bwd(sb, bf, a, b);
+    S->dep(a, b);
+    prof_after("scan_bwd", a);
+    if (e != hipSuccess) break;
+    S->dep(s, a);
 
-  FinalizeArgs fa{};
-  fa.N = d.N;
-  fa.d_v = p->d_v;
-  fa.k = p->k_w;
-  fa.stash = sb.stash;
-  fa.out = d_v;
-  fa.dgam = sb.dgam;
-  fa.d_gamma = d_gamma;
-  prof_before("finalize_bwd", s);
-  e = launch_finalize(fa, bf, s);
-  prof_after("finalize_bwd", s);
-  return hip_status(e);
+    DecodeBwdArgs db{};
+    db.logits[0] = adv(wlogits, r0 * d.S, io);
+    db.logits[1] = adv(rlogits, r0 * d.S, io);
+    db.lse[0] = (const float*)(w + L.lse_w) + r0;
+    db.lse[1] = (const float*)(w + L.lse_r) + r0;
+    db.idx[0] = (const int32_t*)(w + L.idx_w) + r0 * p->k_w;
+    db.idx[1] = (const int32_t*)(w + L.idx_r) + r0 * p->k_r;
+    db.w[0] = (const float*)(w + L.w_w) + r0 * p->k_w;
+    db.w[1] = (const float*)(w + L.w_r) + r0 * p->k_r;
+    db.g[0] = sb.dw;
+    db.g[1] = sb.dr;
+    db.dlogits[0] = adv(d_wlogits, r0 * d.S, io);
+    db.dlogits[1] = adv(d_rlogits, r0 * d.S, io);
+    db.k[0] = p->k_w;
+    db.k[1] = p->k_r;
+    db.renorm[0] = p->renorm_w;
+    db.renorm[1] = p->renorm_r;
+    db.N = rows;
+    db.S = (int)d.S;
+    db.nsides = 2;
+    prof_before("decode_bwd", s);
+    e = launch_decode_bwd(db, bf, s);
+    prof_after("decode_bwd", s);
+    if (e != hipSuccess) break;
+
+    FinalizeArgs fa{};
+    fa.N = rows;
+    fa.d_v = p->d_v;
+    fa.k = p->k_w;
+    fa.stash = sb.stash;
+    fa.out = adv(d_v, r0 * p->d_v, io);
+    fa.dgam = sb.dgam;
+    fa.d_gamma = adv(d_gamma, r0, io);
+    prof_before("finalize_bwd", s);
+    e = launch_finalize(fa, bf, s);
+    prof_after("finalize_bwd", s);
+  }
+  S->dep(s, a);
+  S->dep(s, b);
+  if (e != hipSuccess || S->err != hipSuccess) return RAM_EHIP;
+  return RAM_OK;
 }
 
 int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,

@@ -58,16 +58,25 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketArgs a) {
   const int tid = threadIdx.x;
   const int S = a.S;
   int32_t* th = a.tile_hist + (int64_t)bh * a.ntiles * S;
-  const int64_t base = (int64_t)bh * a.T * (a.k_w + a.k_r);
+  const int64_t base = a.ev_base + (int64_t)bh * a.T * (a.k_w + a.k_r);
   int carry = 0;
   for (int s0 = 0; s0 < S; s0 += 1024) {
     const int s = s0 + tid;
     int cnt = 0;
     if (s < S) {
-      for (int tile = 0; tile < a.ntiles; ++tile) {
-        const int c = th[(int64_t)tile * S + s];
-        th[(int64_t)tile * S + s] = cnt;
-        cnt += c;
+      // exclusive prefix over the tiles, in place; loads in groups of TG so
+      // that a group costs one memory round trip
+      constexpr int TG = 8;
+      for (int t0 = 0; t0 < a.ntiles; t0 += TG) {
+        int c[TG];
+#pragma unroll
+        for (int u = 0; u < TG; ++u)
+          c[u] = (t0 + u < a.ntiles) ? th[(int64_t)(t0 + u) * S + s] : 0;
+#pragma unroll
+        for (int u = 0; u < TG; ++u) {
+          if (t0 + u < a.ntiles) th[(int64_t)(t0 + u) * S + s] = cnt;
+          cnt += c[u];
+        }
       }
     }
     const int incl = wave_incl_scan(cnt);
@@ -93,7 +102,8 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketArgs a) {
     __syncthreads();
   }
   if (bh == a.B * a.H - 1 && tid == 0)
-    a.seg_offset[(int64_t)a.B * a.H * S] = (int32_t)((int64_t)a.B * a.H * a.T * (a.k_w + a.k_r));
+    a.seg_offset[(int64_t)a.B * a.H * S] =
+        (int32_t)(a.ev_base + (int64_t)a.B * a.H * a.T * (a.k_w + a.k_r));
 }
 
 template <typename IO>

@@ -34,8 +34,10 @@ struct BucketArgs {
   int ntiles;             // ceil(T / TILE_TOKENS)
   int nbits;              // bits needed for a slot index
   int32_t* tile_hist;     // (B*H, ntiles, S)
-  int32_t* seg_offset;    // (B*H*S + 1)
-  EventRec* events;       // (E)
+  int32_t* seg_offset;    // (B*H*S + 1): absolute positions in `events`
+  int64_t ev_base;        // position of these rows' first event (B counts the batches
+                          // of this call's piece; events is the whole list)
+  EventRec* events;       // (all events of the call)
   int32_t* long_list;     // (NBIN, long_cap): segments with more than LONG_EVENTS events
   int32_t* long_count;    // (NBIN): entries per class
   int long_cap;

@@ -1004,14 +1004,14 @@ int resident_blocks(void (*kern)(Args), int threads) {
   return cus > 0 && per_cu > 0 ? cus * per_cu : 0;
 }
 
-// Short kernel on `side`, long kernel on `st` (the caller orders the two
+// Long kernel on `st`, short kernel on `side` (the caller orders the two
 // streams).  The long grid is the resident workgroup count, capped by the
-// list capacity: a grid-stride walk needs no more.
+// list capacity: a grid-stride walk needs no more.  The long kernel is
+// enqueued first so that its workgroups, which hold the critical path, are
+// resident before the short kernel's many small ones fill the device.
 template <typename Args>
 hipError_t launch_pair(void (*shortk)(Args), void (*longk)(Args), int& resident, const Args& a,
                        hipStream_t st, hipStream_t side) {
-  const unsigned sgrid = (unsigned)((a.nseg + SHORT_WAVES - 1) / SHORT_WAVES);
-  hipLaunchKernelGGL(shortk, dim3(sgrid), dim3(SHORT_WAVES * WAVE), 0, side, a);
   if (a.use_long) {
     if (resident == 0) resident = resident_blocks(longk, NWL * WAVE);
     if (resident == 0) return hipErrorInvalidDeviceFunction;
@@ -1019,6 +1019,8 @@ hipError_t launch_pair(void (*shortk)(Args), void (*longk)(Args), int& resident,
     const unsigned lgrid = (unsigned)(cap < resident ? cap : resident);
     hipLaunchKernelGGL(longk, dim3(lgrid), dim3(NWL * WAVE), 0, st, a);
   }
+  const unsigned sgrid = (unsigned)((a.nseg + SHORT_WAVES - 1) / SHORT_WAVES);
+  hipLaunchKernelGGL(shortk, dim3(sgrid), dim3(SHORT_WAVES * WAVE), 0, side, a);
   return hipGetLastError();
 }
 }  // namespace
