@@ -22,7 +22,7 @@ namespace ramk {
 
 // One wave per row; rows of side 0 first, then side 1.  NV > 0: rows of at
 // most NV * 64 vectors, held in registers; NV = 0: any length, streamed.
-template <typename IO, int NV>
+template <typename IO, int NV, bool FULL = false>
 __global__ __launch_bounds__(256) void decode_fwd_kernel(DecodeFwdArgs a) {
   __shared__ DecodeScratch scratch[4];
   __shared__ int s_idx[4][MAX_K];
@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256) void decode_fwd_kernel(DecodeFwdArgs a) {
   const int k = a.k[side];
   float lse;
   if constexpr (NV > 0)
-    lse = decode_row_resident<IO, NV>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
+    lse = decode_row_resident<IO, NV, FULL>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv],
+                                            s_w[wv]);
   else
     lse = decode_row_wave<IO>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
   wave_sync();
@@ -129,13 +130,15 @@ hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st) 
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   const int nvec = a.S / (bf16 ? 8 : 4);
   if (bf16) {
-    if (nvec <= 64) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 1>), grid, block, 0, st, a);
+    if (nvec == 512) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 8, true>), grid, block, 0, st, a);
+    else if (nvec <= 64) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 1>), grid, block, 0, st, a);
     else if (nvec <= 128) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 2>), grid, block, 0, st, a);
     else if (nvec <= 256) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 4>), grid, block, 0, st, a);
     else if (nvec <= 512) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 8>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 0>), grid, block, 0, st, a);
   } else {
-    if (nvec <= 64) hipLaunchKernelGGL((decode_fwd_kernel<float, 1>), grid, block, 0, st, a);
+    if (nvec == 512) hipLaunchKernelGGL((decode_fwd_kernel<float, 8, true>), grid, block, 0, st, a);
+    else if (nvec <= 64) hipLaunchKernelGGL((decode_fwd_kernel<float, 1>), grid, block, 0, st, a);
     else if (nvec <= 128) hipLaunchKernelGGL((decode_fwd_kernel<float, 2>), grid, block, 0, st, a);
     else if (nvec <= 256) hipLaunchKernelGGL((decode_fwd_kernel<float, 4>), grid, block, 0, st, a);
     else if (nvec <= 512) hipLaunchKernelGGL((decode_fwd_kernel<float, 8>), grid, block, 0, st, a);

@@ -64,10 +64,14 @@ __device__ __forceinline__ uint4 load_vec(const IO* row, int c, int nvec) {
   return (c < nvec) ? *reinterpret_cast<const uint4*>(row + (int64_t)c * vec16<IO>::E)
                     : neg_inf16<IO>();
 }
-// Same for a row that is read exactly once.
-template <typename IO>
+// Same for a row that is read exactly once.  The load itself is
+// unconditional (a clamped address), so all of a lane's loads stay in flight
+// together; FULL: the caller knows c < nvec.
+template <typename IO, bool FULL>
 __device__ __forceinline__ uint4 load_vec_nt(const IO* row, int c, int nvec) {
-  return (c < nvec) ? ld_nt16(row + (int64_t)c * vec16<IO>::E) : neg_inf16<IO>();
+  if constexpr (FULL) return ld_nt16(row + (int64_t)c * vec16<IO>::E);
+  const uint4 t = ld_nt16(row + (int64_t)min(c, nvec - 1) * vec16<IO>::E);
+  return (c < nvec) ? t : neg_inf16<IO>();
 }
 
 // Makes the compiler forget what it knows about q (emits no code), so values
@@ -162,15 +166,16 @@ __device__ __forceinline__ void finish_weights(const DecodeScratch& sc, int k, f
 // Decodes one row of at most NV * 64 16-byte vectors with the calling wave,
 // holding the whole row in registers (lane l: vectors l, l + 64, ...):
 // one read of the row from memory, then every pass works on registers.
-template <typename IO, int NV>
+// FULL: the row has exactly NV * 64 vectors.
+template <typename IO, int NV, bool FULL>
 __device__ float decode_row_resident(const IO* __restrict__ row, int S, int k, int renorm,
                                      DecodeScratch& sc, int* sel_i, float* sel_w) {
   constexpr int E = vec16<IO>::E;
   const int lane = lane_id();
-  const int nvec = S / E;
+  const int nvec = FULL ? NV * WAVE : S / E;
   uint4 q[NV];
 #pragma unroll
-  for (int u = 0; u < NV; ++u) q[u] = load_vec_nt<IO>(row, u * WAVE + lane, nvec);
+  for (int u = 0; u < NV; ++u) q[u] = load_vec_nt<IO, FULL>(row, u * WAVE + lane, nvec);
   float vm[NV];            // maximum of each of the lane's vectors
   float m = -INFINITY;
 #pragma unroll
