@@ -201,18 +201,22 @@ struct Ev {
   float dl;     // d lambda / d w (writes), 0 for reads
 };
 
-// Record of event cs + (lane & 15) for (lane & 15) < n; issued early so the
-// next chunk's records arrive while the current chunk computes.
-__device__ __forceinline__ float4 load_rec(const EventRec* events, int cs, int n) {
-  const int i = lane_id() & (CHUNK - 1);
-  return (i < n) ? *reinterpret_cast<const float4*>(events + cs + i)
-                 : make_float4(__int_as_float(1 << 6), 0.f, 1.f, 0.f);
+// Raw record of event cs + (lane & 15), clamped into the segment's non-empty
+// range [beg, end).  The load is unconditional and its value is only
+// inspected when the chunk is decoded (lanes past the chunk then become a
+// read of weight 0), so an early load of the next chunk's records stays in
+// flight while the current chunk computes.
+__device__ __forceinline__ float4 load_rec(const EventRec* events, int cs, int n, int beg, int end) {
+  (void)n;
+  const int at = min(max(cs + (lane_id() & (CHUNK - 1)), beg), end - 1);
+  return *reinterpret_cast<const float4*>(events + at);
 }
 
-__device__ __forceinline__ Ev decode_rec(float4 r, int n, int h, int H) {
+__device__ __forceinline__ Ev decode_rec(float4 raw, int n, int h, int H) {
   Ev e;
-  const int code = __float_as_int(r.x);
   e.valid = (lane_id() & (CHUNK - 1)) < n;
+  const float4 r = e.valid ? raw : make_float4(__int_as_float(1 << 6), 0.f, 1.f, 0.f);
+  const int code = __float_as_int(r.x);
   e.side = (code >> 6) & 1;
   e.j = code & 63;
   e.rb = (code >> 7) * H + h;
@@ -307,21 +311,34 @@ __device__ __forceinline__ int chunk_start(int p, int k, int end) {
   return min(end, (p / CHUNK + k) * CHUNK);
 }
 
-// Entry i of the long-segment list, longest class first.
-__device__ __forceinline__ int64_t long_entry(const int32_t* list, const int32_t* count, int cap,
-                                              int i) {
-  for (int c = NBIN - 1; c >= 0; --c) {
-    const int n = count[c];
-    if (i < n) return list[(int64_t)c * cap + i];
-    i -= n;
-  }
-  return -1;
-}
-__device__ __forceinline__ int long_total(const int32_t* count) {
-  int n = 0;
+// Entry counts of the long-segment list's length classes, read once per
+// workgroup (independent loads).
+struct LongCounts {
+  int n[NBIN];
+  int total;
+};
+__device__ __forceinline__ LongCounts long_counts(const int32_t* count) {
+  LongCounts L;
+  L.total = 0;
 #pragma unroll
-  for (int c = 0; c < NBIN; ++c) n += count[c];
-  return n;
+  for (int c = 0; c < NBIN; ++c) L.n[c] = count[c];
+#pragma unroll
+  for (int c = 0; c < NBIN; ++c) L.total += L.n[c];
+  return L;
+}
+// Entry i < total of the list, longest class first.
+__device__ __forceinline__ int64_t long_entry(const int32_t* list, const LongCounts& L, int cap,
+                                              int i) {
+  int64_t pos = 0;
+  bool found = false;
+#pragma unroll
+  for (int c = NBIN - 1; c >= 0; --c) {
+    if (!found) {
+      if (i < L.n[c]) { pos = (int64_t)c * cap + i; found = true; }
+      else i -= L.n[c];
+    }
+  }
+  return list[pos];
 }
 
 // Per-event mass of a chunk from the incoming mass m: mi after the event,
@@ -367,7 +384,8 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
   for (int k = 0; k < CPL; ++k) s[k] = (c.active && a.slot0) ? a.slot0[g * a.d_v + c.c0 + k] : 0.f;
   float m = a.mass0 ? a.mass0[g] : 0.f;
 
-  float4 rec = load_rec(a.events, beg, min(end, (beg / CHUNK + 1) * CHUNK) - beg);
+  float4 rec = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (beg < end) rec = load_rec(a.events, beg, min(end, (beg / CHUNK + 1) * CHUNK) - beg, beg, end);
   for (int p0 = beg; p0 < end;) {
     const int p1 = min(end, (p0 / CHUNK + 1) * CHUNK);
     const int n = p1 - p0;
@@ -386,7 +404,7 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
     const float rr = (ev.side == 1) ? ev.wt : 0.f;
     const uint32_t xo = (ev.valid && ev.side == 0) ? (uint32_t)ev.rb * c.pitch : OOB;
     const uint32_t so = (ev.valid && ev.side == 1) ? ((uint32_t)ev.rb * a.k_r + ev.j) * c.pitch : OOB;
-    rec = load_rec(a.events, p1, min(end, (p1 / CHUNK + 1) * CHUNK) - p1);   // next chunk
+    rec = load_rec(a.events, p1, min(end, (p1 / CHUNK + 1) * CHUNK) - p1, beg, end);   // next chunk
 
     typename LN::Raw x[CHUNK];
     for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo) + c.lb); });
@@ -432,7 +450,7 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
   float m_carry = a.mass0 ? a.mass0[g] : 0.f;
 
   float4 rec = load_rec(a.events, chunk_start(beg, w, end),
-                        chunk_start(beg, w + 1, end) - chunk_start(beg, w, end));
+                        chunk_start(beg, w + 1, end) - chunk_start(beg, w, end), beg, end);
   for (int p = beg; p < end;) {
     const int cs = chunk_start(p, w, end);
     const int n = chunk_start(p, w + 1, end) - cs;
@@ -451,9 +469,10 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
     // content loads do not depend on the mass: issue them before the barrier
     typename LN::Raw x[CHUNK];
     for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo) + c.lb); });
-    if (pn < end)   // next super-chunk's records for this wave
-      rec = load_rec(a.events, chunk_start(pn, w, end),
-                     chunk_start(pn, w + 1, end) - chunk_start(pn, w, end));
+    // next super-chunk's records for this wave (unconditional: past the end
+    // it reloads the last event, unused)
+    rec = load_rec(a.events, chunk_start(pn, w, end),
+                   chunk_start(pn, w + 1, end) - chunk_start(pn, w, end), beg, end);
     __syncthreads();
     float m_in = m_carry, m_next = m_carry;
     for (int k = 0; k < NW; ++k) {
@@ -539,9 +558,9 @@ __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_fwd_short_kernel(Scan
 // longest class first.
 template <typename IO, int CPL>
 __global__ __launch_bounds__(NWL * WAVE) void scan_fwd_long_kernel(ScanFwdArgs a) {
-  const int count = long_total(a.long_count);
-  for (int i = blockIdx.x; i < count; i += gridDim.x)
-    scan_fwd_long<IO, CPL>(a, long_entry(a.long_list, a.long_count, a.long_cap, i));
+  const LongCounts L = long_counts(a.long_count);
+  for (int i = blockIdx.x; i < L.total; i += gridDim.x)
+    scan_fwd_long<IO, CPL>(a, long_entry(a.long_list, L, a.long_cap, i));
 }
 
 // ---------------------------------------------------------------------------
@@ -706,20 +725,28 @@ __device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const SegCtx<I
 
 // State at the start of chunk cs of segment g: the initial state for the
 // segment's first chunk, else the checkpoint the forward saved.
+// The loads are unconditional (a valid address is always chosen: an
+// inactive lane reads the row's last channels, a missing initial state reads
+// checkpoint 0) and the value is selected afterwards, so no wait sits inside
+// a branch.  cs may be the segment end (an empty chunk of the long path):
+// checkpoint cs / 16 <= E / 16 exists.
 template <typename IO, int CPL>
 __device__ __forceinline__ void chunk_state(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
                                             int64_t g, int beg, int cs, float (&s)[CPL],
                                             float& m) {
-  if (cs == beg) {
+  const bool first = cs == beg;
+  const bool zero = first && !a.slot0;
+  const float* sp = first ? (a.slot0 ? a.slot0 + g * a.d_v : a.ckpt_s)
+                          : a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
+  const float* mp = first ? (a.mass0 ? a.mass0 + g : a.ckpt_m) : a.ckpt_m + cs / CHUNK;
+  const int cc = min(c.c0, a.d_v - CPL);
+  float t[CPL];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) s[k] = (c.active && a.slot0) ? a.slot0[g * a.d_v + c.c0 + k] : 0.f;
-    m = a.mass0 ? a.mass0[g] : 0.f;
-  } else {
-    const float* cp = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
+  for (int k = 0; k < CPL; ++k) t[k] = sp[cc + k];
+  const float tm = *mp;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) s[k] = c.active ? cp[c.c0 + k] : 0.f;
-    m = a.ckpt_m[cs / CHUNK];
-  }
+  for (int k = 0; k < CPL; ++k) s[k] = (zero || !c.active) ? 0.f : t[k];
+  m = zero ? 0.f : tm;
 }
 
 template <typename IO, int CPL>
@@ -743,14 +770,14 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
     BwdChunk<IO, CPL, false> ck;
     float pr[CHUNK], pw[CHUNK];
     int cs = max(beg, ((end - 1) / CHUNK) * CHUNK);
-    float4 rec = load_rec(a.events, cs, end - cs);
+    float4 rec = load_rec(a.events, cs, end - cs, beg, end);
     while (true) {
       const int n = min(end, (cs / CHUNK + 1) * CHUNK) - cs;
       const int cp = max(beg, cs - CHUNK);
       float s[CPL], m;
       chunk_state<IO, CPL>(a, c, g, beg, cs, s, m);
       const float4 rec_cur = rec;
-      if (cs != beg) rec = load_rec(a.events, cp, cs - cp);   // previous chunk
+      rec = load_rec(a.events, cp, cs - cp, beg, end);   // previous chunk (unused after the first)
       bwd_setup(a, c, rv, ro, ck, rec_cur, n, m);
       bwd_replay(ck, s, pr);
       const float red_r = batched_sum(pr);
@@ -822,20 +849,18 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
   {
     int cs0, n0;
     chunk_of(((nchunks - 1) / NW) * NW + w, cs0, n0);
-    rec = load_rec(a.events, cs0, n0);
+    rec = load_rec(a.events, cs0, n0, beg, end);
   }
   for (int u0 = ((nchunks - 1) / NW) * NW; u0 >= 0; u0 -= NW) {
     int cs, n;
     chunk_of(u0 + w, cs, n);
-    float s[CPL], m = 0.f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) s[k] = 0.f;
-    if (n > 0) chunk_state<IO, CPL>(a, c, g, beg, cs, s, m);
+    float s[CPL], m;
+    chunk_state<IO, CPL>(a, c, g, beg, cs, s, m);
     const float4 rec_cur = rec;
-    if (u0 >= NW) {   // this wave's chunk of the previous super-chunk
+    {   // this wave's chunk of the previous super-chunk (unconditional; unused after the first)
       int csp, np;
-      chunk_of(u0 - NW + w, csp, np);
-      rec = load_rec(a.events, csp, np);
+      chunk_of(max(u0 - NW, 0) + w, csp, np);
+      rec = load_rec(a.events, csp, np, beg, end);
     }
     bwd_setup(a, c, rv, ro, ck, rec_cur, n, m);
     bwd_replay(ck, s, pr);
@@ -942,9 +967,9 @@ __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_bwd_short_kernel(Scan
 
 template <typename IO, int CPL>
 __global__ __launch_bounds__(NWL * WAVE) void scan_bwd_long_kernel(ScanBwdArgs a) {
-  const int count = long_total(a.long_count);
-  for (int i = blockIdx.x; i < count; i += gridDim.x)
-    scan_bwd_long<IO, CPL>(a, long_entry(a.long_list, a.long_count, a.long_cap, i));
+  const LongCounts L = long_counts(a.long_count);
+  for (int i = blockIdx.x; i < L.total; i += gridDim.x)
+    scan_bwd_long<IO, CPL>(a, long_entry(a.long_list, L, a.long_cap, i));
 }
 
 // ---------------------------------------------------------------------------
