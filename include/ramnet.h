@@ -29,8 +29,12 @@
  *               (paper §4 "Slot-Parallel Execution"; ramnet-ops "CUDA
  *               execution", parallel and autoregressive modes).
  *
- * Supported: one address digit (U = 1, P = S); CAPE (cape_heads) is not
- * supported yet and is rejected.  One batch's rows of v (and of the read-out
+ *   CAPE        heads h < cape_heads address slot (a + t0 + t) mod S for the
+ *               content-selected index a of token t (ramnet-ops "Quick start",
+ *               embed_num; paper App. C); selection and its tie order stay on
+ *               the content logits, gradients flow to logit a.
+ *
+ * Supported: one address digit (U = 1, P = S).  One batch's rows of v (and of the read-out
  * and gradient staging, T*H*max(k_w, k_r)*d_v io values) must fit in
  * 0x7FE00000 bytes, else RAM_ECAPACITY (split T over calls).
  *
@@ -74,7 +78,7 @@ extern "C" {
 #define RAM_EINVAL (-1)       /* bad shape, null pointer, k > S, misalignment  */
 #define RAM_EDTYPE (-2)       /* io_dtype not RAM_F32 / RAM_BF16               */
 #define RAM_ECAPACITY (-3)    /* too many events or tokens, workspace too small */
-#define RAM_EUNSUPPORTED (-4) /* U > 1 or cape_heads > 0                        */
+#define RAM_EUNSUPPORTED (-4) /* U > 1 or S > 16384                              */
 #define RAM_EHIP (-5)         /* HIP launch or runtime error                    */
 
 #define RAM_F32 0
@@ -90,9 +94,9 @@ typedef struct ram_problem {
   float eps;            /* GSU epsilon (finite, >= 0; the paper's default reading 1e-6) */
   int32_t renorm_w;     /* 1: renormalise the kept write weights to sum 1               */
   int32_t renorm_r;     /* 1: same for the read side                                    */
-  int32_t cape_heads;   /* heads using CAPE; must be 0                                  */
+  int32_t cape_heads;   /* heads h < cape_heads use CAPE, 0 <= cape_heads <= H          */
   int32_t reserved;     /* must be 0                                                    */
-  int64_t t0;           /* absolute position of token 0 (CAPE only)                     */
+  int64_t t0;           /* absolute position (>= 0) of token 0 (CAPE only)              */
 } ram_problem;
 
 /* Byte offsets of the arrays that ram_forward leaves in the workspace for
@@ -130,7 +134,8 @@ int ram_workspace_layout(const ram_problem* p, ram_ws_layout* out);
 
 /* Address decode of one side (paper §3.2 with U = 1): for every row
  * (b, t, h) of logits (B,T,H,S), writes idx (B,T,H,k) int32 with the K
- * selected slots in (logit desc, index asc) order, weight (B,T,H,k) float with
+ * selected slots in (logit desc, index asc) order (CAPE heads: the addressed
+ * slot, i.e. the selected index shifted as above), weight (B,T,H,k) float with
  * their probabilities exp(l - lse) (renormalised if the side's renorm flag is
  * set) and lse (B,T,H) float.  side: 0 write (k_w, renorm_w), 1 read. */
 int ram_decode(const ram_problem* p, int side, const void* logits, int32_t* idx, float* weight,
@@ -163,8 +168,9 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
 /* Autoregressive step (ramnet-ops "CUDA execution", autoregressive mode;
  * paper §4: each new token updates and reads its own K slots): p->T == 1;
  * decode both sides of the one token per (b, h), apply its k_w writes to
- * slot / mass in place, then read its k_r slots into o (B,1,H,d_v).  Needs
- * k_w * d_v <= 8192.  No workspace. */
+ * slot / mass in place, then read its k_r slots into o (B,1,H,d_v); o is
+ * the float32 sum of the K terms, rounded once to the io dtype.  For CAPE,
+ * t0 is the position of this token.  Needs k_w * d_v <= 8192.  No workspace. */
 int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
                     const void* gamma, float* slot, float* mass, void* o, void* stream);
 

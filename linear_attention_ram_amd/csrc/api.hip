@@ -26,10 +26,10 @@ struct Dims {
 int check_problem(const ram_problem* p, Dims* d) {
   if (!p) return RAM_EINVAL;
   if (p->io_dtype != RAM_F32 && p->io_dtype != RAM_BF16) return RAM_EDTYPE;
-  if (p->cape_heads != 0) return RAM_EUNSUPPORTED;
   if (p->U != 1) return RAM_EUNSUPPORTED;
   if (p->reserved != 0) return RAM_EINVAL;
   if (p->B < 1 || p->H < 1 || p->T < 0 || p->P < 1) return RAM_EINVAL;
+  if (p->cape_heads < 0 || p->cape_heads > p->H || p->t0 < 0) return RAM_EINVAL;
   const int64_t S = p->P;
   if (S > 16384) return RAM_EUNSUPPORTED;
   const size_t io = p->io_dtype == RAM_F32 ? 4 : 2;
@@ -231,7 +231,7 @@ const char* ram_status_string(int status) {
     case RAM_EINVAL: return "invalid argument (shape, pointer, k, d_v, alignment)";
     case RAM_EDTYPE: return "unsupported io dtype";
     case RAM_ECAPACITY: return "capacity exceeded (events, tokens or workspace size)";
-    case RAM_EUNSUPPORTED: return "unsupported configuration (U > 1, CAPE or S > 16384)";
+    case RAM_EUNSUPPORTED: return "unsupported configuration (U > 1 or S > 16384)";
     case RAM_EHIP: return "HIP runtime or launch error";
     default: return "unknown status";
   }
@@ -272,6 +272,10 @@ int ram_decode(const ram_problem* p, int side, const void* logits, int32_t* idx,
   a.N = d.N;
   a.S = (int)d.S;
   a.nsides = 1;
+  a.H = p->H;
+  a.T = p->T;
+  a.cape_heads = p->cape_heads;
+  a.t0 = p->t0;
   hipStream_t s = (hipStream_t)stream;
   prof_before("decode_fwd", s);
   hipError_t e = launch_decode_fwd(a, p->io_dtype == RAM_BF16, s);
@@ -329,6 +333,10 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
     da.N = rows;
     da.S = (int)d.S;
     da.nsides = 2;
+    da.H = p->H;
+    da.T = p->T;
+    da.cape_heads = p->cape_heads;
+    da.t0 = p->t0;
     prof_before("decode_fwd", s);
     e = launch_decode_fwd(da, bf, s);
     prof_after("decode_fwd", s);
@@ -508,6 +516,10 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
     db.N = rows;
     db.S = (int)d.S;
     db.nsides = 2;
+    db.H = p->H;
+    db.T = p->T;
+    db.cape_heads = p->cape_heads;
+    db.t0 = p->t0;
     prof_before("decode_bwd", s);
     e = launch_decode_bwd(db, bf, s);
     prof_after("decode_bwd", s);
@@ -549,6 +561,8 @@ int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogi
   a.k_r = p->k_r;
   a.renorm_w = p->renorm_w;
   a.renorm_r = p->renorm_r;
+  a.cape_heads = p->cape_heads;
+  a.t0 = p->t0;
   a.eps = p->eps;
   a.wl = wlogits;
   a.rl = rlogits;

@@ -20,7 +20,8 @@
 
 namespace ramk {
 
-// One wave per row; rows of side 0 first, then side 1.  NV > 0: rows of at
+// One wave per row; rows of side 0 first, then side 1.  The stored index is
+// the slot the token addresses (CAPE-shifted for CAPE heads).  NV > 0: rows of at
 // most NV * 64 vectors, held in registers; NV = 0: any length, streamed.
 template <typename IO, int NV, bool FULL = false>
 __global__ __launch_bounds__(256) void decode_fwd_kernel(DecodeFwdArgs a) {
@@ -43,7 +44,9 @@ __global__ __launch_bounds__(256) void decode_fwd_kernel(DecodeFwdArgs a) {
     lse = decode_row_wave<IO>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
   wave_sync();
   if (lane < k) {
-    a.idx[side][row * k + lane] = s_idx[wv][lane];
+    const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
+    const int id = s_idx[wv][lane];
+    a.idx[side][row * k + lane] = (shift < 0) ? id : (id + shift) % a.S;
     a.w[side][row * k + lane] = s_w[wv][lane];
   }
   if (lane == 0) a.lse[side][row] = lse;
@@ -80,6 +83,9 @@ __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
     gj = a.g[side][row * k + lane];
     wj = a.w[side][row * k + lane];
     aj = a.idx[side][row * k + lane];
+    // the logit behind a CAPE slot is the content index (slot - shift)
+    const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
+    if (shift >= 0) aj = (aj - shift + a.S) % a.S;
     lj = to_f32(src[aj]);
   }
   if (a.renorm[side]) {

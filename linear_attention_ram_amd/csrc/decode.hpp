@@ -33,7 +33,22 @@ struct DecodeFwdArgs {
   int nsides;              // 1 or 2 (side 0 = first pointer set)
   float* zero_rows;        // optional (N, zero_width) float rows to clear
   int zero_width;
+  int H, T;                // row r is token (r / H) % T of head r % H
+  int cape_heads;          // heads h < cape_heads shift the chosen slot by (t0 + t) mod S
+  int64_t t0;
 };
+
+// CAPE (ramnet-ops "Quick start", embed_num; paper App. C): for the first
+// cape_heads heads the slot addressed by a token is its content-selected
+// index shifted cyclically by the token's absolute position.  The shift of
+// row r, or -1 for heads without CAPE.
+__device__ __forceinline__ int cape_shift_of(int64_t r, int H, int T, int S, int cape_heads,
+                                             int64_t t0) {
+  const int h = (int)(r % H);
+  if (h >= cape_heads) return -1;
+  const int64_t t = (r / H) % T;
+  return (int)((t0 % S + t) % S);
+}
 
 struct DecodeBwdArgs {
   const void* logits[2];
@@ -47,6 +62,9 @@ struct DecodeBwdArgs {
   int64_t N;
   int S;
   int nsides;
+  int H, T;                // as in DecodeFwdArgs: idx holds shifted slots of CAPE heads
+  int cape_heads;
+  int64_t t0;
 };
 
 hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st);

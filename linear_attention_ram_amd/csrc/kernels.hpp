@@ -100,6 +100,8 @@ struct FinalizeArgs {
 
 struct StepArgs {
   int B, H, S, d_v, k_w, k_r, renorm_w, renorm_r;
+  int cape_heads;         // heads h < cape_heads address (content index + t0) mod S
+  int64_t t0;             // absolute position of the token
   float eps;
   const void* wl;         // (B*H, S) io
   const void* rl;

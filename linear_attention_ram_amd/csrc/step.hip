@@ -24,6 +24,10 @@ __global__ __launch_bounds__(128) void decode_step_kernel(StepArgs a) {
   const IO* logits = reinterpret_cast<const IO*>(wv == 0 ? a.wl : a.rl) + (int64_t)bh * a.S;
   decode_row_wave<IO>(logits, a.S, wv == 0 ? a.k_w : a.k_r, wv == 0 ? a.renorm_w : a.renorm_r,
                       scratch[wv], sel_i[wv], sel_w[wv]);
+  // CAPE heads address the content index shifted by the token's position
+  // (each lane rewrites the entry it wrote)
+  if ((bh % a.H) < a.cape_heads && lane < (wv == 0 ? a.k_w : a.k_r))
+    sel_i[wv][lane] = (int)((sel_i[wv][lane] + a.t0 % a.S) % a.S);
   __syncthreads();
 
   const int d_v = a.d_v;

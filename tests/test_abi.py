@@ -61,7 +61,9 @@ def test_valid_problem_has_positive_workspace():
     (dict(H=0), ram.RAM_EINVAL),
     (dict(eps=-1.0), ram.RAM_EINVAL),
     (dict(S=32768), ram.RAM_EUNSUPPORTED),
-    (dict(cape_heads=1), ram.RAM_EUNSUPPORTED),
+    (dict(cape_heads=4), ram.RAM_EINVAL),     # more CAPE heads than heads
+    (dict(cape_heads=1, t0=-1), ram.RAM_EINVAL),
+    (dict(cape_heads=3, t0=1 << 40), ram.RAM_OK),
     (dict(T=1 << 24), ram.RAM_ECAPACITY),
     (dict(B=4096, T=8192, H=16, S=64, k_w=8, k_r=8), ram.RAM_ECAPACITY),
     # one batch's staging rows (T*H*k*d_v bf16) above the scans' buffer limit
