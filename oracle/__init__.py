@@ -72,9 +72,9 @@ def lib():
         vp = ctypes.c_void_p
         L.orc_set_threads.argtypes = [ctypes.c_int]
         L.orc_decode.argtypes = [P, ctypes.c_int, vp, vp, vp, vp]
-        L.orc_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.orc_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
-        L.orc_backward.argtypes = [P] + [vp] * 17
+        L.orc_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_backward.argtypes = [P] + [vp] * 18
         L.orc_bucket.argtypes = [P, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
@@ -116,38 +116,51 @@ def decode(p: Problem, side: int, logits):
     return idx, w, lse
 
 
-def forward(p: Problem, wlogits, rlogits, v, gamma, slot0=None, mass0=None):
-    """Token-loop forward.  Returns o (B,T,H,d_v), slot1 (B,H,S,d_v), mass1 (B,H,S)."""
+def _mask(mask, shape):
+    if mask is None:
+        return None
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    if m.shape != shape:
+        raise ValueError(f"mask must have shape {shape}, got {m.shape}")
+    return m
+
+
+def forward(p: Problem, wlogits, rlogits, v, gamma, slot0=None, mass0=None, mask=None):
+    """Token-loop forward.  mask: (B,T), nonzero = valid token, or None.
+    Returns o (B,T,H,d_v), slot1 (B,H,S,d_v), mass1 (B,H,S)."""
     wl, rl, vv, gg = _f64in(wlogits), _f64in(rlogits), _f64in(v), _f64in(gamma)
     s0, m0 = _f64(slot0), _f64(mass0)
+    mk = _mask(mask, (p.B, p.T))
     o = np.empty((p.B, p.T, p.H, p.d_v), np.float64)
     s1 = np.empty((p.B, p.H, p.S, p.d_v), np.float64)
     m1 = np.empty((p.B, p.H, p.S), np.float64)
-    _check(lib().orc_forward(ctypes.byref(p), _ptr(wl), _ptr(rl), _ptr(vv), _ptr(gg),
+    _check(lib().orc_forward(ctypes.byref(p), _ptr(wl), _ptr(rl), _ptr(vv), _ptr(gg), _ptr(mk),
                              _ptr(s0), _ptr(m0), _ptr(o), _ptr(s1), _ptr(m1)), "forward")
     return o, s1, m1
 
 
-def decode_step(p: Problem, wlogits, rlogits, v, gamma, slot, mass):
+def decode_step(p: Problem, wlogits, rlogits, v, gamma, slot, mass, mask=None):
     """One autoregressive step (p.T == 1); slot and mass (float64, C-contiguous)
-    are updated in place.  Returns o (B,1,H,d_v)."""
+    are updated in place.  mask: (B,) or None.  Returns o (B,1,H,d_v)."""
     if slot.dtype != np.float64 or not slot.flags.c_contiguous:
         raise ValueError("slot must be a C-contiguous float64 array")
     if mass.dtype != np.float64 or not mass.flags.c_contiguous:
         raise ValueError("mass must be a C-contiguous float64 array")
     wl, rl, vv, gg = _f64in(wlogits), _f64in(rlogits), _f64in(v), _f64in(gamma)
     o = np.empty((p.B, 1, p.H, p.d_v), np.float64)
+    mk = _mask(mask, (p.B,))
     _check(lib().orc_decode_step(ctypes.byref(p), _ptr(wl), _ptr(rl), _ptr(vv), _ptr(gg),
-                                 _ptr(slot), _ptr(mass), _ptr(o)), "decode_step")
+                                 _ptr(mk), _ptr(slot), _ptr(mass), _ptr(o)), "decode_step")
     return o
 
 
 def backward(p: Problem, wlogits, rlogits, v, gamma, slot0, mass0, d_o,
-             d_slot1=None, d_mass1=None):
+             d_slot1=None, d_mass1=None, mask=None):
     """Reverse token loop.  Returns a dict with d_wlogits, d_rlogits (shape of
     the logits), d_v, d_gamma, d_slot0, d_mass0 (None without slot0), and the
-    decoded-weight gradients dw (B,T,H,k_w), dr (B,T,H,k_r)."""
+    decoded-weight gradients dw (B,T,H,k_w), dr (B,T,H,k_r).  mask as in forward."""
     wl, rl, vv, gg, do = _f64in(wlogits), _f64in(rlogits), _f64in(v), _f64in(gamma), _f64in(d_o)
+    mk = _mask(mask, (p.B, p.T))
     s0, m0 = _f64(slot0), _f64(mass0)
     ds1, dm1 = _f64(d_slot1), _f64(d_mass1)
     out = {
@@ -161,7 +174,7 @@ def backward(p: Problem, wlogits, rlogits, v, gamma, slot0, mass0, d_o,
         "dr": np.empty((p.B, p.T, p.H, p.k_r), np.float64),
     }
     _check(lib().orc_backward(
-        ctypes.byref(p), _ptr(wl), _ptr(rl), _ptr(vv), _ptr(gg), _ptr(s0), _ptr(m0),
+        ctypes.byref(p), _ptr(wl), _ptr(rl), _ptr(vv), _ptr(gg), _ptr(mk), _ptr(s0), _ptr(m0),
         _ptr(do), _ptr(ds1), _ptr(dm1),
         _ptr(out["d_wlogits"]), _ptr(out["d_rlogits"]), _ptr(out["d_v"]), _ptr(out["d_gamma"]),
         _ptr(out["d_slot0"]), _ptr(out["d_mass0"]), _ptr(out["dw"]), _ptr(out["dr"])),

@@ -25,6 +25,9 @@
  *   - CAPE (ramnet-ops "Quick start": the first embed_num heads cyclically
  *     shift read and write slot indices by token position; paper App. C: the
  *     index of given content moves by one per step).
+ *   - Token mask (ramnet-ops "Arguments", mask): a masked token is not
+ *     written and its output is to be ignored; read here as a token absent
+ *     from the computation (no write, no read, output 0, zero gradients).
  *   - First-order gradients (ramnet-ops "Autograd and compile").
  *
  * Arithmetic: every floating-point value is held and computed in IEEE double.
@@ -250,7 +253,7 @@ static void decode_token(const orc_problem* p, const double* wl, const double* r
  * every read. */
 static void forward_bh(const orc_problem* p, int b, int h,
                        const double* wlogits, const double* rlogits,
-                       const double* vin, const double* gamma,
+                       const double* vin, const double* gamma, const uint8_t* mask,
                        double* s, double* m, double* o,
                        double* hist_s_old, double* hist_m_old, double* hist_read,
                        int32_t* hid_w, double* hw_w, double* hl_w, double* hs_w,
@@ -267,6 +270,12 @@ static void forward_bh(const orc_problem* p, int b, int h,
   double sw = 0.0, sr = 0.0;
   for (int64_t t = 0; t < p->T; ++t) {
     const int64_t row = ((int64_t)b * p->T + t) * p->H + h;
+    if (mask && !mask[(int64_t)b * p->T + t]) {
+      /* a masked token is absent: no write, no read, output 0 */
+      if (o)
+        for (int c = 0; c < d_v; ++c) o[row * d_v + c] = 0.0;
+      continue;
+    }
     decode_token(p, wlogits + row * rowlen, rlogits + row * rowlen, t, h,
                  iw, ww, lw, &sw, ir, wr, lr, &sr);
     for (int c = 0; c < d_v; ++c) v[c] = (double)vin[row * d_v + c];
@@ -309,9 +318,10 @@ static void forward_bh(const orc_problem* p, int b, int h,
 
 /* Forward over all (b, h).  Shapes: logits (B,T,H,U,P), v (B,T,H,d_v),
  * gamma (B,T,H), slot0/slot1 (B,H,S,d_v), mass0/mass1 (B,H,S), o (B,T,H,d_v).
- * slot0 / mass0 may be NULL (every slot starts empty: content 0, mass 0). */
+ * slot0 / mass0 may be NULL (every slot starts empty: content 0, mass 0).
+ * mask (B,T) uint8, nonzero = valid token, or NULL (all valid). */
 int orc_forward(const orc_problem* p, const double* wlogits, const double* rlogits,
-                const double* v, const double* gamma,
+                const double* v, const double* gamma, const uint8_t* mask,
                 const double* slot0, const double* mass0,
                 double* o, double* slot1, double* mass1) {
   if (check_problem(p) != ORC_OK || !wlogits || !rlogits || !v || !gamma || !o || !slot1 || !mass1)
@@ -331,7 +341,7 @@ int orc_forward(const orc_problem* p, const double* wlogits, const double* rlogi
       memset(s, 0, sizeof(double) * S * p->d_v);
       memset(m, 0, sizeof(double) * S);
     }
-    forward_bh(p, b, h, wlogits, rlogits, v, gamma, s, m, o,
+    forward_bh(p, b, h, wlogits, rlogits, v, gamma, mask, s, m, o,
                NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
   }
   return ORC_OK;
@@ -339,16 +349,17 @@ int orc_forward(const orc_problem* p, const double* wlogits, const double* rlogi
 
 /* Autoregressive step (ramnet-ops "CUDA execution", autoregressive mode):
  * one token per (b, h), state (B,H,S,d_v) / (B,H,S) updated in place.
- * p->T must be 1; p->t0 is the position of that token. */
+ * p->T must be 1; p->t0 is the position of that token.  mask (B) or NULL. */
 int orc_decode_step(const orc_problem* p, const double* wlogits, const double* rlogits,
-                    const double* v, const double* gamma, double* slot, double* mass, double* o) {
+                    const double* v, const double* gamma, const uint8_t* mask,
+                    double* slot, double* mass, double* o) {
   if (check_problem(p) != ORC_OK || p->T != 1 || !slot || !mass || !o) return ORC_EINVAL;
   const int64_t S = slots_of(p);
   const int64_t nbh = (int64_t)p->B * p->H;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t bh = 0; bh < nbh; ++bh) {
     const int b = (int)(bh / p->H), h = (int)(bh % p->H);
-    forward_bh(p, b, h, wlogits, rlogits, v, gamma, slot + bh * S * p->d_v, mass + bh * S, o,
+    forward_bh(p, b, h, wlogits, rlogits, v, gamma, mask, slot + bh * S * p->d_v, mass + bh * S, o,
                NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
   }
   return ORC_OK;
@@ -398,9 +409,10 @@ static void decode_row_backward(const double* l, int U, int P, int k, int renorm
  * Outputs: d_wlogits, d_rlogits (B,T,H,U,P), d_v (B,T,H,d_v), d_gamma
  * (B,T,H), d_slot0 (B,H,S,d_v), d_mass0 (B,H,S) (both may be NULL).
  * Optional dw_out (B,T,H,k_w) and dr_out (B,T,H,k_r): gradients of the
- * decoded weights (the values fed to the decode backward). */
+ * decoded weights (the values fed to the decode backward).  mask as in
+ * orc_forward. */
 int orc_backward(const orc_problem* p, const double* wlogits, const double* rlogits,
-                 const double* vin, const double* gamma,
+                 const double* vin, const double* gamma, const uint8_t* mask,
                  const double* slot0, const double* mass0,
                  const double* d_o, const double* d_slot1, const double* d_mass1,
                  double* d_wlogits, double* d_rlogits, double* d_v, double* d_gamma,
@@ -448,7 +460,7 @@ int orc_backward(const orc_problem* p, const double* wlogits, const double* rlog
         memset(s, 0, sizeof(double) * S * d_v_);
         memset(m, 0, sizeof(double) * S);
       }
-      forward_bh(p, b, h, wlogits, rlogits, vin, gamma, s, m, NULL,
+      forward_bh(p, b, h, wlogits, rlogits, vin, gamma, mask, s, m, NULL,
                  hs_old, hm_old, hread, iw, ww, lw, sw, ir, wr, lr, sr);
       /* 2. reverse sweep */
       for (int64_t a = 0; a < S; ++a) {
@@ -458,6 +470,16 @@ int orc_backward(const orc_problem* p, const double* wlogits, const double* rlog
       }
       for (int64_t t = T - 1; t >= 0; --t) {
         const int64_t row = ((int64_t)b * T + t) * p->H + h;
+        if (mask && !mask[(int64_t)b * T + t]) {
+          /* a masked token takes no part: every gradient of it is zero */
+          for (int64_t i = 0; i < rowlen; ++i) d_wlogits[row * rowlen + i] = 0.0;
+          for (int64_t i = 0; i < rowlen; ++i) d_rlogits[row * rowlen + i] = 0.0;
+          for (int c = 0; c < d_v_; ++c) d_v[row * d_v_ + c] = 0.0;
+          d_gamma[row] = 0.0;
+          if (dw_out) for (int j = 0; j < kw; ++j) dw_out[row * kw + j] = 0.0;
+          if (dr_out) for (int j = 0; j < kr; ++j) dr_out[row * kr + j] = 0.0;
+          continue;
+        }
         const double* dO = d_o + row * d_v_;
         const double* vv = vin + row * d_v_;
         const double g = (double)gamma[row];
