@@ -145,34 +145,42 @@ int ram_decode(const ram_problem* p, int side, const void* logits, int32_t* idx,
  * bucket events into per-slot segments, run the GSU scan per segment and
  * accumulate the reads into o.  slot0 / mass0: initial state, or both NULL
  * for empty slots (content 0, mass 0) (ramnet-ops "Arguments": init_ram).
+ * mask: (B, T) uint8, nonzero = valid token, or NULL for all valid
+ * (ramnet-ops "Arguments": masked tokens are not written and their outputs
+ * are to be ignored); a masked token is absent: it writes and reads nothing
+ * and its o row is 0.  Allocations do not depend on the mask.
  * Writes o, slot1, mass1.  slot1 / mass1 may alias slot0 / mass0 (in-place
  * continuation, ramnet-ops inplace) only when no ram_backward follows.
  * ws: workspace of at least ram_workspace_size bytes; it keeps what the
  * backward needs and must stay untouched until then. */
 int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
-                const void* gamma, const float* slot0, const float* mass0, void* o, float* slot1,
-                float* mass1, void* ws, size_t ws_bytes, void* stream);
+                const void* gamma, const uint8_t* mask, const float* slot0, const float* mass0,
+                void* o, float* slot1, float* mass1, void* ws, size_t ws_bytes, void* stream);
 
 /* First-order backward (ramnet-ops "Autograd and compile") of the forward
- * that filled ws (same problem, same inputs, slot0 / mass0 as given to it).
+ * that filled ws (same problem, same inputs, mask, slot0 / mass0 as given to
+ * it); masked tokens get zero gradients.
  * d_o: gradient of o; d_slot1 / d_mass1: gradients of the final state, NULL
  * for zero.  Writes d_wlogits, d_rlogits (B,T,H,S) io, d_v (B,T,H,d_v) io,
  * d_gamma (B,T,H) io, and, when non-NULL, d_slot0 (B,H,S,d_v) / d_mass0
  * (B,H,S) float.  ws must have been sized with with_backward = 1. */
 int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wlogits,
-                 const void* rlogits, const void* v, const void* gamma, const float* slot0,
-                 const float* mass0, const void* d_o, const float* d_slot1, const float* d_mass1,
-                 void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma, float* d_slot0,
-                 float* d_mass0, void* stream);
+                 const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
+                 const float* slot0, const float* mass0, const void* d_o, const float* d_slot1,
+                 const float* d_mass1, void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma,
+                 float* d_slot0, float* d_mass0, void* stream);
 
 /* Autoregressive step (ramnet-ops "CUDA execution", autoregressive mode;
  * paper §4: each new token updates and reads its own K slots): p->T == 1;
  * decode both sides of the one token per (b, h), apply its k_w writes to
  * slot / mass in place, then read its k_r slots into o (B,1,H,d_v); o is
  * the float32 sum of the K terms, rounded once to the io dtype.  For CAPE,
- * t0 is the position of this token.  Needs k_w * d_v <= 8192.  No workspace. */
+ * t0 is the position of this token.  mask: (B) uint8 or NULL; a masked
+ * sequence's state is untouched and its o rows are 0.  Needs
+ * k_w * d_v <= 8192.  No workspace. */
 int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
-                    const void* gamma, float* slot, float* mass, void* o, void* stream);
+                    const void* gamma, const uint8_t* mask, float* slot, float* mass, void* o,
+                    void* stream);
 
 /* Text of a status code (static storage). */
 const char* ram_status_string(int status);

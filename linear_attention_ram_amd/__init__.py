@@ -91,9 +91,9 @@ def lib() -> ctypes.CDLL:
     L.ram_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
     L.ram_workspace_layout.argtypes = [P, ctypes.POINTER(WsLayout)]
     L.ram_decode.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp]
-    L.ram_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    L.ram_backward.argtypes = [P, vp, sz] + [vp] * 16
-    L.ram_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.ram_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.ram_backward.argtypes = [P, vp, sz] + [vp] * 17
+    L.ram_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.ram_status_string.argtypes = [ctypes.c_int]
     L.ram_status_string.restype = ctypes.c_char_p
     L.ram_prof_enable.argtypes = [ctypes.c_int]
@@ -191,11 +191,13 @@ def ram_decode(p: Problem, side: int, logits, idx, weight, lse, stream=None):
 
 
 def ram_forward(p: Problem, wlogits, rlogits, v, gamma, slot0, mass0, o, slot1, mass1, ws,
-                stream=None):
+                stream=None, mask=None):
+    """mask: optional (B, T) uint8 tensor, nonzero = valid token."""
     io = p.torch_dtype
     N, S, nseg = p.N, p.S, p.B * p.H * p.S
     args = (_ptr(wlogits, "wlogits", io, N * S), _ptr(rlogits, "rlogits", io, N * S),
             _ptr(v, "v", io, N * p.d_v), _ptr(gamma, "gamma", io, N),
+            _ptr(mask, "mask", torch.uint8, p.B * p.T, optional=True),
             _ptr(slot0, "slot0", torch.float32, nseg * p.d_v, optional=True),
             _ptr(mass0, "mass0", torch.float32, nseg, optional=True),
             _ptr(o, "o", io, N * p.d_v),
@@ -206,12 +208,15 @@ def ram_forward(p: Problem, wlogits, rlogits, v, gamma, slot0, mass0, o, slot1, 
 
 
 def ram_backward(p: Problem, ws, wlogits, rlogits, v, gamma, slot0, mass0, d_o, d_slot1, d_mass1,
-                 d_wlogits, d_rlogits, d_v, d_gamma, d_slot0=None, d_mass0=None, stream=None):
+                 d_wlogits, d_rlogits, d_v, d_gamma, d_slot0=None, d_mass0=None, stream=None,
+                 mask=None):
+    """mask: the (B, T) uint8 mask the forward was given, or None."""
     io = p.torch_dtype
     N, S, nseg = p.N, p.S, p.B * p.H * p.S
     args = (_ptr(ws, "ws", torch.uint8), ctypes.c_size_t(ws.numel()),
             _ptr(wlogits, "wlogits", io, N * S), _ptr(rlogits, "rlogits", io, N * S),
             _ptr(v, "v", io, N * p.d_v), _ptr(gamma, "gamma", io, N),
+            _ptr(mask, "mask", torch.uint8, p.B * p.T, optional=True),
             _ptr(slot0, "slot0", torch.float32, nseg * p.d_v, optional=True),
             _ptr(mass0, "mass0", torch.float32, nseg, optional=True),
             _ptr(d_o, "d_o", io, N * p.d_v),
@@ -224,11 +229,14 @@ def ram_backward(p: Problem, ws, wlogits, rlogits, v, gamma, slot0, mass0, d_o, 
     _check(lib().ram_backward(ctypes.byref(p), *args, _stream(stream, ws.device)), "ram_backward")
 
 
-def ram_decode_step(p: Problem, wlogits, rlogits, v, gamma, slot, mass, o, stream=None):
+def ram_decode_step(p: Problem, wlogits, rlogits, v, gamma, slot, mass, o, stream=None,
+                    mask=None):
+    """mask: optional (B,) uint8 tensor, nonzero = the sequence takes this step."""
     io = p.torch_dtype
     BH, S = p.B * p.H, p.S
     args = (_ptr(wlogits, "wlogits", io, BH * S), _ptr(rlogits, "rlogits", io, BH * S),
             _ptr(v, "v", io, BH * p.d_v), _ptr(gamma, "gamma", io, BH),
+            _ptr(mask, "mask", torch.uint8, p.B, optional=True),
             _ptr(slot, "slot", torch.float32, BH * S * p.d_v),
             _ptr(mass, "mass", torch.float32, BH * S), _ptr(o, "o", io, BH * p.d_v))
     _check(lib().ram_decode_step(ctypes.byref(p), *args, _stream(stream, slot.device)),

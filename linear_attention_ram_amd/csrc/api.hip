@@ -284,8 +284,8 @@ int ram_decode(const ram_problem* p, int side, const void* logits, int32_t* idx,
 }
 
 int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
-                const void* gamma, const float* slot0, const float* mass0, void* o, float* slot1,
-                float* mass1, void* ws, size_t ws_bytes, void* stream) {
+                const void* gamma, const uint8_t* mask, const float* slot0, const float* mass0,
+                void* o, float* slot1, float* mass1, void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   int st = check_problem(p, &d);
   if (st != RAM_OK) return st;
@@ -349,6 +349,7 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
     ba.w_w = da.w[0];
     ba.w_r = da.w[1];
     ba.gamma = adv(gamma, r0, io);
+    ba.mask = mask ? mask + (int64_t)b0 * p->T : nullptr;
     ba.B = nb;
     ba.H = p->H;
     ba.T = p->T;
@@ -418,10 +419,10 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
 }
 
 int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wlogits,
-                 const void* rlogits, const void* v, const void* gamma, const float* slot0,
-                 const float* mass0, const void* d_o, const float* d_slot1, const float* d_mass1,
-                 void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma, float* d_slot0,
-                 float* d_mass0, void* stream) {
+                 const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
+                 const float* slot0, const float* mass0, const void* d_o, const float* d_slot1,
+                 const float* d_mass1, void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma,
+                 float* d_slot0, float* d_mass0, void* stream) {
   Dims d;
   int st = check_problem(p, &d);
   if (st != RAM_OK) return st;
@@ -520,6 +521,7 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
     db.T = p->T;
     db.cape_heads = p->cape_heads;
     db.t0 = p->t0;
+    db.mask = mask ? mask + (int64_t)b0 * p->T : nullptr;
     prof_before("decode_bwd", s);
     e = launch_decode_bwd(db, bf, s);
     prof_after("decode_bwd", s);
@@ -544,7 +546,8 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
 }
 
 int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
-                    const void* gamma, float* slot, float* mass, void* o, void* stream) {
+                    const void* gamma, const uint8_t* mask, float* slot, float* mass, void* o,
+                    void* stream) {
   Dims d;
   int st = check_problem(p, &d);
   if (st != RAM_OK) return st;
@@ -563,6 +566,7 @@ int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogi
   a.renorm_r = p->renorm_r;
   a.cape_heads = p->cape_heads;
   a.t0 = p->t0;
+  a.mask = mask;
   a.eps = p->eps;
   a.wl = wlogits;
   a.rl = rlogits;

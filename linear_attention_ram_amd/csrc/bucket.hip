@@ -131,15 +131,19 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(BucketArgs a) {
     if (valid) {
       const int t = t_lo + e / K, p = e % K;
       const int64_t row = ((int64_t)b * a.T + t) * a.H + h;
+      // a masked token keeps its events with weight 0: an exact no-op write
+      // (retention 1, step 0) and a read that contributes 0
+      const bool live = !a.mask || a.mask[(int64_t)b * a.T + t];
       if (p < a.k_w) {
         slot = a.idx_w[row * a.k_w + p];
         rec.code = (t << 7) | p;
-        rec.w = a.w_w[row * a.k_w + p];
-        rec.lam = retention(rec.w, to_f32(gam[row]), &rec.dlam);
+        rec.w = live ? a.w_w[row * a.k_w + p] : 0.f;
+        rec.lam = live ? retention(rec.w, to_f32(gam[row]), &rec.dlam) : 1.f;
+        if (!live) rec.dlam = 0.f;
       } else {
         slot = a.idx_r[row * a.k_r + (p - a.k_w)];
         rec.code = (t << 7) | (1 << 6) | (p - a.k_w);
-        rec.w = a.w_r[row * a.k_r + (p - a.k_w)];
+        rec.w = live ? a.w_r[row * a.k_r + (p - a.k_w)] : 0.f;
       }
       valid = (unsigned)slot < (unsigned)S;   // decoded slots are always < S
     }

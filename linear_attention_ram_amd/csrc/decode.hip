@@ -77,6 +77,11 @@ __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
   const int k = a.k[side];
   const IO* __restrict__ src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
   IO* __restrict__ dst = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)a.S;
+  if (a.mask && !a.mask[(row / ((int64_t)a.T * a.H)) * a.T + (row / a.H) % a.T]) {
+    // a masked token takes no part in the computation: zero gradient
+    for (int c = lane; c < a.S / E; c += WAVE) st_nt16(dst + (int64_t)c * E, make_uint4(0, 0, 0, 0));
+    return;
+  }
   float gw = 0.f, wj = 0.f, gj = 0.f, lj = 0.f;
   int aj = 0;
   if (lane < k) {

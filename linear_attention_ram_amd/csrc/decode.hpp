@@ -65,6 +65,7 @@ struct DecodeBwdArgs {
   int H, T;                // as in DecodeFwdArgs: idx holds shifted slots of CAPE heads
   int cape_heads;
   int64_t t0;
+  const uint8_t* mask;     // (B, T) or null: rows of masked tokens get zero gradients
 };
 
 hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st);

@@ -30,6 +30,7 @@ struct BucketArgs {
   const float* w_w;       // (N, k_w)
   const float* w_r;       // (N, k_r)
   const void* gamma;      // (N) io
+  const uint8_t* mask;    // (B, T): nonzero = valid token, or null (all valid)
   int B, H, T, S, k_w, k_r;
   int ntiles;             // ceil(T / TILE_TOKENS)
   int nbits;              // bits needed for a slot index
@@ -102,6 +103,7 @@ struct StepArgs {
   int B, H, S, d_v, k_w, k_r, renorm_w, renorm_r;
   int cape_heads;         // heads h < cape_heads address (content index + t0) mod S
   int64_t t0;             // absolute position of the token
+  const uint8_t* mask;    // (B): nonzero = valid token, or null
   float eps;
   const void* wl;         // (B*H, S) io
   const void* rl;

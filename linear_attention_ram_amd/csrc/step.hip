@@ -21,6 +21,14 @@ __global__ __launch_bounds__(128) void decode_step_kernel(StepArgs a) {
   const int bh = blockIdx.x;
   const int wv = threadIdx.x >> 6;
   const int lane = lane_id();
+  if (a.mask && !a.mask[bh / a.H]) {
+    // masked sequence: state untouched, output 0
+    if (wv == 0) {
+      IO* o = reinterpret_cast<IO*>(a.o) + (int64_t)bh * a.d_v;
+      for (int c = lane; c < a.d_v; c += WAVE) o[c] = from_f32<IO>(0.f);
+    }
+    return;
+  }
   const IO* logits = reinterpret_cast<const IO*>(wv == 0 ? a.wl : a.rl) + (int64_t)bh * a.S;
   decode_row_wave<IO>(logits, a.S, wv == 0 ? a.k_w : a.k_r, wv == 0 ? a.renorm_w : a.renorm_r,
                       scratch[wv], sel_i[wv], sel_w[wv]);

@@ -96,11 +96,11 @@ def test_forward_rejects_small_workspace_before_touching_the_gpu():
     p = ram.problem(1, 1, 8, 64, 2, 2, 16, io="f32")
     L = ram.lib()
     fake = ctypes.c_void_p(16 * 1024)  # never dereferenced: validation fails first
-    st = L.ram_forward(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, fake, fake,
-                       fake, ctypes.c_size_t(16), None)
+    st = L.ram_forward(ctypes.byref(p), fake, fake, fake, fake, None, None, None, fake, fake,
+                       fake, fake, ctypes.c_size_t(16), None)
     assert st == ram.RAM_ECAPACITY
-    st = L.ram_forward(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, fake, fake,
-                       fake, ctypes.c_size_t(1 << 30), None)
+    st = L.ram_forward(ctypes.byref(p), fake, fake, fake, fake, None, fake, None, fake, fake,
+                       fake, fake, ctypes.c_size_t(1 << 30), None)
     assert st == ram.RAM_EINVAL             # slot0 without mass0
-    st = L.ram_decode_step(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None)
+    st = L.ram_decode_step(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, None)
     assert st == ram.RAM_EINVAL             # T != 1
