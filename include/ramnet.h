@@ -15,6 +15,14 @@
  *               ascending), weights = their probabilities, optionally
  *               renormalised to sum 1 (paper §3.2, App. B.2 "Addressing";
  *               ramnet-ops "Arguments": top_k, top_k_re_norm).
+ *               With U >= 2 digits (product softmax, paper §3.2 and App.
+ *               B.1) a row holds U digit logit vectors of P entries; slot
+ *               a = sum_u a_u P^(U-1-u) has probability prod_u
+ *               softmax(l_u)[a_u] and is ranked by its key, the float32 sum
+ *               l_0[a_0] + l_1[a_1] + ... taken in ascending u from 0
+ *               (log-space score, paper §4 "Efficient Address Decoding");
+ *               the K best by (key desc, index asc) are found exactly by a
+ *               pruned prefix search.
  *   write (GSU) for each selected write slot a with weight w and the token's
  *               forgetting modulator gamma (paper §3.4 "Gated Sparse Update"):
  *                 lambda = sigmoid(logit(1-w) - gamma)
@@ -34,12 +42,13 @@
  *               embed_num; paper App. C); selection and its tie order stay on
  *               the content logits, gradients flow to logit a.
  *
- * Supported: one address digit (U = 1, P = S).  One batch's rows of v (and of the read-out
+ * Supported: 1 <= U <= 14 digits with S = P^U <= 16384.  One batch's rows of v (and of the read-out
  * and gradient staging, T*H*max(k_w, k_r)*d_v io values) must fit in
  * 0x7FE00000 bytes, else RAM_ECAPACITY (split T over calls).
  *
  * Layouts (all row-major, contiguous, device memory):
- *   logits  (B, T, H, S)     io dtype     wlogits: write side, rlogits: read side
+ *   logits  (B, T, H, U, P)  io dtype     wlogits: write side, rlogits: read side
+ *                                         (U = 1: (B, T, H, S))
  *   v, o    (B, T, H, d_v)   io dtype
  *   gamma   (B, T, H)        io dtype
  *   slot    (B, H, S, d_v)   float32
@@ -53,13 +62,12 @@
  * workspace (size from ram_workspace_size).  The library never allocates or
  * frees device memory and never blocks the host.  All work is ordered on the
  * given HIP stream (a hipStream_t passed as void*, NULL = default stream):
- * parts of a call run on two library-owned streams of the same device,
- * which first wait for the work already on the given stream and which the
- * given stream then waits for (event fork and join; capturable in a graph).
- * ram_forward and ram_backward cut a call into up to four pieces of whole
- * batches so that one piece's scans overlap the next piece's decode; calls
- * from several host threads are serialised inside the library.
- * Pointers to logits must be 16-byte aligned.
+ * parts of ram_forward and ram_backward run on a library-owned stream of the
+ * same device, which first waits for the work already on the given stream
+ * and which the given stream then waits for (event fork and join;
+ * capturable in a graph); calls from several host threads are serialised
+ * inside the library.  Pointers to logits must be 16-byte aligned; with
+ * U = 1, S times the io size must be a multiple of 16.
  *
  * Errors: every call returns RAM_OK (0) or a negative code; nothing is
  * enqueued when validation fails.  There is no fallback path.
@@ -78,7 +86,7 @@ extern "C" {
 #define RAM_EINVAL (-1)       /* bad shape, null pointer, k > S, misalignment  */
 #define RAM_EDTYPE (-2)       /* io_dtype not RAM_F32 / RAM_BF16               */
 #define RAM_ECAPACITY (-3)    /* too many events or tokens, workspace too small */
-#define RAM_EUNSUPPORTED (-4) /* U > 1 or S > 16384                              */
+#define RAM_EUNSUPPORTED (-4) /* S = P^U > 16384 or U > 14                       */
 #define RAM_EHIP (-5)         /* HIP launch or runtime error                    */
 
 #define RAM_F32 0
@@ -87,7 +95,7 @@ extern "C" {
 /* One problem description, passed to every call. */
 typedef struct ram_problem {
   int32_t B, H, T;      /* batch, heads, tokens in this call (T = 1 for ram_decode_step) */
-  int32_t U, P;         /* address digits and digit size; S = P^U slots; U must be 1     */
+  int32_t U, P;         /* address digits (1..14) and digit size; S = P^U <= 16384 slots */
   int32_t k_w, k_r;     /* top-K of the write and read side: 1 <= k <= min(S, 64)        */
   int32_t d_v;          /* slot / value width: 1..64, or an even number 66..128          */
   int32_t io_dtype;     /* RAM_F32 or RAM_BF16 for logits, v, gamma, o and gradients    */
@@ -104,10 +112,10 @@ typedef struct ram_problem {
 typedef struct ram_ws_layout {
   size_t idx_w;       /* int32 (N, k_w): selected write slots, sorted by (logit desc, index asc) */
   size_t w_w;         /* float (N, k_w): their weights                                          */
-  size_t lse_w;       /* float (N): logsumexp of the write logits                                */
+  size_t lse_w;       /* float (N, U): logsumexp of each digit of the write logits             */
   size_t idx_r;       /* int32 (N, k_r)                                                           */
   size_t w_r;         /* float (N, k_r)                                                           */
-  size_t lse_r;       /* float (N)                                                                */
+  size_t lse_r;       /* float (N, U)                                                             */
   size_t seg_offset;  /* int32 (B*H*S + 1): first event of segment g = (b*H + h)*S + a          */
   size_t events;      /* (E) 16-byte records {int32 code, float weight, float lambda, float
                          d lambda/d w}; code = (t << 7) | (side << 6) | j; segment-major, time
@@ -132,12 +140,13 @@ int ram_workspace_size(const ram_problem* p, int with_backward, size_t* bytes);
 /* Offsets of the saved arrays inside the workspace. */
 int ram_workspace_layout(const ram_problem* p, ram_ws_layout* out);
 
-/* Address decode of one side (paper §3.2 with U = 1): for every row
- * (b, t, h) of logits (B,T,H,S), writes idx (B,T,H,k) int32 with the K
- * selected slots in (logit desc, index asc) order (CAPE heads: the addressed
- * slot, i.e. the selected index shifted as above), weight (B,T,H,k) float with
- * their probabilities exp(l - lse) (renormalised if the side's renorm flag is
- * set) and lse (B,T,H) float.  side: 0 write (k_w, renorm_w), 1 read. */
+/* Address decode of one side (paper §3.2): for every row (b, t, h) of
+ * logits (B,T,H,U,P), writes idx (B,T,H,k) int32 with the K selected flat
+ * slots in (key desc, index asc) order (U = 1: the key is the logit; CAPE
+ * heads: the addressed slot, i.e. the selected index shifted as above),
+ * weight (B,T,H,k) float with their probabilities exp(sum_u (l_u[a_u] -
+ * lse_u)) (renormalised if the side's renorm flag is set) and lse (B,T,H,U)
+ * float, the logsumexp of each digit.  side: 0 write (k_w, renorm_w), 1 read. */
 int ram_decode(const ram_problem* p, int side, const void* logits, int32_t* idx, float* weight,
                float* lse, void* stream);
 
@@ -161,7 +170,7 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
  * that filled ws (same problem, same inputs, mask, slot0 / mass0 as given to
  * it); masked tokens get zero gradients.
  * d_o: gradient of o; d_slot1 / d_mass1: gradients of the final state, NULL
- * for zero.  Writes d_wlogits, d_rlogits (B,T,H,S) io, d_v (B,T,H,d_v) io,
+ * for zero.  Writes d_wlogits, d_rlogits (B,T,H,U,P) io, d_v (B,T,H,d_v) io,
  * d_gamma (B,T,H) io, and, when non-NULL, d_slot0 (B,H,S,d_v) / d_mass0
  * (B,H,S) float.  ws must have been sized with with_backward = 1. */
 int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wlogits,

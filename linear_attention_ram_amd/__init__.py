@@ -48,6 +48,11 @@ class Problem(ctypes.Structure):
         return int(self.B) * int(self.T) * int(self.H)
 
     @property
+    def row(self) -> int:
+        """Logits per (token, head, side): U * P."""
+        return int(self.U) * int(self.P)
+
+    @property
     def torch_dtype(self) -> torch.dtype:
         return torch.float32 if self.io_dtype == RAM_F32 else torch.bfloat16
 
@@ -64,14 +69,21 @@ class ProfEntry(ctypes.Structure):
                 ("total_ms", ctypes.c_double)]
 
 
-def problem(B, H, T, S, k_w, k_r, d_v, io="bf16", eps=1e-6, renorm=(False, False),
-            cape_heads=0, t0=0) -> Problem:
-    """Problem description with one address digit (U = 1, P = S)."""
+def problem(B, H, T, S=None, k_w=1, k_r=1, d_v=1, io="bf16", eps=1e-6, renorm=(False, False),
+            cape_heads=0, t0=0, *, U=1, P=None) -> Problem:
+    """Problem description.  One address digit: give S (U = 1, P = S).  U >= 2
+    digits of size P: give U and P (S = P**U; if S is given too it must agree)."""
     io_dtype = {"f32": RAM_F32, "bf16": RAM_BF16, torch.float32: RAM_F32,
                 torch.bfloat16: RAM_BF16}[io]
+    if P is None:
+        if S is None or U != 1:
+            raise ValueError("give S (one digit) or U and P")
+        P = S
+    if S is not None and int(P) ** int(U) != S:
+        raise ValueError("S must equal P**U")
     rw, rr = (renorm, renorm) if isinstance(renorm, bool) else renorm
-    return Problem(B, H, T, 1, S, k_w, k_r, d_v, io_dtype, float(eps), int(rw), int(rr),
-                   int(cape_heads), 0, int(t0))
+    return Problem(B, H, T, int(U), int(P), k_w, k_r, d_v, io_dtype, float(eps), int(rw),
+                   int(rr), int(cape_heads), 0, int(t0))
 
 
 _lib = None
@@ -168,10 +180,10 @@ def ws_views(p: Problem, ws: torch.Tensor) -> dict:
     return {
         "idx_w": view(L["idx_w"], N * p.k_w, torch.int32),
         "w_w": view(L["w_w"], N * p.k_w, torch.float32),
-        "lse_w": view(L["lse_w"], N, torch.float32),
+        "lse_w": view(L["lse_w"], N * p.U, torch.float32),
         "idx_r": view(L["idx_r"], N * p.k_r, torch.int32),
         "w_r": view(L["w_r"], N * p.k_r, torch.float32),
-        "lse_r": view(L["lse_r"], N, torch.float32),
+        "lse_r": view(L["lse_r"], N * p.U, torch.float32),
         "seg_offset": view(L["seg_offset"], p.B * p.H * S + 1, torch.int32),
         "events": view(L["events"], 4 * E, torch.int32).view(E, 4)[:, 0],
         "event_w": view(L["events"], 4 * E, torch.float32).view(E, 4)[:, 1],
@@ -182,10 +194,10 @@ def ws_views(p: Problem, ws: torch.Tensor) -> dict:
 
 def ram_decode(p: Problem, side: int, logits, idx, weight, lse, stream=None):
     k = p.k_w if side == 0 else p.k_r
-    args = (_ptr(logits, "logits", p.torch_dtype, p.N * p.S),
+    args = (_ptr(logits, "logits", p.torch_dtype, p.N * p.row),
             _ptr(idx, "idx", torch.int32, p.N * k),
             _ptr(weight, "weight", torch.float32, p.N * k),
-            _ptr(lse, "lse", torch.float32, p.N))
+            _ptr(lse, "lse", torch.float32, p.N * p.U))
     _check(lib().ram_decode(ctypes.byref(p), int(side), *args, _stream(stream, logits.device)),
            "ram_decode")
 
@@ -195,7 +207,7 @@ def ram_forward(p: Problem, wlogits, rlogits, v, gamma, slot0, mass0, o, slot1, 
     """mask: optional (B, T) uint8 tensor, nonzero = valid token."""
     io = p.torch_dtype
     N, S, nseg = p.N, p.S, p.B * p.H * p.S
-    args = (_ptr(wlogits, "wlogits", io, N * S), _ptr(rlogits, "rlogits", io, N * S),
+    args = (_ptr(wlogits, "wlogits", io, N * p.row), _ptr(rlogits, "rlogits", io, N * p.row),
             _ptr(v, "v", io, N * p.d_v), _ptr(gamma, "gamma", io, N),
             _ptr(mask, "mask", torch.uint8, p.B * p.T, optional=True),
             _ptr(slot0, "slot0", torch.float32, nseg * p.d_v, optional=True),
@@ -214,7 +226,7 @@ def ram_backward(p: Problem, ws, wlogits, rlogits, v, gamma, slot0, mass0, d_o, 
     io = p.torch_dtype
     N, S, nseg = p.N, p.S, p.B * p.H * p.S
     args = (_ptr(ws, "ws", torch.uint8), ctypes.c_size_t(ws.numel()),
-            _ptr(wlogits, "wlogits", io, N * S), _ptr(rlogits, "rlogits", io, N * S),
+            _ptr(wlogits, "wlogits", io, N * p.row), _ptr(rlogits, "rlogits", io, N * p.row),
             _ptr(v, "v", io, N * p.d_v), _ptr(gamma, "gamma", io, N),
             _ptr(mask, "mask", torch.uint8, p.B * p.T, optional=True),
             _ptr(slot0, "slot0", torch.float32, nseg * p.d_v, optional=True),
@@ -222,7 +234,8 @@ def ram_backward(p: Problem, ws, wlogits, rlogits, v, gamma, slot0, mass0, d_o, 
             _ptr(d_o, "d_o", io, N * p.d_v),
             _ptr(d_slot1, "d_slot1", torch.float32, nseg * p.d_v, optional=True),
             _ptr(d_mass1, "d_mass1", torch.float32, nseg, optional=True),
-            _ptr(d_wlogits, "d_wlogits", io, N * S), _ptr(d_rlogits, "d_rlogits", io, N * S),
+            _ptr(d_wlogits, "d_wlogits", io, N * p.row),
+            _ptr(d_rlogits, "d_rlogits", io, N * p.row),
             _ptr(d_v, "d_v", io, N * p.d_v), _ptr(d_gamma, "d_gamma", io, N),
             _ptr(d_slot0, "d_slot0", torch.float32, nseg * p.d_v, optional=True),
             _ptr(d_mass0, "d_mass0", torch.float32, nseg, optional=True))
@@ -234,7 +247,7 @@ def ram_decode_step(p: Problem, wlogits, rlogits, v, gamma, slot, mass, o, strea
     """mask: optional (B,) uint8 tensor, nonzero = the sequence takes this step."""
     io = p.torch_dtype
     BH, S = p.B * p.H, p.S
-    args = (_ptr(wlogits, "wlogits", io, BH * S), _ptr(rlogits, "rlogits", io, BH * S),
+    args = (_ptr(wlogits, "wlogits", io, BH * p.row), _ptr(rlogits, "rlogits", io, BH * p.row),
             _ptr(v, "v", io, BH * p.d_v), _ptr(gamma, "gamma", io, BH),
             _ptr(mask, "mask", torch.uint8, p.B, optional=True),
             _ptr(slot, "slot", torch.float32, BH * S * p.d_v),

@@ -8,6 +8,7 @@
 
 #include "../../include/ramnet.h"
 #include "decode.hpp"
+#include "decode_prod.hpp"
 #include "kernels.hpp"
 
 using namespace ramk;
@@ -19,6 +20,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Dims {
   int64_t S, N, E, nseg, nck;
+  int64_t row;   // logits per (token, head, side): U * P
   int ntiles, nbits;
   size_t io_bytes;
 };
@@ -26,14 +28,18 @@ struct Dims {
 int check_problem(const ram_problem* p, Dims* d) {
   if (!p) return RAM_EINVAL;
   if (p->io_dtype != RAM_F32 && p->io_dtype != RAM_BF16) return RAM_EDTYPE;
-  if (p->U != 1) return RAM_EUNSUPPORTED;
   if (p->reserved != 0) return RAM_EINVAL;
-  if (p->B < 1 || p->H < 1 || p->T < 0 || p->P < 1) return RAM_EINVAL;
+  if (p->B < 1 || p->H < 1 || p->T < 0 || p->P < 1 || p->U < 1) return RAM_EINVAL;
   if (p->cape_heads < 0 || p->cape_heads > p->H || p->t0 < 0) return RAM_EINVAL;
-  const int64_t S = p->P;
-  if (S > 16384) return RAM_EUNSUPPORTED;
+  if (p->U > MAX_DIGITS) return RAM_EUNSUPPORTED;
+  int64_t S = 1;
+  for (int u = 0; u < p->U; ++u) {
+    S *= p->P;
+    if (S > 16384) return RAM_EUNSUPPORTED;
+  }
   const size_t io = p->io_dtype == RAM_F32 ? 4 : 2;
-  if ((S * (int64_t)io) % 16 != 0) return RAM_EINVAL;
+  // flat rows are read in 16-byte vectors
+  if (p->U == 1 && (S * (int64_t)io) % 16 != 0) return RAM_EINVAL;
   if (p->k_w < 1 || p->k_r < 1 || p->k_w > 64 || p->k_r > 64 || p->k_w > S || p->k_r > S)
     return RAM_EINVAL;
   if (p->d_v < 1 || p->d_v > 128 || (p->d_v > 64 && (p->d_v % 2) != 0)) return RAM_EINVAL;
@@ -52,6 +58,7 @@ int check_problem(const ram_problem* p, Dims* d) {
     return RAM_ECAPACITY;
   if (d) {
     d->S = S;
+    d->row = (int64_t)p->U * p->P;
     d->N = N;
     d->E = E;
     d->nseg = nseg;
@@ -102,10 +109,10 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   L->idx_w = take(sizeof(int32_t) * d.N * p->k_w);
   L->w_w = take(sizeof(float) * d.N * p->k_w);
-  L->lse_w = take(sizeof(float) * d.N);
+  L->lse_w = take(sizeof(float) * d.N * p->U);
   L->idx_r = take(sizeof(int32_t) * d.N * p->k_r);
   L->w_r = take(sizeof(float) * d.N * p->k_r);
-  L->lse_r = take(sizeof(float) * d.N);
+  L->lse_r = take(sizeof(float) * d.N * p->U);
   L->seg_offset = take(sizeof(int32_t) * (d.nseg + 1));
   L->events = take(sizeof(EventRec) * d.E);
   L->ckpt_s = take(sizeof(float) * d.nck * p->d_v);
@@ -231,7 +238,7 @@ const char* ram_status_string(int status) {
     case RAM_EINVAL: return "invalid argument (shape, pointer, k, d_v, alignment)";
     case RAM_EDTYPE: return "unsupported io dtype";
     case RAM_ECAPACITY: return "capacity exceeded (events, tokens or workspace size)";
-    case RAM_EUNSUPPORTED: return "unsupported configuration (U > 1 or S > 16384)";
+    case RAM_EUNSUPPORTED: return "unsupported configuration (S = P^U > 16384 or U > 14)";
     case RAM_EHIP: return "HIP runtime or launch error";
     default: return "unknown status";
   }
@@ -271,6 +278,8 @@ int ram_decode(const ram_problem* p, int side, const void* logits, int32_t* idx,
   a.renorm[0] = side == 0 ? p->renorm_w : p->renorm_r;
   a.N = d.N;
   a.S = (int)d.S;
+  a.U = p->U;
+  a.P = p->P;
   a.nsides = 1;
   a.H = p->H;
   a.T = p->T;
@@ -318,20 +327,22 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
     const int64_t r0 = (int64_t)b0 * TH, rows = (int64_t)nb * TH;   // token rows of the piece
 
     DecodeFwdArgs da{};
-    da.logits[0] = adv(wlogits, r0 * d.S, io);
-    da.logits[1] = adv(rlogits, r0 * d.S, io);
+    da.logits[0] = adv(wlogits, r0 * d.row, io);
+    da.logits[1] = adv(rlogits, r0 * d.row, io);
     da.idx[0] = (int32_t*)(w + L.idx_w) + r0 * p->k_w;
     da.idx[1] = (int32_t*)(w + L.idx_r) + r0 * p->k_r;
     da.w[0] = (float*)(w + L.w_w) + r0 * p->k_w;
     da.w[1] = (float*)(w + L.w_r) + r0 * p->k_r;
-    da.lse[0] = (float*)(w + L.lse_w) + r0;
-    da.lse[1] = (float*)(w + L.lse_r) + r0;
+    da.lse[0] = (float*)(w + L.lse_w) + r0 * p->U;
+    da.lse[1] = (float*)(w + L.lse_r) + r0 * p->U;
     da.k[0] = p->k_w;
     da.k[1] = p->k_r;
     da.renorm[0] = p->renorm_w;
     da.renorm[1] = p->renorm_r;
     da.N = rows;
     da.S = (int)d.S;
+    da.U = p->U;
+    da.P = p->P;
     da.nsides = 2;
     da.H = p->H;
     da.T = p->T;
@@ -498,24 +509,26 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
     S->dep(s, a);
 
     DecodeBwdArgs db{};
-    db.logits[0] = adv(wlogits, r0 * d.S, io);
-    db.logits[1] = adv(rlogits, r0 * d.S, io);
-    db.lse[0] = (const float*)(w + L.lse_w) + r0;
-    db.lse[1] = (const float*)(w + L.lse_r) + r0;
+    db.logits[0] = adv(wlogits, r0 * d.row, io);
+    db.logits[1] = adv(rlogits, r0 * d.row, io);
+    db.lse[0] = (const float*)(w + L.lse_w) + r0 * p->U;
+    db.lse[1] = (const float*)(w + L.lse_r) + r0 * p->U;
     db.idx[0] = (const int32_t*)(w + L.idx_w) + r0 * p->k_w;
     db.idx[1] = (const int32_t*)(w + L.idx_r) + r0 * p->k_r;
     db.w[0] = (const float*)(w + L.w_w) + r0 * p->k_w;
     db.w[1] = (const float*)(w + L.w_r) + r0 * p->k_r;
     db.g[0] = sb.dw;
     db.g[1] = sb.dr;
-    db.dlogits[0] = adv(d_wlogits, r0 * d.S, io);
-    db.dlogits[1] = adv(d_rlogits, r0 * d.S, io);
+    db.dlogits[0] = adv(d_wlogits, r0 * d.row, io);
+    db.dlogits[1] = adv(d_rlogits, r0 * d.row, io);
     db.k[0] = p->k_w;
     db.k[1] = p->k_r;
     db.renorm[0] = p->renorm_w;
     db.renorm[1] = p->renorm_r;
     db.N = rows;
     db.S = (int)d.S;
+    db.U = p->U;
+    db.P = p->P;
     db.nsides = 2;
     db.H = p->H;
     db.T = p->T;
@@ -559,6 +572,8 @@ int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogi
   a.B = p->B;
   a.H = p->H;
   a.S = (int)d.S;
+  a.U = p->U;
+  a.P = p->P;
   a.d_v = p->d_v;
   a.k_w = p->k_w;
   a.k_r = p->k_r;

@@ -1,5 +1,7 @@
-// Address decoding of the RAM-Net attention core (paper §3.1-3.2, one digit:
-// U = 1): per (token, head, side) row of S logits, lse = logsumexp, the K
+// Address decoding of the RAM-Net attention core (paper §3.1-3.2).  Rows of
+// U >= 2 digits go through the product decoder of decode_prod.hpp; the rest
+// of this comment is the one-digit case (U = 1).
+// Per (token, head, side) row of S logits, lse = logsumexp, the K
 // largest logits by (value descending, index ascending), and their
 // un-renormalised probabilities exp(l - lse), optionally renormalised
 // (paper App. B.2 "Addressing"; ramnet-ops "Arguments", top_k_re_norm).
@@ -17,6 +19,7 @@
 //           candidate's rank is counted exactly.  Rows with more than
 //           CAND_CAP candidates (massive ties) take an exact K-pass fallback.
 #include "decode.hpp"
+#include "decode_prod.hpp"
 
 namespace ramk {
 
@@ -135,10 +138,106 @@ __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
   }
 }
 
+// Product rows (U >= 2 digits, see decode_prod.hpp): one wave per row, rows
+// of side 0 first.  lse holds the U per-digit logsumexps of each row.
+template <typename IO>
+__global__ __launch_bounds__(256) void decode_fwd_prod_kernel(DecodeFwdArgs a) {
+  __shared__ ProdScratch scratch[4];
+  __shared__ int s_idx[4][MAX_K];
+  __shared__ float s_w[4][MAX_K];
+  const int wv = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int64_t grow = (int64_t)blockIdx.x * 4 + wv;
+  if (grow >= (int64_t)a.nsides * a.N) return;
+  const int side = (int)(grow / a.N);
+  const int64_t row = grow - (int64_t)side * a.N;
+  const int UP = a.U * a.P;
+  const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)UP;
+  const int k = a.k[side];
+  decode_row_product<IO>(src, a.U, a.P, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
+  wave_sync();
+  if (lane < k) {
+    const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
+    const int id = s_idx[wv][lane];
+    a.idx[side][row * k + lane] = (shift < 0) ? id : (id + shift) % a.S;
+    a.w[side][row * k + lane] = s_w[wv][lane];
+  }
+  if (lane < a.U) a.lse[side][row * a.U + lane] = scratch[wv].dlse[lane];
+  if (a.zero_rows && side == a.nsides - 1) {
+    float* z = a.zero_rows + row * (int64_t)a.zero_width;
+    for (int c = lane; c < a.zero_width; c += WAVE) z[c] = 0.f;
+  }
+}
+
+// Decode backward of product rows (one wave per row): with gw_j as for one
+// digit, dl_u[i] = sum_j gw_j [digit u of a_j = i] - p_u[i] sum_j gw_j,
+// p_u = exp(l_u - lse_u) the digit softmax (paper App. B.1: the slot
+// probability is the product of the digit softmaxes).  The selected-slot
+// terms are added in ascending j.
+template <typename IO>
+__global__ __launch_bounds__(256) void decode_bwd_prod_kernel(DecodeBwdArgs a) {
+  __shared__ int s_pos[4][MAX_K * MAX_DIGITS];   // element u * P + a_{j,u} of each (j, u)
+  __shared__ float s_gw[4][MAX_K];
+  const int wv = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int64_t grow = (int64_t)blockIdx.x * 4 + wv;
+  if (grow >= (int64_t)a.nsides * a.N) return;
+  const int side = (int)(grow / a.N);
+  const int64_t row = grow - (int64_t)side * a.N;
+  const int k = a.k[side];
+  const int U = a.U, P = a.P, UP = U * P;
+  const IO* __restrict__ src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)UP;
+  IO* __restrict__ dst = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)UP;
+  if (a.mask && !a.mask[(row / ((int64_t)a.T * a.H)) * a.T + (row / a.H) % a.T]) {
+    for (int e = lane; e < UP; e += WAVE) dst[e] = from_f32<IO>(0.f);
+    return;
+  }
+  float gj = 0.f, wj = 0.f;
+  int aj = 0;
+  if (lane < k) {
+    gj = a.g[side][row * k + lane];
+    wj = a.w[side][row * k + lane];
+    aj = a.idx[side][row * k + lane];
+    const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
+    if (shift >= 0) aj = (aj - shift + a.S) % a.S;
+  }
+  float gw;
+  if (a.renorm[side]) {
+    const float dot = wave_sum(gj * wj);
+    gw = (gj - dot) * wj;
+  } else {
+    gw = gj * wj;
+  }
+  const float ntot = -wave_sum(gw);
+  if (lane < k) {
+    s_gw[wv][lane] = gw;
+    int rem = aj;
+    for (int u = U - 1; u >= 0; --u) {
+      s_pos[wv][lane * U + u] = u * P + rem % P;
+      rem /= P;
+    }
+  }
+  wave_sync();
+  const float* lse = a.lse[side] + row * U;
+  for (int e = lane; e < UP; e += WAVE) {
+    const int u = e / P;
+    const float x = to_f32(src[e]);
+    float acc = ntot * fast_exp2(fmaf(x, LOG2E, -lse[u] * LOG2E));
+    for (int j = 0; j < k; ++j)
+      if (s_pos[wv][j * U + u] == e) acc += s_gw[wv][j];
+    dst[e] = from_f32<IO>(acc);
+  }
+}
+
 hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st) {
   const int64_t rows = (int64_t)a.nsides * a.N;
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (a.U > 1) {
+    if (bf16) hipLaunchKernelGGL(decode_fwd_prod_kernel<bf16_t>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(decode_fwd_prod_kernel<float>, grid, block, 0, st, a);
+    return hipGetLastError();
+  }
   const int nvec = a.S / (bf16 ? 8 : 4);
   if (bf16) {
     if (nvec == 512) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 8, true>), grid, block, 0, st, a);
@@ -162,6 +261,11 @@ hipError_t launch_decode_bwd(const DecodeBwdArgs& a, bool bf16, hipStream_t st) 
   const int64_t rows = (int64_t)a.nsides * a.N;
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (a.U > 1) {
+    if (bf16) hipLaunchKernelGGL(decode_bwd_prod_kernel<bf16_t>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(decode_bwd_prod_kernel<float>, grid, block, 0, st, a);
+    return hipGetLastError();
+  }
   if (bf16) hipLaunchKernelGGL(decode_bwd_kernel<bf16_t>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(decode_bwd_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();

@@ -22,14 +22,15 @@ struct DecodeScratch {
 };
 
 struct DecodeFwdArgs {
-  const void* logits[2];   // (N, S) io per side
+  const void* logits[2];   // (N, U * P) io per side
   int32_t* idx[2];         // (N, k) per side
   float* w[2];             // (N, k) per side
-  float* lse[2];           // (N,) per side
+  float* lse[2];           // (N, U) per side: logsumexp of each digit
   int k[2];
   int renorm[2];
   int64_t N;               // rows per side
-  int S;
+  int S;                   // slots, P^U
+  int U, P;                // address digits and digit size
   int nsides;              // 1 or 2 (side 0 = first pointer set)
   float* zero_rows;        // optional (N, zero_width) float rows to clear
   int zero_width;
@@ -51,16 +52,17 @@ __device__ __forceinline__ int cape_shift_of(int64_t r, int H, int T, int S, int
 }
 
 struct DecodeBwdArgs {
-  const void* logits[2];
-  const float* lse[2];
+  const void* logits[2];   // (N, U * P) io
+  const float* lse[2];     // (N, U)
   const int32_t* idx[2];
   const float* w[2];
   const float* g[2];       // gradient of the output weights (N, k)
-  void* dlogits[2];        // (N, S) io
+  void* dlogits[2];        // (N, U * P) io
   int k[2];
   int renorm[2];
   int64_t N;
   int S;
+  int U, P;
   int nsides;
   int H, T;                // as in DecodeFwdArgs: idx holds shifted slots of CAPE heads
   int cape_heads;

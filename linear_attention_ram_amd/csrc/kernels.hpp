@@ -101,11 +101,12 @@ struct FinalizeArgs {
 
 struct StepArgs {
   int B, H, S, d_v, k_w, k_r, renorm_w, renorm_r;
+  int U, P;               // address digits and digit size (S = P^U)
   int cape_heads;         // heads h < cape_heads address (content index + t0) mod S
   int64_t t0;             // absolute position of the token
   const uint8_t* mask;    // (B): nonzero = valid token, or null
   float eps;
-  const void* wl;         // (B*H, S) io
+  const void* wl;         // (B*H, U * P) io
   const void* rl;
   const void* v;          // (B*H, d_v) io
   const void* gamma;      // (B*H) io

@@ -5,16 +5,21 @@
 // selected slots are updated in place (GSU, paper §3.4), the updated rows are
 // kept in LDS, and wave 0 reads the k_r selected slots, taking rows written by
 // this token from LDS so the read sees the write.
+#include <type_traits>
+
 #include "decode.hpp"
+#include "decode_prod.hpp"
 #include "kernels.hpp"
 
 namespace ramk {
 
 constexpr int STEP_ROW_CAP = 8192;  // k_w * d_v floats kept in LDS
 
-template <typename IO>
+// PROD: rows of U >= 2 address digits (product decoder)
+template <typename IO, bool PROD>
 __global__ __launch_bounds__(128) void decode_step_kernel(StepArgs a) {
-  __shared__ DecodeScratch scratch[2];
+  using Scratch = typename std::conditional<PROD, ProdScratch, DecodeScratch>::type;
+  __shared__ Scratch scratch[2];
   __shared__ int sel_i[2][MAX_K];
   __shared__ float sel_w[2][MAX_K];
   __shared__ float rows[STEP_ROW_CAP];
@@ -29,9 +34,14 @@ __global__ __launch_bounds__(128) void decode_step_kernel(StepArgs a) {
     }
     return;
   }
-  const IO* logits = reinterpret_cast<const IO*>(wv == 0 ? a.wl : a.rl) + (int64_t)bh * a.S;
-  decode_row_wave<IO>(logits, a.S, wv == 0 ? a.k_w : a.k_r, wv == 0 ? a.renorm_w : a.renorm_r,
-                      scratch[wv], sel_i[wv], sel_w[wv]);
+  const IO* logits =
+      reinterpret_cast<const IO*>(wv == 0 ? a.wl : a.rl) + (int64_t)bh * a.U * a.P;
+  if constexpr (PROD)
+    decode_row_product<IO>(logits, a.U, a.P, wv == 0 ? a.k_w : a.k_r,
+                           wv == 0 ? a.renorm_w : a.renorm_r, scratch[wv], sel_i[wv], sel_w[wv]);
+  else
+    decode_row_wave<IO>(logits, a.S, wv == 0 ? a.k_w : a.k_r, wv == 0 ? a.renorm_w : a.renorm_r,
+                        scratch[wv], sel_i[wv], sel_w[wv]);
   // CAPE heads address the content index shifted by the token's position
   // (each lane rewrites the entry it wrote)
   if ((bh % a.H) < a.cape_heads && lane < (wv == 0 ? a.k_w : a.k_r))
@@ -78,8 +88,13 @@ __global__ __launch_bounds__(128) void decode_step_kernel(StepArgs a) {
 hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t st) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
-  if (bf16) hipLaunchKernelGGL(decode_step_kernel<bf16_t>, dim3(BH), dim3(128), 0, st, a);
-  else hipLaunchKernelGGL(decode_step_kernel<float>, dim3(BH), dim3(128), 0, st, a);
+  if (a.U > 1) {
+    if (bf16) hipLaunchKernelGGL((decode_step_kernel<bf16_t, true>), dim3(BH), dim3(128), 0, st, a);
+    else hipLaunchKernelGGL((decode_step_kernel<float, true>), dim3(BH), dim3(128), 0, st, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL((decode_step_kernel<bf16_t, false>), dim3(BH), dim3(128), 0, st, a);
+    else hipLaunchKernelGGL((decode_step_kernel<float, false>), dim3(BH), dim3(128), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -44,6 +44,21 @@ class Config:
     steps: int | None = None   # autoregressive steps (decode)
     d_k: int | None = None     # key/query width of the projection case
     eps: float = 1e-6
+    U: int = 1                 # address digits; S = P**U
+
+    @property
+    def P(self) -> int:
+        """Digit size."""
+        if self.U == 1:
+            return self.S
+        P = round(self.S ** (1.0 / self.U))
+        assert P ** self.U == self.S, (self.S, self.U)
+        return P
+
+    @property
+    def logit_shape(self) -> tuple:
+        """Trailing shape of one (token, head) logit row: (S,) or (U, P)."""
+        return (self.S,) if self.U == 1 else (self.U, self.P)
 
     @property
     def dtype(self) -> torch.dtype:
@@ -64,6 +79,13 @@ CONFIGS = {
     "long": Config("long", 1, 16, 65536, 16384, 8, 8, 128, "bf16", chunk=4096),
     # autoregressive decode: 256 sequences, one token per step
     "decode": Config("decode", 256, 16, 1, 4096, 8, 8, 128, "bf16", steps=1024),
+    # product-softmax addresses (U >= 2 digits of P logits each):
+    # the 1.3B-layer shape factorised as U = 2 digits of 64 (q/k are the digit logits)
+    "1.3b-u2": Config("1.3b-u2", 8, 16, 4096, 4096, 8, 8, 128, "bf16", U=2),
+    # the ramnet-ops example shape: U = 3 digits of 4, C = 32, top-8
+    "ops-example": Config("ops-example", 2, 4, 32, 64, 8, 8, 32, "f32", U=3),
+    # the paper's default address space 4^5: U = 5 digits of 4
+    "u5": Config("u5", 2, 4, 512, 1024, 8, 8, 64, "bf16", U=5),
 }
 
 
@@ -107,7 +129,8 @@ def layer_inputs(cfg: Config, device="cpu", seed: int = 0, T: int | None = None,
     (if any), write logits, read logits, v, gamma, dO, then the optional
     slot0 ~ N(0,1), mass0 ~ U(0,1), d_slot1 ~ N(0,1), d_mass1 ~ N(0,1).
 
-    Returns a dict of tensors on ``device``: wl, rl (B,T,H,S); v (B,T,H,d_v);
+    Returns a dict of tensors on ``device``: wl, rl (B,T,H,S), or (B,T,H,U,P)
+    for U >= 2 digits; v (B,T,H,d_v);
     gamma (B,T,H); d_o (B,T,H,d_v); slot0 (B,H,S,d_v) f32; mass0 (B,H,S) f32;
     d_slot1, d_mass1 likewise."""
     T = cfg.T if T is None else T
@@ -127,9 +150,11 @@ def layer_inputs(cfg: Config, device="cpu", seed: int = 0, T: int | None = None,
     else:
         bias = None
         if cfg.zipf is not None:
+            assert cfg.U == 1, "the per-slot bias is defined for flat addresses"
             bias = zipf_bias(cfg, g, device)          # (H, S), broadcast over (T, H, S)
-        out["wl"] = _randn((cfg.B, T, cfg.H, cfg.S), g, device, dt, bias=bias)
-        out["rl"] = _randn((cfg.B, T, cfg.H, cfg.S), g, device, dt, bias=bias)
+        shape = (cfg.B, T, cfg.H) + cfg.logit_shape
+        out["wl"] = _randn(shape, g, device, dt, bias=bias)
+        out["rl"] = _randn(shape, g, device, dt, bias=bias)
         out["v"] = _randn((cfg.B, T, cfg.H, cfg.d_v), g, device, dt)
         out["gamma"] = _randn((cfg.B, T, cfg.H), g, device, dt, mean=LN9)
     if with_d_o:

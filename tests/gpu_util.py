@@ -32,7 +32,7 @@ def rel(x, ref):
 def gpu_problem(cfg, T=None, eps=None, renorm=(False, False), cape_heads=0, t0=0):
     return ram.problem(cfg.B, cfg.H, cfg.T if T is None else T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v,
                        io=cfg.io, eps=cfg.eps if eps is None else eps, renorm=renorm,
-                       cape_heads=cape_heads, t0=t0)
+                       cape_heads=cape_heads, t0=t0, U=cfg.U, P=cfg.P)
 
 
 def oracle_problem(gp, B=None, H=None, cape_heads=None):
@@ -40,7 +40,7 @@ def oracle_problem(gp, B=None, H=None, cape_heads=None):
     CAPE head count must be given too (it depends on which heads)."""
     cape = int(gp.cape_heads) if cape_heads is None else cape_heads
     return oracle.problem(gp.B if B is None else B, gp.H if H is None else H, gp.T, gp.S,
-                          gp.k_w, gp.k_r, gp.d_v, eps=float(gp.eps),
+                          gp.k_w, gp.k_r, gp.d_v, U=int(gp.U), P=int(gp.P), eps=float(gp.eps),
                           renorm=(bool(gp.renorm_w), bool(gp.renorm_r)),
                           cape_heads=cape, t0=int(gp.t0))
 

@@ -75,15 +75,47 @@ def test_invalid_problems_are_rejected(kw, code):
     assert st == code, ram.ram_status_string(st)
 
 
-def test_bad_dtype_and_digits():
+def test_bad_dtype():
     p = ram.problem(1, 1, 4, 64, 2, 2, 16)
     p.io_dtype = 7
     n = ctypes.c_size_t(0)
     assert ram.lib().ram_workspace_size(ctypes.byref(p), 1, ctypes.byref(n)) == ram.RAM_EDTYPE
-    p = ram.problem(1, 1, 4, 64, 2, 2, 16)
-    p.U = 2
-    p.P = 8
-    assert ram.lib().ram_workspace_size(ctypes.byref(p), 1, ctypes.byref(n)) == ram.RAM_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("U,P,k,code", [
+    (2, 8, 8, ram.RAM_OK),
+    (3, 4, 8, ram.RAM_OK),            # rows of 12 bf16 logits need no 16-byte multiple
+    (2, 128, 64, ram.RAM_OK),         # S = 16384
+    (2, 129, 8, ram.RAM_EUNSUPPORTED),
+    (14, 2, 8, ram.RAM_OK),
+    (15, 1, 1, ram.RAM_EUNSUPPORTED),  # more digits than the decoder keeps
+    (14, 1, 1, ram.RAM_OK),
+    (14, 1, 2, ram.RAM_EINVAL),        # k > S = 1
+    (0, 8, 1, ram.RAM_EINVAL),
+    (3, 3, 28, ram.RAM_EINVAL),        # k > S = 27
+])
+def test_digit_counts(U, P, k, code):
+    p = ram.problem(1, 2, 4, None, k, k, 16, U=U, P=P) if U >= 1 else None
+    if p is None:
+        p = ram.problem(1, 2, 4, 64, 1, 1, 16)
+        p.U = U
+        p.P = P
+    n = ctypes.c_size_t(0)
+    st = ram.lib().ram_workspace_size(ctypes.byref(p), 1, ctypes.byref(n))
+    assert st == code, ram.ram_status_string(st)
+    if code == ram.RAM_OK:
+        L = ram.ram_workspace_layout(p)
+        # per-digit logsumexp of every row and side
+        assert L["idx_r"] - L["lse_w"] >= 4 * p.N * U
+
+
+def test_problem_helper_checks_digits():
+    p = ram.problem(2, 3, 5, 64, 4, 4, 8, U=3, P=4)
+    assert (p.U, p.P, p.S, p.row) == (3, 4, 64, 12)
+    with pytest.raises(ValueError):
+        ram.problem(2, 3, 5, 60, 4, 4, 8, U=3, P=4)
+    with pytest.raises(ValueError):
+        ram.problem(2, 3, 5, 64, 4, 4, 8, U=3)
 
 
 def test_status_strings():
