@@ -36,31 +36,27 @@ METRIC = "tokens/sec fwd+bwd per layer on 1 MI355X; achieved HBM GB/s vs peak"
 
 def algorithmic_bytes(cfg, b_io=2):
     """Bytes the method must move per fwd+bwd step: each input read once and
-    each output written once per pass (state, logits, values, gradients)."""
+    each output written once per pass (state, logits, values, gradients).
+    A logit row holds U * P values (S for one digit)."""
     N = cfg.B * cfg.T * cfg.H
-    S, d = cfg.S, cfg.d_v
-    nseg = cfg.B * cfg.H * S
-    fwd = N * (2 * S * b_io + d * b_io + b_io + d * b_io) + nseg * (d + 1) * 4
-    bwd = N * (2 * S * b_io + 2 * S * b_io + 3 * d * b_io + 2 * b_io)
+    R, d = cfg.U * cfg.P, cfg.d_v
+    nseg = cfg.B * cfg.H * cfg.S
+    fwd = N * (2 * R * b_io + d * b_io + b_io + d * b_io) + nseg * (d + 1) * 4
+    bwd = N * (2 * R * b_io + 2 * R * b_io + 3 * d * b_io + 2 * b_io)
     return fwd, bwd
 
 
 def decode_bwd_bytes(cfg, b_io=2):
     """Algorithmic bytes of one decode_bwd launch (both sides): per row the
-    S logits read and S gradients written, plus lse and k x (index, weight,
-    weight gradient)."""
+    U * P logits read and as many gradients written, plus the U logsumexps
+    and k x (index, weight, weight gradient)."""
     N = cfg.B * cfg.T * cfg.H
-    per_row = 2 * cfg.S * b_io + 4 + cfg.k_w * 12
+    per_row = 2 * cfg.U * cfg.P * b_io + 4 * cfg.U + cfg.k_w * 12
     return 2 * N * per_row
 
 
-def decode_fwd_bytes(cfg, b_io=2):
-    N = cfg.B * cfg.T * cfg.H
-    per_row = cfg.S * b_io + 4 + cfg.k_w * 8
-    return 2 * N * per_row + N * cfg.d_v * 4   # + clearing the read accumulator
-
-
 DECODE_SOURCES = ("linear_attention_ram_amd/csrc/decode.hip", "linear_attention_ram_amd/csrc/decode.hpp",
+                  "linear_attention_ram_amd/csrc/decode_prod.hpp",
                   "linear_attention_ram_amd/csrc/common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bwd_1.3b_hbm_traffic.txt")
 
@@ -108,7 +104,8 @@ def cpu_baseline(cfg, x, threads, budget_s=15.0):
                 return np.stack([x[key][b, h].double().cpu().numpy() for b, h in group])[:, None]
             return np.stack([x[key][b, :, h].double().cpu().numpy() for b, h in group])[:, :, None]
         h = {k: stack(k) for k in ("wl", "rl", "v", "gamma", "d_o")}
-        op = oracle.problem(n, 1, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, eps=cfg.eps)
+        op = oracle.problem(n, 1, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, U=cfg.U, P=cfg.P,
+                            eps=cfg.eps)
         t0 = time.perf_counter()
         oracle.forward(op, h["wl"], h["rl"], h["v"], h["gamma"])
         oracle.backward(op, h["wl"], h["rl"], h["v"], h["gamma"], None, None, h["d_o"])
@@ -143,8 +140,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--config", default="1.3b",
-                    help="workload: 1.3b (default, the measured one), 340m, or 1.3b-uniform "
-                         "(no hot-slot bias; for analysis only)")
+                    help="workload: 1.3b (default, the measured one), 340m, 1.3b-uniform "
+                         "(no hot-slot bias) or 1.3b-u2 (U = 2 digits of 64); the last "
+                         "three for analysis only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the core shards "
@@ -165,7 +163,8 @@ def main():
     else:
         cfg = synth.CONFIGS[args.config]
     x = synth.layer_inputs(cfg, device=dev, seed=0)
-    p = ram.problem(cfg.B, cfg.H, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io=cfg.io, eps=cfg.eps)
+    p = ram.problem(cfg.B, cfg.H, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io=cfg.io, eps=cfg.eps,
+                    U=cfg.U, P=cfg.P)
     ws = ram.workspace(p, True, dev)
     o = torch.empty_like(x["v"])
     slot1 = torch.empty((cfg.B, cfg.H, cfg.S, cfg.d_v), dtype=torch.float32, device=dev)
@@ -219,7 +218,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"RAM-Net attention core, {cfg.name}-layer shape, fwd+bwd",
                    "B": cfg.B, "H": cfg.H, "T": cfg.T, "S": cfg.S, "k_w": cfg.k_w,
-                   "k_r": cfg.k_r, "d_v": cfg.d_v, "io_dtype": "bf16", "state": "f32",
+                   "k_r": cfg.k_r, "d_v": cfg.d_v, "U": cfg.U, "P": cfg.P,
+                   "io_dtype": "bf16", "state": "f32",
                    "address_bias": f"Zipf({cfg.zipf}) per slot" if cfg.zipf else "none",
                    "tokens_per_step": tokens,
                    "parallelism": "single GPU"},
