@@ -119,6 +119,145 @@ def cpu_baseline(cfg, x, threads, budget_s=15.0):
                       f"{threads} host threads"}
 
 
+def decode_step_bytes(cfg, b_io=2):
+    """Algorithmic bytes of one autoregressive step over the batch: both
+    logit rows, v, gamma and o of every (sequence, head), and the k_w slot
+    rows (content and mass) read and written plus the k_r slot rows read."""
+    BH = cfg.B * cfg.H
+    per = (2 * cfg.S * b_io + 2 * cfg.d_v * b_io + b_io
+           + cfg.k_w * 2 * (cfg.d_v + 1) * 4 + cfg.k_r * (cfg.d_v + 1) * 4)
+    return BH * per
+
+
+def bench_decode(args, torch, ram, synth, dev):
+    """Autoregressive decoding: args.dec_steps calls of ram_decode_step on the
+    state of 256 sequences, inputs from a ring of args.dec_ring pregenerated
+    steps (all resident in HBM), replayed from a HIP graph of one ring pass so
+    that host launch cost is not timed."""
+    cfg = synth.CONFIGS["decode"]
+    slot, mass = synth.decode_state(cfg, device=dev, seed=0)
+    ring = [synth.decode_step_inputs(cfg, s, device=dev, seed=0) for s in range(args.dec_ring)]
+    p = ram.problem(cfg.B, cfg.H, 1, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io=cfg.io, eps=cfg.eps)
+    o = torch.empty((cfg.B, 1, cfg.H, cfg.d_v), dtype=cfg.dtype, device=dev)
+
+    def ring_pass():
+        for x in ring:
+            ram.ram_decode_step(p, x["wl"], x["rl"], x["v"], x["gamma"], slot, mass, o)
+
+    ring_pass()                                   # warm-up (eager)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            ring_pass()
+    torch.cuda.synchronize()
+    reps = max(1, args.dec_steps // args.dec_ring)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    steps = reps * args.dec_ring
+    # per-kernel time: the same ring eagerly with the library's event timing
+    ram.ram_prof_enable(True)
+    ring_pass()
+    torch.cuda.synchronize()
+    prof = ram.ram_prof_collect()
+    ram.ram_prof_enable(False)
+    n, t = prof["decode_step"]
+    per_step = decode_step_bytes(cfg)
+    achieved = per_step / (t / n * 1e-3) / 1e9
+    return {
+        "metric": "tokens/sec of autoregressive decode steps on 1 MI355X; achieved HBM GB/s vs peak",
+        "value": cfg.B * steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.dec_ring, "ms_per_step": el * 1e3 / steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "RAM-Net autoregressive decode step", "sequences": cfg.B,
+                   "H": cfg.H, "S": cfg.S, "k_w": cfg.k_w, "k_r": cfg.k_r, "d_v": cfg.d_v,
+                   "io_dtype": "bf16", "state": "f32, 8.6 GB resident",
+                   "inputs": f"ring of {args.dec_ring} pregenerated steps",
+                   "launch": "HIP graph of one ring pass"},
+        "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": per_step},
+        "kernels": {k: {"launches": a, "avg_ms": b / a} for k, (a, b) in prof.items()},
+    }
+
+
+def long_bytes(cfg, b_io=2):
+    """Algorithmic bytes of the long-context forward: per token-head both
+    logit rows, v, gamma and o; per chunk the state (content and mass)
+    written, and read back by the next chunk."""
+    N = cfg.B * cfg.T * cfg.H
+    per_tok = 2 * cfg.S * b_io + 2 * cfg.d_v * b_io + b_io
+    nchunk = cfg.T // cfg.chunk
+    state = cfg.B * cfg.H * cfg.S * (cfg.d_v + 1) * 4
+    return N * per_tok + nchunk * state + (nchunk - 1) * state
+
+
+def bench_long(args, torch, ram, synth, dev):
+    """Long context: a 65,536-token forward as 16 calls of 4,096 tokens, each
+    starting from the state the previous one left (chunk inputs pregenerated
+    and resident; the first chunk starts from empty slots)."""
+    cfg = synth.CONFIGS["long"]
+    nchunk = cfg.T // cfg.chunk
+    chunks = [synth.chunk_inputs(cfg, c, device=dev, seed=0) for c in range(nchunk)]
+    p = ram.problem(cfg.B, cfg.H, cfg.chunk, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, io=cfg.io,
+                    eps=cfg.eps)
+    ws = ram.workspace(p, False, dev)
+    o = torch.empty_like(chunks[0]["v"])
+    st = [(torch.empty((cfg.B, cfg.H, cfg.S, cfg.d_v), dtype=torch.float32, device=dev),
+           torch.empty((cfg.B, cfg.H, cfg.S), dtype=torch.float32, device=dev)) for _ in range(2)]
+
+    def run():
+        prev = (None, None)
+        for c, x in enumerate(chunks):
+            s1, m1 = st[c % 2]
+            ram.ram_forward(p, x["wl"], x["rl"], x["v"], x["gamma"], prev[0], prev[1], o, s1,
+                            m1, ws)
+            prev = (s1, m1)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 5))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / reps
+    ram.ram_prof_enable(True)
+    run()
+    torch.cuda.synchronize()
+    prof = ram.ram_prof_collect()
+    ram.ram_prof_enable(False)
+    n, t = prof["decode_fwd"]
+    dec_b = 2 * cfg.B * cfg.chunk * cfg.H * (cfg.S * 2 + 4 + cfg.k_w * 8)
+    achieved = dec_b / (t / n * 1e-3) / 1e9
+    alg = long_bytes(cfg)
+    return {
+        "metric": "tokens/sec of a long-context forward (chunked, state carry) on 1 MI355X; "
+                  "achieved HBM GB/s vs peak",
+        "value": cfg.B * cfg.T / el, "unit": "tokens/s", "n_gpus": 1, "steps": reps,
+        "warmup": max(1, args.warmup), "ms_per_step": el * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "RAM-Net forward, 65,536 tokens in 16 chunks of 4,096",
+                   "B": cfg.B, "H": cfg.H, "T": cfg.T, "chunk": cfg.chunk, "S": cfg.S,
+                   "k_w": cfg.k_w, "k_r": cfg.k_r, "d_v": cfg.d_v, "io_dtype": "bf16",
+                   "state": "f32, carried between chunks"},
+        "roofline": {"bound": "hbm", "kernel": "decode_fwd", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": dec_b},
+        "step_hbm": {"algorithmic_bytes": alg, "achieved_GBps": alg / el / 1e9,
+                     "frac_of_peak": alg / el / 1e9 / PEAK_HBM_GBS},
+        "kernels": {k: {"launches": a, "avg_ms": b / a} for k, (a, b) in prof.items()},
+    }
+
+
 def copy_calibration(steps=5):
     import torch
     n = 1 << 30
@@ -141,8 +280,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--config", default="1.3b",
                     help="workload: 1.3b (default, the measured one), 340m, 1.3b-uniform "
-                         "(no hot-slot bias) or 1.3b-u2 (U = 2 digits of 64); the last "
-                         "three for analysis only")
+                         "(no hot-slot bias) or 1.3b-u2 (U = 2 digits of 64): fwd+bwd "
+                         "steps; decode: autoregressive steps of 256 sequences; long: "
+                         "a 65,536-token forward in 4,096-token chunks with state carry")
+    ap.add_argument("--dec-steps", type=int, default=1024,
+                    help="decode: autoregressive steps per timed run")
+    ap.add_argument("--dec-ring", type=int, default=64,
+                    help="decode: distinct pregenerated step inputs, cycled")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the core shards "
@@ -158,6 +302,12 @@ def main():
     from linear_attention_ram_amd import synth
 
     dev = torch.device("cuda:0")
+    if args.config == "decode":
+        print(json.dumps(bench_decode(args, torch, ram, synth, dev)))
+        return
+    if args.config == "long":
+        print(json.dumps(bench_long(args, torch, ram, synth, dev)))
+        return
     if args.config == "1.3b-uniform":
         cfg = synth.CONFIGS["1.3b"].with_(zipf=None, name="1.3b-uniform")
     else:
