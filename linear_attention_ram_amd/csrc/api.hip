@@ -21,7 +21,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 struct Dims {
   int64_t S, N, E, nseg, nck;
   int64_t row;   // logits per (token, head, side): U * P
-  int ntiles, nbits;
+  int tile, ntiles, nbits;
   size_t io_bytes;
 };
 
@@ -63,7 +63,11 @@ int check_problem(const ram_problem* p, Dims* d) {
     d->E = E;
     d->nseg = nseg;
     d->nck = E / CHUNK + 1;
-    d->ntiles = (p->T + TILE_TOKENS - 1) / TILE_TOKENS;
+    // bucketing tiles of 256 tokens, or 128 when 256 would leave fewer than
+    // 1024 scatter workgroups (measured: 1.3B layer 256, long-context chunk 128)
+    d->tile = 256;
+    if ((int64_t)p->B * p->H * ((p->T + 255) / 256) < 1024) d->tile = 128;
+    d->ntiles = (p->T + d->tile - 1) / d->tile;
     int nb = 0;
     while ((1ll << nb) < S) ++nb;
     d->nbits = nb;
@@ -367,6 +371,7 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
     ba.S = (int)d.S;
     ba.k_w = p->k_w;
     ba.k_r = p->k_r;
+    ba.tile = d.tile;
     ba.ntiles = d.ntiles;
     ba.nbits = d.nbits;
     ba.tile_hist = (int32_t*)(w + L.tile_hist) + (int64_t)b0 * p->H * d.ntiles * d.S;

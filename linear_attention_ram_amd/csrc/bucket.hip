@@ -3,7 +3,7 @@
 // "CUDA execution": events of the same (batch, head, slot) form a segment).
 //
 // A stable counting sort per (b, h), in three kernels:
-//   hist     one block per (b, h, tile of TILE_TOKENS tokens): slot histogram
+//   hist     one block per (b, h, tile of `tile` tokens): slot histogram
 //            of the tile's events in LDS;
 //   scan     one block per (b, h): per slot, exclusive prefix of the tile
 //            counts (in place) and, over the slots in blocks of 1024, the
@@ -12,7 +12,9 @@
 //            doubling length (any order inside a class).
 //            Every (b, h) holds exactly T*(k_w+k_r) events, so segment
 //            offsets need no scan across (b, h);
-//   scatter  one wave per (b, h, tile): walks the tile's events in order
+//   scatter  one workgroup per (b, h, tile): all its waves set up the
+//            tile's per-slot write positions in LDS, then one wave
+//            walks the tile's events in order
 //            (t ascending, write side before read side), ranks equal slots
 //            inside each 64-event batch with ballots, and writes each event
 //            as a 16-byte record (code, weight, retention lambda and
@@ -37,8 +39,8 @@ __global__ __launch_bounds__(256) void bucket_hist_kernel(BucketArgs a) {
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
   const int K = a.k_w + a.k_r;
-  const int t_lo = tile * TILE_TOKENS;
-  const int t_hi = min(a.T, t_lo + TILE_TOKENS);
+  const int t_lo = tile * a.tile;
+  const int t_hi = min(a.T, t_lo + a.tile);
   for (int s = threadIdx.x; s < a.S; s += blockDim.x) hist[s] = 0;
   if (tile == 0 && bh == 0 && threadIdx.x < NBIN) a.long_count[threadIdx.x] = 0;
   __syncthreads();
@@ -106,8 +108,10 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketArgs a) {
         (int32_t)(a.ev_base + (int64_t)a.B * a.H * a.T * (a.k_w + a.k_r));
 }
 
+constexpr int SCATTER_THREADS = 256;
+
 template <typename IO>
-__global__ __launch_bounds__(64) void bucket_scatter_kernel(BucketArgs a) {
+__global__ __launch_bounds__(SCATTER_THREADS) void bucket_scatter_kernel(BucketArgs a) {
   extern __shared__ int next[];
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
@@ -116,11 +120,12 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(BucketArgs a) {
   const int32_t* th = a.tile_hist + ((int64_t)bh * a.ntiles + tile) * S;
   const int32_t* so = a.seg_offset + (int64_t)bh * S;
   const IO* gam = reinterpret_cast<const IO*>(a.gamma);
-  for (int s = lane; s < S; s += WAVE) next[s] = so[s] + th[s];
-  wave_sync();
+  for (int s = threadIdx.x; s < S; s += SCATTER_THREADS) next[s] = so[s] + th[s];
+  __syncthreads();
+  if (threadIdx.x >= WAVE) return;   // the ranking below is one wave's walk
   const int K = a.k_w + a.k_r;
-  const int t_lo = tile * TILE_TOKENS;
-  const int t_hi = min(a.T, t_lo + TILE_TOKENS);
+  const int t_lo = tile * a.tile;
+  const int t_hi = min(a.T, t_lo + a.tile);
   const int n = (t_hi - t_lo) * K;
   const uint64_t lt = lanemask_lt();
   for (int e0 = 0; e0 < n; e0 += WAVE) {
@@ -179,8 +184,9 @@ hipError_t launch_bucket(const BucketArgs& a, bool bf16, hipStream_t st,
   after("bucket_scan", st);
   if (a.ntiles > 0) {
     before("bucket_scatter", st);
-    if (bf16) hipLaunchKernelGGL(bucket_scatter_kernel<bf16_t>, dim3(a.ntiles, BH), dim3(64), lds, st, a);
-    else hipLaunchKernelGGL(bucket_scatter_kernel<float>, dim3(a.ntiles, BH), dim3(64), lds, st, a);
+    const dim3 grid(a.ntiles, BH), block(SCATTER_THREADS);
+    if (bf16) hipLaunchKernelGGL(bucket_scatter_kernel<bf16_t>, grid, block, lds, st, a);
+    else hipLaunchKernelGGL(bucket_scatter_kernel<float>, grid, block, lds, st, a);
     after("bucket_scatter", st);
   }
   return hipGetLastError();

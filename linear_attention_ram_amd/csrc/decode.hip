@@ -241,6 +241,8 @@ hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st) 
   const int nvec = a.S / (bf16 ? 8 : 4);
   if (bf16) {
     if (nvec == 512) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 8, true>), grid, block, 0, st, a);
+    else if (nvec == 2048) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 32, true>), grid, block, 0, st, a);
+    else if (nvec == 1024) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 16, true>), grid, block, 0, st, a);
     else if (nvec <= 64) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 1>), grid, block, 0, st, a);
     else if (nvec <= 128) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 2>), grid, block, 0, st, a);
     else if (nvec <= 256) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 4>), grid, block, 0, st, a);

@@ -6,7 +6,6 @@
 namespace ramk {
 
 constexpr int CHUNK = 16;        // scan chunk: checkpoints at 16-aligned events
-constexpr int TILE_TOKENS = 256; // tokens per bucketing tile
 constexpr int NWL = 4;           // waves per long-segment scan workgroup
 constexpr int SHORT_WAVES = 4;   // waves (one short segment each) per short-segment workgroup
 constexpr int LONG_EVENTS = 128; // segments with more events take the cooperative path
@@ -32,7 +31,8 @@ struct BucketArgs {
   const void* gamma;      // (N) io
   const uint8_t* mask;    // (B, T): nonzero = valid token, or null (all valid)
   int B, H, T, S, k_w, k_r;
-  int ntiles;             // ceil(T / TILE_TOKENS)
+  int tile;               // tokens per bucketing tile
+  int ntiles;             // ceil(T / tile)
   int nbits;              // bits needed for a slot index
   int32_t* tile_hist;     // (B*H, ntiles, S)
   int32_t* seg_offset;    // (B*H*S + 1): absolute positions in `events`

@@ -45,7 +45,9 @@ def test_tiny_full(side):
 
 
 @pytest.mark.parametrize("S,k,io,renorm", [(1024, 8, "bf16", False), (4096, 8, "bf16", True),
-                                           (16384, 8, "bf16", False), (64, 64, "f32", False),
+                                           (16384, 8, "bf16", False), (8192, 16, "bf16", True),
+                                           (16384, 64, "bf16", False), (8192, 8, "f32", False),
+                                           (64, 64, "f32", False),
                                            (8, 1, "bf16", False), (2048, 33, "f32", True),
                                            (512, 5, "bf16", False)])
 def test_ties_and_shapes(S, k, io, renorm):
@@ -59,11 +61,12 @@ def test_ties_and_shapes(S, k, io, renorm):
     check_rows(p, 0, lg, host(lg), np.s_[:])
 
 
-def test_all_equal_rows_take_the_exact_fallback():
+@pytest.mark.parametrize("S", [4096, 8192, 16384])
+def test_all_equal_rows_take_the_exact_fallback(S):
     # every logit equal: more candidates than the LDS list holds
-    B, T, H, S, k = 1, 4, 2, 4096, 8
+    B, T, H, k = 1, 4, 2, 8
     lg = torch.zeros((B, T, H, S), dtype=torch.bfloat16, device=DEV)
-    lg[0, 1, 1, 4000] = 1.0
+    lg[0, 1, 1, S - 96] = 1.0
     p = ram.problem(B, H, T, S, k, k, 16, io="bf16")
     check_rows(p, 1, lg, host(lg), np.s_[:])
 
