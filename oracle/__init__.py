@@ -76,6 +76,10 @@ def lib():
         L.orc_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orc_backward.argtypes = [P] + [vp] * 18
         L.orc_bucket.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.orc_epilogue_forward.argtypes = [ctypes.c_int64, ctypes.c_int, vp, vp, vp,
+                                           ctypes.c_double, vp]
+        L.orc_epilogue_backward.argtypes = [ctypes.c_int64, ctypes.c_int, vp, vp, vp,
+                                            ctypes.c_double, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -196,3 +200,37 @@ def bucket(p: Problem, idx_w, idx_r):
     _check(lib().orc_bucket(ctypes.byref(p), _ptr(iw), _ptr(ir), _ptr(seg), _ptr(ev_t),
                             _ptr(ev_s), _ptr(ev_j)), "bucket")
     return seg, ev_t, ev_s, ev_j
+
+
+def epilogue_forward(o, gate, gain=None, eps=1e-6):
+    """Read epilogue y = sigmoid(gate) * RMSNorm(o) over the last axis (d_v):
+    o / sqrt(mean(o^2) + eps) * gain.  o, gate (..., d_v); gain (d_v) or None."""
+    oo, gg = _f64in(o), _f64in(gate)
+    if oo.shape != gg.shape:
+        raise ValueError("o and gate must have the same shape")
+    d_v = oo.shape[-1]
+    gn = None if gain is None else _f64in(gain)
+    if gn is not None and gn.shape != (d_v,):
+        raise ValueError("gain must have d_v entries")
+    y = np.empty_like(oo)
+    _check(lib().orc_epilogue_forward(ctypes.c_int64(oo.size // d_v), d_v, _ptr(oo), _ptr(gg),
+                                      _ptr(gn), ctypes.c_double(eps), _ptr(y)),
+           "epilogue_forward")
+    return y
+
+
+def epilogue_backward(o, gate, d_y, gain=None, eps=1e-6):
+    """Gradients of epilogue_forward: returns d_o, d_gate (shape of o) and
+    d_gain (d_v) summed over all rows (zeros when gain is None)."""
+    oo, gg, dy = _f64in(o), _f64in(gate), _f64in(d_y)
+    if oo.shape != gg.shape or oo.shape != dy.shape:
+        raise ValueError("o, gate and d_y must have the same shape")
+    d_v = oo.shape[-1]
+    gn = None if gain is None else _f64in(gain)
+    d_o, d_g = np.empty_like(oo), np.empty_like(oo)
+    d_gain = np.zeros(d_v)
+    _check(lib().orc_epilogue_backward(ctypes.c_int64(oo.size // d_v), d_v, _ptr(oo), _ptr(gg),
+                                       _ptr(gn), ctypes.c_double(eps), _ptr(dy), _ptr(d_o),
+                                       _ptr(d_g), _ptr(d_gain)),
+           "epilogue_backward")
+    return d_o, d_g, d_gain

@@ -28,6 +28,11 @@
  *   - Token mask (ramnet-ops "Arguments", mask): a masked token is not
  *     written and its output is to be ignored; read here as a token absent
  *     from the computation (no write, no read, output 0, zero gradients).
+ *   - Read epilogue (paper §3.4 "Read-out", its last sentence, and Fig. 2):
+ *     y = sigmoid(g) * RMSNorm(o), RMSNorm head-wise: over the d_v channels
+ *     of one (token, head), o / sqrt(mean(o^2) + eps_n) times a gain vector
+ *     of d_v entries; g are the gate pre-activations (x W_g).  The output
+ *     projection W_o is outside.
  *   - First-order gradients (ramnet-ops "Autograd and compile").
  *
  * Arithmetic: every floating-point value is held and computed in IEEE double.
@@ -600,5 +605,71 @@ int orc_bucket(const orc_problem* p, const int32_t* idx_w, const int32_t* idx_r,
         }
       }
   free(fill);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Read epilogue (paper §3.4 "Read-out", last sentence; Fig. 2): per row of  */
+/* d_v channels (one token and head), n = o / sqrt(mean_c o_c^2 + eps),      */
+/* z = n * gain, y = sigmoid(g) * z.  gain may be NULL (all ones).           */
+/* ------------------------------------------------------------------------ */
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static double inv_rms(const double* o, int d_v, double eps) {
+  double ss = 0.0;
+  for (int c = 0; c < d_v; ++c) ss += o[c] * o[c];
+  return 1.0 / sqrt(ss / d_v + eps);
+}
+
+int orc_epilogue_forward(int64_t rows, int d_v, const double* o, const double* g,
+                         const double* gain, double eps, double* y) {
+  if (rows < 0 || d_v < 1 || !(eps >= 0.0) || (rows > 0 && (!o || !g || !y))) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* orow = o + r * d_v;
+    const double rstd = inv_rms(orow, d_v, eps);
+    for (int c = 0; c < d_v; ++c) {
+      const double z = orow[c] * rstd * (gain ? gain[c] : 1.0);
+      y[r * d_v + c] = sigmoid(g[r * d_v + c]) * z;
+    }
+  }
+  return ORC_OK;
+}
+
+/* Gradients of the epilogue: given dL/dy, writes dL/do, dL/dg and (when
+ * d_gain is non-NULL) dL/dgain summed over all rows.  With s = sigmoid(g),
+ * dz = dy * s, dg = dy * z * s * (1 - s), dn = dz * gain, and the
+ * normalisation's Jacobian: do = rstd * (dn - n * mean_c(dn_c * n_c)). */
+int orc_epilogue_backward(int64_t rows, int d_v, const double* o, const double* g,
+                          const double* gain, double eps, const double* d_y, double* d_o,
+                          double* d_g, double* d_gain) {
+  if (rows < 0 || d_v < 1 || !(eps >= 0.0) ||
+      (rows > 0 && (!o || !g || !d_y || !d_o || !d_g)))
+    return ORC_EINVAL;
+  if (d_gain) for (int c = 0; c < d_v; ++c) d_gain[c] = 0.0;
+  double* n = (double*)malloc(sizeof(double) * d_v);
+  double* dn = (double*)malloc(sizeof(double) * d_v);
+  if (!n || !dn) { free(n); free(dn); return ORC_ENOMEM; }
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* orow = o + r * d_v;
+    const double rstd = inv_rms(orow, d_v, eps);
+    double dot = 0.0;
+    for (int c = 0; c < d_v; ++c) {
+      const double gc = gain ? gain[c] : 1.0;
+      const double s = sigmoid(g[r * d_v + c]);
+      n[c] = orow[c] * rstd;
+      const double z = n[c] * gc;
+      const double dz = d_y[r * d_v + c] * s;
+      d_g[r * d_v + c] = d_y[r * d_v + c] * z * s * (1.0 - s);
+      if (d_gain) d_gain[c] += dz * n[c];
+      dn[c] = dz * gc;
+      dot += dn[c] * n[c];
+    }
+    dot /= d_v;
+    for (int c = 0; c < d_v; ++c) d_o[r * d_v + c] = rstd * (dn[c] - n[c] * dot);
+  }
+  free(n);
+  free(dn);
   return ORC_OK;
 }
