@@ -283,6 +283,9 @@ def main():
                          "(no hot-slot bias) or 1.3b-u2 (U = 2 digits of 64): fwd+bwd "
                          "steps; decode: autoregressive steps of 256 sequences; long: "
                          "a 65,536-token forward in 4,096-token chunks with state carry")
+    ap.add_argument("--gated", action="store_true",
+                    help="fwd+bwd configs: the gated read-out y = sigmoid(gate) * RMSNorm(o) "
+                         "fused into the read (ram_forward_gated / ram_backward_gated)")
     ap.add_argument("--dec-steps", type=int, default=1024,
                     help="decode: autoregressive steps per timed run")
     ap.add_argument("--dec-ring", type=int, default=64,
@@ -321,8 +324,19 @@ def main():
     mass1 = torch.empty((cfg.B, cfg.H, cfg.S), dtype=torch.float32, device=dev)
     d_wl, d_rl = torch.empty_like(x["wl"]), torch.empty_like(x["rl"])
     d_v, d_g = torch.empty_like(x["v"]), torch.empty_like(x["gamma"])
+    if args.gated:
+        gx = synth.gate_inputs(cfg, device=dev, seed=0)
+        ep = ram.epilogue(p, gx["gate"], gx["gain"], 1e-6)
+        d_gate = torch.empty_like(gx["gate"])
+        d_gain = torch.empty_like(gx["gain"])
 
     def step():
+        if args.gated:
+            ram.ram_forward_gated(p, ep, x["wl"], x["rl"], x["v"], x["gamma"], None, None, o,
+                                  slot1, mass1, ws)
+            ram.ram_backward_gated(p, ep, ws, x["wl"], x["rl"], x["v"], x["gamma"], None, None,
+                                   gx["d_y"], None, None, d_wl, d_rl, d_v, d_g, d_gate, d_gain)
+            return
         ram.ram_forward(p, x["wl"], x["rl"], x["v"], x["gamma"], None, None, o, slot1, mass1, ws)
         ram.ram_backward(p, ws, x["wl"], x["rl"], x["v"], x["gamma"], None, None, x["d_o"],
                          None, None, d_wl, d_rl, d_v, d_g)
@@ -380,7 +394,19 @@ def main():
                      "frac_of_peak": step_gbs / PEAK_HBM_GBS},
         "kernels": kernels,
     }
-    if not args.no_cpu_baseline:
+    if args.gated:
+        # kernel bytes of the fused read epilogue: the k_r read contributions
+        # (io) of every row and the gate read, y written; backward: the same
+        # contributions, gate and d_y read, d_o and d_gate written
+        N, b_io = cfg.B * cfg.T * cfg.H, 2
+        epi_b = {"epilogue_fwd": N * cfg.d_v * b_io * (cfg.k_r + 2),
+                 "epilogue_bwd": N * cfg.d_v * b_io * (cfg.k_r + 4)}
+        out["config"]["read_out"] = "gated: sigmoid(gate) * RMSNorm(o), fused"
+        out["epilogue_roofline"] = {
+            k: {"bytes": b, "GBps": b / (prof[k][1] / prof[k][0] * 1e-3) / 1e9,
+                "frac": b / (prof[k][1] / prof[k][0] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            for k, b in epi_b.items()}
+    if not args.no_cpu_baseline and not args.gated:
         threads = min(16, len(os.sched_getaffinity(0)))
         out["cpu_baseline"] = cpu_baseline(cfg, x, threads, args.cpu_budget)
     print(json.dumps(out))

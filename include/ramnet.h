@@ -129,6 +129,8 @@ typedef struct ram_ws_layout {
   size_t dw;          /* float (N, k_w): backward scratch                                      */
   size_t dr;          /* float (N, k_r)                                                         */
   size_t dgam;        /* float (N, k_w)                                                         */
+  size_t epi_d_o;     /* io (N, d_v): gated backward, gradient of o                              */
+  size_t epi_part;    /* float (8192, d_v): gated backward, gain gradient partial sums           */
   size_t fwd_bytes;   /* workspace bytes ram_forward needs                                      */
   size_t total_bytes; /* workspace bytes ram_forward + ram_backward need                       */
 } ram_ws_layout;
@@ -178,6 +180,41 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
                  const float* slot0, const float* mass0, const void* d_o, const float* d_slot1,
                  const float* d_mass1, void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma,
                  float* d_slot0, float* d_mass0, void* stream);
+
+/* Gated read-out (paper §3.4 "Read-out", last step; Fig. 2): the read o of
+ * each (token, head) goes through a head-wise RMSNorm and a sigmoid output
+ * gate, y = sigmoid(gate) * (o / sqrt(mean_c o_c^2 + eps) * gain), the mean
+ * over the d_v channels of the row.  The output projection is the caller's.
+ *   gate  (B,T,H,d_v) io: gate pre-activations (x W_g plus its bias)
+ *   gain  (d_v) float32, or NULL for all ones
+ *   eps   RMSNorm epsilon, finite and >= 0 */
+typedef struct ram_epilogue {
+  const void* gate;
+  const float* gain;
+  float eps;
+} ram_epilogue;
+
+/* ram_forward with the gated read-out fused into the read: writes y
+ * (B,T,H,d_v) io instead of o (o itself is not written; the arithmetic of o
+ * is that of ram_forward, kept in float32 for the norm).  A masked token's
+ * y row is 0.  ws as for ram_forward. */
+int ram_forward_gated(const ram_problem* p, const ram_epilogue* ep, const void* wlogits,
+                      const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
+                      const float* slot0, const float* mass0, void* y, float* slot1, float* mass1,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of ram_forward_gated (same problem, ep, inputs and ws): d_y is
+ * the gradient of y; writes everything ram_backward writes, plus d_gate
+ * (B,T,H,d_v) io and, when non-NULL, d_gain (d_v) float32 summed over all
+ * rows in a fixed order (deterministic).  o is recomputed from the read
+ * contributions the forward left in ws.  Masked tokens get zero d_gate and
+ * add nothing to d_gain. */
+int ram_backward_gated(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t ws_bytes,
+                       const void* wlogits, const void* rlogits, const void* v, const void* gamma,
+                       const uint8_t* mask, const float* slot0, const float* mass0,
+                       const void* d_y, const float* d_slot1, const float* d_mass1,
+                       void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma, void* d_gate,
+                       float* d_gain, float* d_slot0, float* d_mass0, void* stream);
 
 /* Autoregressive step (ramnet-ops "CUDA execution", autoregressive mode;
  * paper §4: each new token updates and reads its own K slots): p->T == 1;

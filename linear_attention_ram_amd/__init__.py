@@ -6,7 +6,9 @@ kernels of ``_lib/libramnet.so`` behind the C ABI declared in
 missing the calls raise.  PyTorch supplies device memory and the stream.
 
 Functions keep the C names: ``ram_workspace_size``, ``ram_workspace_layout``,
-``ram_decode``, ``ram_forward``, ``ram_backward``, ``ram_decode_step``,
+``ram_decode``, ``ram_forward``, ``ram_backward``, ``ram_forward_gated``,
+``ram_backward_gated`` (with ``epilogue`` to build their gate argument),
+``ram_decode_step``,
 ``ram_status_string``, plus ``ram_prof_enable`` / ``ram_prof_collect``.
 Tensors are passed by device pointer; the stream defaults to PyTorch's current
 stream.
@@ -24,8 +26,8 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libramnet.so")
 RAM_OK, RAM_EINVAL, RAM_EDTYPE, RAM_ECAPACITY, RAM_EUNSUPPORTED, RAM_EHIP = 0, -1, -2, -3, -4, -5
 RAM_F32, RAM_BF16 = 0, 1
 EXPORTED = ("ram_workspace_size", "ram_workspace_layout", "ram_decode", "ram_forward",
-            "ram_backward", "ram_decode_step", "ram_status_string", "ram_prof_enable",
-            "ram_prof_collect")
+            "ram_backward", "ram_forward_gated", "ram_backward_gated", "ram_decode_step",
+            "ram_status_string", "ram_prof_enable", "ram_prof_collect")
 
 
 class Problem(ctypes.Structure):
@@ -61,7 +63,13 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "idx_w", "w_w", "lse_w", "idx_r", "w_r", "lse_r", "seg_offset", "events", "ckpt_s",
         "ckpt_m", "stash", "tile_hist", "long_list", "long_count", "dw", "dr", "dgam",
-        "fwd_bytes", "total_bytes")]
+        "epi_d_o", "epi_part", "fwd_bytes", "total_bytes")]
+
+
+class Epilogue(ctypes.Structure):
+    """Gated read-out: y = sigmoid(gate) * RMSNorm(o) (gate io (B,T,H,d_v),
+    gain float (d_v) or NULL, eps)."""
+    _fields_ = [("gate", ctypes.c_void_p), ("gain", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
 class ProfEntry(ctypes.Structure):
@@ -106,6 +114,9 @@ def lib() -> ctypes.CDLL:
     L.ram_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.ram_backward.argtypes = [P, vp, sz] + [vp] * 17
     L.ram_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    EP = ctypes.POINTER(Epilogue)
+    L.ram_forward_gated.argtypes = [P, EP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.ram_backward_gated.argtypes = [P, EP, vp, sz] + [vp] * 19
     L.ram_status_string.argtypes = [ctypes.c_int]
     L.ram_status_string.restype = ctypes.c_char_p
     L.ram_prof_enable.argtypes = [ctypes.c_int]
@@ -240,6 +251,57 @@ def ram_backward(p: Problem, ws, wlogits, rlogits, v, gamma, slot0, mass0, d_o, 
             _ptr(d_slot0, "d_slot0", torch.float32, nseg * p.d_v, optional=True),
             _ptr(d_mass0, "d_mass0", torch.float32, nseg, optional=True))
     _check(lib().ram_backward(ctypes.byref(p), *args, _stream(stream, ws.device)), "ram_backward")
+
+
+def epilogue(p: Problem, gate, gain=None, eps=1e-6) -> Epilogue:
+    """Gated read-out arguments; gate (B,T,H,d_v) io, gain (d_v) float32 or None.
+    The tensors must stay alive while calls that use the result run."""
+    return Epilogue(_ptr(gate, "gate", p.torch_dtype, p.N * p.d_v),
+                    _ptr(gain, "gain", torch.float32, p.d_v, optional=True), float(eps))
+
+
+def ram_forward_gated(p: Problem, ep: Epilogue, wlogits, rlogits, v, gamma, slot0, mass0, y,
+                      slot1, mass1, ws, stream=None, mask=None):
+    """ram_forward with the gated read-out: writes y instead of o."""
+    io = p.torch_dtype
+    N, nseg = p.N, p.B * p.H * p.S
+    args = (_ptr(wlogits, "wlogits", io, N * p.row), _ptr(rlogits, "rlogits", io, N * p.row),
+            _ptr(v, "v", io, N * p.d_v), _ptr(gamma, "gamma", io, N),
+            _ptr(mask, "mask", torch.uint8, p.B * p.T, optional=True),
+            _ptr(slot0, "slot0", torch.float32, nseg * p.d_v, optional=True),
+            _ptr(mass0, "mass0", torch.float32, nseg, optional=True),
+            _ptr(y, "y", io, N * p.d_v),
+            _ptr(slot1, "slot1", torch.float32, nseg * p.d_v),
+            _ptr(mass1, "mass1", torch.float32, nseg),
+            _ptr(ws, "ws", torch.uint8), ctypes.c_size_t(ws.numel()))
+    _check(lib().ram_forward_gated(ctypes.byref(p), ctypes.byref(ep), *args,
+                                   _stream(stream, ws.device)), "ram_forward_gated")
+
+
+def ram_backward_gated(p: Problem, ep: Epilogue, ws, wlogits, rlogits, v, gamma, slot0, mass0,
+                       d_y, d_slot1, d_mass1, d_wlogits, d_rlogits, d_v, d_gamma, d_gate,
+                       d_gain=None, d_slot0=None, d_mass0=None, stream=None, mask=None):
+    """Backward of ram_forward_gated: d_y is the gradient of y."""
+    io = p.torch_dtype
+    N, nseg = p.N, p.B * p.H * p.S
+    args = (_ptr(ws, "ws", torch.uint8), ctypes.c_size_t(ws.numel()),
+            _ptr(wlogits, "wlogits", io, N * p.row), _ptr(rlogits, "rlogits", io, N * p.row),
+            _ptr(v, "v", io, N * p.d_v), _ptr(gamma, "gamma", io, N),
+            _ptr(mask, "mask", torch.uint8, p.B * p.T, optional=True),
+            _ptr(slot0, "slot0", torch.float32, nseg * p.d_v, optional=True),
+            _ptr(mass0, "mass0", torch.float32, nseg, optional=True),
+            _ptr(d_y, "d_y", io, N * p.d_v),
+            _ptr(d_slot1, "d_slot1", torch.float32, nseg * p.d_v, optional=True),
+            _ptr(d_mass1, "d_mass1", torch.float32, nseg, optional=True),
+            _ptr(d_wlogits, "d_wlogits", io, N * p.row),
+            _ptr(d_rlogits, "d_rlogits", io, N * p.row),
+            _ptr(d_v, "d_v", io, N * p.d_v), _ptr(d_gamma, "d_gamma", io, N),
+            _ptr(d_gate, "d_gate", io, N * p.d_v),
+            _ptr(d_gain, "d_gain", torch.float32, p.d_v, optional=True),
+            _ptr(d_slot0, "d_slot0", torch.float32, nseg * p.d_v, optional=True),
+            _ptr(d_mass0, "d_mass0", torch.float32, nseg, optional=True))
+    _check(lib().ram_backward_gated(ctypes.byref(p), ctypes.byref(ep), *args,
+                                    _stream(stream, ws.device)), "ram_backward_gated")
 
 
 def ram_decode_step(p: Problem, wlogits, rlogits, v, gamma, slot, mass, o, stream=None,

@@ -130,6 +130,8 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   L->dw = take(sizeof(float) * d.N * p->k_w);
   L->dr = take(sizeof(float) * d.N * p->k_r);
   L->dgam = take(sizeof(float) * d.N * p->k_w);
+  L->epi_d_o = take(d.io_bytes * d.N * p->d_v);
+  L->epi_part = take(sizeof(float) * EPI_BWD_WAVES * p->d_v);
   L->total_bytes = off;
 }
 
@@ -296,13 +298,25 @@ int ram_decode(const ram_problem* p, int side, const void* logits, int32_t* idx,
   return hip_status(e);
 }
 
-int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
-                const void* gamma, const uint8_t* mask, const float* slot0, const float* mass0,
-                void* o, float* slot1, float* mass1, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+bool epilogue_ok(const ram_epilogue* ep, int64_t N) {
+  return ep && (N == 0 || ep->gate) && ep->eps >= 0.f && ep->eps <= 3.0e38f;
+}
+
+// ram_forward, or with ep the gated read-out y = sigmoid(gate) * RMSNorm(o)
+// written to o.
+int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogits,
+                 const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
+                 const float* slot0, const float* mass0, void* o, float* slot1, float* mass1,
+                 void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   int st = check_problem(p, &d);
   if (st != RAM_OK) return st;
   if (!slot1 || !mass1 || !ws) return RAM_EINVAL;
+  if (ep && !epilogue_ok(ep, d.N)) return RAM_EINVAL;
   if (d.N > 0 && (!wlogits || !rlogits || !v || !gamma || !o)) return RAM_EINVAL;
   if ((slot0 == nullptr) != (mass0 == nullptr)) return RAM_EINVAL;
   if (d.N > 0 && (!aligned16(wlogits) || !aligned16(rlogits))) return RAM_EINVAL;
@@ -418,15 +432,32 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
     prof_after("scan_fwd", a);
     if (e != hipSuccess) break;
 
-    FinalizeArgs fa{};
-    fa.N = rows;
-    fa.d_v = p->d_v;
-    fa.k = p->k_r;
-    fa.stash = sa.stash;
-    fa.out = adv(o, r0 * p->d_v, io);
-    prof_before("finalize_o", a);
-    e = launch_finalize(fa, bf, a);
-    prof_after("finalize_o", a);
+    if (ep) {
+      EpilogueArgs ea{};
+      ea.N = rows;
+      ea.d_v = p->d_v;
+      ea.k = p->k_r;
+      ea.T = p->T;
+      ea.H = p->H;
+      ea.stash = sa.stash;
+      ea.gate = adv(ep->gate, r0 * p->d_v, io);
+      ea.gain = ep->gain;
+      ea.eps = ep->eps;
+      ea.y = adv(o, r0 * p->d_v, io);
+      prof_before("epilogue_fwd", a);
+      e = launch_epilogue_fwd(ea, bf, a);
+      prof_after("epilogue_fwd", a);
+    } else {
+      FinalizeArgs fa{};
+      fa.N = rows;
+      fa.d_v = p->d_v;
+      fa.k = p->k_r;
+      fa.stash = sa.stash;
+      fa.out = adv(o, r0 * p->d_v, io);
+      prof_before("finalize_o", a);
+      e = launch_finalize(fa, bf, a);
+      prof_after("finalize_o", a);
+    }
   }
   S->dep(s, a);
   S->dep(s, b);
@@ -434,15 +465,19 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
   return RAM_OK;
 }
 
-int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wlogits,
-                 const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
-                 const float* slot0, const float* mass0, const void* d_o, const float* d_slot1,
-                 const float* d_mass1, void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma,
-                 float* d_slot0, float* d_mass0, void* stream) {
+// ram_backward, or with ep the backward of the gated read-out: d_o is then
+// the gradient of y, and d_gate / d_gain receive the epilogue's gradients.
+int backward_impl(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t ws_bytes,
+                  const void* wlogits, const void* rlogits, const void* v, const void* gamma,
+                  const uint8_t* mask, const float* slot0, const float* mass0, const void* d_o,
+                  const float* d_slot1, const float* d_mass1, void* d_wlogits, void* d_rlogits,
+                  void* d_v, void* d_gamma, void* d_gate, float* d_gain, float* d_slot0,
+                  float* d_mass0, void* stream) {
   Dims d;
   int st = check_problem(p, &d);
   if (st != RAM_OK) return st;
   if (!ws) return RAM_EINVAL;
+  if (ep && (!epilogue_ok(ep, d.N) || (d.N > 0 && !d_gate))) return RAM_EINVAL;
   if (d.N > 0 && (!wlogits || !rlogits || !v || !gamma || !d_o || !d_wlogits || !d_rlogits ||
                   !d_v || !d_gamma))
     return RAM_EINVAL;
@@ -471,6 +506,30 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   hipStream_t a = P.n > 1 ? S->side[1] : s, b = S->side[0];
   S->dep(a, s);
   hipError_t e = hipSuccess;
+  if (ep) {
+    // gradient of o from that of y, for all rows at once; the stash still
+    // holds the forward's read contributions until the reverse scan
+    // overwrites it
+    EpilogueArgs ea{};
+    ea.N = d.N;
+    ea.d_v = p->d_v;
+    ea.k = p->k_r;
+    ea.T = p->T;
+    ea.H = p->H;
+    ea.stash = w + L.stash;
+    ea.gate = ep->gate;
+    ea.gain = ep->gain;
+    ea.eps = ep->eps;
+    ea.d_y = d_o;
+    ea.d_o = w + L.epi_d_o;
+    ea.d_gate = d_gate;
+    ea.part = (float*)(w + L.epi_part);
+    ea.d_gain = d_gain;
+    ea.mask = mask;
+    prof_before("epilogue_bwd", a);
+    e = launch_epilogue_bwd(ea, bf, a);
+    prof_after("epilogue_bwd", a);
+  }
   for (int q = 0; q < P.n && e == hipSuccess && S->err == hipSuccess; ++q) {
     const int b0 = P.b0[q], nb = P.b0[q + 1] - P.b0[q];
     const int64_t r0 = (int64_t)b0 * TH, rows = (int64_t)nb * TH;
@@ -493,6 +552,7 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
     sb.events = (const EventRec*)(w + L.events);
     sb.v = adv(v, r0 * p->d_v, io);
     sb.d_o = adv(d_o, r0 * p->d_v, io);
+    if (ep) sb.d_o = w + L.epi_d_o + r0 * p->d_v * (int64_t)io;
     sb.slot0 = adv(slot0, (int64_t)b0 * HS * p->d_v, sizeof(float));
     sb.mass0 = adv(mass0, (int64_t)b0 * HS, sizeof(float));
     sb.ckpt_s = (const float*)(w + L.ckpt_s);
@@ -561,6 +621,48 @@ int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wl
   S->dep(s, b);
   if (e != hipSuccess || S->err != hipSuccess) return RAM_EHIP;
   return RAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
+                const void* gamma, const uint8_t* mask, const float* slot0, const float* mass0,
+                void* o, float* slot1, float* mass1, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(p, nullptr, wlogits, rlogits, v, gamma, mask, slot0, mass0, o, slot1, mass1,
+                      ws, ws_bytes, stream);
+}
+
+int ram_forward_gated(const ram_problem* p, const ram_epilogue* ep, const void* wlogits,
+                      const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
+                      const float* slot0, const float* mass0, void* y, float* slot1, float* mass1,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!ep) return RAM_EINVAL;
+  return forward_impl(p, ep, wlogits, rlogits, v, gamma, mask, slot0, mass0, y, slot1, mass1, ws,
+                      ws_bytes, stream);
+}
+
+int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wlogits,
+                 const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
+                 const float* slot0, const float* mass0, const void* d_o, const float* d_slot1,
+                 const float* d_mass1, void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma,
+                 float* d_slot0, float* d_mass0, void* stream) {
+  return backward_impl(p, nullptr, ws, ws_bytes, wlogits, rlogits, v, gamma, mask, slot0, mass0,
+                       d_o, d_slot1, d_mass1, d_wlogits, d_rlogits, d_v, d_gamma, nullptr, nullptr,
+                       d_slot0, d_mass0, stream);
+}
+
+int ram_backward_gated(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t ws_bytes,
+                       const void* wlogits, const void* rlogits, const void* v, const void* gamma,
+                       const uint8_t* mask, const float* slot0, const float* mass0,
+                       const void* d_y, const float* d_slot1, const float* d_mass1,
+                       void* d_wlogits, void* d_rlogits, void* d_v, void* d_gamma, void* d_gate,
+                       float* d_gain, float* d_slot0, float* d_mass0, void* stream) {
+  if (!ep) return RAM_EINVAL;
+  return backward_impl(p, ep, ws, ws_bytes, wlogits, rlogits, v, gamma, mask, slot0, mass0, d_y,
+                       d_slot1, d_mass1, d_wlogits, d_rlogits, d_v, d_gamma, d_gate, d_gain,
+                       d_slot0, d_mass0, stream);
 }
 
 int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,

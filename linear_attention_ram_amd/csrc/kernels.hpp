@@ -99,6 +99,25 @@ struct FinalizeArgs {
   void* d_gamma;          // (N) io or null
 };
 
+// Read epilogue y = sigmoid(gate) * RMSNorm(o) fused into the read-out.
+constexpr int EPI_BWD_WAVES = 8192;   // waves of the epilogue backward (gain partial sums)
+struct EpilogueArgs {
+  int64_t N;              // (token, head) rows
+  int d_v, k;             // k = k_r: read contributions per row in the stash
+  int T, H;               // row r is token (r / H) % T of batch r / (T * H)
+  const void* stash;      // (N, k, d_v) io: read contributions of the forward
+  const void* gate;       // (N, d_v) io: gate pre-activations
+  const float* gain;      // (d_v) or null (ones)
+  float eps;
+  void* y;                // forward: (N, d_v) io
+  const void* d_y;        // backward: (N, d_v) io
+  void* d_o;              // backward: (N, d_v) io, input of the reverse scan
+  void* d_gate;           // backward: (N, d_v) io
+  float* part;            // backward: (EPI_BWD_WAVES, d_v) gain partial sums
+  float* d_gain;          // backward: (d_v) or null
+  const uint8_t* mask;    // (B, T) or null: masked rows get zero gradients
+};
+
 struct StepArgs {
   int B, H, S, d_v, k_w, k_r, renorm_w, renorm_r;
   int U, P;               // address digits and digit size (S = P^U)
@@ -124,5 +143,7 @@ hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st, hipS
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st, hipStream_t side);
 hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_epilogue_fwd(const EpilogueArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_epilogue_bwd(const EpilogueArgs& a, bool bf16, hipStream_t st);
 
 }  // namespace ramk

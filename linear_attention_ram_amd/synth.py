@@ -168,6 +168,20 @@ def layer_inputs(cfg: Config, device="cpu", seed: int = 0, T: int | None = None,
     return out
 
 
+def gate_inputs(cfg: Config, device="cpu", seed: int = 0, T: int | None = None):
+    """Inputs of the gated read-out, from their own seeded stream (seed * 7 +
+    3): gate pre-activations (B,T,H,d_v) ~ N(3, 1) in the io dtype (3 is the
+    paper's output-gate bias initialisation, App. A "Bias Initialization"),
+    RMSNorm gain (d_v) ~ 1 + 0.1 N(0, 1) float32, and the gradient d_y of the
+    gated output (B,T,H,d_v) ~ N(0, 1) io."""
+    T = cfg.T if T is None else T
+    g = generator(device, seed * 7 + 3)
+    shape = (cfg.B, T, cfg.H, cfg.d_v)
+    return {"gate": _randn(shape, g, device, cfg.dtype, mean=3.0),
+            "gain": 1.0 + 0.1 * torch.randn((cfg.d_v,), generator=g, device=device),
+            "d_y": _randn(shape, g, device, cfg.dtype)}
+
+
 def chunk_inputs(cfg: Config, chunk: int, device="cpu", seed: int = 0):
     """Inputs of chunk ``chunk`` of the long-context forward: its own seeded
     stream (seed * 1_000_003 + chunk) so any chunk can be regenerated alone."""

@@ -30,7 +30,8 @@ def test_library_exports_every_declared_function():
 
 def test_problem_struct_matches_header_size():
     assert ctypes.sizeof(ram.Problem) == 64
-    assert ctypes.sizeof(ram.WsLayout) == 19 * ctypes.sizeof(ctypes.c_size_t)
+    assert ctypes.sizeof(ram.WsLayout) == 21 * ctypes.sizeof(ctypes.c_size_t)
+    assert ctypes.sizeof(ram.Epilogue) == 24
 
 
 def status_of(**kw):
@@ -136,3 +137,30 @@ def test_forward_rejects_small_workspace_before_touching_the_gpu():
     assert st == ram.RAM_EINVAL             # slot0 without mass0
     st = L.ram_decode_step(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, None)
     assert st == ram.RAM_EINVAL             # T != 1
+
+
+def test_gated_calls_validate_before_touching_the_gpu():
+    p = ram.problem(1, 1, 8, 64, 2, 2, 16, io="f32")
+    L = ram.lib()
+    fake = ctypes.c_void_p(16 * 1024)  # never dereferenced: validation fails first
+    big = ctypes.c_size_t(1 << 40)
+    fwd = (fake, fake, fake, fake, None, None, None, fake, fake, fake, fake, big, None)
+    assert L.ram_forward_gated(ctypes.byref(p), None, *fwd) == ram.RAM_EINVAL
+    no_gate = ram.Epilogue(None, None, 1e-6)
+    assert L.ram_forward_gated(ctypes.byref(p), ctypes.byref(no_gate), *fwd) == ram.RAM_EINVAL
+    bad_eps = ram.Epilogue(fake, None, -1.0)
+    assert L.ram_forward_gated(ctypes.byref(p), ctypes.byref(bad_eps), *fwd) == ram.RAM_EINVAL
+    ok = ram.Epilogue(fake, None, 1e-6)
+    bwd = [fake, big, fake, fake, fake, fake, None, None, None, fake, None, None, fake, fake,
+           fake, fake, None, None, None, None, None]
+    # d_gate (position 16 after ep) missing
+    assert L.ram_backward_gated(ctypes.byref(p), ctypes.byref(ok), *bwd) == ram.RAM_EINVAL
+    assert L.ram_backward_gated(ctypes.byref(p), None, *bwd) == ram.RAM_EINVAL
+
+
+def test_gated_workspace_areas():
+    p = ram.problem(2, 3, 40, 64, 4, 4, 24, io="bf16")
+    L = ram.ram_workspace_layout(p)
+    assert L["fwd_bytes"] <= L["epi_d_o"] < L["epi_part"] < L["total_bytes"]
+    assert L["epi_part"] - L["epi_d_o"] >= 2 * p.N * p.d_v
+    assert L["total_bytes"] - L["epi_part"] >= 4 * 8192 * p.d_v
