@@ -290,7 +290,7 @@ int ram_decode(const ram_problem* p, int side, const void* logits, int32_t* idx,
   a.H = p->H;
   a.T = p->T;
   a.cape_heads = p->cape_heads;
-  a.t0 = p->t0;
+  a.t0 = p->t0 % d.S;
   hipStream_t s = (hipStream_t)stream;
   prof_before("decode_fwd", s);
   hipError_t e = launch_decode_fwd(a, p->io_dtype == RAM_BF16, s);
@@ -365,7 +365,7 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
     da.H = p->H;
     da.T = p->T;
     da.cape_heads = p->cape_heads;
-    da.t0 = p->t0;
+    da.t0 = p->t0 % d.S;
     prof_before("decode_fwd", s);
     e = launch_decode_fwd(da, bf, s);
     prof_after("decode_fwd", s);
@@ -598,7 +598,7 @@ int backward_impl(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t
     db.H = p->H;
     db.T = p->T;
     db.cape_heads = p->cape_heads;
-    db.t0 = p->t0;
+    db.t0 = p->t0 % d.S;
     db.mask = mask ? mask + (int64_t)b0 * p->T : nullptr;
     prof_before("decode_bwd", s);
     e = launch_decode_bwd(db, bf, s);
@@ -687,7 +687,7 @@ int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogi
   a.renorm_w = p->renorm_w;
   a.renorm_r = p->renorm_r;
   a.cape_heads = p->cape_heads;
-  a.t0 = p->t0;
+  a.t0 = p->t0 % d.S;
   a.mask = mask;
   a.eps = p->eps;
   a.wl = wlogits;

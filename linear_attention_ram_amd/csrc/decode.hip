@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void decode_fwd_kernel(DecodeFwdArgs a) {
   const int lane = lane_id();
   const int64_t grow = (int64_t)blockIdx.x * 4 + wv;
   if (grow >= (int64_t)a.nsides * a.N) return;
-  const int side = (int)(grow / a.N);
+  const int side = grow >= a.N ? 1 : 0;   // nsides <= 2
   const int64_t row = grow - (int64_t)side * a.N;
   const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
   const int k = a.k[side];
@@ -75,12 +75,12 @@ __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
   const int lane = lane_id();
   const int64_t grow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (grow >= (int64_t)a.nsides * a.N) return;
-  const int side = (int)(grow / a.N);
+  const int side = grow >= a.N ? 1 : 0;   // nsides <= 2
   const int64_t row = grow - (int64_t)side * a.N;
   const int k = a.k[side];
   const IO* __restrict__ src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
   IO* __restrict__ dst = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)a.S;
-  if (a.mask && !a.mask[(row / ((int64_t)a.T * a.H)) * a.T + (row / a.H) % a.T]) {
+  if (a.mask && !a.mask[token_of(row, a.H)]) {
     // a masked token takes no part in the computation: zero gradient
     for (int c = lane; c < a.S / E; c += WAVE) st_nt16(dst + (int64_t)c * E, make_uint4(0, 0, 0, 0));
     return;
@@ -115,9 +115,11 @@ __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
       const int c = c0 + u * WAVE + lane;
       if (c < nvec) q[u] = ld_nt16(src + (int64_t)c * E);
     }
+    // every vector of the tile is finished before the first store: loads and
+    // stores share one completion counter, so a store between two vectors
+    // would make the next vector wait for it
 #pragma unroll
     for (int u = 0; u < TILE; ++u) {
-      const int c = c0 + u * WAVE + lane;
       float x[E];
       unpack16(q[u], x);
 #pragma unroll
@@ -133,7 +135,12 @@ __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) x[e] = (mine && id % E == e) ? v : x[e];
       }
-      if (c < nvec) st_nt16(dst + (int64_t)c * E, pack16(x));
+      q[u] = pack16(x);
+    }
+#pragma unroll
+    for (int u = 0; u < TILE; ++u) {
+      const int c = c0 + u * WAVE + lane;
+      if (c < nvec) st_nt16(dst + (int64_t)c * E, q[u]);
     }
   }
 }
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(256) void decode_fwd_prod_kernel(DecodeFwdArgs a) {
   const int lane = lane_id();
   const int64_t grow = (int64_t)blockIdx.x * 4 + wv;
   if (grow >= (int64_t)a.nsides * a.N) return;
-  const int side = (int)(grow / a.N);
+  const int side = grow >= a.N ? 1 : 0;   // nsides <= 2
   const int64_t row = grow - (int64_t)side * a.N;
   const int UP = a.U * a.P;
   const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)UP;
@@ -182,13 +189,13 @@ __global__ __launch_bounds__(256) void decode_bwd_prod_kernel(DecodeBwdArgs a) {
   const int lane = lane_id();
   const int64_t grow = (int64_t)blockIdx.x * 4 + wv;
   if (grow >= (int64_t)a.nsides * a.N) return;
-  const int side = (int)(grow / a.N);
+  const int side = grow >= a.N ? 1 : 0;   // nsides <= 2
   const int64_t row = grow - (int64_t)side * a.N;
   const int k = a.k[side];
   const int U = a.U, P = a.P, UP = U * P;
   const IO* __restrict__ src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)UP;
   IO* __restrict__ dst = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)UP;
-  if (a.mask && !a.mask[(row / ((int64_t)a.T * a.H)) * a.T + (row / a.H) % a.T]) {
+  if (a.mask && !a.mask[token_of(row, a.H)]) {
     for (int e = lane; e < UP; e += WAVE) dst[e] = from_f32<IO>(0.f);
     return;
   }

@@ -36,19 +36,27 @@ struct DecodeFwdArgs {
   int zero_width;
   int H, T;                // row r is token (r / H) % T of head r % H
   int cape_heads;          // heads h < cape_heads shift the chosen slot by (t0 + t) mod S
-  int64_t t0;
+  int64_t t0;              // reduced mod S
 };
 
 // CAPE (ramnet-ops "Quick start", embed_num; paper App. C): for the first
 // cape_heads heads the slot addressed by a token is its content-selected
 // index shifted cyclically by the token's absolute position.  The shift of
-// row r, or -1 for heads without CAPE.
+// row r, or -1 for heads without CAPE.  t0 is already reduced mod S; the
+// rows of one call number less than 2^31 (the event count is checked on the
+// host), so 32-bit arithmetic suffices.
 __device__ __forceinline__ int cape_shift_of(int64_t r, int H, int T, int S, int cape_heads,
                                              int64_t t0) {
-  const int h = (int)(r % H);
-  if (h >= cape_heads) return -1;
-  const int64_t t = (r / H) % T;
-  return (int)((t0 % S + t) % S);
+  if (cape_heads == 0) return -1;
+  const uint32_t r32 = (uint32_t)r;
+  const uint32_t q = r32 / (uint32_t)H;           // token row b * T + t
+  if ((int)(r32 - q * (uint32_t)H) >= cape_heads) return -1;
+  return (int)(((uint32_t)t0 + q % (uint32_t)T) % (uint32_t)S);
+}
+
+// Token index b * T + t of row r = (b * T + t) * H + h (the mask index).
+__device__ __forceinline__ uint32_t token_of(int64_t r, int H) {
+  return (uint32_t)r / (uint32_t)H;
 }
 
 struct DecodeBwdArgs {
@@ -74,6 +82,14 @@ hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_decode_bwd(const DecodeBwdArgs& a, bool bf16, hipStream_t st);
 
 namespace {
+
+// Pairwise sum of an array of 4 or 8 values.
+template <int N>
+__device__ __forceinline__ float tree_sum(const float (&x)[N]) {
+  static_assert(N == 4 || N == 8, "vector of 4 or 8");
+  if constexpr (N == 4) return (x[0] + x[1]) + (x[2] + x[3]);
+  else return ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+}
 
 // (value, index) order of the selection: larger value first, then lower index.
 __device__ __forceinline__ bool before(float v, int i, float v2, int i2) {
@@ -218,8 +234,11 @@ __device__ float decode_row_resident(const IO* __restrict__ row, int S, int k, i
     for (int u = 0; u < NV; ++u) {
       float x[E];
       unpack16(q[u], x);
+      // all exponentials of the vector first, then a tree sum: no sum waits
+      // on the exponential just issued
 #pragma unroll
-      for (int e = 0; e < E; ++e) s += fast_exp2(fmaf(x[e], LOG2E, nm));
+      for (int e = 0; e < E; ++e) x[e] = fast_exp2(fmaf(x[e], LOG2E, nm));
+      s += tree_sum(x);
     }
   }
   const float lse = M + logf(wave_sum(s));
@@ -305,7 +324,8 @@ __device__ float decode_row_wave(const IO* __restrict__ row, int S, int k, int r
         float x[E];
         unpack16(q[u], x);
 #pragma unroll
-        for (int e = 0; e < E; ++e) s += fast_exp2(fmaf(x[e], LOG2E, nml));
+        for (int e = 0; e < E; ++e) x[e] = fast_exp2(fmaf(x[e], LOG2E, nml));
+        s += tree_sum(x);
       }
       m = mn;
     }

@@ -110,7 +110,8 @@ __device__ __forceinline__ void store_pair(IO* p, bool even, int c, int d_v, flo
 }
 
 __device__ __forceinline__ bool row_valid(const EpilogueArgs& a, int64_t row) {
-  return !a.mask || a.mask[(row / ((int64_t)a.T * a.H)) * a.T + (row / a.H) % a.T];
+  // row = (b * T + t) * H + h; rows of one call number less than 2^31
+  return !a.mask || a.mask[(uint32_t)row / (uint32_t)a.H];
 }
 
 }  // namespace
