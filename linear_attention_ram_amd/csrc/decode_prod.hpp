@@ -20,7 +20,8 @@
 //   the bound is the key itself and the kept slots are ranked exactly.
 //
 // Rows whose kept list would overflow KEEP_CAP (massive ties) take K exact
-// passes over all P^U slots instead.
+// passes over all P^U slots instead.  Two digits of at most 64 values take
+// a shorter register-resident search first (decode_row_u2).
 #pragma once
 #include "decode.hpp"
 
@@ -28,7 +29,7 @@ namespace ramk {
 
 constexpr int MAX_DIGITS = 14;   // P >= 2 and P^U <= 16384; P = 1 allows U <= 14
 constexpr int MAX_ROW = 256;     // U * P of a product row (P <= 128 when U >= 2)
-constexpr int KEEP_CAP = 256;    // prefixes kept per level
+constexpr int KEEP_CAP = 128;    // prefixes kept per level
 
 struct ProdScratch {
   float dig[MAX_ROW];            // the row's logits as float, digit-major
@@ -95,6 +96,84 @@ __device__ __noinline__ void product_k_passes(ProdScratch& sc, int U, int P, int
   }
 }
 
+// Two digits of at most 64 values, in registers (lane L holds l0[L] and
+// l1[L]).  The best key with digit-1 value L is fl(M0 + l1[L]) (M0 the
+// largest digit-0 logit); tau = the K-th largest of these over the lanes is
+// the key of K distinct slots, so at most the K-th best key.  Only digit-1
+// values whose bound reaches tau can appear in the top K; for each of them
+// one wave-wide add gives the keys of all its slots, and those reaching tau
+// are listed and ranked exactly.  Returns false, having written nothing to
+// sel_i / sel_w, when the list would overflow (massive ties).
+template <typename IO>
+__device__ bool decode_row_u2(const IO* __restrict__ row, int P, int k, int renorm,
+                              ProdScratch& sc, int* sel_i, float* sel_w) {
+  const int lane = lane_id();
+  const bool in = lane < P;
+  const float l0 = in ? to_f32(row[lane]) : -INFINITY;
+  const float l1 = in ? to_f32(row[P + lane]) : -INFINITY;
+  const float M0 = wave_max(l0), M1 = wave_max(l1);
+  float s0 = 0.f, s1 = 0.f;
+  if (M0 != -INFINITY) s0 = fast_exp2(fmaf(l0, LOG2E, -M0 * LOG2E));
+  if (M1 != -INFINITY) s1 = fast_exp2(fmaf(l1, LOG2E, -M1 * LOG2E));
+  const float lse0 = M0 + logf(wave_sum(s0));
+  const float lse1 = M1 + logf(wave_sum(s1));
+  if (lane == 0) {
+    sc.dmax[0] = M0;
+    sc.dmax[1] = M1;
+    sc.dlse[0] = lse0;
+    sc.dlse[1] = lse1;
+  }
+  const float b1 = in ? M0 + l1 : -INFINITY;
+  const float tau = kth_lane_max(b1, k);
+  uint64_t qual = __ballot(in && b1 >= tau);
+  const uint64_t lt = lanemask_lt();
+  int count = 0;
+  while (qual) {
+    const int L = (int)__builtin_ctzll(qual);
+    qual &= qual - 1;
+    const float l1L = readlane_f(l1, L);
+    const float key = l0 + l1L;
+    const bool c = in && key >= tau;
+    const uint64_t bal = __ballot(c);
+    const int pos = count + __popcll(bal & lt);
+    if (c && pos < KEEP_CAP) {
+      sc.kk[0][pos] = key;
+      sc.ki[0][pos] = lane * P + L;
+      sc.kk[1][pos] = (l0 - lse0) + (l1L - lse1);   // log-probability of the slot
+    }
+    count += __popcll(bal);
+  }
+  if (count > KEEP_CAP) return false;
+  wave_sync();
+  // exact rank of every listed slot; the K best to sv / si, and their
+  // log-probabilities to the lanes that hold them
+  float lp = 0.f;
+  for (int c = lane; c < count; c += WAVE) {
+    const float v = sc.kk[0][c];
+    const int id = sc.ki[0][c];
+    int rank = 0;
+    for (int o = 0; o < count; ++o) rank += before(sc.kk[0][o], sc.ki[0][o], v, id) ? 1 : 0;
+    if (rank < k) {
+      sc.si[rank] = id;
+      sc.sv[rank] = sc.kk[1][c];
+    }
+  }
+  wave_sync();
+  float w = 0.f;
+  int id = 0;
+  if (lane < k) {
+    id = sc.si[lane];
+    lp = sc.sv[lane];
+    w = expf(lp);
+  }
+  if (renorm) {
+    const float tot = wave_sum(lane < k ? w : 0.f);
+    w = w / tot;
+  }
+  if (lane < k) { sel_i[lane] = id; sel_w[lane] = w; }
+  return true;
+}
+
 }  // namespace
 
 // Decodes one product row (U * P logits) with the calling wave: the K
@@ -104,6 +183,10 @@ __device__ __noinline__ void product_k_passes(ProdScratch& sc, int U, int P, int
 template <typename IO>
 __device__ void decode_row_product(const IO* __restrict__ row, int U, int P, int k, int renorm,
                                    ProdScratch& sc, int* sel_i, float* sel_w) {
+  if (U == 2 && P <= WAVE) {
+    if (decode_row_u2<IO>(row, P, k, renorm, sc, sel_i, sel_w)) return;
+    wave_sync();
+  }
   const int lane = lane_id();
   const int UP = U * P;
   for (int e = lane; e < UP; e += WAVE) sc.dig[e] = to_f32(row[e]);
