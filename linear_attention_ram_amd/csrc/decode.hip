@@ -216,6 +216,28 @@ __global__ __launch_bounds__(256) void decode_bwd_prod_kernel(DecodeBwdArgs a) {
     gw = gj * wj;
   }
   const float ntot = -wave_sum(gw);
+  if (U == 2 && P <= WAVE) {
+    // two digits: lane i holds element i of each; the selected slots' terms
+    // are added in ascending j, each to the lane that holds its digit value
+    const bool in = lane < P;
+    const float* lse = a.lse[side] + row * 2;
+    const float x0 = in ? to_f32(src[lane]) : 0.f;
+    const float x1 = in ? to_f32(src[P + lane]) : 0.f;
+    float acc0 = ntot * fast_exp2(fmaf(x0, LOG2E, -lse[0] * LOG2E));
+    float acc1 = ntot * fast_exp2(fmaf(x1, LOG2E, -lse[1] * LOG2E));
+    const int aj0 = aj / P;
+    const int aj1 = aj - aj0 * P;
+    for (int j = 0; j < k; ++j) {
+      const float g = readlane_f(gw, j);
+      if (lane == readlane_i(aj0, j)) acc0 += g;
+      if (lane == readlane_i(aj1, j)) acc1 += g;
+    }
+    if (in) {
+      dst[lane] = from_f32<IO>(acc0);
+      dst[P + lane] = from_f32<IO>(acc1);
+    }
+    return;
+  }
   if (lane < k) {
     s_gw[wv][lane] = gw;
     int rem = aj;
