@@ -449,8 +449,18 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
     s_carry[k] = (c.active && a.slot0) ? a.slot0[g * a.d_v + c.c0 + k] : 0.f;
   float m_carry = a.mass0 ? a.mass0[g] : 0.f;
 
+  // the v rows of a wave's next chunk are requested as soon as its replay of
+  // the current chunk is done, so the loads overlap the closing barrier and
+  // the next chunk's mass fold
   float4 rec = load_rec(a.events, chunk_start(beg, w, end),
                         chunk_start(beg, w + 1, end) - chunk_start(beg, w, end), beg, end);
+  typename LN::Raw x[CHUNK];
+  {
+    const int n0 = chunk_start(beg, w + 1, end) - chunk_start(beg, w, end);
+    const Ev ev0 = decode_rec(rec, n0, c.h, a.H);
+    const uint32_t xo0 = (ev0.valid && ev0.side == 0) ? (uint32_t)ev0.rb * c.pitch : OOB;
+    for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo0) + c.lb); });
+  }
   for (int p = beg; p < end;) {
     const int cs = chunk_start(p, w, end);
     const int n = chunk_start(p, w + 1, end) - cs;
@@ -464,11 +474,7 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
       mapB[w] = B_tot;
     }
     const float rr = (ev.side == 1) ? ev.wt : 0.f;
-    const uint32_t xo = (ev.valid && ev.side == 0) ? (uint32_t)ev.rb * c.pitch : OOB;
     const uint32_t so = (ev.valid && ev.side == 1) ? ((uint32_t)ev.rb * a.k_r + ev.j) * c.pitch : OOB;
-    // content loads do not depend on the mass: issue them before the barrier
-    typename LN::Raw x[CHUNK];
-    for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo) + c.lb); });
     // next super-chunk's records for this wave (unconditional: past the end
     // it reloads the last event, unused)
     rec = load_rec(a.events, chunk_start(pn, w, end),
@@ -529,6 +535,12 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
       }
       LN::store(rs, bcu<I>(so) + c.lb, ctr);
     });
+    {   // rows of this wave's next chunk (past the end: no valid event, no load)
+      const int n_n = chunk_start(pn, w + 1, end) - chunk_start(pn, w, end);
+      const Ev ev_n = decode_rec(rec, n_n, c.h, a.H);
+      const uint32_t xo_n = (ev_n.valid && ev_n.side == 0) ? (uint32_t)ev_n.rb * c.pitch : OOB;
+      for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo_n) + c.lb); });
+    }
     m_carry = m_next;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) s_carry[k] = s_next[k];
@@ -623,24 +635,42 @@ struct BwdChunk {
   }
 };
 
+// Row gathers of a chunk: the v row of each write and the dO row of each read
+// (one of the two loads of an event is out of range and gives 0).
 template <typename IO, int CPL, bool SO>
-__device__ __forceinline__ void bwd_setup(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
-                                          rsrc_t rv, rsrc_t ro, BwdChunk<IO, CPL, SO>& ck, float4 rec,
-                                          int n, float m) {
+__device__ __forceinline__ void bwd_gather(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                           rsrc_t rv, rsrc_t ro, BwdChunk<IO, CPL, SO>& ck,
+                                           float4 rec, int n) {
   using LN = Lanes<IO, CPL>;
+  const Ev ev = decode_rec(rec, n, c.h, a.H);
+  const uint32_t roff = (uint32_t)ev.rb * c.pitch;
+  const uint32_t xv = (ev.valid && ev.side == 0) ? roff : OOB;
+  const uint32_t xd = (ev.valid && ev.side == 1) ? roff : OOB;
+  for_up<0, CHUNK>([&](auto I) {
+    ck.x[I] = LN::merge(LN::load(rv, bcu<I>(xv) + c.lb), LN::load(ro, bcu<I>(xd) + c.lb));
+  });
+}
+
+// Scalars of a chunk whose rows are gathered: event fields, masses and step
+// sizes, read weights and stash offsets.
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ void bwd_prepare(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                            BwdChunk<IO, CPL, SO>& ck, float4 rec, int n,
+                                            float m) {
   ck.ev = decode_rec(rec, n, c.h, a.H);
   const Ev& ev = ck.ev;
   ck.M = mass_prefix(ev);
   mass_apply(ck.M, ev, m, a.eps);
   ck.rr = (ev.side == 1) ? ev.wt : 0.f;
-  const uint32_t roff = (uint32_t)ev.rb * c.pitch;
-  const uint32_t xv = (ev.valid && ev.side == 0) ? roff : OOB;
-  const uint32_t xd = (ev.valid && ev.side == 1) ? roff : OOB;
   ck.sw = (ev.valid && ev.side == 0) ? ((uint32_t)ev.rb * a.k_w + ev.j) * c.pitch : OOB;
-  // one of the two loads is out of range and gives 0
-  for_up<0, CHUNK>([&](auto I) {
-    ck.x[I] = LN::merge(LN::load(rv, bcu<I>(xv) + c.lb), LN::load(ro, bcu<I>(xd) + c.lb));
-  });
+}
+
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ void bwd_setup(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                          rsrc_t rv, rsrc_t ro, BwdChunk<IO, CPL, SO>& ck, float4 rec,
+                                          int n, float m) {
+  bwd_gather(a, c, rv, ro, ck, rec, n);
+  bwd_prepare(a, c, ck, rec, n, m);
 }
 
 // Forward replay of a chunk from s: keeps the content before each event and
@@ -845,24 +875,24 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
       n = chunk_start(beg, k + 1, end) - cs;
     }
   };
-  float4 rec;
+  // The rows and the start state of a chunk are requested as soon as the
+  // previous chunk of this wave no longer needs its registers (after its
+  // reverse walk), so the loads overlap the scalar part and the barriers.
+  float4 rec, rec_next;
+  float s[CPL], m;
+  int cs, n;
   {
-    int cs0, n0;
-    chunk_of(((nchunks - 1) / NW) * NW + w, cs0, n0);
-    rec = load_rec(a.events, cs0, n0, beg, end);
+    const int u_first = ((nchunks - 1) / NW) * NW;
+    chunk_of(u_first + w, cs, n);
+    rec = load_rec(a.events, cs, n, beg, end);
+    int csp, np;
+    chunk_of(max(u_first - NW, 0) + w, csp, np);
+    rec_next = load_rec(a.events, csp, np, beg, end);
+    chunk_state<IO, CPL>(a, c, g, beg, cs, s, m);
+    bwd_gather(a, c, rv, ro, ck, rec, n);
   }
   for (int u0 = ((nchunks - 1) / NW) * NW; u0 >= 0; u0 -= NW) {
-    int cs, n;
-    chunk_of(u0 + w, cs, n);
-    float s[CPL], m;
-    chunk_state<IO, CPL>(a, c, g, beg, cs, s, m);
-    const float4 rec_cur = rec;
-    {   // this wave's chunk of the previous super-chunk (unconditional; unused after the first)
-      int csp, np;
-      chunk_of(max(u0 - NW, 0) + w, csp, np);
-      rec = load_rec(a.events, csp, np, beg, end);
-    }
-    bwd_setup(a, c, rv, ro, ck, rec_cur, n, m);
+    bwd_prepare(a, c, ck, rec, n, m);
     bwd_replay(ck, s, pr);
     const float red_r = batched_sum(pr);   // dr of the reads
     const Ev& ev = ck.ev;
@@ -932,8 +962,23 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
     for (int kk = NW - 1; kk > w; --kk) mh = fmaf(mL[kk], mh, mD[kk] + mK[kk]);
     // exact reverse step of this wave's chunk
     bwd_walk(ck, c, rs, sh, pw);
+    // next chunk of this wave: rows, start state and the record after it
+    // (unconditional: past the segment's start the chunk is empty)
+    int csn, nn;
+    chunk_of(max(u0 - NW, 0) + w, csn, nn);
+    if (u0 < NW) { csn = end; nn = 0; }
+    const float4 rec_n = rec_next;
+    {
+      int csp, np;
+      chunk_of(max(u0 - 2 * NW, 0) + w, csp, np);
+      rec_next = load_rec(a.events, csp, np, beg, end);
+    }
+    float s_n[CPL], m_n;
+    chunk_state<IO, CPL>(a, c, g, beg, csn, s_n, m_n);
     const float red2 = batched_sum(pw);     // deta of the writes
-    bwd_scalars(a, c, ck, ev.side == 1 ? red_r : red2, mh);
+    const Ev ev_cur = ev;
+    bwd_gather(a, c, rv, ro, ck, rec_n, nn);
+    bwd_scalars(a, c, ck, ev_cur.side == 1 ? red_r : red2, mh);
     if (w == 0) {
       if (c.active) {
 #pragma unroll
@@ -946,6 +991,12 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
     for (int k = 0; k < CPL; ++k) sh_carry[k] = c.active ? carry_s[c.c0 + k] : 0.f;
     mh_carry = carry_m;
     __syncthreads();
+    rec = rec_n;
+    cs = csn;
+    n = nn;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) s[k] = s_n[k];
+    m = m_n;
   }
   if (w == 0) {
     if (a.d_slot0 && c.active) {
