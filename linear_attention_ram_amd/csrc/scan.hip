@@ -434,6 +434,7 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
   using LN = Lanes<IO, CPL>;
   __shared__ float mapA[NW], mapB[NW], mapP[NW];
   __shared__ float mapb[NW][MAX_DV];
+  __shared__ float carry_s[MAX_DV];
   const SegCtx<IO, CPL> c = seg_ctx<IO, CPL>(g, a.S, a.H, a.T, a.d_v);
   const int lane = lane_id();
   const int w = wave_index();
@@ -486,34 +487,35 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
       m_next = fmaf(mapA[k], m_next, mapB[k]);
     }
     mass_apply(M, ev, m_in, a.eps);
-    // content map of the chunk from a zero start: s -> P*s + sz
-    float sz[CPL];
+    // content map of the chunk from a zero start, s -> P*s + sz; only later
+    // waves fold it, so the last wave forms none
+    if (w != NW - 1) {
+      float sz[CPL];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) sz[k] = 0.f;
-    for_up<0, CHUNK>([&](auto I) {
-      float xf[CPL];
-      LN::get(x[I], xf);
-      const float e = bc<I>(M.eta), om = bc<I>(M.keep);
+      for (int k = 0; k < CPL; ++k) sz[k] = 0.f;
+      for_up<0, CHUNK>([&](auto I) {
+        float xf[CPL];
+        LN::get(x[I], xf);
+        const float e = bc<I>(M.eta), om = bc<I>(M.keep);
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) sz[k] = fmaf(om, sz[k], e * xf[k]);
-    });
-    const float P = row_prod(M.keep);
-    if (c.active) {
+        for (int k = 0; k < CPL; ++k) sz[k] = fmaf(om, sz[k], e * xf[k]);
+      });
+      const float P = row_prod(M.keep);
+      if (c.active) {
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) mapb[w][c.c0 + k] = sz[k];
+        for (int k = 0; k < CPL; ++k) mapb[w][c.c0 + k] = sz[k];
+      }
+      if (lane == 0) mapP[w] = P;
     }
-    if (lane == 0) mapP[w] = P;
     __syncthreads();
-    float s[CPL], s_next[CPL];
+    // this wave's start state: the carry through the earlier chunks' maps
+    float s[CPL];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) s_next[k] = s_carry[k];
-    for (int kk = 0; kk < NW; ++kk) {
+    for (int k = 0; k < CPL; ++k) s[k] = s_carry[k];
+    for (int kk = 0; kk < w; ++kk) {
       const float Pk = mapP[kk];
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        if (kk == w) s[k] = s_next[k];
-        s_next[k] = fmaf(Pk, s_next[k], c.active ? mapb[kk][c.c0 + k] : 0.f);
-      }
+      for (int k = 0; k < CPL; ++k) s[k] = fmaf(Pk, s[k], c.active ? mapb[kk][c.c0 + k] : 0.f);
     }
     if (n > 0 && cs != beg) {
       float* ck = a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
@@ -541,11 +543,16 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
       const uint32_t xo_n = (ev_n.valid && ev_n.side == 0) ? (uint32_t)ev_n.rb * c.pitch : OOB;
       for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo_n) + c.lb); });
     }
-    m_carry = m_next;
+    // the last wave's state after its replay is the carry into the next chunks
+    if (w == NW - 1 && c.active) {
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) s_carry[k] = s_next[k];
+      for (int k = 0; k < CPL; ++k) carry_s[c.c0 + k] = s[k];
+    }
+    m_carry = m_next;
     p = pn;
     __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) s_carry[k] = c.active ? carry_s[c.c0 + k] : 0.f;
   }
   if (w == 0) {
     if (c.active) {
@@ -911,35 +918,40 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
     const float den = ck.M.mi + a.eps;
     const float gq = (wr && ev.wt > 0.f) ? ev.wt / (den * den) : 0.f;
     const float coef = -Lp * gq * Qx;
-    float q[CPL], U[CPL];
+    // only earlier waves fold a chunk's map, so wave 0 forms none
+    float U[CPL];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) { q[k] = 0.f; U[k] = 0.f; }
-    for_down<CHUNK>([&](auto I) {
-      float xf[CPL], so[CPL];
-      LN::get(ck.x[I], xf);
-      ck.template get_so<I>(so);
-      const float e = bc<I>(ck.M.eta), r = bc<I>(ck.rr), cf = bc<I>(coef);
-      float d = 0.f;
+    for (int k = 0; k < CPL; ++k) U[k] = 0.f;
+    if (w != 0) {
+      float q[CPL];
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const float u = xf[k] - so[k];
-        d = fmaf(q[k], u, d);
-        U[k] = fmaf(cf, u, U[k]);
-        q[k] = fmaf(r, xf[k], fmaf(-e, q[k], q[k]));
+      for (int k = 0; k < CPL; ++k) q[k] = 0.f;
+      for_down<CHUNK>([&](auto I) {
+        float xf[CPL], so[CPL];
+        LN::get(ck.x[I], xf);
+        ck.template get_so<I>(so);
+        const float e = bc<I>(ck.M.eta), r = bc<I>(ck.rr), cf = bc<I>(coef);
+        float d = 0.f;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          const float u = xf[k] - so[k];
+          d = fmaf(q[k], u, d);
+          U[k] = fmaf(cf, u, U[k]);
+          q[k] = fmaf(r, xf[k], fmaf(-e, q[k], q[k]));
+        }
+        pw[I] = d;
+        sched_fence<I>();
+      });
+      const float red1 = batched_sum(pw);    // <q_after, u> of the writes
+      const float K = row_sum(wr ? -Lp * gq * red1 : 0.f);
+      const float L = bc<15>(Lp);
+      const float Q = bc<0>(Qs);
+      if (c.active) {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) mq[w][c.c0 + k] = q[k];
       }
-      pw[I] = d;
-      sched_fence<I>();
-    sched_fence<I>();
-    });
-    const float red1 = batched_sum(pw);    // <q_after, u> of the writes
-    const float K = row_sum(wr ? -Lp * gq * red1 : 0.f);
-    const float L = bc<15>(Lp);
-    const float Q = bc<0>(Qs);
-    if (c.active) {
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) mq[w][c.c0 + k] = q[k];
+      if (lane == 0) { mQ[w] = Q; mL[w] = L; mK[w] = K; }
     }
-    if (lane == 0) { mQ[w] = Q; mL[w] = L; mK[w] = K; }
     __syncthreads();
     // content adjoint after this wave's chunk: fold the later content maps
     float sh[CPL];
@@ -950,7 +962,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
 #pragma unroll
       for (int k = 0; k < CPL; ++k) sh[k] = fmaf(Qk, sh[k], c.active ? mq[kk][c.c0 + k] : 0.f);
     }
-    {
+    if (w != 0) {
       float d = 0.f;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) d = fmaf(sh[k], U[k], d);
