@@ -119,18 +119,31 @@ __device__ __forceinline__ void hide_regs(uint4 (&q)[NV]) {
   for (int u = 0; u < NV; ++u) asm volatile("" : "+v"(q[u].x), "+v"(q[u].y), "+v"(q[u].z), "+v"(q[u].w));
 }
 
+// Order-preserving map of a float to an unsigned integer, and back
+// (negative values reversed below the positive ones; -0 just below +0).
+__device__ __forceinline__ uint32_t ordered_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
 // tau = K-th largest lane value m (counted with multiplicity).  Every top-K
 // element of the row is >= tau, and lies in a lane whose maximum is >= tau.
+// Found bit by bit, from the top, as the largest ordered threshold that K
+// lanes reach: one compare and a ballot count per bit, no cross-lane moves.
 __device__ __forceinline__ float kth_lane_max(float m, int k) {
-  const int lane = lane_id();
-  float cur = m, tau = -INFINITY;
-  for (int r = 0; r < k; ++r) {
-    const float mx = wave_max(cur);
-    tau = mx;
-    const uint64_t hit = __ballot(cur == mx);
-    if (lane == (int)__builtin_ctzll(hit)) cur = -INFINITY;
+  const uint32_t mb = ordered_bits(m);
+  const int ku = __builtin_amdgcn_readfirstlane(k);   // uniform: kept in scalar registers
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    t = (__popcll(__ballot(mb >= c)) >= ku) ? c : t;
+    t = __builtin_amdgcn_readfirstlane(t);
   }
-  return tau;
+  return from_ordered(t);
 }
 
 // Exact rank of every one of the `count` candidates in sc among the
