@@ -611,6 +611,7 @@ struct BwdChunk {
   Mass M;
   float rr;                        // read weight, 0 for writes and padding
   uint32_t sw;                     // stash offset of a write's dv row, else OOB
+  uint32_t wm, rm;                 // bit i: event i is a write / a read (wave-uniform)
   typename Lanes<IO, CPL>::Raw x[CHUNK];
   float so_reg[SO_LDS ? 1 : CHUNK][CPL];
   float* so_lds;                   // [CHUNK][MAX_DV] floats at the lane's channel c0
@@ -670,6 +671,8 @@ __device__ __forceinline__ void bwd_prepare(const ScanBwdArgs& a, const SegCtx<I
   mass_apply(ck.M, ev, m, a.eps);
   ck.rr = (ev.side == 1) ? ev.wt : 0.f;
   ck.sw = (ev.valid && ev.side == 0) ? ((uint32_t)ev.rb * a.k_w + ev.j) * c.pitch : OOB;
+  ck.wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
+  ck.rm = (uint32_t)__ballot(ev.valid && ev.side == 1) & 0xFFFFu;
 }
 
 template <typename IO, int CPL, bool SO>
@@ -680,49 +683,74 @@ __device__ __forceinline__ void bwd_setup(const ScanBwdArgs& a, const SegCtx<IO,
   bwd_prepare(a, c, ck, rec, n, m);
 }
 
-// Forward replay of a chunk from s: keeps the content before each event and
-// pr[i] = <x_i, s_i> (lane-local), which for a read is its dr partial.
+// Forward replay of a chunk from s: keeps the content before each write
+// and pr[i] = <x_i, s_i> (lane-local) of each read, its dr partial.  An
+// event is either a write (step eta, no read weight) or a read (the
+// reverse), and its kind is the same in every lane, so each event takes only
+// its kind's arithmetic; the results equal those of the common form with
+// the other kind's terms zero.
 template <typename IO, int CPL, bool SO>
 __device__ __forceinline__ void bwd_replay(BwdChunk<IO, CPL, SO>& ck, float (&s)[CPL],
                                            float (&pr)[CHUNK]) {
   using LN = Lanes<IO, CPL>;
   for_up<0, CHUNK>([&](auto I) {
-    float xf[CPL];
-    LN::get(ck.x[I], xf);
-    const float e = bc<I>(ck.M.eta), om = bc<I>(ck.M.keep);
-    float d = 0.f;
-    ck.template put_so<I>(s);
+    pr[I] = 0.f;
+    if ((ck.wm >> I) & 1u) {
+      float xf[CPL];
+      LN::get(ck.x[I], xf);
+      const float e = bc<I>(ck.M.eta), om = bc<I>(ck.M.keep);
+      ck.template put_so<I>(s);
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      s[k] = fmaf(om, s[k], e * xf[k]);
-      d = fmaf(xf[k], s[k], d);
+      for (int k = 0; k < CPL; ++k) s[k] = fmaf(om, s[k], e * xf[k]);
+    } else if ((ck.rm >> I) & 1u) {
+      float xf[CPL];
+      LN::get(ck.x[I], xf);
+      float d = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) d = fmaf(xf[k], s[k], d);
+      pr[I] = d;
     }
-    pr[I] = d;
     sched_fence<I>();
   });
 }
 
 // Reverse walk of the content adjoint from sh (after the chunk) to sh (before
-// it): stores the dv contributions e * s_hat and leaves the lane-local
-// partials <s_hat_after, x - s_old> (the deta of a write) in pw.
+// it): stores the dv contributions e * s_hat of the writes and leaves the
+// lane-local partials <s_hat_after, x - s_old> (the deta of a write) in pw.
 template <typename IO, int CPL, bool SO>
 __device__ __forceinline__ void bwd_walk(const BwdChunk<IO, CPL, SO>& ck, const SegCtx<IO, CPL>& c,
                                          rsrc_t rs, float (&sh)[CPL], float (&pw)[CHUNK]) {
   using LN = Lanes<IO, CPL>;
+  // each event's pre-write content is read from LDS one event ahead, outside
+  // the per-kind branches, so the read has an event's work to complete in
+  float so_n[CPL];
+  ck.template get_so<CHUNK - 1>(so_n);
   for_down<CHUNK>([&](auto I) {
-    float xf[CPL], ctr[CPL], so[CPL];
-    LN::get(ck.x[I], xf);
-    ck.template get_so<I>(so);
-    const float e = bc<I>(ck.M.eta), r = bc<I>(ck.rr);
-    float d = 0.f;
+    float so[CPL];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      ctr[k] = e * sh[k];
-      d = fmaf(sh[k], xf[k] - so[k], d);
-      sh[k] = fmaf(r, xf[k], fmaf(-e, sh[k], sh[k]));
+    for (int k = 0; k < CPL; ++k) so[k] = so_n[k];
+    if constexpr (I > 0) ck.template get_so<I - 1>(so_n);
+    pw[I] = 0.f;
+    if ((ck.wm >> I) & 1u) {
+      float xf[CPL], ctr[CPL];
+      LN::get(ck.x[I], xf);
+      const float e = bc<I>(ck.M.eta);
+      float d = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        ctr[k] = e * sh[k];
+        d = fmaf(sh[k], xf[k] - so[k], d);
+        sh[k] = fmaf(-e, sh[k], sh[k]);
+      }
+      LN::store(rs, bcu<I>(ck.sw) + c.lb, ctr);
+      pw[I] = d;
+    } else if ((ck.rm >> I) & 1u) {
+      float xf[CPL];
+      LN::get(ck.x[I], xf);
+      const float r = bc<I>(ck.rr);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) sh[k] = fmaf(r, xf[k], sh[k]);
     }
-    LN::store(rs, bcu<I>(ck.sw) + c.lb, ctr);
-    pw[I] = d;
     sched_fence<I>();
   });
 }
@@ -926,20 +954,34 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
       float q[CPL];
 #pragma unroll
       for (int k = 0; k < CPL; ++k) q[k] = 0.f;
+      float so_n[CPL];
+      ck.template get_so<CHUNK - 1>(so_n);
       for_down<CHUNK>([&](auto I) {
-        float xf[CPL], so[CPL];
-        LN::get(ck.x[I], xf);
-        ck.template get_so<I>(so);
-        const float e = bc<I>(ck.M.eta), r = bc<I>(ck.rr), cf = bc<I>(coef);
-        float d = 0.f;
+        float so[CPL];
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          const float u = xf[k] - so[k];
-          d = fmaf(q[k], u, d);
-          U[k] = fmaf(cf, u, U[k]);
-          q[k] = fmaf(r, xf[k], fmaf(-e, q[k], q[k]));
+        for (int k = 0; k < CPL; ++k) so[k] = so_n[k];
+        if constexpr (I > 0) ck.template get_so<I - 1>(so_n);
+        pw[I] = 0.f;
+        if ((ck.wm >> I) & 1u) {
+          float xf[CPL];
+          LN::get(ck.x[I], xf);
+          const float e = bc<I>(ck.M.eta), cf = bc<I>(coef);
+          float d = 0.f;
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) {
+            const float u = xf[k] - so[k];
+            d = fmaf(q[k], u, d);
+            U[k] = fmaf(cf, u, U[k]);
+            q[k] = fmaf(-e, q[k], q[k]);
+          }
+          pw[I] = d;
+        } else if ((ck.rm >> I) & 1u) {
+          float xf[CPL];
+          LN::get(ck.x[I], xf);
+          const float r = bc<I>(ck.rr);
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) q[k] = fmaf(r, xf[k], q[k]);
         }
-        pw[I] = d;
         sched_fence<I>();
       });
       const float red1 = batched_sum(pw);    // <q_after, u> of the writes
