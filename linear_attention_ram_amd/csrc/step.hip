@@ -5,9 +5,11 @@
 // register-resident decoder when the row fits, one pass over HBM); then the
 // k_w selected slots are updated in place (GSU, paper §3.4), each wave taking
 // every other slot with all of its row loads in flight together, and the
-// updated rows are kept in LDS; last, each wave reads the k_r selected slots
-// for half of the channels, taking rows written by this token from LDS so
-// the read sees the write.
+// updated rows are kept in LDS; last, wave 1 reads the k_r selected slots,
+// taking rows written by this token from LDS so the read sees the write.
+// Wave 1 requests its first read rows as soon as its own decode is done, so
+// those loads overlap the write phase (a row this token writes is taken from
+// LDS instead, and its early copy is dropped).
 #include <type_traits>
 
 #include "decode.hpp"
@@ -18,6 +20,7 @@ namespace ramk {
 
 constexpr int STEP_ROW_CAP = 8192;  // k_w * d_v floats kept in LDS
 constexpr int STEP_BATCH = 4;       // slot rows per wave with loads in flight together
+constexpr int STEP_PREFETCH = 8;    // read rows requested before the write phase
 
 // DEC: -1 product rows (U >= 2); 0 flat rows of any length, streamed;
 // NV > 0 flat rows of at most NV * 64 16-byte vectors held in registers
@@ -56,6 +59,21 @@ __global__ __launch_bounds__(128) void decode_step_kernel(StepArgs a) {
   // (each lane rewrites the entry it wrote)
   if ((bh % a.H) < a.cape_heads && lane < k)
     sel_i[wv][lane] = (int)((sel_i[wv][lane] + a.t0 % a.S) % a.S);
+  wave_sync();
+  const int c0 = lane, c1 = lane + WAVE;
+  const bool ok0 = c0 < d_v, ok1 = c1 < d_v;
+  float* const slot_bh = a.slot + (int64_t)bh * a.S * d_v;
+  float* const mass_bh = a.mass + (int64_t)bh * a.S;
+  // wave 1: the first read rows, channels c0 and c1
+  float pre0[STEP_PREFETCH], pre1[STEP_PREFETCH];
+  if (wv == 1) {
+#pragma unroll
+    for (int u = 0; u < STEP_PREFETCH; ++u) {
+      const float* srow = slot_bh + (int64_t)sel_i[1][min(u, a.k_r - 1)] * d_v;
+      pre0[u] = ok0 ? srow[c0] : 0.f;
+      pre1[u] = ok1 ? srow[c1] : 0.f;
+    }
+  }
   __syncthreads();
   if (wv == 1 && lane < a.k_r) {
     const int slot = sel_i[1][lane];
@@ -67,12 +85,8 @@ __global__ __launch_bounds__(128) void decode_step_kernel(StepArgs a) {
   // GSU writes: wave wv updates rows j = wv, wv + 2, ...
   const IO* v = reinterpret_cast<const IO*>(a.v) + (int64_t)bh * d_v;
   const float g = to_f32(reinterpret_cast<const IO*>(a.gamma)[bh]);
-  const int c0 = lane, c1 = lane + WAVE;
-  const bool ok0 = c0 < d_v, ok1 = c1 < d_v;
   const float v0 = ok0 ? to_f32(v[c0]) : 0.f;
   const float v1 = ok1 ? to_f32(v[c1]) : 0.f;
-  float* const slot_bh = a.slot + (int64_t)bh * a.S * d_v;
-  float* const mass_bh = a.mass + (int64_t)bh * a.S;
   for (int j0 = wv; j0 < a.k_w; j0 += 2 * STEP_BATCH) {
     float m_old[STEP_BATCH], x0[STEP_BATCH], x1[STEP_BATCH];
     int slot[STEP_BATCH];
@@ -109,23 +123,40 @@ __global__ __launch_bounds__(128) void decode_step_kernel(StepArgs a) {
   }
   __syncthreads();
 
-  // read-out: wave wv sums channel wv * 64 + lane over the k_r read slots
-  const int c = wv * WAVE + lane;
-  if (c < d_v) {
-    float acc = 0.f;
-    for (int j0 = 0; j0 < a.k_r; j0 += STEP_BATCH) {
-      float s[STEP_BATCH];
+  // read-out by wave 1: o = sum_j r_j s_j in ascending j, channels c0 and c1
+  if (wv == 1) {
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < STEP_PREFETCH; ++u) {
+      if (u < a.k_r) {
+        const int hit = hit_of[u];
+        const float r = sel_w[1][u];
+        const float s0 = (hit >= 0 && ok0) ? rows[hit * d_v + c0] : pre0[u];
+        const float s1 = (hit >= 0 && ok1) ? rows[hit * d_v + c1] : pre1[u];
+        acc0 = fmaf(r, s0, acc0);
+        acc1 = fmaf(r, s1, acc1);
+      }
+    }
+    for (int j0 = STEP_PREFETCH; j0 < a.k_r; j0 += STEP_BATCH) {
+      float s0[STEP_BATCH], s1[STEP_BATCH];
 #pragma unroll
       for (int u = 0; u < STEP_BATCH; ++u) {
         const int j = min(j0 + u, a.k_r - 1);
         const int hit = hit_of[j];
-        s[u] = (hit >= 0) ? rows[hit * d_v + c] : slot_bh[(int64_t)sel_i[1][j] * d_v + c];
+        const float* srow = slot_bh + (int64_t)sel_i[1][j] * d_v;
+        s0[u] = !ok0 ? 0.f : (hit >= 0) ? rows[hit * d_v + c0] : srow[c0];
+        s1[u] = !ok1 ? 0.f : (hit >= 0) ? rows[hit * d_v + c1] : srow[c1];
       }
 #pragma unroll
       for (int u = 0; u < STEP_BATCH; ++u)
-        if (j0 + u < a.k_r) acc = fmaf(sel_w[1][j0 + u], s[u], acc);
+        if (j0 + u < a.k_r) {
+          acc0 = fmaf(sel_w[1][j0 + u], s0[u], acc0);
+          acc1 = fmaf(sel_w[1][j0 + u], s1[u], acc1);
+        }
     }
-    reinterpret_cast<IO*>(a.o)[(int64_t)bh * d_v + c] = from_f32<IO>(acc);
+    IO* o = reinterpret_cast<IO*>(a.o) + (int64_t)bh * d_v;
+    if (ok0) o[c0] = from_f32<IO>(acc0);
+    if (ok1) o[c1] = from_f32<IO>(acc1);
   }
 }
 

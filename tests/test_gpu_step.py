@@ -42,6 +42,12 @@ def test_small_bf16_wide():
     run_steps(cfg, 30, list(range(3)), TOL["bf16"])
 
 
+def test_many_read_slots():
+    # more read slots than the step requests before its write phase
+    cfg = synth.Config("many-reads", 3, 2, 1, 256, 5, 13, 96, "f32")
+    run_steps(cfg, 25, list(range(3)), TOL["f32"])
+
+
 def test_decode_config_sampled_sequences():
     cfg = synth.CONFIGS["decode"]
     say("decode config: 64 steps, oracle on sequences 0, 100, 255")
