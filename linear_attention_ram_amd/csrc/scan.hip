@@ -15,12 +15,13 @@
 // through a scalar register, and every per-row DPP scan or reduction sees all
 // 16 events.  Lanes past the chunk's end hold a read of weight 0.
 //
-// Branch-free event loops.  Every event runs the same straight-line code:
-// a write has step size eta and read weight 0, a read the reverse, and the
-// row loads and stores go through buffer resources whose range check turns
-// an offset of OOB into a load of zero or a dropped store.  Reads therefore
-// load nothing, writes store nothing in the forward, and padded events do
-// neither.
+// Event loops.  The row loads and stores go through buffer resources whose
+// range check turns an offset of OOB into a load of zero or a dropped store,
+// so a chunk's row loads are issued for all 16 events at once without
+// branches (the load of an event that has no such row reads nothing).  The
+// arithmetic of event i then runs under a branch on its kind, which is the
+// same in every lane (all lanes work on the same event), so each event does
+// only its own kind's work and padding does none.
 //
 // Inside a chunk:
 //   * the mass recurrence m <- lambda*m + w is affine, so one inclusive scan
@@ -64,6 +65,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+
+// Waits until every vector memory access the wave has issued is complete
+// (s_waitcnt vmcnt(0); the other counters are left alone).  Loads and stores
+// share that counter, so once a chunk's row loads are known to be done, the
+// stores of its event loop are never waited on inside it.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Index of the wave in its workgroup, as a value the compiler knows to be
 // uniform (buffer resources built from it stay in scalar registers).
@@ -362,6 +369,33 @@ __device__ __forceinline__ void mass_apply(Mass& M, const Ev& ev, float m, float
   M.keep = 1.f - M.eta;
 }
 
+// Forward pass over a chunk from s: a write (bit i of wm) moves the content
+// toward its v row, s <- (1 - eta) s + eta v; a read (bit i of rm) stores
+// r * s to its own stash row.  The kind of event i is the same in every lane,
+// so each event runs only its kind's arithmetic; padding runs none.
+template <typename IO, int CPL>
+__device__ __forceinline__ void fwd_replay(const typename Lanes<IO, CPL>::Raw (&x)[CHUNK],
+                                           const Mass& M, float rr, uint32_t so, uint32_t wm,
+                                           uint32_t rm, rsrc_t rs, uint32_t lb, float (&s)[CPL]) {
+  using LN = Lanes<IO, CPL>;
+  for_up<0, CHUNK>([&](auto I) {
+    if ((wm >> I) & 1u) {
+      float xf[CPL];
+      LN::get(x[I], xf);
+      const float e = bc<I>(M.eta), om = bc<I>(M.keep);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) s[k] = fmaf(om, s[k], e * xf[k]);
+    } else if ((rm >> I) & 1u) {
+      const float r = bc<I>(rr);
+      float ctr[CPL];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) ctr[k] = r * s[k];
+      LN::store(rs, bcu<I>(so) + lb, ctr);
+    }
+    sched_fence<I>();
+  });
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -406,19 +440,13 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
     const uint32_t so = (ev.valid && ev.side == 1) ? ((uint32_t)ev.rb * a.k_r + ev.j) * c.pitch : OOB;
     rec = load_rec(a.events, p1, min(end, (p1 / CHUNK + 1) * CHUNK) - p1, beg, end);   // next chunk
 
+    const uint32_t wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
+    const uint32_t rm = (uint32_t)__ballot(ev.valid && ev.side == 1) & 0xFFFFu;
+
     typename LN::Raw x[CHUNK];
     for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo) + c.lb); });
-    for_up<0, CHUNK>([&](auto I) {
-      float xf[CPL], ctr[CPL];
-      LN::get(x[I], xf);
-      const float e = bc<I>(M.eta), om = bc<I>(M.keep), r = bc<I>(rr);
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        s[k] = fmaf(om, s[k], e * xf[k]);
-        ctr[k] = r * s[k];
-      }
-      LN::store(rs, bcu<I>(so) + c.lb, ctr);
-    });
+    wait_vmem();
+    fwd_replay<IO, CPL>(x, M, rr, so, wm, rm, rs, c.lb, s);
     p0 = p1;
   }
   if (c.active) {
@@ -476,6 +504,8 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
     }
     const float rr = (ev.side == 1) ? ev.wt : 0.f;
     const uint32_t so = (ev.valid && ev.side == 1) ? ((uint32_t)ev.rb * a.k_r + ev.j) * c.pitch : OOB;
+    const uint32_t wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
+    const uint32_t rm = (uint32_t)__ballot(ev.valid && ev.side == 1) & 0xFFFFu;
     // next super-chunk's records for this wave (unconditional: past the end
     // it reloads the last event, unused)
     rec = load_rec(a.events, chunk_start(pn, w, end),
@@ -494,11 +524,14 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
 #pragma unroll
       for (int k = 0; k < CPL; ++k) sz[k] = 0.f;
       for_up<0, CHUNK>([&](auto I) {
-        float xf[CPL];
-        LN::get(x[I], xf);
-        const float e = bc<I>(M.eta), om = bc<I>(M.keep);
+        if ((wm >> I) & 1u) {
+          float xf[CPL];
+          LN::get(x[I], xf);
+          const float e = bc<I>(M.eta), om = bc<I>(M.keep);
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) sz[k] = fmaf(om, sz[k], e * xf[k]);
+          for (int k = 0; k < CPL; ++k) sz[k] = fmaf(om, sz[k], e * xf[k]);
+        }
+        sched_fence<I>();
       });
       const float P = row_prod(M.keep);
       if (c.active) {
@@ -508,6 +541,8 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
       if (lane == 0) mapP[w] = P;
     }
     __syncthreads();
+    // the rows and records requested before the barriers have arrived by now
+    wait_vmem();
     // this wave's start state: the carry through the earlier chunks' maps
     float s[CPL];
 #pragma unroll
@@ -526,17 +561,7 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
       if (lane == 0) a.ckpt_m[cs / CHUNK] = m_in;
     }
     // replay from the true start state; reads store their contributions
-    for_up<0, CHUNK>([&](auto I) {
-      float xf[CPL], ctr[CPL];
-      LN::get(x[I], xf);
-      const float e = bc<I>(M.eta), om = bc<I>(M.keep), r = bc<I>(rr);
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        s[k] = fmaf(om, s[k], e * xf[k]);
-        ctr[k] = r * s[k];
-      }
-      LN::store(rs, bcu<I>(so) + c.lb, ctr);
-    });
+    fwd_replay<IO, CPL>(x, M, rr, so, wm, rm, rs, c.lb, s);
     {   // rows of this wave's next chunk (past the end: no valid event, no load)
       const int n_n = chunk_start(pn, w + 1, end) - chunk_start(pn, w, end);
       const Ev ev_n = decode_rec(rec, n_n, c.h, a.H);
