@@ -125,7 +125,7 @@ typedef struct ram_ws_layout {
   size_t stash;       /* io (N, max(k_w,k_r), d_v): per-(token, j) read / dv contributions      */
   size_t tile_hist;   /* int32: bucketing scratch                                              */
   size_t long_list;   /* int32: segments that take the cooperative scan path                   */
-  size_t long_count;  /* int32: their number                                                   */
+  size_t long_count;  /* int32: their number per length class, and the scans' work counters     */
   size_t dw;          /* float (N, k_w): backward scratch                                      */
   size_t dr;          /* float (N, k_r)                                                         */
   size_t dgam;        /* float (N, k_w)                                                         */

@@ -125,7 +125,7 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   L->tile_hist = take(sizeof(int32_t) * (size_t)p->B * p->H * d.ntiles * d.S);
   const int pieces = make_pieces(p->B).n;
   L->long_list = take(sizeof(int32_t) * pieces * NBIN * long_cap(p, d));
-  L->long_count = take(sizeof(int32_t) * pieces * NBIN);
+  L->long_count = take(sizeof(int32_t) * pieces * LONG_WORDS);
   L->fwd_bytes = off;
   L->dw = take(sizeof(float) * d.N * p->k_w);
   L->dr = take(sizeof(float) * d.N * p->k_r);
@@ -393,7 +393,7 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
     ba.ev_base = r0 * K;
     ba.events = (EventRec*)(w + L.events);
     ba.long_list = (int32_t*)(w + L.long_list) + (int64_t)q * NBIN * cap;
-    ba.long_count = (int32_t*)(w + L.long_count) + q * NBIN;
+    ba.long_count = (int32_t*)(w + L.long_count) + q * LONG_WORDS;
     ba.long_cap = cap;
     e = launch_bucket(ba, bf, a, prof_before, prof_after);
     if (e != hipSuccess) break;
@@ -410,6 +410,7 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
     sa.nseg = (int64_t)nb * HS;
     sa.long_list = ba.long_list;
     sa.long_count = ba.long_count;
+    sa.queue = ba.long_count + NBIN;
     sa.long_cap = cap;
     sa.use_long = d.ntiles > 0;
     sa.seg_offset = ba.seg_offset;
@@ -545,7 +546,8 @@ int backward_impl(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t
     sb.eps = p->eps;
     sb.nseg = (int64_t)nb * HS;
     sb.long_list = (const int32_t*)(w + L.long_list) + (int64_t)q * NBIN * cap;
-    sb.long_count = (const int32_t*)(w + L.long_count) + q * NBIN;
+    sb.long_count = (const int32_t*)(w + L.long_count) + q * LONG_WORDS;
+    sb.queue = (int32_t*)(w + L.long_count) + q * LONG_WORDS + NBIN + 2;
     sb.long_cap = cap;
     sb.use_long = d.ntiles > 0;
     sb.seg_offset = (const int32_t*)(w + L.seg_offset) + (int64_t)b0 * HS;

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void bucket_hist_kernel(BucketArgs a) {
   const int t_lo = tile * a.tile;
   const int t_hi = min(a.T, t_lo + a.tile);
   for (int s = threadIdx.x; s < a.S; s += blockDim.x) hist[s] = 0;
-  if (tile == 0 && bh == 0 && threadIdx.x < NBIN) a.long_count[threadIdx.x] = 0;
+  if (tile == 0 && bh == 0 && threadIdx.x < LONG_WORDS) a.long_count[threadIdx.x] = 0;
   __syncthreads();
   const int n = (t_hi - t_lo) * K;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {

@@ -12,6 +12,10 @@ constexpr int LONG_EVENTS = 128; // segments with more events take the cooperati
 constexpr int NBIN = 8;          // length classes of the long-segment list: class c holds
                                  // segments of [129 * 2^c, 129 * 2^(c+1)) events (the last
                                  // class is open-ended); scans take the longest first
+constexpr int LONG_WORDS = NBIN + 4;  // int32 words per long-segment list header:
+                                      //   [0, NBIN)  entries per class
+                                      //   NBIN, +1   forward scan: next ticket, finished workgroups
+                                      //   NBIN+2, +3 reverse scan: the same
 constexpr int MAX_DV = 128;      // widest slot
 constexpr uint32_t MAX_BUF_BYTES = 0x7FE00000u;  // one batch's v, dO or stash rows (scans)
 
@@ -40,7 +44,7 @@ struct BucketArgs {
                           // of this call's piece; events is the whole list)
   EventRec* events;       // (all events of the call)
   int32_t* long_list;     // (NBIN, long_cap): segments with more than LONG_EVENTS events
-  int32_t* long_count;    // (NBIN): entries per class
+  int32_t* long_count;    // (LONG_WORDS): entries per class, then the scans' work queues
   int long_cap;
 };
 
@@ -50,6 +54,7 @@ struct ScanFwdArgs {
   int64_t nseg;
   const int32_t* long_list;   // (NBIN, long_cap)
   const int32_t* long_count;  // (NBIN)
+  int32_t* queue;             // (2): next ticket, finished workgroups; zero at launch
   int long_cap;
   int use_long;           // long_list / long_count are valid
   const int32_t* seg_offset;
@@ -70,6 +75,7 @@ struct ScanBwdArgs {
   int64_t nseg;
   const int32_t* long_list;
   const int32_t* long_count;
+  int32_t* queue;         // (2), as in the forward
   int long_cap;
   int use_long;
   const int32_t* seg_offset;

@@ -348,6 +348,25 @@ __device__ __forceinline__ int64_t long_entry(const int32_t* list, const LongCou
   return list[pos];
 }
 
+// Work queue of the long-segment kernels.  A workgroup takes list entries one
+// at a time from a ticket counter (longest class first), so the entries
+// spread over the resident workgroups by their length rather than by a
+// fixed stride.  The counter is zero at launch; the last workgroup to run
+// out of entries clears it, and its finished count, for the next launch.
+__device__ __forceinline__ int take_ticket(int32_t* queue) {
+  __shared__ int ticket;
+  __syncthreads();   // the previous ticket has been read by every wave
+  if (threadIdx.x == 0) ticket = atomicAdd(queue, 1);
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(ticket);
+}
+__device__ __forceinline__ void release_queue(int32_t* queue) {
+  if (threadIdx.x == 0 && atomicAdd(queue + 1, 1) == (int)gridDim.x - 1) {
+    atomicExch(queue, 0);
+    atomicExch(queue + 1, 0);
+  }
+}
+
 // Per-event mass of a chunk from the incoming mass m: mi after the event,
 // mo before it, and the write step size eta (0 for reads and padding).
 struct Mass {
@@ -598,13 +617,14 @@ __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_fwd_short_kernel(Scan
   scan_fwd_short<IO, CPL>(a, g);
 }
 
-// Long segments: a resident grid of NWL-wave workgroups walks the list,
-// longest class first.
+// Long segments: a resident grid of NWL-wave workgroups takes the list's
+// entries from the work queue, longest class first.
 template <typename IO, int CPL>
 __global__ __launch_bounds__(NWL * WAVE) void scan_fwd_long_kernel(ScanFwdArgs a) {
   const LongCounts L = long_counts(a.long_count);
-  for (int i = blockIdx.x; i < L.total; i += gridDim.x)
+  for (int i = take_ticket(a.queue); i < L.total; i = take_ticket(a.queue))
     scan_fwd_long<IO, CPL>(a, long_entry(a.long_list, L, a.long_cap, i));
+  release_queue(a.queue);
 }
 
 // ---------------------------------------------------------------------------
@@ -1098,8 +1118,9 @@ __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_bwd_short_kernel(Scan
 template <typename IO, int CPL>
 __global__ __launch_bounds__(NWL * WAVE) void scan_bwd_long_kernel(ScanBwdArgs a) {
   const LongCounts L = long_counts(a.long_count);
-  for (int i = blockIdx.x; i < L.total; i += gridDim.x)
+  for (int i = take_ticket(a.queue); i < L.total; i = take_ticket(a.queue))
     scan_bwd_long<IO, CPL>(a, long_entry(a.long_list, L, a.long_cap, i));
+  release_queue(a.queue);
 }
 
 // ---------------------------------------------------------------------------
@@ -1148,27 +1169,37 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
 // ---------------------------------------------------------------------------
 
 namespace {
-// Workgroups of a kernel that fit on the device at once.
+// Long-kernel workgroups per CU at most.  The long kernel pulls work until
+// its queue is empty, so the wave slots it leaves free are the ones the
+// short-segment kernel beside it runs in.  Measured on the 1.3B-layer
+// shape: 3 for the forward (its waves are light enough for 8 per CU), 4 for
+// the reverse (which its LDS allows at most).
+constexpr int LONG_GROUPS_FWD = 3;
+constexpr int LONG_GROUPS_BWD = 4;
+
+// Workgroups of the long kernel that run at once: as many as fit, at most
+// `cap` per CU.
 template <typename Args>
-int resident_blocks(void (*kern)(Args), int threads) {
+int resident_blocks(void (*kern)(Args), int threads, int cap) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess)
     return 0;
+  if (per_cu > cap) per_cu = cap;
   return cus > 0 && per_cu > 0 ? cus * per_cu : 0;
 }
 
 // Long kernel on `st`, short kernel on `side` (the caller orders the two
-// streams).  The long grid is the resident workgroup count, capped by the
-// list capacity: a grid-stride walk needs no more.  The long kernel is
-// enqueued first so that its workgroups, which hold the critical path, are
-// resident before the short kernel's many small ones fill the device.
+// streams).  The long grid is the resident count above, capped by the list
+// capacity: the work queue needs no more.  The long kernel is enqueued
+// first so that its workgroups, which hold the critical path, are resident
+// before the short kernel's many small ones fill the device.
 template <typename Args>
-hipError_t launch_pair(void (*shortk)(Args), void (*longk)(Args), int& resident, const Args& a,
-                       hipStream_t st, hipStream_t side) {
+hipError_t launch_pair(void (*shortk)(Args), void (*longk)(Args), int& resident, int per_cu,
+                       const Args& a, hipStream_t st, hipStream_t side) {
   if (a.use_long) {
-    if (resident == 0) resident = resident_blocks(longk, NWL * WAVE);
+    if (resident == 0) resident = resident_blocks(longk, NWL * WAVE, per_cu);
     if (resident == 0) return hipErrorInvalidDeviceFunction;
     const int64_t cap = (int64_t)a.long_cap * NBIN;
     const unsigned lgrid = (unsigned)(cap < resident ? cap : resident);
@@ -1185,12 +1216,12 @@ hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st, hipS
   static int res[4] = {0, 0, 0, 0};
   if (bf16) {
     if (a.d_v > 64)
-      return launch_pair(scan_fwd_short_kernel<bf16_t, 2>, scan_fwd_long_kernel<bf16_t, 2>, res[0], a, st, side);
-    return launch_pair(scan_fwd_short_kernel<bf16_t, 1>, scan_fwd_long_kernel<bf16_t, 1>, res[1], a, st, side);
+      return launch_pair(scan_fwd_short_kernel<bf16_t, 2>, scan_fwd_long_kernel<bf16_t, 2>, res[0], LONG_GROUPS_FWD, a, st, side);
+    return launch_pair(scan_fwd_short_kernel<bf16_t, 1>, scan_fwd_long_kernel<bf16_t, 1>, res[1], LONG_GROUPS_FWD, a, st, side);
   }
   if (a.d_v > 64)
-    return launch_pair(scan_fwd_short_kernel<float, 2>, scan_fwd_long_kernel<float, 2>, res[2], a, st, side);
-  return launch_pair(scan_fwd_short_kernel<float, 1>, scan_fwd_long_kernel<float, 1>, res[3], a, st, side);
+    return launch_pair(scan_fwd_short_kernel<float, 2>, scan_fwd_long_kernel<float, 2>, res[2], LONG_GROUPS_FWD, a, st, side);
+  return launch_pair(scan_fwd_short_kernel<float, 1>, scan_fwd_long_kernel<float, 1>, res[3], LONG_GROUPS_FWD, a, st, side);
 }
 
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st, hipStream_t side) {
@@ -1198,12 +1229,12 @@ hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st, hipS
   static int res[4] = {0, 0, 0, 0};
   if (bf16) {
     if (a.d_v > 64)
-      return launch_pair(scan_bwd_short_kernel<bf16_t, 2>, scan_bwd_long_kernel<bf16_t, 2>, res[0], a, st, side);
-    return launch_pair(scan_bwd_short_kernel<bf16_t, 1>, scan_bwd_long_kernel<bf16_t, 1>, res[1], a, st, side);
+      return launch_pair(scan_bwd_short_kernel<bf16_t, 2>, scan_bwd_long_kernel<bf16_t, 2>, res[0], LONG_GROUPS_BWD, a, st, side);
+    return launch_pair(scan_bwd_short_kernel<bf16_t, 1>, scan_bwd_long_kernel<bf16_t, 1>, res[1], LONG_GROUPS_BWD, a, st, side);
   }
   if (a.d_v > 64)
-    return launch_pair(scan_bwd_short_kernel<float, 2>, scan_bwd_long_kernel<float, 2>, res[2], a, st, side);
-  return launch_pair(scan_bwd_short_kernel<float, 1>, scan_bwd_long_kernel<float, 1>, res[3], a, st, side);
+    return launch_pair(scan_bwd_short_kernel<float, 2>, scan_bwd_long_kernel<float, 2>, res[2], LONG_GROUPS_BWD, a, st, side);
+  return launch_pair(scan_bwd_short_kernel<float, 1>, scan_bwd_long_kernel<float, 1>, res[3], LONG_GROUPS_BWD, a, st, side);
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st) {
