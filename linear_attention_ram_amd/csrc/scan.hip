@@ -119,7 +119,6 @@ template <> struct Lanes<bf16_t, 1> {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
   }
   static __device__ __forceinline__ void get(Raw x, float (&f)[1]) { f[0] = __uint_as_float(x << 16); }
-  static __device__ __forceinline__ Raw merge(Raw a, Raw b) { return a | b; }
   static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[1]) {
     const f32x2_t x = {f[0], 0.f};
     const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
@@ -135,7 +134,6 @@ template <> struct Lanes<bf16_t, 2> {
     f[0] = __uint_as_float(x << 16);
     f[1] = __uint_as_float(x & 0xffff0000u);
   }
-  static __device__ __forceinline__ Raw merge(Raw a, Raw b) { return a | b; }
   static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[2]) {
     const f32x2_t x = {f[0], f[1]};
     __builtin_amdgcn_raw_buffer_store_b32(
@@ -148,7 +146,6 @@ template <> struct Lanes<float, 1> {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
   static __device__ __forceinline__ void get(Raw x, float (&f)[1]) { f[0] = __uint_as_float(x); }
-  static __device__ __forceinline__ Raw merge(Raw a, Raw b) { return a | b; }
   static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[1]) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f[0]), r, off, 0, 0);
   }
@@ -163,7 +160,6 @@ template <> struct Lanes<float, 2> {
     f[0] = __uint_as_float(x.x);
     f[1] = __uint_as_float(x.y);
   }
-  static __device__ __forceinline__ Raw merge(Raw a, Raw b) { return make_uint2(a.x | b.x, a.y | b.y); }
   static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[2]) {
     typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
     const u32x2_t v = {__float_as_uint(f[0]), __float_as_uint(f[1])};
@@ -265,6 +261,17 @@ __device__ __forceinline__ void affine_suffix_scan(float& A, float& B) {
   affine_suffix_step<2>(A, B);
   affine_suffix_step<4>(A, B);
   affine_suffix_step<8>(A, B);
+}
+
+// Inclusive suffix product across the 16 lanes of each row (lane i ends with
+// x_i * x_i+1 * ... * x_15), in the same order as the A part of
+// affine_suffix_scan.
+__device__ __forceinline__ float suffix_prod(float A) {
+  A = A * dpp_or<DppShl<1>::v>(1.f, A);
+  A = A * dpp_or<DppShl<2>::v>(1.f, A);
+  A = A * dpp_or<DppShl<4>::v>(1.f, A);
+  A = A * dpp_or<DppShl<8>::v>(1.f, A);
+  return A;
 }
 
 // Product of x over the 16 lanes of each row (every lane gets it).
@@ -657,6 +664,8 @@ struct BwdChunk {
   float rr;                        // read weight, 0 for writes and padding
   uint32_t sw;                     // stash offset of a write's dv row, else OOB
   uint32_t wm, rm;                 // bit i: event i is a write / a read (wave-uniform)
+  float den;                       // m' + eps: mass after the event plus eps
+  float gq;                        // w / (m' + eps)^2 of a write, else 0
   typename Lanes<IO, CPL>::Raw x[CHUNK];
   float so_reg[SO_LDS ? 1 : CHUNK][CPL];
   float* so_lds;                   // [CHUNK][MAX_DV] floats at the lane's channel c0
@@ -688,19 +697,19 @@ struct BwdChunk {
   }
 };
 
-// Row gathers of a chunk: the v row of each write and the dO row of each read
-// (one of the two loads of an event is out of range and gives 0).
+// Row gathers of a chunk: the v row of each write and the dO row of each read.
+// The kind of event i is the same in every lane, so its one load takes the
+// buffer of its kind (a scalar select); padding loads nothing.
 template <typename IO, int CPL, bool SO>
 __device__ __forceinline__ void bwd_gather(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
                                            rsrc_t rv, rsrc_t ro, BwdChunk<IO, CPL, SO>& ck,
                                            float4 rec, int n) {
   using LN = Lanes<IO, CPL>;
   const Ev ev = decode_rec(rec, n, c.h, a.H);
-  const uint32_t roff = (uint32_t)ev.rb * c.pitch;
-  const uint32_t xv = (ev.valid && ev.side == 0) ? roff : OOB;
-  const uint32_t xd = (ev.valid && ev.side == 1) ? roff : OOB;
+  const uint32_t xo = ev.valid ? (uint32_t)ev.rb * c.pitch : OOB;
+  const uint32_t wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
   for_up<0, CHUNK>([&](auto I) {
-    ck.x[I] = LN::merge(LN::load(rv, bcu<I>(xv) + c.lb), LN::load(ro, bcu<I>(xd) + c.lb));
+    ck.x[I] = LN::load(((wm >> I) & 1u) ? rv : ro, bcu<I>(xo) + c.lb);
   });
 }
 
@@ -718,6 +727,8 @@ __device__ __forceinline__ void bwd_prepare(const ScanBwdArgs& a, const SegCtx<I
   ck.sw = (ev.valid && ev.side == 0) ? ((uint32_t)ev.rb * a.k_w + ev.j) * c.pitch : OOB;
   ck.wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
   ck.rm = (uint32_t)__ballot(ev.valid && ev.side == 1) & 0xFFFFu;
+  ck.den = ck.M.mi + a.eps;
+  ck.gq = (ev.valid && ev.side == 0 && ev.wt > 0.f) ? ev.wt / (ck.den * ck.den) : 0.f;
 }
 
 template <typename IO, int CPL, bool SO>
@@ -760,11 +771,14 @@ __device__ __forceinline__ void bwd_replay(BwdChunk<IO, CPL, SO>& ck, float (&s)
 }
 
 // Reverse walk of the content adjoint from sh (after the chunk) to sh (before
-// it): stores the dv contributions e * s_hat of the writes and leaves the
-// lane-local partials <s_hat_after, x - s_old> (the deta of a write) in pw.
+// it): stores the dv contributions e * s_hat of the writes and leaves in pw
+// the lane-local partials of each event's scalar gradient: <s_hat_after,
+// x - s_old> (the deta of a write), or the replay's partial pr of a read (its
+// dr), so that one batched reduction serves both kinds.
 template <typename IO, int CPL, bool SO>
 __device__ __forceinline__ void bwd_walk(const BwdChunk<IO, CPL, SO>& ck, const SegCtx<IO, CPL>& c,
-                                         rsrc_t rs, float (&sh)[CPL], float (&pw)[CHUNK]) {
+                                         rsrc_t rs, float (&sh)[CPL], const float (&pr)[CHUNK],
+                                         float (&pw)[CHUNK]) {
   using LN = Lanes<IO, CPL>;
   // each event's pre-write content is read from LDS one event ahead, outside
   // the per-kind branches, so the read has an event's work to complete in
@@ -795,6 +809,7 @@ __device__ __forceinline__ void bwd_walk(const BwdChunk<IO, CPL, SO>& ck, const 
       const float r = bc<I>(ck.rr);
 #pragma unroll
       for (int k = 0; k < CPL; ++k) sh[k] = fmaf(r, xf[k], sh[k]);
+      pw[I] = pr[I];
     }
     sched_fence<I>();
   });
@@ -809,8 +824,8 @@ __device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const SegCtx<I
   const int lane = lane_id();
   const Ev& ev = ck.ev;
   const bool wr = ev.valid && ev.side == 0;
-  const float den = ck.M.mi + a.eps;
-  const float g = (wr && ev.wt > 0.f) ? ev.wt / (den * den) : 0.f;
+  const float den = ck.den;
+  const float g = ck.gq;
   const float deta = wr ? red : 0.f;
   float A = wr ? ev.lam : 1.f;
   float B = wr ? -ev.lam * g * deta : 0.f;
@@ -840,23 +855,41 @@ __device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const SegCtx<I
 // checkpoint 0) and the value is selected afterwards, so no wait sits inside
 // a branch.  cs may be the segment end (an empty chunk of the long path):
 // checkpoint cs / 16 <= E / 16 exists.
+// The loaded values and the selection are kept apart (ChunkStart holds the
+// raw loads), so a caller can carry the loads in flight across a loop
+// iteration and select once they have arrived.
+template <int CPL>
+struct ChunkStart {
+  float t[CPL], tm;   // loaded content and mass
+  bool zero;          // the segment's first chunk with no initial state
+};
 template <typename IO, int CPL>
-__device__ __forceinline__ void chunk_state(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
-                                            int64_t g, int beg, int cs, float (&s)[CPL],
-                                            float& m) {
+__device__ __forceinline__ void chunk_state_load(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                                 int64_t g, int beg, int cs, ChunkStart<CPL>& st) {
   const bool first = cs == beg;
-  const bool zero = first && !a.slot0;
+  st.zero = first && !a.slot0;
   const float* sp = first ? (a.slot0 ? a.slot0 + g * a.d_v : a.ckpt_s)
                           : a.ckpt_s + (int64_t)(cs / CHUNK) * a.d_v;
   const float* mp = first ? (a.mass0 ? a.mass0 + g : a.ckpt_m) : a.ckpt_m + cs / CHUNK;
   const int cc = min(c.c0, a.d_v - CPL);
-  float t[CPL];
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) t[k] = sp[cc + k];
-  const float tm = *mp;
+  for (int k = 0; k < CPL; ++k) st.t[k] = sp[cc + k];
+  st.tm = *mp;
+}
+template <typename IO, int CPL>
+__device__ __forceinline__ void chunk_state_take(const SegCtx<IO, CPL>& c, const ChunkStart<CPL>& st,
+                                                 float (&s)[CPL], float& m) {
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) s[k] = (zero || !c.active) ? 0.f : t[k];
-  m = zero ? 0.f : tm;
+  for (int k = 0; k < CPL; ++k) s[k] = (st.zero || !c.active) ? 0.f : st.t[k];
+  m = st.zero ? 0.f : st.tm;
+}
+template <typename IO, int CPL>
+__device__ __forceinline__ void chunk_state(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                            int64_t g, int beg, int cs, float (&s)[CPL],
+                                            float& m) {
+  ChunkStart<CPL> st;
+  chunk_state_load(a, c, g, beg, cs, st);
+  chunk_state_take(c, st, s, m);
 }
 
 template <typename IO, int CPL>
@@ -889,11 +922,12 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
       const float4 rec_cur = rec;
       rec = load_rec(a.events, cp, cs - cp, beg, end);   // previous chunk (unused after the first)
       bwd_setup(a, c, rv, ro, ck, rec_cur, n, m);
+      // the row loads are done before the event loops, whose stores then
+      // never wait (a padded event's load is never consumed)
+      wait_vmem();
       bwd_replay(ck, s, pr);
-      const float red_r = batched_sum(pr);
-      bwd_walk(ck, c, rs, sh, pw);
-      const float red_w = batched_sum(pw);
-      bwd_scalars(a, c, ck, ck.ev.side == 1 ? red_r : red_w, mh);
+      bwd_walk(ck, c, rs, sh, pr, pw);
+      bwd_scalars(a, c, ck, batched_sum(pw), mh);
       if (cs == beg) break;
       cs = cp;
     }
@@ -946,7 +980,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
   __shared__ float so_lds[NW][CHUNK][MAX_DV];   // pre-write contents, per wave
   BwdChunk<IO, CPL, true> ck;
   ck.so_lds = &so_lds[w][0][0] + c.c0;
-  float pr[CHUNK], pw[CHUNK];
+  float pr[CHUNK], pw[CHUNK], pm[CHUNK];
   auto chunk_of = [&](int k, int& cs, int& n) {
     cs = end;
     n = 0;
@@ -957,9 +991,10 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
   };
   // The rows and the start state of a chunk are requested as soon as the
   // previous chunk of this wave no longer needs its registers (after its
-  // reverse walk), so the loads overlap the scalar part and the barriers.
+  // reverse walk), so the loads overlap the closing barriers; they are
+  // carried into the next iteration as loaded and used there.
   float4 rec, rec_next;
-  float s[CPL], m;
+  ChunkStart<CPL> st;
   int cs, n;
   {
     const int u_first = ((nchunks - 1) / NW) * NW;
@@ -968,28 +1003,28 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
     int csp, np;
     chunk_of(max(u_first - NW, 0) + w, csp, np);
     rec_next = load_rec(a.events, csp, np, beg, end);
-    chunk_state<IO, CPL>(a, c, g, beg, cs, s, m);
+    chunk_state_load<IO, CPL>(a, c, g, beg, cs, st);
     bwd_gather(a, c, rv, ro, ck, rec, n);
   }
   for (int u0 = ((nchunks - 1) / NW) * NW; u0 >= 0; u0 -= NW) {
+    // this chunk's rows and start state, requested before the previous
+    // chunk's closing barriers, are in by now; once they are known to be
+    // done the event loops' stores never wait
+    wait_vmem();
+    float s[CPL], m;
+    chunk_state_take(c, st, s, m);
     bwd_prepare(a, c, ck, rec, n, m);
     bwd_replay(ck, s, pr);
-    const float red_r = batched_sum(pr);   // dr of the reads
     const Ev& ev = ck.ev;
     // adjoint map of the chunk: a reverse walk from zero.  coef_i is the
     // factor of u_i = x_i - s_old_i in U: -(prefix product of lambda) *
-    // g_i * (product of (1 - eta) over the later events).
+    // g_i * (product of (1 - eta) over the later events).  The prefix
+    // product of lambda over the writes is the A part of the mass scan.
     const bool wr = ev.valid && ev.side == 0;
-    float Lp = wr ? ev.lam : 1.f;
-    {
-      float dummy = 0.f;
-      affine_scan(Lp, dummy);
-    }
-    float Qs = ck.M.keep, dz = 0.f;
-    affine_suffix_scan(Qs, dz);
+    const float Lp = ck.M.A;
+    const float Qs = suffix_prod(ck.M.keep);
     const float Qx = dpp_or<DPP_SHL1>(1.f, Qs);
-    const float den = ck.M.mi + a.eps;
-    const float gq = (wr && ev.wt > 0.f) ? ev.wt / (den * den) : 0.f;
+    const float gq = ck.gq;
     const float coef = -Lp * gq * Qx;
     // only earlier waves fold a chunk's map, so wave 0 forms none
     float U[CPL];
@@ -1006,7 +1041,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
 #pragma unroll
         for (int k = 0; k < CPL; ++k) so[k] = so_n[k];
         if constexpr (I > 0) ck.template get_so<I - 1>(so_n);
-        pw[I] = 0.f;
+        pm[I] = 0.f;
         if ((ck.wm >> I) & 1u) {
           float xf[CPL];
           LN::get(ck.x[I], xf);
@@ -1019,7 +1054,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
             U[k] = fmaf(cf, u, U[k]);
             q[k] = fmaf(-e, q[k], q[k]);
           }
-          pw[I] = d;
+          pm[I] = d;
         } else if ((ck.rm >> I) & 1u) {
           float xf[CPL];
           LN::get(ck.x[I], xf);
@@ -1029,7 +1064,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
         }
         sched_fence<I>();
       });
-      const float red1 = batched_sum(pw);    // <q_after, u> of the writes
+      const float red1 = batched_sum(pm);    // <q_after, u> of the writes
       const float K = row_sum(wr ? -Lp * gq * red1 : 0.f);
       const float L = bc<15>(Lp);
       const float Q = bc<0>(Qs);
@@ -1060,7 +1095,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
     float mh = mh_carry;
     for (int kk = NW - 1; kk > w; --kk) mh = fmaf(mL[kk], mh, mD[kk] + mK[kk]);
     // exact reverse step of this wave's chunk
-    bwd_walk(ck, c, rs, sh, pw);
+    bwd_walk(ck, c, rs, sh, pr, pw);
     // next chunk of this wave: rows, start state and the record after it
     // (unconditional: past the segment's start the chunk is empty)
     int csn, nn;
@@ -1072,12 +1107,9 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
       chunk_of(max(u0 - 2 * NW, 0) + w, csp, np);
       rec_next = load_rec(a.events, csp, np, beg, end);
     }
-    float s_n[CPL], m_n;
-    chunk_state<IO, CPL>(a, c, g, beg, csn, s_n, m_n);
-    const float red2 = batched_sum(pw);     // deta of the writes
-    const Ev ev_cur = ev;
+    bwd_scalars(a, c, ck, batched_sum(pw), mh);   // deta of the writes, dr of the reads
+    chunk_state_load<IO, CPL>(a, c, g, beg, csn, st);
     bwd_gather(a, c, rv, ro, ck, rec_n, nn);
-    bwd_scalars(a, c, ck, ev_cur.side == 1 ? red_r : red2, mh);
     if (w == 0) {
       if (c.active) {
 #pragma unroll
@@ -1093,9 +1125,6 @@ __device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
     rec = rec_n;
     cs = csn;
     n = nn;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) s[k] = s_n[k];
-    m = m_n;
   }
   if (w == 0) {
     if (a.d_slot0 && c.active) {
