@@ -72,6 +72,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // stores of its event loop are never waited on inside it.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Kernel arguments are read with wide scalar loads, and the registers of one
+// load stay allocated together while any of its fields is in use.  fresh()
+// turns a field into a value of its own (an empty asm the compiler cannot see
+// through), so a long loop that needs a few fields keeps only those, and the
+// rest are freed instead of spilled.
+template <typename T>
+__device__ __forceinline__ void fresh(T& x) { asm volatile("" : "+s"(x)); }
+
 // Index of the wave in its workgroup, as a value the compiler knows to be
 // uniform (buffer resources built from it stay in scalar registers).
 __device__ __forceinline__ int wave_index() {
@@ -953,7 +961,12 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
 // exact reverse step; wave 0's result is the carry into the previous NWL
 // chunks.
 template <typename IO, int CPL>
-__device__ void scan_bwd_long(const ScanBwdArgs& a, int64_t g) {
+__device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
+  ScanBwdArgs a = args;
+  fresh(a.events), fresh(a.ckpt_s), fresh(a.ckpt_m), fresh(a.slot0), fresh(a.mass0);
+  fresh(a.dw), fresh(a.dr), fresh(a.dgam), fresh(a.d_slot0), fresh(a.d_mass0);
+  fresh(a.d_slot1), fresh(a.d_mass1), fresh(a.stash), fresh(a.v), fresh(a.d_o);
+  fresh(a.seg_offset);
   constexpr int NW = NWL;
   using LN = Lanes<IO, CPL>;
   __shared__ float mQ[NW], mL[NW], mK[NW], mD[NW];
