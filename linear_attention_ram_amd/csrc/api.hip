@@ -98,6 +98,9 @@ Pieces make_pieces(int B) {
 
 // Entries per length class of one piece's long-segment list: every long
 // segment has more than LONG_EVENTS events.
+// Workgroups of the bucketing scan per (b, h): blocks of SCAN_SLOTS slots.
+int scan_blocks(int64_t S) { return (int)((S + SCAN_SLOTS - 1) / SCAN_SLOTS); }
+
 int long_cap(const ram_problem* p, const Dims& d) {
   const Pieces P = make_pieces(p->B);
   int nb = 0;
@@ -122,7 +125,9 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   L->ckpt_s = take(sizeof(float) * d.nck * p->d_v);
   L->ckpt_m = take(sizeof(float) * d.nck);
   L->stash = take(d.io_bytes * d.N * (p->k_w > p->k_r ? p->k_w : p->k_r) * p->d_v);
-  L->tile_hist = take(sizeof(int32_t) * (size_t)p->B * p->H * d.ntiles * d.S);
+  // tile histograms, then the per-block event counts of the bucketing scan
+  L->tile_hist = take(sizeof(int32_t) * (size_t)p->B * p->H *
+                      ((size_t)d.ntiles * d.S + scan_blocks(d.S)));
   const int pieces = make_pieces(p->B).n;
   L->long_list = take(sizeof(int32_t) * pieces * NBIN * long_cap(p, d));
   L->long_count = take(sizeof(int32_t) * pieces * LONG_WORDS);
@@ -389,6 +394,9 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
     ba.ntiles = d.ntiles;
     ba.nbits = d.nbits;
     ba.tile_hist = (int32_t*)(w + L.tile_hist) + (int64_t)b0 * p->H * d.ntiles * d.S;
+    ba.nblk = scan_blocks(d.S);
+    ba.blk_tot = (int32_t*)(w + L.tile_hist) + (int64_t)p->B * p->H * d.ntiles * d.S +
+                 (int64_t)b0 * p->H * ba.nblk;
     ba.seg_offset = (int32_t*)(w + L.seg_offset) + (int64_t)b0 * HS;
     ba.ev_base = r0 * K;
     ba.events = (EventRec*)(w + L.events);

@@ -5,16 +5,20 @@
 // A stable counting sort per (b, h), in three kernels:
 //   hist     one block per (b, h, tile of `tile` tokens): slot histogram
 //            of the tile's events in LDS;
-//   scan     one block per (b, h): per slot, exclusive prefix of the tile
-//            counts (in place) and, over the slots in blocks of 1024, the
-//            segment offsets; segments with more than LONG_EVENTS events
-//            are listed for the cooperative scan path, in NBIN classes of
-//            doubling length (any order inside a class).
-//            Every (b, h) holds exactly T*(k_w+k_r) events, so segment
-//            offsets need no scan across (b, h);
+//   scan     one workgroup per (b, h, block of SCAN_SLOTS slots): per slot,
+//            exclusive prefix of the tile counts (in place), and the slot's
+//            offset inside its block, which takes the place of tile 0's
+//            entry (always 0); the block's event count goes to blk_tot.
+//            Segments with more than LONG_EVENTS events are listed for the
+//            cooperative scan path, in NBIN classes of doubling length (any
+//            order inside a class).  Every (b, h) holds exactly
+//            T*(k_w+k_r) events, so segment offsets need no scan across
+//            (b, h);
 //   scatter  one workgroup per (b, h, tile): all its waves set up the
-//            tile's per-slot write positions in LDS, then one wave
-//            walks the tile's events in order
+//            tile's per-slot write positions in LDS (the (b, h) base, the
+//            event counts of the earlier blocks, the offset inside the
+//            block and the tile prefix; the tile-0 workgroup also stores the
+//            segment offsets), then one wave walks the tile's events in order
 //            (t ascending, write side before read side), ranks equal slots
 //            inside each 64-event batch with ballots, and writes each event
 //            as a 16-byte record (code, weight, retention lambda and
@@ -54,56 +58,58 @@ __global__ __launch_bounds__(256) void bucket_hist_kernel(BucketArgs a) {
   for (int s = threadIdx.x; s < a.S; s += blockDim.x) out[s] = hist[s];
 }
 
-__global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketArgs a) {
+__global__ __launch_bounds__(SCAN_SLOTS) void bucket_scan_kernel(BucketArgs a) {
+  static_assert(SCAN_SLOTS == 16 * WAVE, "one slot per thread, 16 waves");
   __shared__ int wave_tot[16];
-  const int bh = blockIdx.x;
+  __shared__ int cls_n[NBIN], cls_at[NBIN];   // long segments of the block per class
+  const int blk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x;
+  if (tid < NBIN) cls_n[tid] = 0;
   const int S = a.S;
+  const int s = blk * SCAN_SLOTS + tid;
   int32_t* th = a.tile_hist + (int64_t)bh * a.ntiles * S;
-  const int64_t base = a.ev_base + (int64_t)bh * a.T * (a.k_w + a.k_r);
-  int carry = 0;
-  for (int s0 = 0; s0 < S; s0 += 1024) {
-    const int s = s0 + tid;
-    int cnt = 0;
-    if (s < S) {
-      // exclusive prefix over the tiles, in place; loads in groups of TG so
-      // that a group costs one memory round trip
-      constexpr int TG = 8;
-      for (int t0 = 0; t0 < a.ntiles; t0 += TG) {
-        int c[TG];
+  int cnt = 0;
+  if (s < S) {
+    // exclusive prefix over the tiles, in place; loads in groups of TG so
+    // that a group costs one memory round trip
+    constexpr int TG = 8;
+    for (int t0 = 0; t0 < a.ntiles; t0 += TG) {
+      int c[TG];
 #pragma unroll
-        for (int u = 0; u < TG; ++u)
-          c[u] = (t0 + u < a.ntiles) ? th[(int64_t)(t0 + u) * S + s] : 0;
+      for (int u = 0; u < TG; ++u)
+        c[u] = (t0 + u < a.ntiles) ? th[(int64_t)(t0 + u) * S + s] : 0;
 #pragma unroll
-        for (int u = 0; u < TG; ++u) {
-          if (t0 + u < a.ntiles) th[(int64_t)(t0 + u) * S + s] = cnt;
-          cnt += c[u];
-        }
+      for (int u = 0; u < TG; ++u) {
+        if (t0 + u < a.ntiles) th[(int64_t)(t0 + u) * S + s] = cnt;
+        cnt += c[u];
       }
     }
-    const int incl = wave_incl_scan(cnt);
-    if (lane_id() == WAVE - 1) wave_tot[tid / WAVE] = incl;
-    __syncthreads();
-    int before = carry;
-    int all = 0;
-    for (int w = 0; w < 16; ++w) {
-      const int wt = wave_tot[w];
-      if (w < tid / WAVE) before += wt;
-      all += wt;
-    }
-    if (s < S) {
-      a.seg_offset[(int64_t)bh * S + s] = (int32_t)(base + before + incl - cnt);
-      if (cnt > LONG_EVENTS) {
-        const int q = cnt / (LONG_EVENTS + 1);            // >= 1
-        const int cls = min(NBIN - 1, 31 - __clz(q));
-        a.long_list[(int64_t)cls * a.long_cap + atomicAdd(&a.long_count[cls], 1)] =
-            (int32_t)((int64_t)bh * S + s);
-      }
-    }
-    carry += all;
-    __syncthreads();
   }
-  if (bh == a.B * a.H - 1 && tid == 0)
+  const int incl = wave_incl_scan(cnt);
+  if (lane_id() == WAVE - 1) wave_tot[tid / WAVE] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int wt = wave_tot[w];
+    if (w < tid / WAVE) before += wt;
+    all += wt;
+  }
+  // long segments: a place in the block's share of their class, then one
+  // global counter update per class and block (hot slots make the global
+  // counters contended)
+  const bool lng = s < S && cnt > LONG_EVENTS;
+  const int cls = lng ? min(NBIN - 1, 31 - __clz(cnt / (LONG_EVENTS + 1))) : 0;
+  const int rank = lng ? atomicAdd(&cls_n[cls], 1) : 0;
+  if (s < S) {
+    if (a.ntiles > 0) th[s] = before + incl - cnt;   // offset inside the block
+    else a.seg_offset[(int64_t)bh * S + s] = (int32_t)a.ev_base;   // no events at all
+  }
+  __syncthreads();
+  if (tid < NBIN && cls_n[tid] > 0) cls_at[tid] = atomicAdd(&a.long_count[tid], cls_n[tid]);
+  __syncthreads();
+  if (lng) a.long_list[(int64_t)cls * a.long_cap + cls_at[cls] + rank] = (int32_t)((int64_t)bh * S + s);
+  if (tid == 0) a.blk_tot[(int64_t)bh * a.nblk + blk] = all;
+  if (blk == 0 && bh == a.B * a.H - 1 && tid == 0)
     a.seg_offset[(int64_t)a.B * a.H * S] =
         (int32_t)(a.ev_base + (int64_t)a.B * a.H * a.T * (a.k_w + a.k_r));
 }
@@ -112,15 +118,24 @@ constexpr int SCATTER_THREADS = 256;
 
 template <typename IO>
 __global__ __launch_bounds__(SCATTER_THREADS) void bucket_scatter_kernel(BucketArgs a) {
-  extern __shared__ int next[];
+  extern __shared__ int next[];   // S write positions
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
   const int lane = lane_id();
   const int S = a.S;
-  const int32_t* th = a.tile_hist + ((int64_t)bh * a.ntiles + tile) * S;
-  const int32_t* so = a.seg_offset + (int64_t)bh * S;
+  const int32_t* th0 = a.tile_hist + (int64_t)bh * a.ntiles * S;   // offsets inside the blocks
+  const int32_t* th = th0 + (int64_t)tile * S;                       // tile prefixes
   const IO* gam = reinterpret_cast<const IO*>(a.gamma);
-  for (int s = threadIdx.x; s < S; s += SCATTER_THREADS) next[s] = so[s] + th[s];
+  int start = (int)(a.ev_base + (int64_t)bh * a.T * (a.k_w + a.k_r));   // of the block
+  for (int blk = 0; blk < a.nblk; ++blk) {
+    const int s1 = min(S, (blk + 1) * SCAN_SLOTS);
+    for (int s = blk * SCAN_SLOTS + (int)threadIdx.x; s < s1; s += SCATTER_THREADS) {
+      const int seg = start + th0[s];
+      next[s] = seg + (tile > 0 ? th[s] : 0);
+      if (tile == 0) a.seg_offset[(int64_t)bh * S + s] = seg;
+    }
+    start += a.blk_tot[(int64_t)bh * a.nblk + blk];
+  }
   __syncthreads();
   if (threadIdx.x >= WAVE) return;   // the ranking below is one wave's walk
   const int K = a.k_w + a.k_r;
@@ -180,7 +195,7 @@ hipError_t launch_bucket(const BucketArgs& a, bool bf16, hipStream_t st,
     after("bucket_hist", st);
   }
   before("bucket_scan", st);
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(BH), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(bucket_scan_kernel, dim3(a.nblk, BH), dim3(SCAN_SLOTS), 0, st, a);
   after("bucket_scan", st);
   if (a.ntiles > 0) {
     before("bucket_scatter", st);

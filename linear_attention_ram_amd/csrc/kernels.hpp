@@ -16,6 +16,7 @@ constexpr int LONG_WORDS = NBIN + 4;  // int32 words per long-segment list heade
                                       //   [0, NBIN)  entries per class
                                       //   NBIN, +1   forward scan: next ticket, finished workgroups
                                       //   NBIN+2, +3 reverse scan: the same
+constexpr int SCAN_SLOTS = 1024; // slots per workgroup of the bucketing scan
 constexpr int MAX_DV = 128;      // widest slot
 constexpr uint32_t MAX_BUF_BYTES = 0x7FE00000u;  // one batch's v, dO or stash rows (scans)
 
@@ -39,6 +40,8 @@ struct BucketArgs {
   int ntiles;             // ceil(T / tile)
   int nbits;              // bits needed for a slot index
   int32_t* tile_hist;     // (B*H, ntiles, S)
+  int32_t* blk_tot;       // (B*H, nblk): events of each block of SCAN_SLOTS slots
+  int nblk;               // ceil(S / SCAN_SLOTS)
   int32_t* seg_offset;    // (B*H*S + 1): absolute positions in `events`
   int64_t ev_base;        // position of these rows' first event (B counts the batches
                           // of this call's piece; events is the whole list)
