@@ -14,16 +14,17 @@
 //            order inside a class).  Every (b, h) holds exactly
 //            T*(k_w+k_r) events, so segment offsets need no scan across
 //            (b, h);
-//   scatter  one workgroup per (b, h, tile): all its waves set up the
-//            tile's per-slot write positions in LDS (the (b, h) base, the
-//            event counts of the earlier blocks, the offset inside the
-//            block and the tile prefix; the tile-0 workgroup also stores the
-//            segment offsets), then one wave walks the tile's events in order
-//            (t ascending, write side before read side), ranks equal slots
-//            inside each 64-event batch with ballots, and writes each event
-//            as a 16-byte record (code, weight, retention lambda and
-//            d lambda / d w of a write) to its final position, so the scans
-//            read their events with one coalesced load and gather nothing.
+//   scatter  one workgroup per (b, h, tile): its waves set up the tile's
+//            per-slot write positions in LDS (the (b, h) base, the event
+//            counts of the earlier blocks, the offset inside the block and
+//            the tile prefix; the tile-0 workgroup also stores the segment
+//            offsets).  The tile's events, in order (t ascending, write side
+//            before read side), are ranked among equal slots inside each
+//            64-event batch with ballots (all waves), given positions batch
+//            after batch (one wave), and written as 16-byte records (code,
+//            weight, retention lambda and d lambda / d w of a write) to their
+//            final positions (all waves), so the scans read their events
+//            with one coalesced load and gather nothing.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -115,71 +116,160 @@ __global__ __launch_bounds__(SCAN_SLOTS) void bucket_scan_kernel(BucketArgs a) {
 }
 
 constexpr int SCATTER_THREADS = 256;
+constexpr int SCATTER_CHUNK = 4096;   // events of a tile ranked per round (LDS)
+constexpr int SCATTER_PER = SCATTER_CHUNK / SCATTER_THREADS;   // events per thread and round
 
+// Slot of event e of a tile (-1 past the tile's events).
+__device__ __forceinline__ int tile_event_slot(const BucketArgs& a, int b, int h, int t_lo, int K,
+                                               int n, int e) {
+  if (e >= n) return -1;
+  const int t = t_lo + e / K, p = e % K;
+  const int64_t row = ((int64_t)b * a.T + t) * a.H + h;
+  return (p < a.k_w) ? a.idx_w[row * a.k_w + p] : a.idx_r[row * a.k_r + (p - a.k_w)];
+}
+
+// 16-byte record of event e (< n) of a tile.  A masked token keeps its
+// events with weight 0: an exact no-op write (retention 1, step 0) and a
+// read that contributes 0.
+template <typename IO>
+__device__ __forceinline__ EventRec tile_event_rec(const BucketArgs& a, int b, int h, int t_lo,
+                                                   int K, int e) {
+  const int t = t_lo + e / K, p = e % K;
+  const int64_t row = ((int64_t)b * a.T + t) * a.H + h;
+  const bool live = !a.mask || a.mask[(int64_t)b * a.T + t];
+  EventRec rec{0, 0.f, 1.f, 0.f};
+  if (p < a.k_w) {
+    rec.code = (t << 7) | p;
+    rec.w = live ? a.w_w[row * a.k_w + p] : 0.f;
+    if (live) rec.lam = retention(rec.w, to_f32(reinterpret_cast<const IO*>(a.gamma)[row]), &rec.dlam);
+  } else {
+    rec.code = (t << 7) | (1 << 6) | (p - a.k_w);
+    rec.w = live ? a.w_r[row * a.k_r + (p - a.k_w)] : 0.f;
+  }
+  return rec;
+}
+
+// Per tile, in rounds of SCATTER_CHUNK events:
+//   1. every wave ranks batches of 64 events: lanes with equal slots find
+//      each other with one ballot per slot bit, giving each event its rank
+//      among its batch's events of the same slot and their number;
+//   2. one wave takes the batches in order and turns (slot, rank) into a
+//      final position from the running per-slot counts in LDS;
+//   3. every wave writes the records of its batches to their positions.
+// Only step 2 is serial, and it is a few LDS operations per batch.
 template <typename IO>
 __global__ __launch_bounds__(SCATTER_THREADS) void bucket_scatter_kernel(BucketArgs a) {
-  extern __shared__ int next[];   // S write positions
+  extern __shared__ int lds[];
+  const int S = a.S;
+  int* next = lds;                                        // S write positions
+  uint32_t* ev = reinterpret_cast<uint32_t*>(lds + S);    // SCATTER_CHUNK per-event words
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
   const int lane = lane_id();
-  const int S = a.S;
+  const int wave = threadIdx.x / WAVE;
+  constexpr int NWAVES = SCATTER_THREADS / WAVE;
   const int32_t* th0 = a.tile_hist + (int64_t)bh * a.ntiles * S;   // offsets inside the blocks
   const int32_t* th = th0 + (int64_t)tile * S;                       // tile prefixes
-  const IO* gam = reinterpret_cast<const IO*>(a.gamma);
+  // event counts of the (at most 16) slot blocks, requested together
+  static_assert(16 * SCAN_SLOTS >= 16384, "S <= 16384 has at most 16 blocks");
+  int bt[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) bt[k] = k < a.nblk ? a.blk_tot[(int64_t)bh * a.nblk + k] : 0;
+  // per block, each thread's SCAN_SLOTS / SCATTER_THREADS slots, their loads
+  // requested together
+  constexpr int SPT = SCAN_SLOTS / SCATTER_THREADS;
+  static_assert(SPT * SCATTER_THREADS == SCAN_SLOTS, "whole slots per thread");
   int start = (int)(a.ev_base + (int64_t)bh * a.T * (a.k_w + a.k_r));   // of the block
-  for (int blk = 0; blk < a.nblk; ++blk) {
-    const int s1 = min(S, (blk + 1) * SCAN_SLOTS);
-    for (int s = blk * SCAN_SLOTS + (int)threadIdx.x; s < s1; s += SCATTER_THREADS) {
-      const int seg = start + th0[s];
-      next[s] = seg + (tile > 0 ? th[s] : 0);
-      if (tile == 0) a.seg_offset[(int64_t)bh * S + s] = seg;
+#pragma unroll
+  for (int blk = 0; blk < 16; ++blk) {
+    if (blk < a.nblk) {
+      int off[SPT], pre[SPT];
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) {
+        const int s = blk * SCAN_SLOTS + u * SCATTER_THREADS + (int)threadIdx.x;
+        off[u] = s < S ? th0[s] : 0;
+        pre[u] = (s < S && tile > 0) ? th[s] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) {
+        const int s = blk * SCAN_SLOTS + u * SCATTER_THREADS + (int)threadIdx.x;
+        if (s < S) {
+          const int seg = start + off[u];
+          next[s] = seg + pre[u];
+          if (tile == 0) a.seg_offset[(int64_t)bh * S + s] = seg;
+        }
+      }
     }
-    start += a.blk_tot[(int64_t)bh * a.nblk + blk];
+    start += bt[blk];
   }
-  __syncthreads();
-  if (threadIdx.x >= WAVE) return;   // the ranking below is one wave's walk
   const int K = a.k_w + a.k_r;
   const int t_lo = tile * a.tile;
   const int t_hi = min(a.T, t_lo + a.tile);
   const int n = (t_hi - t_lo) * K;
   const uint64_t lt = lanemask_lt();
-  for (int e0 = 0; e0 < n; e0 += WAVE) {
-    const int e = e0 + lane;
-    bool valid = e < n;
-    int slot = 0;
-    EventRec rec{0, 0.f, 1.f, 0.f};
-    if (valid) {
-      const int t = t_lo + e / K, p = e % K;
-      const int64_t row = ((int64_t)b * a.T + t) * a.H + h;
-      // a masked token keeps its events with weight 0: an exact no-op write
-      // (retention 1, step 0) and a read that contributes 0
-      const bool live = !a.mask || a.mask[(int64_t)b * a.T + t];
-      if (p < a.k_w) {
-        slot = a.idx_w[row * a.k_w + p];
-        rec.code = (t << 7) | p;
-        rec.w = live ? a.w_w[row * a.k_w + p] : 0.f;
-        rec.lam = live ? retention(rec.w, to_f32(gam[row]), &rec.dlam) : 1.f;
-        if (!live) rec.dlam = 0.f;
-      } else {
-        slot = a.idx_r[row * a.k_r + (p - a.k_w)];
-        rec.code = (t << 7) | (1 << 6) | (p - a.k_w);
-        rec.w = live ? a.w_r[row * a.k_r + (p - a.k_w)] : 0.f;
+  constexpr uint32_t NONE = 0xFFFFFFFFu;
+  for (int c0 = 0; c0 < n; c0 += SCATTER_CHUNK) {
+    const int cn = min(SCATTER_CHUNK, n - c0);
+    // 1. slot | rank << 14 | count << 21 of every event (slots < 2^14, ranks
+    //    and counts <= 64); the wave's batches are e0 = (j * NWAVES + wave) *
+    //    WAVE, their slots all requested before the first is ranked
+    constexpr int NB = SCATTER_CHUNK / (NWAVES * WAVE);
+    int sl[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      sl[j] = tile_event_slot(a, b, h, t_lo, K, c0 + cn, c0 + (j * NWAVES + wave) * WAVE + lane);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int e0 = (j * NWAVES + wave) * WAVE;
+      if (e0 < cn) {
+        const int slot = sl[j];
+        const bool valid = e0 + lane < cn && (unsigned)slot < (unsigned)S;
+        uint64_t peers = __ballot(valid);
+        for (int bit = 0; bit < a.nbits; ++bit) {
+          const bool one = (slot >> bit) & 1;
+          const uint64_t bal = __ballot(valid && one);
+          peers &= one ? bal : ~bal;
+        }
+        const uint32_t rank = (uint32_t)__popcll(peers & lt);
+        const uint32_t tot = (uint32_t)__popcll(peers);
+        if (e0 + lane < cn) ev[e0 + lane] = valid ? ((uint32_t)slot | rank << 14 | tot << 21) : NONE;
       }
-      valid = (unsigned)slot < (unsigned)S;   // decoded slots are always < S
     }
-    uint64_t peers = __ballot(valid);
-    for (int bit = 0; bit < a.nbits; ++bit) {
-      const bool one = (slot >> bit) & 1;
-      const uint64_t bal = __ballot(valid && one);
-      peers &= one ? bal : ~bal;
+    __syncthreads();   // (also orders the initial positions before the first round)
+    // 2. positions, batch after batch
+    if (wave == 0) {
+      for (int e0 = 0; e0 < cn; e0 += WAVE) {
+        const bool in = e0 + lane < cn;
+        const uint32_t q = in ? ev[e0 + lane] : NONE;
+        const bool valid = q != NONE;
+        const int slot = (int)(q & 0x3FFFu);
+        const int rank = (int)((q >> 14) & 0x7Fu), tot = (int)((q >> 21) & 0x7Fu);
+        const int base = valid ? next[slot] : 0;
+        wave_sync();
+        if (valid && rank == 0) next[slot] = base + tot;
+        wave_sync();
+        if (in) ev[e0 + lane] = valid ? (uint32_t)(base + rank) : NONE;
+      }
     }
-    const int rank = __popcll(peers & lt);
-    const int tot = __popcll(peers);
-    const int base = valid ? next[slot] : 0;
-    wave_sync();
-    if (valid && rank == 0) next[slot] = base + tot;
-    wave_sync();
-    if (valid) a.events[base + rank] = rec;
+    __syncthreads();
+    // 3. records, in groups of REC_GROUP per thread whose inputs are all
+    //    requested before the first record is formed
+    constexpr int REC_GROUP = 8;
+    static_assert(SCATTER_PER % REC_GROUP == 0, "whole groups");
+    for (int j0 = 0; j0 < SCATTER_PER; j0 += REC_GROUP) {
+      uint32_t pos[REC_GROUP];
+      EventRec rec[REC_GROUP];
+#pragma unroll
+      for (int j = 0; j < REC_GROUP; ++j) {
+        const int e = (j0 + j) * SCATTER_THREADS + (int)threadIdx.x;
+        pos[j] = e < cn ? ev[e] : NONE;
+        if (pos[j] != NONE) rec[j] = tile_event_rec<IO>(a, b, h, t_lo, K, c0 + e);
+      }
+#pragma unroll
+      for (int j = 0; j < REC_GROUP; ++j)
+        if (pos[j] != NONE) a.events[pos[j]] = rec[j];
+    }
+    __syncthreads();   // ev is rewritten by the next round
   }
 }
 
@@ -200,8 +290,10 @@ hipError_t launch_bucket(const BucketArgs& a, bool bf16, hipStream_t st,
   if (a.ntiles > 0) {
     before("bucket_scatter", st);
     const dim3 grid(a.ntiles, BH), block(SCATTER_THREADS);
-    if (bf16) hipLaunchKernelGGL(bucket_scatter_kernel<bf16_t>, grid, block, lds, st, a);
-    else hipLaunchKernelGGL(bucket_scatter_kernel<float>, grid, block, lds, st, a);
+    const int64_t n = (int64_t)a.tile * (a.k_w + a.k_r);
+    const size_t slds = lds + sizeof(uint32_t) * (size_t)(n < SCATTER_CHUNK ? n : SCATTER_CHUNK);
+    if (bf16) hipLaunchKernelGGL(bucket_scatter_kernel<bf16_t>, grid, block, slds, st, a);
+    else hipLaunchKernelGGL(bucket_scatter_kernel<float>, grid, block, slds, st, a);
     after("bucket_scatter", st);
   }
   return hipGetLastError();
