@@ -126,3 +126,11 @@ def test_backward_repeats_on_the_same_workspace(hot):
         assert torch.equal(g2[name], g1[name]), name
         assert torch.equal(g3[name], g1[name]), name
     assert torch.equal(r2["o"], r["o"])
+
+
+def test_hot_slots_over_ragged_slot_blocks():
+    # as the forward case: a partial last 1024-slot block of the bucketing
+    # scan and hot slots on the cooperative reverse path
+    cfg = synth.Config("hot-ragged", 2, 2, 1024, 2504, 8, 8, 64, "bf16", zipf=1.1)
+    x = synth.layer_inputs(cfg, device=DEV, seed=41, with_state=True, with_state_grads=True)
+    full_check(cfg, x, gpu_problem(cfg), True, True, TOL["bf16"])

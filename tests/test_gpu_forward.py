@@ -192,3 +192,16 @@ def test_untouched_slots_bitwise_and_overwrite_limit():
     assert (~touched).sum() > 0
     np.testing.assert_array_equal(host(r["slot1"])[~touched], h["slot0"][~touched])
     assert rel(host(r["o"]), oo) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("S", [1504, 2504])   # rows of whole 16-byte vectors
+def test_hot_slots_over_ragged_slot_blocks(S):
+    # the bucketing scan works in blocks of 1024 slots: S here leaves a
+    # partial last block, and the Zipf bias makes hot slots whose segments
+    # (thousands of events) take the cooperative scan path
+    cfg = synth.Config("hot-ragged", 2, 2, 1024, S, 8, 8, 64, "bf16", zipf=1.1)
+    x = synth.layer_inputs(cfg, device=DEV, seed=40 + S, with_state=True, with_d_o=False)
+    p = gpu_problem(cfg)
+    r = full_check(cfg, x, p, True, TOL["bf16"])
+    seg = ram.ws_views(p, r["ws"])["seg_offset"].cpu().numpy()
+    assert (seg[1:] - seg[:-1]).max() > 1000
