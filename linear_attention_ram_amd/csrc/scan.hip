@@ -672,7 +672,7 @@ struct BwdChunk {
   float rr;                        // read weight, 0 for writes and padding
   uint32_t sw;                     // stash offset of a write's dv row, else OOB
   uint32_t wm, rm;                 // bit i: event i is a write / a read (wave-uniform)
-  float den;                       // m' + eps: mass after the event plus eps
+  float rden;                      // 1 / (m' + eps): mass after the event plus eps
   float gq;                        // w / (m' + eps)^2 of a write, else 0
   typename Lanes<IO, CPL>::Raw x[CHUNK];
   float so_reg[SO_LDS ? 1 : CHUNK][CPL];
@@ -735,8 +735,11 @@ __device__ __forceinline__ void bwd_prepare(const ScanBwdArgs& a, const SegCtx<I
   ck.sw = (ev.valid && ev.side == 0) ? ((uint32_t)ev.rb * a.k_w + ev.j) * c.pitch : OOB;
   ck.wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
   ck.rm = (uint32_t)__ballot(ev.valid && ev.side == 1) & 0xFFFFu;
-  ck.den = ck.M.mi + a.eps;
-  ck.gq = (ev.valid && ev.side == 0 && ev.wt > 0.f) ? ev.wt / (ck.den * ck.den) : 0.f;
+  // the gradient scalars divide by m' + eps through its reciprocal (the
+  // hardware instruction, within 1 ulp); eta keeps the exact quotient the
+  // forward used, so the replay reproduces the forward's contents
+  ck.rden = __builtin_amdgcn_rcpf(ck.M.mi + a.eps);
+  ck.gq = (ev.valid && ev.side == 0 && ev.wt > 0.f) ? ck.M.eta * ck.rden : 0.f;
 }
 
 template <typename IO, int CPL, bool SO>
@@ -832,7 +835,6 @@ __device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const SegCtx<I
   const int lane = lane_id();
   const Ev& ev = ck.ev;
   const bool wr = ev.valid && ev.side == 0;
-  const float den = ck.den;
   const float g = ck.gq;
   const float deta = wr ? red : 0.f;
   float A = wr ? ev.lam : 1.f;
@@ -844,7 +846,7 @@ __device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const SegCtx<I
   if (lane < CHUNK) {
     if (wr) {
       const float M = after - g * deta;
-      const float dwi = ((ev.wt > 0.f) ? deta / den : 0.f) + M + M * ck.M.mo * ev.dl;
+      const float dwi = ((ev.wt > 0.f) ? deta * ck.rden : 0.f) + M + M * ck.M.mo * ev.dl;
       const float dgi = M * ck.M.mo * (-ev.lam * (1.f - ev.lam));
       const int64_t o = row * a.k_w + ev.j;
       a.dw[o] = dwi;
