@@ -174,7 +174,11 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
  * d_o: gradient of o; d_slot1 / d_mass1: gradients of the final state, NULL
  * for zero.  Writes d_wlogits, d_rlogits (B,T,H,U,P) io, d_v (B,T,H,d_v) io,
  * d_gamma (B,T,H) io, and, when non-NULL, d_slot0 (B,H,S,d_v) / d_mass0
- * (B,H,S) float.  ws must have been sized with with_backward = 1. */
+ * (B,H,S) float.  ws must have been sized with with_backward = 1.  The
+ * backward keeps its own scratch and work counters in ws, which it leaves
+ * as it found them: several ram_backward calls after one ram_forward each
+ * give the same result, but calls that share one workspace must not overlap
+ * on the device (order them on one stream). */
 int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wlogits,
                  const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
                  const float* slot0, const float* mass0, const void* d_o, const float* d_slot1,
