@@ -243,7 +243,9 @@ __device__ __forceinline__ Ev decode_rec(float4 raw, int n, int h, int H) {
 template <int O>
 __device__ __forceinline__ void affine_step(float& A, float& B) {
   const float Ap = dpp_or<DppShr<O>::v>(1.f, A);
-  const float Bp = dpp_or<DppShr<O>::v>(0.f, B);
+  // B's identity is 0, which the zero-filling move gives for free (it then
+  // folds into the fma as a DPP operand)
+  const float Bp = dpp<DppShr<O>::v>(B);
   B = fmaf(A, Bp, B);
   A = A * Ap;
 }
@@ -260,7 +262,7 @@ __device__ __forceinline__ void affine_scan(float& A, float& B) {
 template <int O>
 __device__ __forceinline__ void affine_suffix_step(float& A, float& B) {
   const float An = dpp_or<DppShl<O>::v>(1.f, A);
-  const float Bn = dpp_or<DppShl<O>::v>(0.f, B);
+  const float Bn = dpp<DppShl<O>::v>(B);
   B = fmaf(A, Bn, B);
   A = A * An;
 }
