@@ -134,3 +134,9 @@ def test_hot_slots_over_ragged_slot_blocks():
     cfg = synth.Config("hot-ragged", 2, 2, 1024, 2504, 8, 8, 64, "bf16", zipf=1.1)
     x = synth.layer_inputs(cfg, device=DEV, seed=41, with_state=True, with_state_grads=True)
     full_check(cfg, x, gpu_problem(cfg), True, True, TOL["bf16"])
+
+
+def test_widest_address_space():
+    cfg = synth.Config("widest", 1, 2, 512, 16384, 8, 8, 64, "bf16", zipf=1.1)
+    x = synth.layer_inputs(cfg, device=DEV, seed=45, with_state=True, with_state_grads=True)
+    full_check(cfg, x, gpu_problem(cfg), True, True, TOL["bf16"])

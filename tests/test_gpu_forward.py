@@ -205,3 +205,11 @@ def test_hot_slots_over_ragged_slot_blocks(S):
     r = full_check(cfg, x, p, True, TOL["bf16"])
     seg = ram.ws_views(p, r["ws"])["seg_offset"].cpu().numpy()
     assert (seg[1:] - seg[:-1]).max() > 1000
+
+
+def test_widest_address_space():
+    # S = 16384, the largest flat address space: 16 blocks in the bucketing
+    # scan and the largest LDS tables of the bucketing scatter
+    cfg = synth.Config("widest", 1, 2, 512, 16384, 8, 8, 64, "bf16", zipf=1.1)
+    x = synth.layer_inputs(cfg, device=DEV, seed=44, with_state=True, with_d_o=False)
+    full_check(cfg, x, gpu_problem(cfg), True, TOL["bf16"])
