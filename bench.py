@@ -292,9 +292,9 @@ def main():
                     help="decode: distinct pregenerated step inputs, cycled")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the core shards "
-                                   "over (batch, head) with no communication, and multi-GPU "
-                                   "runs are not part of this build", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark measures one GPU; the core shards over (batch, head) "
+                                   "with no communication between the shards, so N GPUs run N "
+                                   "independent copies of the one-GPU workload", "n_gpus": args.gpus}))
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
