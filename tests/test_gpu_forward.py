@@ -213,3 +213,12 @@ def test_widest_address_space():
     cfg = synth.Config("widest", 1, 2, 512, 16384, 8, 8, 64, "bf16", zipf=1.1)
     x = synth.layer_inputs(cfg, device=DEV, seed=44, with_state=True, with_d_o=False)
     full_check(cfg, x, gpu_problem(cfg), True, TOL["bf16"])
+
+
+def test_bucketing_in_several_rounds():
+    # 48 events per token: a bucketing tile of 128 tokens holds 6,144 events,
+    # more than one round (4,096) of the scatter's ranking
+    cfg = synth.Config("rounds", 1, 2, 300, 64, 24, 24, 16, "f32")
+    x = synth.layer_inputs(cfg, device=DEV, seed=46, with_state=True, with_d_o=False)
+    p = ram.problem(1, 2, 300, 64, 24, 24, 16, io="f32")
+    full_check(cfg, x, p, True, TOL["f32"])
