@@ -26,34 +26,64 @@ namespace ramk {
 // One wave per row; rows of side 0 first, then side 1.  The stored index is
 // the slot the token addresses (CAPE-shifted for CAPE heads).  NV > 0: rows of at
 // most NV * 64 vectors, held in registers; NV = 0: any length, streamed.
+// The results of the workgroup's rows are gathered in LDS and written as
+// contiguous pieces (k indices, k weights and one lse per row) with
+// streaming stores: small stores scattered through the read stream cost far
+// more HBM time than their bytes.
+constexpr int FWD_ROWS = 4;   // rows (waves) per decode_fwd workgroup
+
 template <typename IO, int NV, bool FULL = false>
-__global__ __launch_bounds__(256) void decode_fwd_kernel(DecodeFwdArgs a) {
-  __shared__ DecodeScratch scratch[4];
-  __shared__ int s_idx[4][MAX_K];
-  __shared__ float s_w[4][MAX_K];
+__global__ __launch_bounds__(FWD_ROWS * WAVE) void decode_fwd_kernel(DecodeFwdArgs a) {
+  __shared__ DecodeScratch scratch[FWD_ROWS];
+  __shared__ int s_idx[FWD_ROWS][MAX_K];
+  __shared__ float s_w[FWD_ROWS][MAX_K];
+  __shared__ float s_lse[FWD_ROWS];
   const int wv = threadIdx.x >> 6;
   const int lane = lane_id();
-  const int64_t grow = (int64_t)blockIdx.x * 4 + wv;
-  if (grow >= (int64_t)a.nsides * a.N) return;
+  const int64_t total = (int64_t)a.nsides * a.N;
+  const int64_t r0 = (int64_t)blockIdx.x * FWD_ROWS;
+  const int64_t grow = r0 + wv;
   const int side = grow >= a.N ? 1 : 0;   // nsides <= 2
   const int64_t row = grow - (int64_t)side * a.N;
-  const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
   const int k = a.k[side];
-  float lse;
-  if constexpr (NV > 0)
-    lse = decode_row_resident<IO, NV, FULL>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv],
-                                            s_w[wv]);
-  else
-    lse = decode_row_wave<IO>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
-  wave_sync();
-  if (lane < k) {
-    const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
-    const int id = s_idx[wv][lane];
-    a.idx[side][row * k + lane] = (shift < 0) ? id : (id + shift) % a.S;
-    a.w[side][row * k + lane] = s_w[wv][lane];
+  if (grow < total) {
+    const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
+    float lse;
+    if constexpr (NV > 0)
+      lse = decode_row_resident<IO, NV, FULL>(src, a.S, k, a.renorm[side], scratch[wv],
+                                              s_idx[wv], s_w[wv]);
+    else
+      lse = decode_row_wave<IO>(src, a.S, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
+    wave_sync();
+    if (lane < k) {
+      const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
+      const int id = s_idx[wv][lane];
+      s_idx[wv][lane] = (shift < 0) ? id : (id + shift) % a.S;
+    }
+    if (lane == 0) s_lse[wv] = lse;
   }
-  if (lane == 0) a.lse[side][row] = lse;
-  if (a.zero_rows && side == a.nsides - 1) {
+  __syncthreads();
+  const int side_last = r0 + FWD_ROWS - 1 >= a.N ? 1 : 0;
+  if (r0 + FWD_ROWS - 1 < total && side_last == (r0 >= a.N ? 1 : 0)) {
+    // all rows of one side: FWD_ROWS * k entries of idx and of w from row0 * k, FWD_ROWS of lse
+    const int sd = side_last;
+    const int kk = a.k[sd];
+    const int64_t row0 = r0 - (int64_t)sd * a.N;
+    for (int e = threadIdx.x; e < 2 * FWD_ROWS * kk; e += FWD_ROWS * WAVE) {
+      const int f = e < FWD_ROWS * kk ? e : e - FWD_ROWS * kk;
+      const int j = f / kk, c = f - j * kk;
+      if (e < FWD_ROWS * kk) __builtin_nontemporal_store(s_idx[j][c], a.idx[sd] + row0 * kk + f);
+      else __builtin_nontemporal_store(s_w[j][c], a.w[sd] + row0 * kk + f);
+    }
+    if (threadIdx.x < FWD_ROWS) __builtin_nontemporal_store(s_lse[threadIdx.x], a.lse[sd] + row0 + threadIdx.x);
+  } else if (grow < total) {
+    if (lane < k) {
+      a.idx[side][row * k + lane] = s_idx[wv][lane];
+      a.w[side][row * k + lane] = s_w[wv][lane];
+    }
+    if (lane == 0) a.lse[side][row] = s_lse[wv];
+  }
+  if (grow < total && a.zero_rows && side == a.nsides - 1) {
     float* z = a.zero_rows + row * (int64_t)a.zero_width;
     for (int c = lane; c < a.zero_width; c += WAVE) z[c] = 0.f;
   }
@@ -261,12 +291,13 @@ __global__ __launch_bounds__(256) void decode_bwd_prod_kernel(DecodeBwdArgs a) {
 hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st) {
   const int64_t rows = (int64_t)a.nsides * a.N;
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   if (a.U > 1) {
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     if (bf16) hipLaunchKernelGGL(decode_fwd_prod_kernel<bf16_t>, grid, block, 0, st, a);
     else hipLaunchKernelGGL(decode_fwd_prod_kernel<float>, grid, block, 0, st, a);
     return hipGetLastError();
   }
+  const dim3 grid((unsigned)((rows + FWD_ROWS - 1) / FWD_ROWS)), block(FWD_ROWS * WAVE);
   const int nvec = a.S / (bf16 ? 8 : 4);
   if (bf16) {
     if (nvec == 512) hipLaunchKernelGGL((decode_fwd_kernel<bf16_t, 8, true>), grid, block, 0, st, a);
