@@ -710,17 +710,24 @@ struct BwdChunk {
 // Row gathers of a chunk: the v row of each write and the dO row of each read.
 // The kind of event i is the same in every lane, so its one load takes the
 // buffer of its kind (a scalar select); padding loads nothing.
-template <typename IO, int CPL, bool SO>
-__device__ __forceinline__ void bwd_gather(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
-                                           rsrc_t rv, rsrc_t ro, BwdChunk<IO, CPL, SO>& ck,
-                                           float4 rec, int n) {
+template <typename IO, int CPL>
+__device__ __forceinline__ void bwd_gather_rows(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                                rsrc_t rv, rsrc_t ro,
+                                                typename Lanes<IO, CPL>::Raw (&x)[CHUNK],
+                                                float4 rec, int n) {
   using LN = Lanes<IO, CPL>;
   const Ev ev = decode_rec(rec, n, c.h, a.H);
   const uint32_t xo = ev.valid ? (uint32_t)ev.rb * c.pitch : OOB;
   const uint32_t wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
   for_up<0, CHUNK>([&](auto I) {
-    ck.x[I] = LN::load(((wm >> I) & 1u) ? rv : ro, bcu<I>(xo) + c.lb);
+    x[I] = LN::load(((wm >> I) & 1u) ? rv : ro, bcu<I>(xo) + c.lb);
   });
+}
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ void bwd_gather(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                           rsrc_t rv, rsrc_t ro, BwdChunk<IO, CPL, SO>& ck,
+                                           float4 rec, int n) {
+  bwd_gather_rows<IO, CPL>(a, c, rv, ro, ck.x, rec, n);
 }
 
 // Scalars of a chunk whose rows are gathered: event fields, masses and step
@@ -1006,10 +1013,10 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
       n = chunk_start(beg, k + 1, end) - cs;
     }
   };
-  // The rows and the start state of a chunk are requested as soon as the
-  // previous chunk of this wave no longer needs its registers (after its
-  // reverse walk), so the loads overlap the closing barriers; they are
-  // carried into the next iteration as loaded and used there.
+  // The rows and the start state of a wave's next chunk are requested at the
+  // start of the current chunk's work, into a second set of registers, so
+  // that the loads are in flight during the whole iteration.
+  typename LN::Raw xn[CHUNK];
   float4 rec, rec_next;
   ChunkStart<CPL> st;
   int cs, n;
@@ -1021,16 +1028,30 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
     chunk_of(max(u_first - NW, 0) + w, csp, np);
     rec_next = load_rec(a.events, csp, np, beg, end);
     chunk_state_load<IO, CPL>(a, c, g, beg, cs, st);
-    bwd_gather(a, c, rv, ro, ck, rec, n);
+    bwd_gather_rows<IO, CPL>(a, c, rv, ro, xn, rec, n);
   }
   for (int u0 = ((nchunks - 1) / NW) * NW; u0 >= 0; u0 -= NW) {
-    // this chunk's rows and start state, requested before the previous
-    // chunk's closing barriers, are in by now; once they are known to be
-    // done the event loops' stores never wait
+    // this chunk's rows and start state, requested at the start of the
+    // previous iteration, are in by now; once they are known to be done the
+    // event loops' stores never wait
     wait_vmem();
+    for_up<0, CHUNK>([&](auto I) { ck.x[I] = xn[I]; });
     float s[CPL], m;
     chunk_state_take(c, st, s, m);
     bwd_prepare(a, c, ck, rec, n, m);
+    // next chunk of this wave: rows, start state and the record after it
+    // (unconditional: past the segment's start the chunk is empty)
+    int csn, nn;
+    chunk_of(max(u0 - NW, 0) + w, csn, nn);
+    if (u0 < NW) { csn = end; nn = 0; }
+    const float4 rec_n = rec_next;
+    {
+      int csp, np;
+      chunk_of(max(u0 - 2 * NW, 0) + w, csp, np);
+      rec_next = load_rec(a.events, csp, np, beg, end);
+    }
+    chunk_state_load<IO, CPL>(a, c, g, beg, csn, st);
+    bwd_gather_rows<IO, CPL>(a, c, rv, ro, xn, rec_n, nn);
     bwd_replay(ck, s, pr);
     const Ev& ev = ck.ev;
     // adjoint map of the chunk: a reverse walk from zero.  coef_i is the
@@ -1113,20 +1134,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
     for (int kk = NW - 1; kk > w; --kk) mh = fmaf(mL[kk], mh, mD[kk] + mK[kk]);
     // exact reverse step of this wave's chunk
     bwd_walk(ck, c, rs, sh, pr, pw);
-    // next chunk of this wave: rows, start state and the record after it
-    // (unconditional: past the segment's start the chunk is empty)
-    int csn, nn;
-    chunk_of(max(u0 - NW, 0) + w, csn, nn);
-    if (u0 < NW) { csn = end; nn = 0; }
-    const float4 rec_n = rec_next;
-    {
-      int csp, np;
-      chunk_of(max(u0 - 2 * NW, 0) + w, csp, np);
-      rec_next = load_rec(a.events, csp, np, beg, end);
-    }
     bwd_scalars(a, c, ck, batched_sum(pw), mh);   // deta of the writes, dr of the reads
-    chunk_state_load<IO, CPL>(a, c, g, beg, csn, st);
-    bwd_gather(a, c, rv, ro, ck, rec_n, nn);
     if (w == 0) {
       if (c.active) {
 #pragma unroll
@@ -1161,8 +1169,10 @@ __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_bwd_short_kernel(Scan
   scan_bwd_short<IO, CPL>(a, g);
 }
 
+// At most 128 registers, so that 4 workgroups fit on a CU (the rows of the
+// next chunk held in flight take 16 of them).
 template <typename IO, int CPL>
-__global__ __launch_bounds__(NWL * WAVE) void scan_bwd_long_kernel(ScanBwdArgs a) {
+__global__ __launch_bounds__(NWL * WAVE, 4) void scan_bwd_long_kernel(ScanBwdArgs a) {
   const LongCounts L = long_counts(a.long_count);
   for (int i = take_ticket(a.queue); i < L.total; i = take_ticket(a.queue))
     scan_bwd_long<IO, CPL>(a, long_entry(a.long_list, L, a.long_cap, i));
