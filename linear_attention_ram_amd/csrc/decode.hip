@@ -26,14 +26,17 @@ namespace ramk {
 // One wave per row; rows of side 0 first, then side 1.  The stored index is
 // the slot the token addresses (CAPE-shifted for CAPE heads).  NV > 0: rows of at
 // most NV * 64 vectors, held in registers; NV = 0: any length, streamed.
-// The results of the workgroup's rows are gathered in LDS and written as
-// contiguous pieces (k indices, k weights and one lse per row) with
-// streaming stores: small stores scattered through the read stream cost far
-// more HBM time than their bytes.
+// For rows of up to 16 KiB the results of the workgroup's rows are gathered
+// in LDS and written as contiguous pieces (k indices, k weights and one lse
+// per row) with streaming stores: small stores scattered through the read
+// stream cost far more HBM time than their bytes.
 constexpr int FWD_ROWS = 4;   // rows (waves) per decode_fwd workgroup
 
 template <typename IO, int NV, bool FULL = false>
 __global__ __launch_bounds__(FWD_ROWS * WAVE) void decode_fwd_kernel(DecodeFwdArgs a) {
+  // rows of up to 16 KiB: their results are a large enough share of the
+  // traffic to be worth the workgroup barrier
+  constexpr bool STAGED = NV > 0 && NV <= 16;
   __shared__ DecodeScratch scratch[FWD_ROWS];
   __shared__ int s_idx[FWD_ROWS][MAX_K];
   __shared__ float s_w[FWD_ROWS][MAX_K];
@@ -62,9 +65,10 @@ __global__ __launch_bounds__(FWD_ROWS * WAVE) void decode_fwd_kernel(DecodeFwdAr
     }
     if (lane == 0) s_lse[wv] = lse;
   }
-  __syncthreads();
+  if constexpr (STAGED) __syncthreads();
+  else wave_sync();
   const int side_last = r0 + FWD_ROWS - 1 >= a.N ? 1 : 0;
-  if (r0 + FWD_ROWS - 1 < total && side_last == (r0 >= a.N ? 1 : 0)) {
+  if (STAGED && r0 + FWD_ROWS - 1 < total && side_last == (r0 >= a.N ? 1 : 0)) {
     // all rows of one side: FWD_ROWS * k entries of idx and of w from row0 * k, FWD_ROWS of lse
     const int sd = side_last;
     const int kk = a.k[sd];
