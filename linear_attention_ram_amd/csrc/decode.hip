@@ -87,10 +87,6 @@ __global__ __launch_bounds__(FWD_ROWS * WAVE) void decode_fwd_kernel(DecodeFwdAr
     }
     if (lane == 0) a.lse[side][row] = s_lse[wv];
   }
-  if (grow < total && a.zero_rows && side == a.nsides - 1) {
-    float* z = a.zero_rows + row * (int64_t)a.zero_width;
-    for (int c = lane; c < a.zero_width; c += WAVE) z[c] = 0.f;
-  }
 }
 
 // Decode backward (one wave per row): with g_j the gradient of the j-th
@@ -204,10 +200,6 @@ __global__ __launch_bounds__(256) void decode_fwd_prod_kernel(DecodeFwdArgs a) {
     a.w[side][row * k + lane] = s_w[wv][lane];
   }
   if (lane < a.U) a.lse[side][row * a.U + lane] = scratch[wv].dlse[lane];
-  if (a.zero_rows && side == a.nsides - 1) {
-    float* z = a.zero_rows + row * (int64_t)a.zero_width;
-    for (int c = lane; c < a.zero_width; c += WAVE) z[c] = 0.f;
-  }
 }
 
 // Decode backward of product rows (one wave per row): with gw_j as for one

@@ -32,8 +32,6 @@ struct DecodeFwdArgs {
   int S;                   // slots, P^U
   int U, P;                // address digits and digit size
   int nsides;              // 1 or 2 (side 0 = first pointer set)
-  float* zero_rows;        // optional (N, zero_width) float rows to clear
-  int zero_width;
   int H, T;                // row r is token (r / H) % T of head r % H
   int cape_heads;          // heads h < cape_heads shift the chosen slot by (t0 + t) mod S
   int64_t t0;              // reduced mod S
