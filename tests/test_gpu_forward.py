@@ -222,3 +222,14 @@ def test_bucketing_in_several_rounds():
     x = synth.layer_inputs(cfg, device=DEV, seed=46, with_state=True, with_d_o=False)
     p = ram.problem(1, 2, 300, 64, 24, 24, 16, io="f32")
     full_check(cfg, x, p, True, TOL["f32"])
+
+
+@pytest.mark.parametrize("S", [4096, 16384])
+def test_decoder_rows_across_the_side_boundary(S):
+    # 111 (token, head) rows per side and k_w != k_r: the decoder workgroup of
+    # rows 108..111 holds three write-side rows and the first read-side row.
+    # S = 4096 takes the register-resident decoder whose workgroups gather
+    # their results in LDS, S = 16384 the one whose waves store their own rows.
+    cfg = synth.Config("sides", 1, 3, 37, S, 8, 5, 32, "bf16")
+    x = synth.layer_inputs(cfg, device=DEV, seed=48, with_state=False, with_d_o=False)
+    full_check(cfg, x, gpu_problem(cfg), False, TOL["bf16"])
