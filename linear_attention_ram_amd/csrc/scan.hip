@@ -1226,10 +1226,11 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
 
 namespace {
 // Long-kernel workgroups per CU at most.  The long kernel pulls work until
-// its queue is empty, so the wave slots it leaves free are the ones the
-// short-segment kernel beside it runs in.  Measured on the 1.3B-layer
-// shape: 3 for the forward (its waves are light enough for 8 per CU), 4 for
-// the reverse (which its LDS allows at most).
+// its queue is empty, so the wave slots and registers it leaves free are the
+// ones the short-segment kernel beside it runs in.  Measured on the
+// 1.3B-layer shape: 3 for the forward (2, 4 and 6 are slower), 4 for the
+// reverse (its LDS allows no more; at 128 registers its 4 workgroups then
+// hold all of a CU's registers until their queue runs dry, and 3 is slower).
 constexpr int LONG_GROUPS_FWD = 3;
 constexpr int LONG_GROUPS_BWD = 4;
 
