@@ -284,6 +284,16 @@ __device__ __forceinline__ float suffix_prod(float A) {
   return A;
 }
 
+// Inclusive prefix product across the 16 lanes of each row (lane i ends with
+// x_0 * x_1 * ... * x_i).
+__device__ __forceinline__ float prefix_prod(float A) {
+  A = A * dpp_or<DppShr<1>::v>(1.f, A);
+  A = A * dpp_or<DppShr<2>::v>(1.f, A);
+  A = A * dpp_or<DppShr<4>::v>(1.f, A);
+  A = A * dpp_or<DppShr<8>::v>(1.f, A);
+  return A;
+}
+
 // Product of x over the 16 lanes of each row (every lane gets it).
 __device__ __forceinline__ float row_prod(float x) {
   x *= dpp<DPP_XOR1>(x);
@@ -553,23 +563,27 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
       m_next = fmaf(mapA[k], m_next, mapB[k]);
     }
     mass_apply(M, ev, m_in, a.eps);
-    // content map of the chunk from a zero start, s -> P*s + sz; only later
-    // waves fold it, so the last wave forms none
+    // the chunk from a zero content: sz after each event (kept at every
+    // event for the reads) and the chunk's map s -> P*s + sz, which the
+    // later waves fold
+    float sz[CPL], szr[CHUNK][CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) sz[k] = 0.f;
+    for_up<0, CHUNK>([&](auto I) {
+      if ((wm >> I) & 1u) {
+        float xf[CPL];
+        LN::get(x[I], xf);
+        const float e = bc<I>(M.eta), om = bc<I>(M.keep);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) sz[k] = fmaf(om, sz[k], e * xf[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) szr[I][k] = sz[k];
+      sched_fence<I>();
+    });
+    const float Pi = prefix_prod(M.keep);   // lane i: product of (1 - eta) over events 0..i
+    const float P = bc<15>(Pi);
     if (w != NW - 1) {
-      float sz[CPL];
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) sz[k] = 0.f;
-      for_up<0, CHUNK>([&](auto I) {
-        if ((wm >> I) & 1u) {
-          float xf[CPL];
-          LN::get(x[I], xf);
-          const float e = bc<I>(M.eta), om = bc<I>(M.keep);
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) sz[k] = fmaf(om, sz[k], e * xf[k]);
-        }
-        sched_fence<I>();
-      });
-      const float P = row_prod(M.keep);
       if (c.active) {
 #pragma unroll
         for (int k = 0; k < CPL; ++k) mapb[w][c.c0 + k] = sz[k];
@@ -596,18 +610,28 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
       }
       if (lane == 0) a.ckpt_m[cs / CHUNK] = m_in;
     }
-    // replay from the true start state; reads store their contributions
-    fwd_replay<IO, CPL>(x, M, rr, so, wm, rm, rs, c.lb, s);
+    // each read sees P_i * s + sz_i (a read's own factor is 1) and stores
+    // r times it to its stash row
+    for_up<0, CHUNK>([&](auto I) {
+      if ((rm >> I) & 1u) {
+        const float r = bc<I>(rr), pi = bc<I>(Pi);
+        float ctr[CPL];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) ctr[k] = r * fmaf(pi, s[k], szr[I][k]);
+        LN::store(rs, bcu<I>(so) + c.lb, ctr);
+      }
+      sched_fence<I>();
+    });
     {   // rows of this wave's next chunk (past the end: no valid event, no load)
       const int n_n = chunk_start(pn, w + 1, end) - chunk_start(pn, w, end);
       const Ev ev_n = decode_rec(rec, n_n, c.h, a.H);
       const uint32_t xo_n = (ev_n.valid && ev_n.side == 0) ? (uint32_t)ev_n.rb * c.pitch : OOB;
       for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo_n) + c.lb); });
     }
-    // the last wave's state after its replay is the carry into the next chunks
+    // the last wave's state after its chunk is the carry into the next chunks
     if (w == NW - 1 && c.active) {
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) carry_s[c.c0 + k] = s[k];
+      for (int k = 0; k < CPL; ++k) carry_s[c.c0 + k] = fmaf(P, s[k], sz[k]);
     }
     m_carry = m_next;
     p = pn;
