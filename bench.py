@@ -48,11 +48,11 @@ def algorithmic_bytes(cfg, b_io=2):
 
 def decode_bwd_bytes(cfg, b_io=2):
     """Algorithmic bytes of one decode_bwd launch (both sides): per row the
-    U * P logits read and as many gradients written, plus the U logsumexps
-    and k x (index, weight, weight gradient)."""
+    U * P logits read and as many gradients written.  The workspace it also
+    reads (the U logsumexps and k x (index, weight, weight gradient), 4U + 12k
+    bytes per row) is not algorithmic."""
     N = cfg.B * cfg.T * cfg.H
-    per_row = 2 * cfg.U * cfg.P * b_io + 4 * cfg.U + cfg.k_w * 12
-    return 2 * N * per_row
+    return 2 * N * 2 * cfg.U * cfg.P * b_io
 
 
 DECODE_SOURCES = ("linear_attention_ram_amd/csrc/decode.hip", "linear_attention_ram_amd/csrc/decode.hpp",
@@ -87,6 +87,17 @@ def measured_traffic():
         return None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, x, threads, budget_s=15.0):
     """Time the oracle's fwd+bwd on (b, h) slices of the workload, `threads`
     slices per call (one per OpenMP thread), until the budget is spent."""
@@ -114,6 +125,7 @@ def cpu_baseline(cfg, x, threads, budget_s=15.0):
         del h
     tokens = done * cfg.T / cfg.H          # a (b, h) slice is 1/H of T tokens' work
     return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"fwd+bwd of {done} of {cfg.B * cfg.H} (b,h) slices of the same workload "
                       f"(T={cfg.T} tokens each, = {tokens:.0f} tokens), {spent:.1f} s on "
                       f"{threads} host threads"}
@@ -391,7 +403,8 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes},
         "step_hbm": {"algorithmic_bytes": fwd_b + bwd_b, "achieved_GBps": step_gbs,
-                     "frac_of_peak": step_gbs / PEAK_HBM_GBS},
+                     "frac_of_peak": step_gbs / PEAK_HBM_GBS, "target_frac": 0.60,
+                     "meets_target": step_gbs / PEAK_HBM_GBS >= 0.60},
         "kernels": kernels,
     }
     if args.gated:
@@ -407,8 +420,14 @@ def main():
                 "frac": b / (prof[k][1] / prof[k][0] * 1e-3) / 1e9 / PEAK_HBM_GBS}
             for k, b in epi_b.items()}
     if not args.no_cpu_baseline and not args.gated:
-        threads = min(16, len(os.sched_getaffinity(0)))
+        # every core the process may run on, unless the box's share of the
+        # host (OMP_NUM_THREADS) is smaller
+        affinity = len(os.sched_getaffinity(0))
+        threads = affinity
+        if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+            threads = max(1, min(threads, int(os.environ["OMP_NUM_THREADS"])))
         out["cpu_baseline"] = cpu_baseline(cfg, x, threads, args.cpu_budget)
+        out["cpu_baseline"]["affinity_cores"] = affinity
     print(json.dumps(out))
 
 

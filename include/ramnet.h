@@ -122,13 +122,14 @@ typedef struct ram_ws_layout {
                          order inside a segment, a token's write before its read            */
   size_t ckpt_s;      /* float (E/16 + 1, d_v): slot content at every 16-aligned event        */
   size_t ckpt_m;      /* float (E/16 + 1): slot mass at the same points                      */
-  size_t stash;       /* io (N, max(k_w,k_r), d_v): per-(token, j) read / dv contributions      */
+  size_t stash;       /* io (N, k_r, d_v): read contributions r_j * s_t[a_j] of each (token, j) */
   size_t tile_hist;   /* int32: bucketing scratch                                              */
   size_t long_list;   /* int32: segments that take the cooperative scan path                   */
   size_t long_count;  /* int32: their number per length class, and the scans' work counters     */
-  size_t dw;          /* float (N, k_w): backward scratch                                      */
-  size_t dr;          /* float (N, k_r)                                                         */
-  size_t dgam;        /* float (N, k_w)                                                         */
+  size_t stash_b;     /* io (N, k_w, d_v): backward scratch, d_v contributions of each write     */
+  size_t dw;          /* float (N, k_w): gradient of each write weight                          */
+  size_t dr;          /* float (N, k_r): gradient of each read weight                           */
+  size_t dgam;        /* float (N, k_w): gamma gradient part of each write                      */
   size_t epi_d_o;     /* io (N, d_v): gated backward, gradient of o                              */
   size_t epi_part;    /* float (8192, d_v): gated backward, gain gradient partial sums           */
   size_t fwd_bytes;   /* workspace bytes ram_forward needs                                      */

@@ -4,6 +4,7 @@
 #include <mutex>
 #include <string.h>
 #include <string>
+#include <unordered_set>
 #include <vector>
 
 #include "../../include/ramnet.h"
@@ -76,39 +77,14 @@ int check_problem(const ram_problem* p, Dims* d) {
   return RAM_OK;
 }
 
-// A call can be cut into pieces of whole batches that go through the path
-// one after the other, so that one piece's bucketing and scans
-// (latency-bound) run while the next piece's address decode
-// (bandwidth-bound) streams.  With the present kernels one piece is fastest
-// (measured at the 1.3B shape: 2 and 4 pieces lose 0.4 and 1.0 ms): the
-// longest segment of a piece is as long as that of the whole call, so the
-// pieces' scans do not shrink, and the decode starves their small
-// workgroups of the device.
-constexpr int MAX_PIECES = 1;
-struct Pieces {
-  int n;
-  int b0[MAX_PIECES + 1];   // piece q holds batches [b0[q], b0[q + 1])
-};
-Pieces make_pieces(int B) {
-  Pieces P;
-  P.n = B < MAX_PIECES ? B : MAX_PIECES;
-  for (int q = 0; q <= P.n; ++q) P.b0[q] = (int)((int64_t)B * q / P.n);
-  return P;
-}
-
-// Entries per length class of one piece's long-segment list: every long
-// segment has more than LONG_EVENTS events.
 // Workgroups of the bucketing scan per (b, h): blocks of SCAN_SLOTS slots.
 int scan_blocks(int64_t S) { return (int)((S + SCAN_SLOTS - 1) / SCAN_SLOTS); }
 
-int long_cap(const ram_problem* p, const Dims& d) {
-  const Pieces P = make_pieces(p->B);
-  int nb = 0;
-  for (int q = 0; q < P.n; ++q) nb = std::max(nb, P.b0[q + 1] - P.b0[q]);
-  const int64_t E = (int64_t)nb * p->H * p->T * (p->k_w + p->k_r);
-  const int64_t nseg = (int64_t)nb * p->H * d.S;
-  const int64_t c = E / (LONG_EVENTS + 1) + 1;
-  return (int)(c < nseg ? c : nseg);
+// Entries per length class of the long-segment list: every long segment has
+// more than LONG_EVENTS events.
+int long_cap(const Dims& d) {
+  const int64_t c = d.E / (LONG_EVENTS + 1) + 1;
+  return (int)(c < d.nseg ? c : d.nseg);
 }
 
 void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
@@ -124,14 +100,14 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   L->events = take(sizeof(EventRec) * d.E);
   L->ckpt_s = take(sizeof(float) * d.nck * p->d_v);
   L->ckpt_m = take(sizeof(float) * d.nck);
-  L->stash = take(d.io_bytes * d.N * (p->k_w > p->k_r ? p->k_w : p->k_r) * p->d_v);
+  L->stash = take(d.io_bytes * d.N * p->k_r * p->d_v);
   // tile histograms, then the per-block event counts of the bucketing scan
   L->tile_hist = take(sizeof(int32_t) * (size_t)p->B * p->H *
                       ((size_t)d.ntiles * d.S + scan_blocks(d.S)));
-  const int pieces = make_pieces(p->B).n;
-  L->long_list = take(sizeof(int32_t) * pieces * NBIN * long_cap(p, d));
-  L->long_count = take(sizeof(int32_t) * pieces * LONG_WORDS);
+  L->long_list = take(sizeof(int32_t) * NBIN * long_cap(d));
+  L->long_count = take(sizeof(int32_t) * LONG_WORDS);
   L->fwd_bytes = off;
+  L->stash_b = take(d.io_bytes * d.N * p->k_w * p->d_v);
   L->dw = take(sizeof(float) * d.N * p->k_w);
   L->dr = take(sizeof(float) * d.N * p->k_r);
   L->dgam = take(sizeof(float) * d.N * p->k_w);
@@ -187,15 +163,15 @@ void prof_after(const char*, hipStream_t st) {
 int hip_status(hipError_t e) { return e == hipSuccess ? RAM_OK : RAM_EHIP; }
 
 // ---- library streams ---------------------------------------------------------
-// The kernels of a call run on the caller's stream and on two library
-// streams of the same device (default priority, non-blocking with respect to
+// The kernels of a call run on the caller's stream and on one library
+// stream of the same device (default priority, non-blocking with respect to
 // the null stream).  Every dependency goes through an event: the library
 // streams first wait for everything already on the caller's stream (fork),
 // and the caller's stream ends waiting for the library streams' work
 // (join), so the call as a whole is ordered on the caller's stream.
-constexpr int EV_POOL = 8 * MAX_PIECES + 8;
+constexpr int EV_POOL = 16;
 struct Sched {
-  hipStream_t side[2] = {nullptr, nullptr};
+  hipStream_t side[1] = {nullptr};
   hipEvent_t ev[EV_POOL] = {};
   int used = 0;
   hipError_t err = hipSuccess;
@@ -221,12 +197,10 @@ hipError_t get_sched(Sched** out) {
     for (auto& ev : S.ev)
       if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
   }
-  // streams are created on first use only: each one takes a hardware queue,
-  // and a stream that shares its queue with the caller's serialises with it
-  const int nside = MAX_PIECES > 1 ? 2 : 1;
-  for (int i = 0; i < nside; ++i)
-    if (!S.side[i] && (e = hipStreamCreateWithFlags(&S.side[i], hipStreamNonBlocking)) != hipSuccess)
-      return e;
+  // the stream is created on first use only: it takes a hardware queue, and
+  // a stream that shares its queue with the caller's serialises with it
+  if (!S.side[0] && (e = hipStreamCreateWithFlags(&S.side[0], hipStreamNonBlocking)) != hipSuccess)
+    return e;
   S.used = 0;
   S.err = hipSuccess;
   *out = &S;
@@ -311,12 +285,38 @@ bool epilogue_ok(const ram_epilogue* ep, int64_t N) {
   return ep && (N == 0 || ep->gate) && ep->eps >= 0.f && ep->eps <= 3.0e38f;
 }
 
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// In-place continuation (ramnet-ops "Arguments", inplace: no gradients): a
+// forward whose final state overlaps its initial state overwrites what a
+// backward would need.  The library keeps the workspace addresses whose last
+// forward ran in place; ram_backward on such a workspace returns RAM_EINVAL
+// before it enqueues anything.
+std::mutex alias_mu;
+std::unordered_set<uintptr_t> inplace_ws;
+
+void note_forward(const void* ws, bool inplace) {
+  std::lock_guard<std::mutex> lk(alias_mu);
+  if (inplace) inplace_ws.insert((uintptr_t)ws);
+  else inplace_ws.erase((uintptr_t)ws);
+}
+
+bool ran_in_place(const void* ws) {
+  std::lock_guard<std::mutex> lk(alias_mu);
+  return inplace_ws.count((uintptr_t)ws) != 0;
+}
+
 // ram_forward, or with ep the gated read-out y = sigmoid(gate) * RMSNorm(o)
-// written to o.
+// written to o.  one_stream: every kernel on the caller's stream (no library
+// streams or events are created or used).
 int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogits,
                  const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
                  const float* slot0, const float* mass0, void* o, float* slot1, float* mass1,
-                 void* ws, size_t ws_bytes, void* stream) {
+                 void* ws, size_t ws_bytes, void* stream, bool one_stream) {
   Dims d;
   int st = check_problem(p, &d);
   if (st != RAM_OK) return st;
@@ -328,154 +328,147 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
   ram_ws_layout L;
   make_layout(p, d, &L);
   if (ws_bytes < L.fwd_bytes) return RAM_ECAPACITY;
+  const size_t sb = (size_t)d.nseg * p->d_v * sizeof(float), mb = (size_t)d.nseg * sizeof(float);
+  note_forward(ws, overlaps(slot1, sb, slot0, sb) || overlaps(mass1, mb, mass0, mb) ||
+                       overlaps(slot1, sb, mass0, mb) || overlaps(mass1, mb, slot0, sb));
   char* w = (char*)ws;
   hipStream_t s = (hipStream_t)stream;
   const bool bf = p->io_dtype == RAM_BF16;
-  const size_t io = d.io_bytes;
-  const int64_t TH = (int64_t)p->T * p->H, HS = (int64_t)p->H * d.S;
-  const int K = p->k_w + p->k_r, kmax = std::max(p->k_w, p->k_r);
-  const int cap = long_cap(p, d);
-  const Pieces P = make_pieces(p->B);
+  const int cap = long_cap(d);
 
   std::lock_guard<std::mutex> lk(sched_mu);
-  Sched* S = nullptr;
-  if (get_sched(&S) != hipSuccess) return RAM_EHIP;
-  // one piece: the serial part stays on the caller's stream (fewer
-  // cross-stream waits); only the short-segment scans run beside it
-  hipStream_t a = P.n > 1 ? S->side[1] : s, b = S->side[0];
-  S->dep(a, s);
+  Sched local;
+  Sched* S = &local;
+  if (!one_stream && get_sched(&S) != hipSuccess) return RAM_EHIP;
+  // the short-segment scans run beside the long-segment ones on a library
+  // stream; everything else on the caller's stream
+  hipStream_t b = one_stream ? s : S->side[0];
   hipError_t e = hipSuccess;
-  for (int q = 0; q < P.n && e == hipSuccess && S->err == hipSuccess; ++q) {
-    const int b0 = P.b0[q], nb = P.b0[q + 1] - P.b0[q];
-    const int64_t r0 = (int64_t)b0 * TH, rows = (int64_t)nb * TH;   // token rows of the piece
 
-    DecodeFwdArgs da{};
-    da.logits[0] = adv(wlogits, r0 * d.row, io);
-    da.logits[1] = adv(rlogits, r0 * d.row, io);
-    da.idx[0] = (int32_t*)(w + L.idx_w) + r0 * p->k_w;
-    da.idx[1] = (int32_t*)(w + L.idx_r) + r0 * p->k_r;
-    da.w[0] = (float*)(w + L.w_w) + r0 * p->k_w;
-    da.w[1] = (float*)(w + L.w_r) + r0 * p->k_r;
-    da.lse[0] = (float*)(w + L.lse_w) + r0 * p->U;
-    da.lse[1] = (float*)(w + L.lse_r) + r0 * p->U;
-    da.k[0] = p->k_w;
-    da.k[1] = p->k_r;
-    da.renorm[0] = p->renorm_w;
-    da.renorm[1] = p->renorm_r;
-    da.N = rows;
-    da.S = (int)d.S;
-    da.U = p->U;
-    da.P = p->P;
-    da.nsides = 2;
-    da.H = p->H;
-    da.T = p->T;
-    da.cape_heads = p->cape_heads;
-    da.t0 = p->t0 % d.S;
-    prof_before("decode_fwd", s);
-    e = launch_decode_fwd(da, bf, s);
-    prof_after("decode_fwd", s);
-    if (e != hipSuccess) break;
-    S->dep(a, s);
+  DecodeFwdArgs da{};
+  da.logits[0] = wlogits;
+  da.logits[1] = rlogits;
+  da.idx[0] = (int32_t*)(w + L.idx_w);
+  da.idx[1] = (int32_t*)(w + L.idx_r);
+  da.w[0] = (float*)(w + L.w_w);
+  da.w[1] = (float*)(w + L.w_r);
+  da.lse[0] = (float*)(w + L.lse_w);
+  da.lse[1] = (float*)(w + L.lse_r);
+  da.k[0] = p->k_w;
+  da.k[1] = p->k_r;
+  da.renorm[0] = p->renorm_w;
+  da.renorm[1] = p->renorm_r;
+  da.N = d.N;
+  da.S = (int)d.S;
+  da.U = p->U;
+  da.P = p->P;
+  da.nsides = 2;
+  da.H = p->H;
+  da.T = p->T;
+  da.cape_heads = p->cape_heads;
+  da.t0 = p->t0 % d.S;
+  prof_before("decode_fwd", s);
+  e = launch_decode_fwd(da, bf, s);
+  prof_after("decode_fwd", s);
+  if (e != hipSuccess) return RAM_EHIP;
 
-    BucketArgs ba{};
-    ba.idx_w = da.idx[0];
-    ba.idx_r = da.idx[1];
-    ba.w_w = da.w[0];
-    ba.w_r = da.w[1];
-    ba.gamma = adv(gamma, r0, io);
-    ba.mask = mask ? mask + (int64_t)b0 * p->T : nullptr;
-    ba.B = nb;
-    ba.H = p->H;
-    ba.T = p->T;
-    ba.S = (int)d.S;
-    ba.k_w = p->k_w;
-    ba.k_r = p->k_r;
-    ba.tile = d.tile;
-    ba.ntiles = d.ntiles;
-    ba.nbits = d.nbits;
-    ba.tile_hist = (int32_t*)(w + L.tile_hist) + (int64_t)b0 * p->H * d.ntiles * d.S;
-    ba.nblk = scan_blocks(d.S);
-    ba.blk_tot = (int32_t*)(w + L.tile_hist) + (int64_t)p->B * p->H * d.ntiles * d.S +
-                 (int64_t)b0 * p->H * ba.nblk;
-    ba.seg_offset = (int32_t*)(w + L.seg_offset) + (int64_t)b0 * HS;
-    ba.ev_base = r0 * K;
-    ba.events = (EventRec*)(w + L.events);
-    ba.long_list = (int32_t*)(w + L.long_list) + (int64_t)q * NBIN * cap;
-    ba.long_count = (int32_t*)(w + L.long_count) + q * LONG_WORDS;
-    ba.long_cap = cap;
-    e = launch_bucket(ba, bf, a, prof_before, prof_after);
-    if (e != hipSuccess) break;
+  BucketArgs ba{};
+  ba.idx_w = da.idx[0];
+  ba.idx_r = da.idx[1];
+  ba.w_w = da.w[0];
+  ba.w_r = da.w[1];
+  ba.gamma = gamma;
+  ba.mask = mask;
+  ba.B = p->B;
+  ba.H = p->H;
+  ba.T = p->T;
+  ba.S = (int)d.S;
+  ba.k_w = p->k_w;
+  ba.k_r = p->k_r;
+  ba.tile = d.tile;
+  ba.ntiles = d.ntiles;
+  ba.nbits = d.nbits;
+  ba.tile_hist = (int32_t*)(w + L.tile_hist);
+  ba.nblk = scan_blocks(d.S);
+  ba.blk_tot = (int32_t*)(w + L.tile_hist) + (int64_t)p->B * p->H * d.ntiles * d.S;
+  ba.seg_offset = (int32_t*)(w + L.seg_offset);
+  ba.ev_base = 0;
+  ba.events = (EventRec*)(w + L.events);
+  ba.long_list = (int32_t*)(w + L.long_list);
+  ba.long_count = (int32_t*)(w + L.long_count);
+  ba.long_cap = cap;
+  e = launch_bucket(ba, bf, s, prof_before, prof_after);
+  if (e != hipSuccess) return RAM_EHIP;
 
-    ScanFwdArgs sa{};
-    sa.B = nb;
-    sa.H = p->H;
-    sa.T = p->T;
-    sa.S = (int)d.S;
-    sa.d_v = p->d_v;
-    sa.k_w = p->k_w;
-    sa.k_r = p->k_r;
-    sa.eps = p->eps;
-    sa.nseg = (int64_t)nb * HS;
-    sa.long_list = ba.long_list;
-    sa.long_count = ba.long_count;
-    sa.queue = ba.long_count + NBIN;
-    sa.long_cap = cap;
-    sa.use_long = d.ntiles > 0;
-    sa.seg_offset = ba.seg_offset;
-    sa.events = ba.events;
-    sa.v = adv(v, r0 * p->d_v, io);
-    sa.slot0 = adv(slot0, (int64_t)b0 * HS * p->d_v, sizeof(float));
-    sa.mass0 = adv(mass0, (int64_t)b0 * HS, sizeof(float));
-    sa.slot1 = adv(slot1, (int64_t)b0 * HS * p->d_v, sizeof(float));
-    sa.mass1 = adv(mass1, (int64_t)b0 * HS, sizeof(float));
-    sa.stash = w + L.stash + r0 * kmax * p->d_v * (int64_t)io;
-    sa.ckpt_s = (float*)(w + L.ckpt_s);
-    sa.ckpt_m = (float*)(w + L.ckpt_m);
-    // The short-segment stream forks off just before the launch and joins
-    // right after it; the timing events bracket the fork and the join (an
-    // event recorded between the launch and the join slows the scans down).
-    prof_before("scan_fwd", a);
-    S->dep(b, a);
-    e = launch_scan_fwd(sa, bf, a, b);
-    S->dep(a, b);
-    prof_after("scan_fwd", a);
-    if (e != hipSuccess) break;
-
-    if (ep) {
-      EpilogueArgs ea{};
-      ea.N = rows;
-      ea.d_v = p->d_v;
-      ea.k = p->k_r;
-      ea.T = p->T;
-      ea.H = p->H;
-      ea.stash = sa.stash;
-      ea.gate = adv(ep->gate, r0 * p->d_v, io);
-      ea.gain = ep->gain;
-      ea.eps = ep->eps;
-      ea.y = adv(o, r0 * p->d_v, io);
-      prof_before("epilogue_fwd", a);
-      e = launch_epilogue_fwd(ea, bf, a);
-      prof_after("epilogue_fwd", a);
-    } else {
-      FinalizeArgs fa{};
-      fa.N = rows;
-      fa.d_v = p->d_v;
-      fa.k = p->k_r;
-      fa.stash = sa.stash;
-      fa.out = adv(o, r0 * p->d_v, io);
-      prof_before("finalize_o", a);
-      e = launch_finalize(fa, bf, a);
-      prof_after("finalize_o", a);
-    }
-  }
-  S->dep(s, a);
+  ScanFwdArgs sa{};
+  sa.B = p->B;
+  sa.H = p->H;
+  sa.T = p->T;
+  sa.S = (int)d.S;
+  sa.d_v = p->d_v;
+  sa.k_w = p->k_w;
+  sa.k_r = p->k_r;
+  sa.eps = p->eps;
+  sa.nseg = d.nseg;
+  sa.long_list = ba.long_list;
+  sa.long_count = ba.long_count;
+  sa.queue = ba.long_count + NBIN;
+  sa.long_cap = cap;
+  sa.use_long = d.ntiles > 0;
+  sa.seg_offset = ba.seg_offset;
+  sa.events = ba.events;
+  sa.v = v;
+  sa.slot0 = slot0;
+  sa.mass0 = mass0;
+  sa.slot1 = slot1;
+  sa.mass1 = mass1;
+  sa.stash = w + L.stash;
+  sa.ckpt_s = (float*)(w + L.ckpt_s);
+  sa.ckpt_m = (float*)(w + L.ckpt_m);
+  // The short-segment stream forks off just before the launch and joins
+  // right after it; the timing events bracket the fork and the join (an
+  // event recorded between the launch and the join slows the scans down).
+  prof_before("scan_fwd", s);
+  S->dep(b, s);
+  e = launch_scan_fwd(sa, bf, s, b);
   S->dep(s, b);
+  prof_after("scan_fwd", s);
   if (e != hipSuccess || S->err != hipSuccess) return RAM_EHIP;
-  return RAM_OK;
+
+  if (ep) {
+    EpilogueArgs ea{};
+    ea.N = d.N;
+    ea.d_v = p->d_v;
+    ea.k = p->k_r;
+    ea.T = p->T;
+    ea.H = p->H;
+    ea.stash = sa.stash;
+    ea.gate = ep->gate;
+    ea.gain = ep->gain;
+    ea.eps = ep->eps;
+    ea.y = o;
+    prof_before("epilogue_fwd", s);
+    e = launch_epilogue_fwd(ea, bf, s);
+    prof_after("epilogue_fwd", s);
+  } else {
+    FinalizeArgs fa{};
+    fa.N = d.N;
+    fa.d_v = p->d_v;
+    fa.k = p->k_r;
+    fa.stash = sa.stash;
+    fa.out = o;
+    prof_before("finalize_o", s);
+    e = launch_finalize(fa, bf, s);
+    prof_after("finalize_o", s);
+  }
+  return e == hipSuccess ? RAM_OK : RAM_EHIP;
 }
 
 // ram_backward, or with ep the backward of the gated read-out: d_o is then
 // the gradient of y, and d_gate / d_gain receive the epilogue's gradients.
+// The reverse scan runs its long-segment kernel on the caller's stream and
+// its short-segment kernel beside it on a library stream; the decode
+// backward of both sides and the d_v / d_gamma sums follow.
 int backward_impl(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t ws_bytes,
                   const void* wlogits, const void* rlogits, const void* v, const void* gamma,
                   const uint8_t* mask, const float* slot0, const float* mass0, const void* d_o,
@@ -497,28 +490,22 @@ int backward_impl(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t
   ram_ws_layout L;
   make_layout(p, d, &L);
   if (ws_bytes < L.total_bytes) return RAM_ECAPACITY;
+  if (ran_in_place(ws)) return RAM_EINVAL;
   char* w = (char*)ws;
   hipStream_t s = (hipStream_t)stream;
   const bool bf = p->io_dtype == RAM_BF16;
-  const size_t io = d.io_bytes;
-  const int64_t TH = (int64_t)p->T * p->H, HS = (int64_t)p->H * d.S;
-  const int kmax = std::max(p->k_w, p->k_r);
-  const int cap = long_cap(p, d);
-  const Pieces P = make_pieces(p->B);
+  const int cap = long_cap(d);
   (void)gamma;   // the event records carry lambda and d lambda / d w
 
   std::lock_guard<std::mutex> lk(sched_mu);
   Sched* S = nullptr;
   if (get_sched(&S) != hipSuccess) return RAM_EHIP;
-  // one piece: the serial part stays on the caller's stream (fewer
-  // cross-stream waits); only the short-segment scans run beside it
-  hipStream_t a = P.n > 1 ? S->side[1] : s, b = S->side[0];
-  S->dep(a, s);
+  hipStream_t b = S->side[0];
   hipError_t e = hipSuccess;
+  const void* dO = d_o;
   if (ep) {
-    // gradient of o from that of y, for all rows at once; the stash still
-    // holds the forward's read contributions until the reverse scan
-    // overwrites it
+    // gradient of o from that of y; o is recomputed from the forward's read
+    // contributions, which the backward never overwrites
     EpilogueArgs ea{};
     ea.N = d.N;
     ea.d_v = p->d_v;
@@ -535,102 +522,95 @@ int backward_impl(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t
     ea.part = (float*)(w + L.epi_part);
     ea.d_gain = d_gain;
     ea.mask = mask;
-    prof_before("epilogue_bwd", a);
-    e = launch_epilogue_bwd(ea, bf, a);
-    prof_after("epilogue_bwd", a);
+    prof_before("epilogue_bwd", s);
+    e = launch_epilogue_bwd(ea, bf, s);
+    prof_after("epilogue_bwd", s);
+    if (e != hipSuccess) return RAM_EHIP;
+    dO = w + L.epi_d_o;
   }
-  for (int q = 0; q < P.n && e == hipSuccess && S->err == hipSuccess; ++q) {
-    const int b0 = P.b0[q], nb = P.b0[q + 1] - P.b0[q];
-    const int64_t r0 = (int64_t)b0 * TH, rows = (int64_t)nb * TH;
 
-    ScanBwdArgs sb{};
-    sb.B = nb;
-    sb.H = p->H;
-    sb.T = p->T;
-    sb.S = (int)d.S;
-    sb.d_v = p->d_v;
-    sb.k_w = p->k_w;
-    sb.k_r = p->k_r;
-    sb.eps = p->eps;
-    sb.nseg = (int64_t)nb * HS;
-    sb.long_list = (const int32_t*)(w + L.long_list) + (int64_t)q * NBIN * cap;
-    sb.long_count = (const int32_t*)(w + L.long_count) + q * LONG_WORDS;
-    sb.queue = (int32_t*)(w + L.long_count) + q * LONG_WORDS + NBIN + 2;
-    sb.long_cap = cap;
-    sb.use_long = d.ntiles > 0;
-    sb.seg_offset = (const int32_t*)(w + L.seg_offset) + (int64_t)b0 * HS;
-    sb.events = (const EventRec*)(w + L.events);
-    sb.v = adv(v, r0 * p->d_v, io);
-    sb.d_o = adv(d_o, r0 * p->d_v, io);
-    if (ep) sb.d_o = w + L.epi_d_o + r0 * p->d_v * (int64_t)io;
-    sb.slot0 = adv(slot0, (int64_t)b0 * HS * p->d_v, sizeof(float));
-    sb.mass0 = adv(mass0, (int64_t)b0 * HS, sizeof(float));
-    sb.ckpt_s = (const float*)(w + L.ckpt_s);
-    sb.ckpt_m = (const float*)(w + L.ckpt_m);
-    sb.d_slot1 = adv(d_slot1, (int64_t)b0 * HS * p->d_v, sizeof(float));
-    sb.d_mass1 = adv(d_mass1, (int64_t)b0 * HS, sizeof(float));
-    sb.d_slot0 = adv(d_slot0, (int64_t)b0 * HS * p->d_v, sizeof(float));
-    sb.d_mass0 = adv(d_mass0, (int64_t)b0 * HS, sizeof(float));
-    sb.stash = w + L.stash + r0 * kmax * p->d_v * (int64_t)io;
-    sb.dw = (float*)(w + L.dw) + r0 * p->k_w;
-    sb.dr = (float*)(w + L.dr) + r0 * p->k_r;
-    sb.dgam = (float*)(w + L.dgam) + r0 * p->k_w;
-    prof_before("scan_bwd", a);
-    S->dep(b, a);
-    e = launch_scan_bwd(sb, bf, a, b);
-    S->dep(a, b);
-    prof_after("scan_bwd", a);
-    if (e != hipSuccess) break;
-    S->dep(s, a);
-
-    DecodeBwdArgs db{};
-    db.logits[0] = adv(wlogits, r0 * d.row, io);
-    db.logits[1] = adv(rlogits, r0 * d.row, io);
-    db.lse[0] = (const float*)(w + L.lse_w) + r0 * p->U;
-    db.lse[1] = (const float*)(w + L.lse_r) + r0 * p->U;
-    db.idx[0] = (const int32_t*)(w + L.idx_w) + r0 * p->k_w;
-    db.idx[1] = (const int32_t*)(w + L.idx_r) + r0 * p->k_r;
-    db.w[0] = (const float*)(w + L.w_w) + r0 * p->k_w;
-    db.w[1] = (const float*)(w + L.w_r) + r0 * p->k_r;
-    db.g[0] = sb.dw;
-    db.g[1] = sb.dr;
-    db.dlogits[0] = adv(d_wlogits, r0 * d.row, io);
-    db.dlogits[1] = adv(d_rlogits, r0 * d.row, io);
-    db.k[0] = p->k_w;
-    db.k[1] = p->k_r;
-    db.renorm[0] = p->renorm_w;
-    db.renorm[1] = p->renorm_r;
-    db.N = rows;
-    db.S = (int)d.S;
-    db.U = p->U;
-    db.P = p->P;
-    db.nsides = 2;
-    db.H = p->H;
-    db.T = p->T;
-    db.cape_heads = p->cape_heads;
-    db.t0 = p->t0 % d.S;
-    db.mask = mask ? mask + (int64_t)b0 * p->T : nullptr;
-    prof_before("decode_bwd", s);
-    e = launch_decode_bwd(db, bf, s);
-    prof_after("decode_bwd", s);
-    if (e != hipSuccess) break;
-
-    FinalizeArgs fa{};
-    fa.N = rows;
-    fa.d_v = p->d_v;
-    fa.k = p->k_w;
-    fa.stash = sb.stash;
-    fa.out = adv(d_v, r0 * p->d_v, io);
-    fa.dgam = sb.dgam;
-    fa.d_gamma = adv(d_gamma, r0, io);
-    prof_before("finalize_bwd", s);
-    e = launch_finalize(fa, bf, s);
-    prof_after("finalize_bwd", s);
-  }
-  S->dep(s, a);
+  ScanBwdArgs sb{};
+  sb.B = p->B;
+  sb.H = p->H;
+  sb.T = p->T;
+  sb.S = (int)d.S;
+  sb.d_v = p->d_v;
+  sb.k_w = p->k_w;
+  sb.k_r = p->k_r;
+  sb.eps = p->eps;
+  sb.nseg = d.nseg;
+  sb.long_list = (const int32_t*)(w + L.long_list);
+  sb.long_count = (const int32_t*)(w + L.long_count);
+  sb.queue = (int32_t*)(w + L.long_count) + NBIN + 2;
+  sb.long_cap = cap;
+  sb.use_long = d.ntiles > 0;
+  sb.seg_offset = (const int32_t*)(w + L.seg_offset);
+  sb.events = (const EventRec*)(w + L.events);
+  sb.v = v;
+  sb.d_o = dO;
+  sb.slot0 = slot0;
+  sb.mass0 = mass0;
+  sb.ckpt_s = (const float*)(w + L.ckpt_s);
+  sb.ckpt_m = (const float*)(w + L.ckpt_m);
+  sb.d_slot1 = d_slot1;
+  sb.d_mass1 = d_mass1;
+  sb.d_slot0 = d_slot0;
+  sb.d_mass0 = d_mass0;
+  sb.stash = w + L.stash_b;
+  sb.dw = (float*)(w + L.dw);
+  sb.dr = (float*)(w + L.dr);
+  sb.dgam = (float*)(w + L.dgam);
+  prof_before("scan_bwd", s);
+  S->dep(b, s);
+  e = launch_scan_bwd(sb, bf, s, b);
   S->dep(s, b);
+  prof_after("scan_bwd", s);
   if (e != hipSuccess || S->err != hipSuccess) return RAM_EHIP;
-  return RAM_OK;
+
+  DecodeBwdArgs db{};
+  db.logits[0] = wlogits;
+  db.logits[1] = rlogits;
+  db.lse[0] = (const float*)(w + L.lse_w);
+  db.lse[1] = (const float*)(w + L.lse_r);
+  db.idx[0] = (const int32_t*)(w + L.idx_w);
+  db.idx[1] = (const int32_t*)(w + L.idx_r);
+  db.w[0] = (const float*)(w + L.w_w);
+  db.w[1] = (const float*)(w + L.w_r);
+  db.g[0] = sb.dw;
+  db.g[1] = sb.dr;
+  db.dlogits[0] = d_wlogits;
+  db.dlogits[1] = d_rlogits;
+  db.k[0] = p->k_w;
+  db.k[1] = p->k_r;
+  db.renorm[0] = p->renorm_w;
+  db.renorm[1] = p->renorm_r;
+  db.N = d.N;
+  db.S = (int)d.S;
+  db.U = p->U;
+  db.P = p->P;
+  db.nsides = 2;
+  db.H = p->H;
+  db.T = p->T;
+  db.cape_heads = p->cape_heads;
+  db.t0 = p->t0 % d.S;
+  db.mask = mask;
+  prof_before("decode_bwd", s);
+  e = launch_decode_bwd(db, bf, s);
+  prof_after("decode_bwd", s);
+  if (e != hipSuccess) return RAM_EHIP;
+
+  FinalizeArgs fa{};
+  fa.N = d.N;
+  fa.d_v = p->d_v;
+  fa.k = p->k_w;
+  fa.stash = sb.stash;
+  fa.out = d_v;
+  fa.dgam = sb.dgam;
+  fa.d_gamma = d_gamma;
+  prof_before("finalize_bwd", s);
+  e = launch_finalize(fa, bf, s);
+  prof_after("finalize_bwd", s);
+  return e == hipSuccess ? RAM_OK : RAM_EHIP;
 }
 
 }  // namespace
@@ -641,7 +621,7 @@ int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, 
                 const void* gamma, const uint8_t* mask, const float* slot0, const float* mass0,
                 void* o, float* slot1, float* mass1, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(p, nullptr, wlogits, rlogits, v, gamma, mask, slot0, mass0, o, slot1, mass1,
-                      ws, ws_bytes, stream);
+                      ws, ws_bytes, stream, false);
 }
 
 int ram_forward_gated(const ram_problem* p, const ram_epilogue* ep, const void* wlogits,
@@ -650,7 +630,7 @@ int ram_forward_gated(const ram_problem* p, const ram_epilogue* ep, const void* 
                       void* ws, size_t ws_bytes, void* stream) {
   if (!ep) return RAM_EINVAL;
   return forward_impl(p, ep, wlogits, rlogits, v, gamma, mask, slot0, mass0, y, slot1, mass1, ws,
-                      ws_bytes, stream);
+                      ws_bytes, stream, false);
 }
 
 int ram_backward(const ram_problem* p, void* ws, size_t ws_bytes, const void* wlogits,

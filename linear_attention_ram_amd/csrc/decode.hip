@@ -89,6 +89,14 @@ __global__ __launch_bounds__(FWD_ROWS * WAVE) void decode_fwd_kernel(DecodeFwdAr
   }
 }
 
+// gw_j = g_j w_j of lane j < k (0 in the other lanes, where g and w are 0).
+// Renormalised weights w = p / sum p: the gradient reaching the
+// un-renormalised p_j times p_j is (g_j - sum_i g_i w_i) w_j.
+__device__ __forceinline__ float decode_gw(float gj, float wj, int renorm) {
+  if (renorm) return (gj - wave_sum(gj * wj)) * wj;
+  return gj * wj;
+}
+
 // Decode backward (one wave per row): with g_j the gradient of the j-th
 // output weight, gw_j = g_j w_j (renormalised: gw_j = (g_j - sum_i g_i w_i) w_j),
 // dl_i = [i = a_j] gw_j - p_i sum_j gw_j, p = softmax(l) = exp(l - lse).
@@ -126,12 +134,7 @@ __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
     if (shift >= 0) aj = (aj - shift + a.S) % a.S;
     lj = to_f32(src[aj]);
   }
-  if (a.renorm[side]) {
-    const float dot = wave_sum(gj * wj);
-    gw = (gj - dot) * wj;
-  } else {
-    gw = gj * wj;
-  }
+  gw = decode_gw(gj, wj, a.renorm[side]);
   const float tot = wave_sum(gw);
   const float nl = -a.lse[side][row] * LOG2E;
   const float ntot = -tot;
@@ -234,13 +237,7 @@ __global__ __launch_bounds__(256) void decode_bwd_prod_kernel(DecodeBwdArgs a) {
     const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
     if (shift >= 0) aj = (aj - shift + a.S) % a.S;
   }
-  float gw;
-  if (a.renorm[side]) {
-    const float dot = wave_sum(gj * wj);
-    gw = (gj - dot) * wj;
-  } else {
-    gw = gj * wj;
-  }
+  const float gw = decode_gw(gj, wj, a.renorm[side]);
   const float ntot = -wave_sum(gw);
   if (U == 2 && P <= WAVE) {
     // two digits: lane i holds element i of each; the selected slots' terms

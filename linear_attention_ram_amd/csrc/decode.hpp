@@ -156,37 +156,56 @@ __device__ __forceinline__ void rank_candidates(DecodeScratch& sc, int count, in
   }
 }
 
-// Rows with more than CAND_CAP candidates (massive ties): K exact passes
-// over the row in memory, each taking the best element after the previous
-// pick in (value desc, index asc) order, to sc.sv / sc.si.  Kept out of line
-// so its registers do not count against the common path.
+// Total order of the exact passes: the ordered bits of a value, with -0 and
+// +0 equal and NaN below every number (0), so that a row holding NaN still
+// yields K distinct in-range slots.
+__device__ __forceinline__ uint32_t sel_key(float x) {
+  if (x != x) return 0u;
+  return ordered_bits(x == 0.f ? 0.f : x);
+}
+__device__ __forceinline__ bool key_before(uint32_t v, int i, uint32_t v2, int i2) {
+  return (v > v2) || (v == v2 && i < i2);
+}
+
+// Rows with more than CAND_CAP candidates (massive ties), or fewer than K
+// (NaN logits): K exact passes over the row in memory, each taking the best
+// element after the previous pick in (value desc, index asc) order, to
+// sc.sv / sc.si.  Kept out of line so its registers do not count against the
+// common path.
 template <typename IO>
 __device__ __noinline__ void exact_k_passes(const IO* __restrict__ row, int nvec, int k,
                                             DecodeScratch& sc) {
   constexpr int E = vec16<IO>::E;
   const int lane = lane_id();
-  float pv = INFINITY;
+  uint32_t pk = 0xFFFFFFFFu;   // above every key: the first pass may take any element
   int pi = -1;
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
+    uint32_t bk = 0u;
     int bi = 0x7fffffff;
+    float bv = -INFINITY;
     for (int c = lane; c < nvec; c += WAVE) {
       float x[E];
       unpack16(load_vec<IO>(row, c, nvec), x);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int id = c * E + e;
-        if (before(pv, pi, x[e], id) && before(x[e], id, bv, bi)) { bv = x[e]; bi = id; }
+        const uint32_t key = sel_key(x[e]);
+        if (key_before(pk, pi, key, id) && key_before(key, id, bk, bi)) {
+          bk = key;
+          bi = id;
+          bv = x[e];
+        }
       }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, WAVE);
+      const uint32_t ok = (uint32_t)__shfl_xor((int)bk, o, WAVE);
       const int oi = __shfl_xor(bi, o, WAVE);
-      if (before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      const float ov = __shfl_xor(bv, o, WAVE);
+      if (key_before(ok, oi, bk, bi)) { bk = ok; bi = oi; bv = ov; }
     }
     if (lane == 0) { sc.sv[r] = bv; sc.si[r] = bi; }
-    pv = bv;
+    pk = bk;
     pi = bi;
   }
 }
@@ -293,6 +312,8 @@ __device__ float decode_row_resident(const IO* __restrict__ row, int S, int k, i
         if (x[e] >= tau) { sc.cv[pos] = x[e]; sc.ci[pos] = base + e; ++pos; }
     }
   }
+  // fewer than K candidates: NaN logits (they compare false with tau)
+  if (count < k) overflow = true;
   wave_sync();
   if (!overflow) rank_candidates(sc, count, k);
   else exact_k_passes<IO>(row, nvec, k, sc);
@@ -383,6 +404,7 @@ __device__ float decode_row_wave(const IO* __restrict__ row, int S, int k, int r
     }
     count += total;
   }
+  if (count < k) overflow = true;   // NaN logits
   wave_sync();
 
   if (!overflow) {

@@ -63,16 +63,18 @@ __device__ __forceinline__ void rank_list(const float* cv, const int* ci, int co
 }
 
 // K exact passes over all S = P^U slots (keys from the digits in LDS), each
-// taking the best slot after the previous pick.  Out of line so that its
-// registers do not count against the common path.
+// taking the best slot after the previous pick (NaN keys below every
+// number, as in exact_k_passes).  Out of line so that its registers do not
+// count against the common path.
 __device__ __noinline__ void product_k_passes(ProdScratch& sc, int U, int P, int S, int k) {
   const int lane = lane_id();
   const int top = S / P;   // P^(U-1)
-  float pv = INFINITY;
+  uint32_t pk = 0xFFFFFFFFu;
   int pi = -1;
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
+    uint32_t bk = 0u;
     int bi = 0x7fffffff;
+    float bv = -INFINITY;
     for (int a = lane; a < S; a += WAVE) {
       float key = 0.f;
       int rem = a, stride = top;
@@ -82,16 +84,18 @@ __device__ __noinline__ void product_k_passes(ProdScratch& sc, int U, int P, int
         key += sc.dig[u * P + du];
         stride /= P;
       }
-      if (before(pv, pi, key, a) && before(key, a, bv, bi)) { bv = key; bi = a; }
+      const uint32_t kb = sel_key(key);
+      if (key_before(pk, pi, kb, a) && key_before(kb, a, bk, bi)) { bk = kb; bi = a; bv = key; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, WAVE);
+      const uint32_t ok = (uint32_t)__shfl_xor((int)bk, o, WAVE);
       const int oi = __shfl_xor(bi, o, WAVE);
-      if (before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      const float ov = __shfl_xor(bv, o, WAVE);
+      if (key_before(ok, oi, bk, bi)) { bk = ok; bi = oi; bv = ov; }
     }
     if (lane == 0) { sc.sv[r] = bv; sc.si[r] = bi; }
-    pv = bv;
+    pk = bk;
     pi = bi;
   }
 }
@@ -143,7 +147,8 @@ __device__ bool decode_row_u2(const IO* __restrict__ row, int P, int k, int reno
     }
     count += __popcll(bal);
   }
-  if (count > KEEP_CAP) return false;
+  // overflow (massive ties) or fewer than K listed slots (NaN logits)
+  if (count > KEEP_CAP || count < k) return false;
   wave_sync();
   // exact rank of every listed slot; the K best to sv / si, and their
   // log-probabilities to the lanes that hold them
@@ -258,6 +263,7 @@ __device__ void decode_row_product(const IO* __restrict__ row, int U, int P, int
     nk = count;
     if (count > KEEP_CAP) { overflow = true; break; }
   }
+  if (nk < k) overflow = true;   // NaN logits: fewer than K slots survive
   if (!overflow) {
     rank_list(sc.kk[cur], sc.ki[cur], nk, k, sc.sv, sc.si);
   } else {

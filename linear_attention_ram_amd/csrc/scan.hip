@@ -482,7 +482,7 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
     mass_apply(M, ev, m, a.eps);
     m = readlane_f(M.mi, n - 1);
     const float rr = (ev.side == 1) ? ev.wt : 0.f;
-    const uint32_t xo = (ev.valid && ev.side == 0) ? (uint32_t)ev.rb * c.pitch : OOB;
+    const uint32_t xo = (ev.valid && ev.side == 0 && ev.wt > 0.f) ? (uint32_t)ev.rb * c.pitch : OOB;
     const uint32_t so = (ev.valid && ev.side == 1) ? ((uint32_t)ev.rb * a.k_r + ev.j) * c.pitch : OOB;
     rec = load_rec(a.events, p1, min(end, (p1 / CHUNK + 1) * CHUNK) - p1, beg, end);   // next chunk
 
@@ -533,7 +533,7 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
   {
     const int n0 = chunk_start(beg, w + 1, end) - chunk_start(beg, w, end);
     const Ev ev0 = decode_rec(rec, n0, c.h, a.H);
-    const uint32_t xo0 = (ev0.valid && ev0.side == 0) ? (uint32_t)ev0.rb * c.pitch : OOB;
+    const uint32_t xo0 = (ev0.valid && ev0.side == 0 && ev0.wt > 0.f) ? (uint32_t)ev0.rb * c.pitch : OOB;
     for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo0) + c.lb); });
   }
   for (int p = beg; p < end;) {
@@ -625,7 +625,7 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
     {   // rows of this wave's next chunk (past the end: no valid event, no load)
       const int n_n = chunk_start(pn, w + 1, end) - chunk_start(pn, w, end);
       const Ev ev_n = decode_rec(rec, n_n, c.h, a.H);
-      const uint32_t xo_n = (ev_n.valid && ev_n.side == 0) ? (uint32_t)ev_n.rb * c.pitch : OOB;
+      const uint32_t xo_n = (ev_n.valid && ev_n.side == 0 && ev_n.wt > 0.f) ? (uint32_t)ev_n.rb * c.pitch : OOB;
       for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo_n) + c.lb); });
     }
     // the last wave's state after its chunk is the carry into the next chunks
@@ -733,7 +733,8 @@ struct BwdChunk {
 
 // Row gathers of a chunk: the v row of each write and the dO row of each read.
 // The kind of event i is the same in every lane, so its one load takes the
-// buffer of its kind (a scalar select); padding loads nothing.
+// buffer of its kind (a scalar select); padding and events of weight 0 (the
+// no-op events of masked tokens, whose rows may hold anything) load nothing.
 template <typename IO, int CPL>
 __device__ __forceinline__ void bwd_gather_rows(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
                                                 rsrc_t rv, rsrc_t ro,
@@ -741,7 +742,7 @@ __device__ __forceinline__ void bwd_gather_rows(const ScanBwdArgs& a, const SegC
                                                 float4 rec, int n) {
   using LN = Lanes<IO, CPL>;
   const Ev ev = decode_rec(rec, n, c.h, a.H);
-  const uint32_t xo = ev.valid ? (uint32_t)ev.rb * c.pitch : OOB;
+  const uint32_t xo = (ev.valid && ev.wt > 0.f) ? (uint32_t)ev.rb * c.pitch : OOB;
   const uint32_t wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
   for_up<0, CHUNK>([&](auto I) {
     x[I] = LN::load(((wm >> I) & 1u) ? rv : ro, bcu<I>(xo) + c.lb);

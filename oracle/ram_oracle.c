@@ -37,10 +37,15 @@
  *
  * Arithmetic: every floating-point value is held and computed in IEEE double.
  * Inputs arrive as double arrays (bf16 and fp32 io values convert exactly).
- * One decision is deliberately taken in float:
- * for U >= 2 the ranking key of a slot is the float sum of its raw digit
- * logits, ascending u, because that is the precision in which the GPU decoder
- * takes the same decision.  For U = 1 the key is the logit itself, exact.
+ * One decision is taken in float, by reading: for U >= 2 the ranking key of a
+ * slot is the float32 sum of its raw digit logits, taken in ascending u
+ * starting from 0.  The pages rank slots by a sum of per-digit log-scores
+ * (paper §4 "Efficient Address Decoding"; the slot probability is the
+ * product of the digit softmaxes, App. B.1) but fix neither the precision
+ * nor the order of that sum; near-ties rank one way or the other depending
+ * on both, so the reading fixes them (float32, the precision of the state
+ * and of all arithmetic on the path; ascending u, the digits' order).  For
+ * U = 1 the key is the logit itself, exact.
  *
  * Parallelism: OpenMP over independent (batch, head) pairs or rows only.
  * Compile with -ffp-contract=off so no fused multiply-add changes rounding.

@@ -8,6 +8,8 @@ import torch
 
 import linear_attention_ram_amd as ram
 import oracle
+import parity
+from parity import rel  # noqa: F401  (re-exported for the tests)
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
@@ -21,12 +23,26 @@ def host(t):
     return t.detach().double().cpu().numpy()
 
 
-def rel(x, ref):
-    x = np.asarray(x, np.float64)
-    ref = np.asarray(ref, np.float64)
-    den = float(np.max(np.abs(ref))) if ref.size else 0.0
-    num = float(np.max(np.abs(x - ref))) if ref.size else 0.0
-    return num / den if den > 0 else num
+def check_grads(got, ref, op, h, tol, names=("d_wlogits", "d_rlogits", "d_v", "d_gamma")):
+    """Gradients against the oracle's: the logit gradients with the split bar
+    of parity.check_logit_grad (selected entries normwise, the dense term
+    against its scale p_i * sum_j |g_j w_j|), the others normwise.  got: name -> tensor or host array; h:
+    the host inputs the oracle ran on (its decode gives the selected slots)."""
+    for name in names:
+        x = host(got[name]) if isinstance(got[name], torch.Tensor) else got[name]
+        if name in ("d_wlogits", "d_rlogits"):
+            side = 0 if name == "d_wlogits" else 1
+            logits = h["wl" if side == 0 else "rl"]
+            idx, w, lse = oracle.decode(op, side, logits)
+            U, P = int(op.U), int(op.P)
+            sel = parity.selected_entries(idx, U, P, int(op.cape_heads), int(op.t0))
+            renorm = bool(op.renorm_w if side == 0 else op.renorm_r)
+            gw = parity.gw_products(ref["dw" if side == 0 else "dr"], w, renorm)
+            scale = parity.dense_scale(logits, lse, gw, U, P)
+            parity.check_logit_grad(x, ref[name], sel, tol, name, scale)
+        else:
+            err = rel(x, ref[name])
+            assert err <= tol, (name, err)
 
 
 def gpu_problem(cfg, T=None, eps=None, renorm=(False, False), cape_heads=0, t0=0):

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def test_problem_struct_matches_header_size():
     assert ctypes.sizeof(ram.Problem) == 64
-    assert ctypes.sizeof(ram.WsLayout) == 21 * ctypes.sizeof(ctypes.c_size_t)
+    assert ctypes.sizeof(ram.WsLayout) == 22 * ctypes.sizeof(ctypes.c_size_t)
     assert ctypes.sizeof(ram.Epilogue) == 24
 
 
@@ -164,3 +164,17 @@ def test_gated_workspace_areas():
     assert L["fwd_bytes"] <= L["epi_d_o"] < L["epi_part"] < L["total_bytes"]
     assert L["epi_part"] - L["epi_d_o"] >= 2 * p.N * p.d_v
     assert L["total_bytes"] - L["epi_part"] >= 4 * 8192 * p.d_v
+
+
+def test_backward_scratch_leaves_the_forward_arrays_alone():
+    # the forward's read contributions (stash) stay intact through any number
+    # of backward calls: the reverse pass has its own d_v staging (stash_b),
+    # past fwd_bytes like the rest of its scratch
+    p = ram.problem(2, 3, 40, 64, 4, 5, 24, io="bf16")
+    L = ram.ram_workspace_layout(p)
+    assert L["stash"] < L["fwd_bytes"]
+    assert L["long_count"] - L["stash"] >= 2 * p.N * p.k_r * p.d_v
+    for name in ("stash_b", "dw", "dr", "dgam", "epi_d_o", "epi_part"):
+        assert L[name] >= L["fwd_bytes"], name
+    assert L["dw"] - L["stash_b"] >= 2 * p.N * p.k_w * p.d_v
+    assert L["dgam"] - L["dr"] >= 4 * p.N * p.k_r

@@ -7,8 +7,8 @@ import torch
 
 import linear_attention_ram_amd as ram
 import oracle
-from gpu_util import (TOL, bh_slice, gpu_problem, host, oracle_problem, rel, run_backward,
-                      run_forward, say)
+from gpu_util import (TOL, bh_slice, check_grads, gpu_problem, host, oracle_problem, rel,
+                      run_backward, run_forward, say)
 from linear_attention_ram_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -29,9 +29,8 @@ def full_check(cfg, x, p, with_state, with_state_grads, tol):
                          h["slot0"] if with_state else None, h["mass0"] if with_state else None,
                          h["d_o"], h["d_slot1"] if with_state_grads else None,
                          h["d_mass1"] if with_state_grads else None)
-    for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma"):
-        err = rel(host(g[name]), rg[name])
-        assert err <= tol, (name, err)
+    op = oracle_problem(p)
+    check_grads(g, rg, op, h, tol)
     views = ram.ws_views(p, r["ws"])
     # float32 internals computed from the same io values: tighter than the io bar
     assert rel(views["dw"].cpu().numpy().reshape(rg["dw"].shape), rg["dw"]) <= 1e-4
@@ -76,10 +75,9 @@ def test_1_3b_sampled_slices():
         s = bh_slice(x, b, h)
         op = oracle.problem(1, 1, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, eps=cfg.eps)
         rg = oracle.backward(op, s["wl"], s["rl"], s["v"], s["gamma"], None, None, s["d_o"])
-        for name, key in (("d_wlogits", "d_wlogits"), ("d_rlogits", "d_rlogits"),
-                          ("d_v", "d_v"), ("d_gamma", "d_gamma")):
-            err = rel(host(g[name][b:b + 1, :, h:h + 1]), rg[key])
-            assert err <= TOL["bf16"], (name, b, h, err)
+        got = {name: host(g[name][b:b + 1, :, h:h + 1])
+               for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma")}
+        check_grads(got, rg, op, s, TOL["bf16"])
 
 
 EDGE = [

@@ -8,7 +8,8 @@ import torch
 
 import linear_attention_ram_amd as ram
 import oracle
-from gpu_util import TOL, gpu_problem, host, oracle_problem, rel, run_backward, run_forward, say
+from gpu_util import (TOL, check_grads, gpu_problem, host, oracle_problem, rel, run_backward,
+                      run_forward, say)
 from linear_attention_ram_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -61,9 +62,7 @@ def full_fwd_bwd(cfg, p, x, tol, with_state):
                          h.get("slot0") if with_state else None, h.get("mass0") if with_state else None,
                          h["d_o"], h.get("d_slot1") if with_state else None,
                          h.get("d_mass1") if with_state else None)
-    for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma"):
-        err = rel(host(g[name]), rg[name])
-        assert err <= tol, (name, err)
+    check_grads(g, rg, op, h, tol)
     if with_state:
         assert rel(host(g["d_slot0"]), rg["d_slot0"]) <= tol
         assert rel(host(g["d_mass0"]), rg["d_mass0"]) <= tol

@@ -89,3 +89,49 @@ def test_1_3b_sampled_heads():
             say("1.3b side", side, "slice", b, h)
             rows = host(x[key][b:b + 1, :, h:h + 1])
             check_rows(p, side, x[key], rows, np.s_[b:b + 1, :, h:h + 1])
+
+
+@pytest.mark.parametrize("S,k,io,U", [(4096, 8, "bf16", 1), (16384, 8, "bf16", 1),
+                                      (64, 8, "f32", 1), (1024, 8, "bf16", 2),
+                                      (64, 5, "f32", 3)])
+def test_nan_logits_give_valid_distinct_slots(S, k, io, U):
+    # NaN logits rank below every number (the decoder's exact fallback), so a
+    # row always yields K distinct slots in range; rows without NaN decode as
+    # the oracle does, bit for bit
+    P = S if U == 1 else round(S ** (1.0 / U))
+    B, T, H = 1, 24, 2
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    g = torch.Generator(device=DEV).manual_seed(S + k + U)
+    shape = (B, T, H, S) if U == 1 else (B, T, H, U, P)
+    lg = torch.randn(shape, generator=g, device=DEV).to(dt)
+    flat = lg.view(B, T, H, U * P)
+    flat[0, 0, 0] = float("nan")                      # all NaN
+    flat[0, 1, 1, 3:] = float("nan")                  # 3 numbers, the rest NaN
+    flat[0, 2, 0, ::2] = float("nan")                 # every other entry NaN
+    flat[0, 3, 1, : U * P - 1] = float("nan")         # one number
+    p = ram.problem(B, H, T, None if U > 1 else S, k, k, 16, io=io, U=U, P=P)
+    idx = torch.empty((B, T, H, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((B, T, H, k), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, T, H, U), dtype=torch.float32, device=DEV)
+    ram.ram_decode(p, 0, lg, idx, w, lse)
+    torch.cuda.synchronize()
+    gi, gw = idx.cpu().numpy(), w.cpu().numpy()
+    assert gi.min() >= 0 and gi.max() < S
+    for b in range(B):
+        for t in range(T):
+            for h in range(H):
+                assert len(set(gi[b, t, h].tolist())) == k, (t, h)
+    # rows with a single digit and a few numbers: the numbers come first, in
+    # (value desc, index asc) order
+    if U == 1:
+        row = host(flat[0, 1, 1])
+        fin = np.flatnonzero(~np.isnan(row))
+        order = fin[np.lexsort((fin, -row[fin]))]
+        assert gi[0, 1, 1, :len(order)].tolist() == order[:k].tolist()
+        assert gi[0, 3, 1, 0] == U * P - 1
+    clean = np.ones((B, T, H), bool)
+    clean[0, 0, 0] = clean[0, 1, 1] = clean[0, 2, 0] = clean[0, 3, 1] = False
+    op = oracle.problem(B, H, T, S, k, k, 1, U=U, P=P)
+    oi, ow, _ = oracle.decode(op, 0, host(lg))
+    np.testing.assert_array_equal(gi[clean], oi[clean])
+    assert rel(gw[clean], ow[clean]) <= 1e-5

@@ -9,7 +9,7 @@ import torch
 
 import linear_attention_ram_amd as ram
 import oracle
-from gpu_util import TOL, bh_slice, gpu_problem, host, oracle_problem, rel, say
+from gpu_util import TOL, bh_slice, check_grads, gpu_problem, host, oracle_problem, rel, say
 from linear_attention_ram_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -54,13 +54,12 @@ def oracle_gated(op, h, hg, with_gain=True, eps=1e-6, with_state=False, mask=Non
     return rg
 
 
-def compare(p, y, slot1, mass1, g, ref, tol):
+def compare(p, y, slot1, mass1, g, ref, tol, h):
     assert rel(host(y), ref["y"]) <= tol
     assert rel(host(slot1), ref["slot1"]) <= tol
     assert rel(host(mass1), ref["mass1"]) <= tol
-    for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma", "d_gate"):
-        err = rel(host(g[name]), ref[name])
-        assert err <= tol, (name, err)
+    check_grads(g, ref, oracle_problem(p), h, tol,
+                ("d_wlogits", "d_rlogits", "d_v", "d_gamma", "d_gate"))
     err = rel(host(g["d_gain"]), ref["d_gain"])
     assert err <= tol, ("d_gain", err)
 
@@ -76,7 +75,7 @@ def test_tiny_full(with_gain, eps, with_state):
     h = {k: host(v) for k, v in x.items()}
     hg = {k: host(v) for k, v in gx.items()}
     ref = oracle_gated(oracle_problem(p), h, hg, with_gain, eps, with_state)
-    compare(p, y, s1, m1, g, ref, TOL["f32"])
+    compare(p, y, s1, m1, g, ref, TOL["f32"], h)
 
 
 GATED_EDGE = [
@@ -99,7 +98,7 @@ def test_edge_shapes(case):
     h = {k: host(v) for k, v in x.items()}
     hg = {k: host(v) for k, v in gx.items()}
     ref = oracle_gated(oracle_problem(p), h, hg, True, 1e-6, case % 2 == 0)
-    compare(p, y, s1, m1, g, ref, TOL[io])
+    compare(p, y, s1, m1, g, ref, TOL[io], h)
 
 
 @pytest.mark.parametrize("d_v", [32, 12])   # vector rows, and rows taken pair by pair
@@ -115,7 +114,7 @@ def test_masked_tokens(d_v):
     h = {k: host(v) for k, v in x.items()}
     hg = {k: host(v) for k, v in gx.items()}
     ref = oracle_gated(oracle_problem(p), h, hg, mask=mask)
-    compare(p, y, s1, m1, g, ref, TOL["f32"])
+    compare(p, y, s1, m1, g, ref, TOL["f32"], h)
     assert np.all(host(y)[mask == 0] == 0.0)
     assert np.all(host(g["d_gate"])[mask == 0] == 0.0)
 
@@ -130,7 +129,7 @@ def test_340m_full():
     hg = {k: host(v) for k, v in gx.items()}
     say("oracle gated 340m")
     ref = oracle_gated(oracle_problem(p), h, hg)
-    compare(p, y, s1, m1, g, ref, TOL["bf16"])
+    compare(p, y, s1, m1, g, ref, TOL["bf16"], h)
 
 
 def test_plain_and_gated_read_out_agree():
@@ -149,6 +148,40 @@ def test_plain_and_gated_read_out_agree():
     torch.cuda.synchronize()
     ref = oracle.epilogue_forward(host(o), host(gx["gate"]), host(gx["gain"]), 1e-6)
     assert rel(host(y), ref) <= 1e-5
+
+
+def test_gated_backward_repeats_on_one_forward():
+    # the backward recomputes o from the forward's read contributions, which
+    # it never overwrites: further gated backward calls after one forward
+    # (as with retain_graph) repeat the first bit for bit
+    cfg = synth.Config("gated-retain", 2, 2, 700, 128, 8, 8, 64, "bf16", zipf=1.1)
+    x = synth.layer_inputs(cfg, device=DEV, seed=92)
+    gx = synth.gate_inputs(cfg, device=DEV, seed=92)
+    p = gpu_problem(cfg)
+    ep = ram.epilogue(p, gx["gate"], gx["gain"], 1e-6)
+    ws = ram.workspace(p, True, DEV)
+    y = torch.empty_like(x["v"])
+    slot1 = torch.empty((p.B, p.H, p.S, p.d_v), dtype=torch.float32, device=DEV)
+    mass1 = torch.empty((p.B, p.H, p.S), dtype=torch.float32, device=DEV)
+    ram.ram_forward_gated(p, ep, x["wl"], x["rl"], x["v"], x["gamma"], None, None, y, slot1,
+                          mass1, ws)
+    outs = []
+    for _ in range(2):
+        g = {"d_wlogits": torch.empty_like(x["wl"]), "d_rlogits": torch.empty_like(x["rl"]),
+             "d_v": torch.empty_like(x["v"]), "d_gamma": torch.empty_like(x["gamma"]),
+             "d_gate": torch.empty_like(gx["gate"]),
+             "d_gain": torch.empty((p.d_v,), dtype=torch.float32, device=DEV)}
+        ram.ram_backward_gated(p, ep, ws, x["wl"], x["rl"], x["v"], x["gamma"], None, None,
+                               gx["d_y"], None, None, g["d_wlogits"], g["d_rlogits"], g["d_v"],
+                               g["d_gamma"], g["d_gate"], g["d_gain"])
+        outs.append(g)
+    torch.cuda.synchronize()
+    for name in outs[0]:
+        assert torch.equal(outs[0][name], outs[1][name]), name
+    h = {k: host(v) for k, v in x.items()}
+    hg = {k: host(v) for k, v in gx.items()}
+    ref = oracle_gated(oracle_problem(p), h, hg)
+    compare(p, y, slot1, mass1, outs[1], ref, TOL["bf16"], h)
 
 
 def test_gain_gradient_is_repeatable():
@@ -177,6 +210,6 @@ def test_1_3b_sampled_slices():
         op = oracle.problem(1, 1, cfg.T, cfg.S, cfg.k_w, cfg.k_r, cfg.d_v, eps=cfg.eps)
         ref = oracle_gated(op, s, sg)
         assert rel(host(y[b:b + 1, :, h:h + 1]), ref["y"]) <= TOL["bf16"]
-        for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma", "d_gate"):
-            err = rel(host(g[name][b:b + 1, :, h:h + 1]), ref[name])
-            assert err <= TOL["bf16"], (name, b, h, err)
+        names = ("d_wlogits", "d_rlogits", "d_v", "d_gamma", "d_gate")
+        got = {name: host(g[name][b:b + 1, :, h:h + 1]) for name in names}
+        check_grads(got, ref, op, s, TOL["bf16"], names)

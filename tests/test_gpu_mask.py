@@ -8,7 +8,7 @@ import torch
 
 import linear_attention_ram_amd as ram
 import oracle
-from gpu_util import TOL, gpu_problem, host, oracle_problem, rel, say
+from gpu_util import TOL, check_grads, gpu_problem, host, oracle_problem, rel, say
 from linear_attention_ram_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -54,8 +54,7 @@ def check(cfg, x, p, mask, with_state, tol):
     rg = oracle.backward(op, h["wl"], h["rl"], h["v"], h["gamma"],
                          h["slot0"] if with_state else None, h["mass0"] if with_state else None,
                          h["d_o"], mask=mk)
-    for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma"):
-        assert rel(host(g[name]), rg[name]) <= tol, name
+    check_grads(g, rg, op, h, tol)
     off = mk == 0
     assert not np.any(host(o)[off])
     for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma"):
@@ -104,3 +103,22 @@ def test_masked_decode_steps():
         assert rel(host(o), ref) <= TOL["f32"], step
     assert rel(host(slot), o_slot) <= TOL["f32"]
     assert rel(host(mass), o_mass) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_nan_inputs_at_masked_tokens(with_state):
+    # a masked token is absent, so whatever its rows hold (NaN here: logits
+    # of both sides, v, gamma and d_o) reaches nothing; hot slots put its
+    # no-op events on the cooperative scan path as well
+    cfg = synth.Config("mask-nan", 2, 3, 700, 128, 8, 8, 64, "bf16", zipf=1.1)
+    x = synth.layer_inputs(cfg, device=DEV, seed=34, with_state=True)
+    mask = random_mask(cfg.B, cfg.T, 3)
+    off = mask == 0
+    for key in ("wl", "rl", "v", "gamma", "d_o"):
+        x[key][off] = float("nan")
+    o, slot1, mass1, g = run(cfg, x, gpu_problem(cfg), mask, with_state)
+    assert torch.all(torch.isfinite(slot1)) and torch.all(torch.isfinite(mass1))
+    assert torch.all(torch.isfinite(o.float()))
+    for name, t in g.items():
+        assert torch.all(torch.isfinite(t.float())), name
+    check(cfg, x, gpu_problem(cfg), mask, with_state, TOL["bf16"])

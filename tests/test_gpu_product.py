@@ -9,8 +9,8 @@ import torch
 
 import linear_attention_ram_amd as ram
 import oracle
-from gpu_util import (TOL, bh_slice, gpu_problem, host, oracle_problem, rel, run_backward,
-                      run_forward, say)
+from gpu_util import (TOL, bh_slice, check_grads, gpu_problem, host, oracle_problem, rel,
+                      run_backward, run_forward, say)
 from linear_attention_ram_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -133,9 +133,7 @@ def full_check(cfg, p, x, tol, with_state=False, mask=None):
                          h["slot0"] if with_state else None, h["mass0"] if with_state else None,
                          h["d_o"], h["d_slot1"] if with_state else None,
                          h["d_mass1"] if with_state else None, mask=mask)
-    for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma"):
-        err = rel(host(g[name]), rg[name])
-        assert err <= tol, (name, err)
+    check_grads(g, rg, op, h, tol)
     # decoded-weight gradients (float32 internals) of valid tokens; a masked
     # token's events are weight-0 no-ops whose internal gradient feeds nothing
     valid = np.ones((p.B, p.T), bool) if mask is None else np.asarray(mask, bool)
@@ -205,9 +203,9 @@ def test_1_3b_factorised_sampled_slices():
         oo, _, _ = oracle.forward(op, s["wl"], s["rl"], s["v"], s["gamma"])
         assert rel(host(r["o"][b:b + 1, :, h:h + 1]), oo) <= TOL["bf16"]
         rg = oracle.backward(op, s["wl"], s["rl"], s["v"], s["gamma"], None, None, s["d_o"])
-        for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma"):
-            err = rel(host(g[name][b:b + 1, :, h:h + 1]), rg[name])
-            assert err <= TOL["bf16"], (name, b, h, err)
+        got = {name: host(g[name][b:b + 1, :, h:h + 1])
+               for name in ("d_wlogits", "d_rlogits", "d_v", "d_gamma")}
+        check_grads(got, rg, op, s, TOL["bf16"])
 
 
 def test_decode_step():
