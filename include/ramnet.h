@@ -118,7 +118,8 @@ typedef struct ram_ws_layout {
   size_t lse_r;       /* float (N, U)                                                             */
   size_t seg_offset;  /* int32 (B*H*S + 1): first event of segment g = (b*H + h)*S + a          */
   size_t events;      /* (E) 16-byte records {int32 code, float weight, float lambda, float
-                         d lambda/d w}; code = (t << 7) | (side << 6) | j; segment-major, time
+                         d lambda/d w}; code = (t << 7) | (side << 6) | j, bit 31 set for
+                         the (weight 0, no-op) events of masked tokens; segment-major, time
                          order inside a segment, a token's write before its read            */
   size_t ckpt_s;      /* float (E/16 + 1, d_v): slot content at every 16-aligned event        */
   size_t ckpt_m;      /* float (E/16 + 1): slot mass at the same points                      */

@@ -129,8 +129,9 @@ __device__ __forceinline__ int tile_event_slot(const BucketArgs& a, int b, int h
 }
 
 // 16-byte record of event e (< n) of a tile.  A masked token keeps its
-// events with weight 0: an exact no-op write (retention 1, step 0) and a
-// read that contributes 0.
+// events with weight 0, flagged by bit 31 of the code: an exact no-op write
+// (retention 1, step 0) and a read that contributes 0, neither of which loads
+// the token's rows.
 template <typename IO>
 __device__ __forceinline__ EventRec tile_event_rec(const BucketArgs& a, int b, int h, int t_lo,
                                                    int K, int e) {
@@ -146,6 +147,7 @@ __device__ __forceinline__ EventRec tile_event_rec(const BucketArgs& a, int b, i
     rec.code = (t << 7) | (1 << 6) | (p - a.k_w);
     rec.w = live ? a.w_r[row * a.k_r + (p - a.k_w)] : 0.f;
   }
+  if (!live) rec.code = (int32_t)((uint32_t)rec.code | 0x80000000u);
   return rec;
 }
 

@@ -22,7 +22,7 @@ constexpr uint32_t MAX_BUF_BYTES = 0x7FE00000u;  // one batch's v, dO or stash r
 
 // One event of the segment lists: 16 bytes, read with one vector load.
 struct EventRec {
-  int32_t code;           // (t << 7) | (side << 6) | j
+  int32_t code;           // (t << 7) | (side << 6) | j; bit 31: a masked token's no-op event
   float w;                // write weight or read weight
   float lam;              // retention of a write (1 for a read)
   float dlam;             // d lambda / d w of a write (0 for a read)

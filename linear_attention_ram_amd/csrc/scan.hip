@@ -204,6 +204,7 @@ __device__ __forceinline__ SegCtx<IO, CPL> seg_ctx(int64_t g, int S, int H, int 
 // Scalars of event (lane & 15) of a chunk.
 struct Ev {
   bool valid;   // the chunk has this event
+  bool live;    // not the no-op event of a masked token (its rows are never loaded)
   int side;     // 0 write, 1 read (padding: read of weight 0)
   int rb;       // token row inside the batch: t*H + h
   int j;        // rank inside the side's top-K
@@ -228,9 +229,10 @@ __device__ __forceinline__ Ev decode_rec(float4 raw, int n, int h, int H) {
   e.valid = (lane_id() & (CHUNK - 1)) < n;
   const float4 r = e.valid ? raw : make_float4(__int_as_float(1 << 6), 0.f, 1.f, 0.f);
   const int code = __float_as_int(r.x);
+  e.live = code >= 0;
   e.side = (code >> 6) & 1;
   e.j = code & 63;
-  e.rb = (code >> 7) * H + h;
+  e.rb = ((code & 0x7FFFFFFF) >> 7) * H + h;
   e.wt = r.y;
   e.lam = r.z;
   e.dl = r.w;
@@ -482,7 +484,7 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
     mass_apply(M, ev, m, a.eps);
     m = readlane_f(M.mi, n - 1);
     const float rr = (ev.side == 1) ? ev.wt : 0.f;
-    const uint32_t xo = (ev.valid && ev.side == 0 && ev.wt > 0.f) ? (uint32_t)ev.rb * c.pitch : OOB;
+    const uint32_t xo = (ev.valid && ev.live && ev.side == 0) ? (uint32_t)ev.rb * c.pitch : OOB;
     const uint32_t so = (ev.valid && ev.side == 1) ? ((uint32_t)ev.rb * a.k_r + ev.j) * c.pitch : OOB;
     rec = load_rec(a.events, p1, min(end, (p1 / CHUNK + 1) * CHUNK) - p1, beg, end);   // next chunk
 
@@ -533,7 +535,7 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
   {
     const int n0 = chunk_start(beg, w + 1, end) - chunk_start(beg, w, end);
     const Ev ev0 = decode_rec(rec, n0, c.h, a.H);
-    const uint32_t xo0 = (ev0.valid && ev0.side == 0 && ev0.wt > 0.f) ? (uint32_t)ev0.rb * c.pitch : OOB;
+    const uint32_t xo0 = (ev0.valid && ev0.live && ev0.side == 0) ? (uint32_t)ev0.rb * c.pitch : OOB;
     for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo0) + c.lb); });
   }
   for (int p = beg; p < end;) {
@@ -625,7 +627,7 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
     {   // rows of this wave's next chunk (past the end: no valid event, no load)
       const int n_n = chunk_start(pn, w + 1, end) - chunk_start(pn, w, end);
       const Ev ev_n = decode_rec(rec, n_n, c.h, a.H);
-      const uint32_t xo_n = (ev_n.valid && ev_n.side == 0 && ev_n.wt > 0.f) ? (uint32_t)ev_n.rb * c.pitch : OOB;
+      const uint32_t xo_n = (ev_n.valid && ev_n.live && ev_n.side == 0) ? (uint32_t)ev_n.rb * c.pitch : OOB;
       for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo_n) + c.lb); });
     }
     // the last wave's state after its chunk is the carry into the next chunks
@@ -733,8 +735,8 @@ struct BwdChunk {
 
 // Row gathers of a chunk: the v row of each write and the dO row of each read.
 // The kind of event i is the same in every lane, so its one load takes the
-// buffer of its kind (a scalar select); padding and events of weight 0 (the
-// no-op events of masked tokens, whose rows may hold anything) load nothing.
+// buffer of its kind (a scalar select); padding and the no-op events of
+// masked tokens (whose rows may hold anything) load nothing.
 template <typename IO, int CPL>
 __device__ __forceinline__ void bwd_gather_rows(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
                                                 rsrc_t rv, rsrc_t ro,
@@ -742,7 +744,7 @@ __device__ __forceinline__ void bwd_gather_rows(const ScanBwdArgs& a, const SegC
                                                 float4 rec, int n) {
   using LN = Lanes<IO, CPL>;
   const Ev ev = decode_rec(rec, n, c.h, a.H);
-  const uint32_t xo = (ev.valid && ev.wt > 0.f) ? (uint32_t)ev.rb * c.pitch : OOB;
+  const uint32_t xo = (ev.valid && ev.live) ? (uint32_t)ev.rb * c.pitch : OOB;
   const uint32_t wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
   for_up<0, CHUNK>([&](auto I) {
     x[I] = LN::load(((wm >> I) & 1u) ? rv : ro, bcu<I>(xo) + c.lb);
