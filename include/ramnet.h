@@ -234,6 +234,26 @@ int ram_decode_step(const ram_problem* p, const void* wlogits, const void* rlogi
                     const void* gamma, const uint8_t* mask, float* slot, float* mass, void* o,
                     void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments (less the workspace), kernels and results as
+ * ram_forward.  Its workspace is an array of RAM_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each device it runs on, from the library's load on
+ * that device until the process ends; the call itself allocates nothing and
+ * creates no stream or event, and every kernel runs on the given stream.
+ * A problem whose forward workspace (ram_workspace_size with
+ * with_backward = 0) exceeds the array returns RAM_ECAPACITY with nothing
+ * enqueued (64 MiB holds the 340M-layer shape, B=4, H=8, T=2048, S=1024,
+ * k=4, d_v=64, and 1,024 tokens of 16 heads at S=4096, k=8, d_v=128).
+ * Every call on a device shares that device's array and leaves its contents
+ * to the next call: calls that overlap on one device (several streams or
+ * host threads) race and must be ordered by the caller, and no ram_backward
+ * can follow (use ram_forward with a workspace for training). */
+#define RAM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ram_forward_noalloc(const ram_problem* p, const void* wlogits, const void* rlogits,
+                        const void* v, const void* gamma, const uint8_t* mask, const float* slot0,
+                        const float* mass0, void* o, float* slot1, float* mass1, void* stream);
+
 /* Text of a status code (static storage). */
 const char* ram_status_string(int status);
 

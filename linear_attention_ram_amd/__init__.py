@@ -6,7 +6,8 @@ kernels of ``_lib/libramnet.so`` behind the C ABI declared in
 missing the calls raise.  PyTorch supplies device memory and the stream.
 
 Functions keep the C names: ``ram_workspace_size``, ``ram_workspace_layout``,
-``ram_decode``, ``ram_forward``, ``ram_backward``, ``ram_forward_gated``,
+``ram_decode``, ``ram_forward``, ``ram_forward_noalloc``, ``ram_backward``,
+``ram_forward_gated``,
 ``ram_backward_gated`` (with ``epilogue`` to build their gate argument),
 ``ram_decode_step``,
 ``ram_status_string``, plus ``ram_prof_enable`` / ``ram_prof_collect``.
@@ -27,7 +28,8 @@ RAM_OK, RAM_EINVAL, RAM_EDTYPE, RAM_ECAPACITY, RAM_EUNSUPPORTED, RAM_EHIP = 0, -
 RAM_F32, RAM_BF16 = 0, 1
 EXPORTED = ("ram_workspace_size", "ram_workspace_layout", "ram_decode", "ram_forward",
             "ram_backward", "ram_forward_gated", "ram_backward_gated", "ram_decode_step",
-            "ram_status_string", "ram_prof_enable", "ram_prof_collect")
+            "ram_forward_noalloc", "ram_status_string", "ram_prof_enable", "ram_prof_collect")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # RAM_NOALLOC_SCRATCH_BYTES
 
 
 class Problem(ctypes.Structure):
@@ -114,6 +116,7 @@ def lib() -> ctypes.CDLL:
     L.ram_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.ram_backward.argtypes = [P, vp, sz] + [vp] * 17
     L.ram_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.ram_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     EP = ctypes.POINTER(Epilogue)
     L.ram_forward_gated.argtypes = [P, EP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.ram_backward_gated.argtypes = [P, EP, vp, sz] + [vp] * 19
@@ -251,6 +254,24 @@ def ram_backward(p: Problem, ws, wlogits, rlogits, v, gamma, slot0, mass0, d_o, 
             _ptr(d_slot0, "d_slot0", torch.float32, nseg * p.d_v, optional=True),
             _ptr(d_mass0, "d_mass0", torch.float32, nseg, optional=True))
     _check(lib().ram_backward(ctypes.byref(p), *args, _stream(stream, ws.device)), "ram_backward")
+
+
+def ram_forward_noalloc(p: Problem, wlogits, rlogits, v, gamma, slot0, mass0, o, slot1, mass1,
+                        stream=None, mask=None):
+    """ram_forward without a workspace (the library's per-device array of
+    NOALLOC_SCRATCH_BYTES); no backward can follow it."""
+    io = p.torch_dtype
+    N, nseg = p.N, p.B * p.H * p.S
+    args = (_ptr(wlogits, "wlogits", io, N * p.row), _ptr(rlogits, "rlogits", io, N * p.row),
+            _ptr(v, "v", io, N * p.d_v), _ptr(gamma, "gamma", io, N),
+            _ptr(mask, "mask", torch.uint8, p.B * p.T, optional=True),
+            _ptr(slot0, "slot0", torch.float32, nseg * p.d_v, optional=True),
+            _ptr(mass0, "mass0", torch.float32, nseg, optional=True),
+            _ptr(o, "o", io, N * p.d_v),
+            _ptr(slot1, "slot1", torch.float32, nseg * p.d_v),
+            _ptr(mass1, "mass1", torch.float32, nseg))
+    _check(lib().ram_forward_noalloc(ctypes.byref(p), *args, _stream(stream, o.device)),
+           "ram_forward_noalloc")
 
 
 def epilogue(p: Problem, gate, gain=None, eps=1e-6) -> Epilogue:

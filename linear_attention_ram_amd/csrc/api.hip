@@ -160,6 +160,8 @@ void prof_after(const char*, hipStream_t st) {
   if (r.b) (void)hipEventRecord(r.b, st);
 }
 
+void prof_none(const char*, hipStream_t) {}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? RAM_OK : RAM_EHIP; }
 
 // ---- library streams ---------------------------------------------------------
@@ -311,8 +313,8 @@ bool ran_in_place(const void* ws) {
 }
 
 // ram_forward, or with ep the gated read-out y = sigmoid(gate) * RMSNorm(o)
-// written to o.  one_stream: every kernel on the caller's stream (no library
-// streams or events are created or used).
+// written to o.  one_stream: every kernel on the caller's stream, and no
+// library stream, event or timing record is created or used.
 int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogits,
                  const void* rlogits, const void* v, const void* gamma, const uint8_t* mask,
                  const float* slot0, const float* mass0, void* o, float* slot1, float* mass1,
@@ -336,6 +338,8 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
   const bool bf = p->io_dtype == RAM_BF16;
   const int cap = long_cap(d);
 
+  void (*before)(const char*, hipStream_t) = one_stream ? prof_none : prof_before;
+  void (*after)(const char*, hipStream_t) = one_stream ? prof_none : prof_after;
   std::lock_guard<std::mutex> lk(sched_mu);
   Sched local;
   Sched* S = &local;
@@ -367,9 +371,9 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
   da.T = p->T;
   da.cape_heads = p->cape_heads;
   da.t0 = p->t0 % d.S;
-  prof_before("decode_fwd", s);
+  before("decode_fwd", s);
   e = launch_decode_fwd(da, bf, s);
-  prof_after("decode_fwd", s);
+  after("decode_fwd", s);
   if (e != hipSuccess) return RAM_EHIP;
 
   BucketArgs ba{};
@@ -397,7 +401,7 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
   ba.long_list = (int32_t*)(w + L.long_list);
   ba.long_count = (int32_t*)(w + L.long_count);
   ba.long_cap = cap;
-  e = launch_bucket(ba, bf, s, prof_before, prof_after);
+  e = launch_bucket(ba, bf, s, before, after);
   if (e != hipSuccess) return RAM_EHIP;
 
   ScanFwdArgs sa{};
@@ -428,11 +432,11 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
   // The short-segment stream forks off just before the launch and joins
   // right after it; the timing events bracket the fork and the join (an
   // event recorded between the launch and the join slows the scans down).
-  prof_before("scan_fwd", s);
+  before("scan_fwd", s);
   S->dep(b, s);
   e = launch_scan_fwd(sa, bf, s, b);
   S->dep(s, b);
-  prof_after("scan_fwd", s);
+  after("scan_fwd", s);
   if (e != hipSuccess || S->err != hipSuccess) return RAM_EHIP;
 
   if (ep) {
@@ -447,9 +451,9 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
     ea.gain = ep->gain;
     ea.eps = ep->eps;
     ea.y = o;
-    prof_before("epilogue_fwd", s);
+    before("epilogue_fwd", s);
     e = launch_epilogue_fwd(ea, bf, s);
-    prof_after("epilogue_fwd", s);
+    after("epilogue_fwd", s);
   } else {
     FinalizeArgs fa{};
     fa.N = d.N;
@@ -457,9 +461,9 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
     fa.k = p->k_r;
     fa.stash = sa.stash;
     fa.out = o;
-    prof_before("finalize_o", s);
+    before("finalize_o", s);
     e = launch_finalize(fa, bf, s);
-    prof_after("finalize_o", s);
+    after("finalize_o", s);
   }
   return e == hipSuccess ? RAM_OK : RAM_EHIP;
 }
@@ -613,9 +617,53 @@ int backward_impl(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t
   return e == hipSuccess ? RAM_OK : RAM_EHIP;
 }
 
+// ---- allocation-free forward -------------------------------------------------
+// The workspace of ram_forward_noalloc: one array per device in the library's
+// code object (allocated when the library is loaded on a device, held until
+// the process ends).  Host code never uses the array's name as an address:
+// its device address comes from hipGetSymbolAddress, once per device, with
+// that device current.
+static __device__ __align__(256) unsigned char scratch[RAM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+hipError_t device_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
+
+int ram_forward_noalloc(const ram_problem* p, const void* wlogits, const void* rlogits,
+                        const void* v, const void* gamma, const uint8_t* mask, const float* slot0,
+                        const float* mass0, void* o, float* slot1, float* mass1, void* stream) {
+  Dims d;
+  const int st = check_problem(p, &d);
+  if (st != RAM_OK) return st;
+  ram_ws_layout L;
+  make_layout(p, d, &L);
+  if (L.fwd_bytes > RAM_NOALLOC_SCRATCH_BYTES) return RAM_ECAPACITY;
+  void* ws = nullptr;
+  if (device_scratch(&ws) != hipSuccess) return RAM_EHIP;
+  return forward_impl(p, nullptr, wlogits, rlogits, v, gamma, mask, slot0, mass0, o, slot1, mass1,
+                      ws, RAM_NOALLOC_SCRATCH_BYTES, stream, true);
+}
 
 int ram_forward(const ram_problem* p, const void* wlogits, const void* rlogits, const void* v,
                 const void* gamma, const uint8_t* mask, const float* slot0, const float* mass0,
