@@ -18,6 +18,8 @@ plain oracle on a bounded sample of (b, h) slices of the same workload on
 the host cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --config 340m [--flush]   # the 340M layer, caches warm or flushed
+  python bench.py --config stream      # HBM read and copy roofs of the decoders' pattern
   python bench.py --copy-calibration   # plain 1 GiB copies (HBM counter scale)
 """
 import argparse
@@ -270,6 +272,49 @@ def bench_long(args, torch, ram, synth, dev):
     }
 
 
+def bench_stream(args, torch, ram, dev):
+    """HBM streaming roofs with the decoders' access pattern (ram_stream_probe):
+    read-only and copy (read a row, write a row) of a 4 GiB buffer, per probe
+    variant, median of args.steps repetitions after args.warmup; torch's own
+    copy of the same buffer for reference.  GB/s count the bytes read plus the
+    bytes written."""
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(7)
+    reps = max(3, args.steps)
+
+    def timed(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            out.append(a.elapsed_time(b) * 1e-3)
+        return sorted(out)[len(out) // 2]
+
+    read, copy = {}, {}
+    for v, name in enumerate(ram.STREAM_PROBE_VARIANTS):
+        read[name] = n / timed(lambda: ram.ram_stream_probe(0, v, src, dst)) / 1e9
+        copy[name] = 2 * n / timed(lambda: ram.ram_stream_probe(1, v, src, dst)) / 1e9
+    torch_copy = 2 * n / timed(lambda: dst.copy_(src)) / 1e9
+    own = ram.STREAM_PROBE_VARIANTS[0]
+    return {
+        "metric": "HBM streaming roofs of the decoders' access pattern on 1 MI355X",
+        "value": copy[own], "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "higher_is_better": True, "vs_baseline": None, "data": "synthetic",
+        "config": {"workload": "stream 4 GiB: read-only and copy", "bytes": n,
+                   "value_is": f"copy, {own}"},
+        "read_GBps": read, "copy_GBps": copy, "torch_copy_GBps": torch_copy,
+        "read_frac_of_peak": {k: v / PEAK_HBM_GBS for k, v in read.items()},
+        "copy_frac_of_peak": {k: v / PEAK_HBM_GBS for k, v in copy.items()},
+    }
+
+
 def copy_calibration(steps=5):
     import torch
     n = 1 << 30
@@ -294,7 +339,11 @@ def main():
                     help="workload: 1.3b (default, the measured one), 340m, 1.3b-uniform "
                          "(no hot-slot bias) or 1.3b-u2 (U = 2 digits of 64): fwd+bwd "
                          "steps; decode: autoregressive steps of 256 sequences; long: "
-                         "a 65,536-token forward in 4,096-token chunks with state carry")
+                         "a 65,536-token forward in 4,096-token chunks with state carry; "
+                         "stream: the HBM read and copy roofs of the decoders' pattern")
+    ap.add_argument("--flush", action="store_true",
+                    help="fwd+bwd configs: overwrite a 1 GiB buffer before every step (evicts "
+                         "L2 and the 256 MB Infinity Cache) and time only the steps")
     ap.add_argument("--gated", action="store_true",
                     help="fwd+bwd configs: the gated read-out y = sigmoid(gate) * RMSNorm(o) "
                          "fused into the read (ram_forward_gated / ram_backward_gated)")
@@ -322,6 +371,9 @@ def main():
         return
     if args.config == "long":
         print(json.dumps(bench_long(args, torch, ram, synth, dev)))
+        return
+    if args.config == "stream":
+        print(json.dumps(bench_stream(args, torch, ram, dev)))
         return
     if args.config == "1.3b-uniform":
         cfg = synth.CONFIGS["1.3b"].with_(zipf=None, name="1.3b-uniform")
@@ -353,18 +405,39 @@ def main():
         ram.ram_backward(p, ws, x["wl"], x["rl"], x["v"], x["gamma"], None, None, x["d_o"],
                          None, None, d_wl, d_rl, d_v, d_g)
 
-    for _ in range(args.warmup):
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+
+    def flush(i):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 255)
+
+    for i in range(args.warmup):
+        flush(i)
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    if args.flush:
+        # each step bracketed by events on the current stream (the library
+        # joins its own stream back into it), the flush left out
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i, (a, b) in enumerate(evs):
+            flush(i)
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        elapsed = sum(a.elapsed_time(b) for a, b in evs) * 1e-3
+    else:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     # second pass: per-kernel events
     ram.ram_prof_enable(True)
     torch.cuda.synchronize()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        flush(i)
         step()
     torch.cuda.synchronize()
     prof = ram.ram_prof_collect()
@@ -398,6 +471,8 @@ def main():
                    "io_dtype": "bf16", "state": "f32",
                    "address_bias": f"Zipf({cfg.zipf}) per slot" if cfg.zipf else "none",
                    "tokens_per_step": tokens,
+                   "caches": ("flushed before every step (1 GiB overwrite)" if args.flush
+                              else "warm (no flush between steps)"),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "decode_bwd", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,

@@ -257,6 +257,20 @@ int ram_forward_noalloc(const ram_problem* p, const void* wlogits, const void* r
 /* Text of a status code (static storage). */
 const char* ram_status_string(int status);
 
+/* Measurement only (not part of the method): the HBM streaming roofs the
+ * decoders work against.  Streams `bytes` from src with the decoders' access
+ * pattern (a wave reads one contiguous row with 16-byte vector loads, all of
+ * its loads in flight at once) and, with mode 1, writes it to dst (a copy,
+ * the pattern of a decode backward row: read a row, write a row); mode 0
+ * only reads.  variant: 0 = 8 KiB rows, 4 waves per workgroup, nontemporal
+ * loads and stores (the decoders' own); 1 = the same with plain loads and
+ * stores; 2 = 16 KiB rows; 3 = 4 KiB rows; 4 = 8 waves per workgroup.  src
+ * and dst are device buffers of `bytes` each, 16-byte aligned; bytes must be a
+ * multiple of the variant's workgroup tile (128 KiB covers every variant),
+ * else RAM_EINVAL.  Asynchronous on the given stream. */
+int ram_stream_probe(int mode, int variant, const void* src, void* dst, size_t bytes,
+                     void* stream);
+
 /* Optional kernel timing: while enabled, every kernel the library launches
  * is bracketed by HIP events on its stream.  ram_prof_collect waits for
  * those events and returns, per kernel name, the launch count and summed

@@ -28,7 +28,8 @@ RAM_OK, RAM_EINVAL, RAM_EDTYPE, RAM_ECAPACITY, RAM_EUNSUPPORTED, RAM_EHIP = 0, -
 RAM_F32, RAM_BF16 = 0, 1
 EXPORTED = ("ram_workspace_size", "ram_workspace_layout", "ram_decode", "ram_forward",
             "ram_backward", "ram_forward_gated", "ram_backward_gated", "ram_decode_step",
-            "ram_forward_noalloc", "ram_status_string", "ram_prof_enable", "ram_prof_collect")
+            "ram_forward_noalloc", "ram_stream_probe", "ram_status_string", "ram_prof_enable",
+            "ram_prof_collect")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # RAM_NOALLOC_SCRATCH_BYTES
 
 
@@ -117,6 +118,7 @@ def lib() -> ctypes.CDLL:
     L.ram_backward.argtypes = [P, vp, sz] + [vp] * 17
     L.ram_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.ram_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.ram_stream_probe.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, sz, vp]
     EP = ctypes.POINTER(Epilogue)
     L.ram_forward_gated.argtypes = [P, EP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.ram_backward_gated.argtypes = [P, EP, vp, sz] + [vp] * 19
@@ -337,6 +339,20 @@ def ram_decode_step(p: Problem, wlogits, rlogits, v, gamma, slot, mass, o, strea
             _ptr(mass, "mass", torch.float32, BH * S), _ptr(o, "o", io, BH * p.d_v))
     _check(lib().ram_decode_step(ctypes.byref(p), *args, _stream(stream, slot.device)),
            "ram_decode_step")
+
+
+STREAM_PROBE_VARIANTS = ("8 KiB rows, 4 waves, nontemporal", "8 KiB rows, 4 waves, plain",
+                         "16 KiB rows, 4 waves, nontemporal", "4 KiB rows, 4 waves, nontemporal",
+                         "8 KiB rows, 8 waves, nontemporal")
+
+
+def ram_stream_probe(mode: int, variant: int, src, dst, stream=None):
+    """HBM streaming roof: mode 0 reads src, mode 1 copies src to dst (uint8
+    device tensors of equal size, a multiple of 128 KiB)."""
+    n = src.numel()
+    _check(lib().ram_stream_probe(int(mode), int(variant), _ptr(src, "src", torch.uint8),
+                                  _ptr(dst, "dst", torch.uint8, n), ctypes.c_size_t(n),
+                                  _stream(stream, src.device)), "ram_stream_probe")
 
 
 def ram_prof_enable(on: bool = True):

@@ -8,7 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libramnet.so")
-SOURCES = ["api.hip", "decode.hip", "bucket.hip", "scan.hip", "step.hip", "epilogue.hip"]
+SOURCES = ["api.hip", "decode.hip", "bucket.hip", "scan.hip", "step.hip", "epilogue.hip",
+           "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
