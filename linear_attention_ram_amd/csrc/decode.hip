@@ -31,6 +31,7 @@ namespace ramk {
 // per row) with streaming stores: small stores scattered through the read
 // stream cost far more HBM time than their bytes.
 constexpr int FWD_ROWS = 4;   // rows (waves) per decode_fwd workgroup
+constexpr int U2_ROWS = 4;    // two-digit rows per wave of the U = 2 kernels
 
 template <typename IO, int NV, bool FULL = false>
 __global__ __launch_bounds__(FWD_ROWS * WAVE) void decode_fwd_kernel(DecodeFwdArgs a) {
@@ -212,6 +213,57 @@ __global__ __launch_bounds__(256) void decode_fwd_prod_kernel(DecodeFwdArgs a) {
   if (lane < a.U) a.lse[side][row * a.U + lane] = scratch[wv].dlse[lane];
 }
 
+// Two-digit rows of at most 64 logits per digit (decode_row_u2_vals): R rows
+// per wave, every row's logits requested before the first row is decoded,
+// so the R rows share one memory round trip.  A row whose register search
+// gives up (massive ties, NaN) takes the general prefix search.
+template <typename IO, int R>
+__global__ __launch_bounds__(256) void decode_fwd_u2_kernel(DecodeFwdArgs a) {
+  __shared__ ProdScratch scratch[4];
+  __shared__ int s_idx[4][MAX_K];
+  __shared__ float s_w[4][MAX_K];
+  const int wv = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int64_t total = (int64_t)a.nsides * a.N;
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + wv) * R;
+  const int P = a.P;
+  const bool in = lane < P;
+  float l0[R], l1[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t grow = g0 + r;
+    const bool valid = grow < total;
+    const int side = grow >= a.N ? 1 : 0;
+    const int64_t row = grow - (int64_t)side * a.N;
+    const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)(2 * P);
+    l0[r] = (valid && in) ? to_f32(src[lane]) : -INFINITY;
+    l1[r] = (valid && in) ? to_f32(src[P + lane]) : -INFINITY;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t grow = g0 + r;
+    if (grow >= total) break;
+    const int side = grow >= a.N ? 1 : 0;
+    const int64_t row = grow - (int64_t)side * a.N;
+    const int k = a.k[side];
+    if (!decode_row_u2_vals(l0[r], l1[r], P, k, a.renorm[side], sizeof(IO) == 2, scratch[wv],
+                            s_idx[wv], s_w[wv])) {
+      wave_sync();
+      const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)(2 * P);
+      decode_row_product<IO>(src, 2, P, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv], false);
+    }
+    wave_sync();
+    if (lane < k) {
+      const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
+      const int id = s_idx[wv][lane];
+      a.idx[side][row * k + lane] = (shift < 0) ? id : (id + shift) % a.S;
+      a.w[side][row * k + lane] = s_w[wv][lane];
+    }
+    if (lane < 2) a.lse[side][row * 2 + lane] = scratch[wv].dlse[lane];
+    wave_sync();   // the next row rewrites the scratch
+  }
+}
+
 // Decode backward of product rows (one wave per row): with gw_j as for one
 // digit, dl_u[i] = sum_j gw_j [digit u of a_j = i] - p_u[i] sum_j gw_j,
 // p_u = exp(l_u - lse_u) the digit softmax (paper App. B.1: the slot
@@ -291,6 +343,12 @@ __global__ __launch_bounds__(256) void decode_bwd_prod_kernel(DecodeBwdArgs a) {
 hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st) {
   const int64_t rows = (int64_t)a.nsides * a.N;
   if (rows == 0) return hipSuccess;
+  if (a.U == 2 && a.P <= WAVE) {
+    const dim3 grid((unsigned)((rows + 4 * U2_ROWS - 1) / (4 * U2_ROWS))), block(256);
+    if (bf16) hipLaunchKernelGGL((decode_fwd_u2_kernel<bf16_t, U2_ROWS>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_fwd_u2_kernel<float, U2_ROWS>), grid, block, 0, st, a);
+    return hipGetLastError();
+  }
   if (a.U > 1) {
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     if (bf16) hipLaunchKernelGGL(decode_fwd_prod_kernel<bf16_t>, grid, block, 0, st, a);

@@ -100,21 +100,39 @@ __device__ __noinline__ void product_k_passes(ProdScratch& sc, int U, int P, int
   }
 }
 
+// K-th largest lane value with multiplicity, for values that are bf16
+// numbers (their ordered bit patterns end in 16 zero bits, or 16 one bits
+// for negative values): the same search as kth_lane_max over the upper 16
+// bits only.
+__device__ __forceinline__ float kth_lane_max_bf16(float m, int k) {
+  const uint32_t mb = ordered_bits(m) >> 16;
+  const int ku = __builtin_amdgcn_readfirstlane(k);
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    t = (__popcll(__ballot(mb >= c)) >= ku) ? c : t;
+    t = __builtin_amdgcn_readfirstlane(t);
+  }
+  return from_ordered((t << 16) | ((t & 0x8000u) ? 0u : 0xFFFFu));
+}
+
 // Two digits of at most 64 values, in registers (lane L holds l0[L] and
-// l1[L]).  The best key with digit-1 value L is fl(M0 + l1[L]) (M0 the
-// largest digit-0 logit); tau = the K-th largest of these over the lanes is
-// the key of K distinct slots, so at most the K-th best key.  Only digit-1
-// values whose bound reaches tau can appear in the top K; for each of them
-// one wave-wide add gives the keys of all its slots, and those reaching tau
-// are listed and ranked exactly.  Returns false, having written nothing to
-// sel_i / sel_w, when the list would overflow (massive ties).
-template <typename IO>
-__device__ bool decode_row_u2(const IO* __restrict__ row, int P, int k, int renorm,
-                              ProdScratch& sc, int* sel_i, float* sel_w) {
+// l1[L], -inf past P).  The best key with digit-1 value L is fl(M0 + l1[L])
+// (M0 the largest digit-0 logit); tau = the K-th largest of these over the
+// lanes is the key of K distinct slots, so at most the K-th best key.  As
+// fl(M0 + x) is non-decreasing in x, tau = fl(M0 + the K-th largest l1),
+// which for bf16 logits is found by a 16-bit search.  Only digit-1 values
+// whose bound reaches tau can appear in the top K; for each of them one
+// wave-wide add gives the keys of all its slots, and those reaching tau are
+// listed and ranked exactly (from registers when at most 64 are listed).
+// Returns false, having written nothing to sel_i / sel_w, when the list
+// would overflow (massive ties) or hold fewer than K slots (NaN logits).
+__device__ __forceinline__ bool decode_row_u2_vals(float l0, float l1, int P, int k, int renorm,
+                                                   bool bf16_logits, ProdScratch& sc,
+                                                   int* sel_i, float* sel_w) {
   const int lane = lane_id();
   const bool in = lane < P;
-  const float l0 = in ? to_f32(row[lane]) : -INFINITY;
-  const float l1 = in ? to_f32(row[P + lane]) : -INFINITY;
   const float M0 = wave_max(l0), M1 = wave_max(l1);
   float s0 = 0.f, s1 = 0.f;
   if (M0 != -INFINITY) s0 = fast_exp2(fmaf(l0, LOG2E, -M0 * LOG2E));
@@ -128,7 +146,8 @@ __device__ bool decode_row_u2(const IO* __restrict__ row, int P, int k, int reno
     sc.dlse[1] = lse1;
   }
   const float b1 = in ? M0 + l1 : -INFINITY;
-  const float tau = kth_lane_max(b1, k);
+  const float l1k = bf16_logits ? kth_lane_max_bf16(l1, k) : kth_lane_max(l1, k);
+  const float tau = (l1k == -INFINITY) ? -INFINITY : M0 + l1k;
   uint64_t qual = __ballot(in && b1 >= tau);
   const uint64_t lt = lanemask_lt();
   int count = 0;
@@ -147,20 +166,35 @@ __device__ bool decode_row_u2(const IO* __restrict__ row, int P, int k, int reno
     }
     count += __popcll(bal);
   }
-  // overflow (massive ties) or fewer than K listed slots (NaN logits)
   if (count > KEEP_CAP || count < k) return false;
   wave_sync();
-  // exact rank of every listed slot; the K best to sv / si, and their
-  // log-probabilities to the lanes that hold them
-  float lp = 0.f;
-  for (int c = lane; c < count; c += WAVE) {
-    const float v = sc.kk[0][c];
-    const int id = sc.ki[0][c];
+  // exact rank of every listed slot; the K best to sv / si with their
+  // log-probabilities
+  if (count <= WAVE) {
+    float v = -INFINITY, lpv = 0.f;
+    int id = 0x7fffffff;
+    if (lane < count) {
+      v = sc.kk[0][lane];
+      id = sc.ki[0][lane];
+      lpv = sc.kk[1][lane];
+    }
     int rank = 0;
-    for (int o = 0; o < count; ++o) rank += before(sc.kk[0][o], sc.ki[0][o], v, id) ? 1 : 0;
-    if (rank < k) {
+    for (int o = 0; o < count; ++o)
+      rank += before(readlane_f(v, o), readlane_i(id, o), v, id) ? 1 : 0;
+    if (lane < count && rank < k) {
       sc.si[rank] = id;
-      sc.sv[rank] = sc.kk[1][c];
+      sc.sv[rank] = lpv;
+    }
+  } else {
+    for (int c = lane; c < count; c += WAVE) {
+      const float v = sc.kk[0][c];
+      const int id = sc.ki[0][c];
+      int rank = 0;
+      for (int o = 0; o < count; ++o) rank += before(sc.kk[0][o], sc.ki[0][o], v, id) ? 1 : 0;
+      if (rank < k) {
+        sc.si[rank] = id;
+        sc.sv[rank] = sc.kk[1][c];
+      }
     }
   }
   wave_sync();
@@ -168,8 +202,7 @@ __device__ bool decode_row_u2(const IO* __restrict__ row, int P, int k, int reno
   int id = 0;
   if (lane < k) {
     id = sc.si[lane];
-    lp = sc.sv[lane];
-    w = expf(lp);
+    w = expf(sc.sv[lane]);
   }
   if (renorm) {
     const float tot = wave_sum(lane < k ? w : 0.f);
@@ -179,16 +212,28 @@ __device__ bool decode_row_u2(const IO* __restrict__ row, int P, int k, int reno
   return true;
 }
 
+template <typename IO>
+__device__ bool decode_row_u2(const IO* __restrict__ row, int P, int k, int renorm,
+                              ProdScratch& sc, int* sel_i, float* sel_w) {
+  const int lane = lane_id();
+  const bool in = lane < P;
+  const float l0 = in ? to_f32(row[lane]) : -INFINITY;
+  const float l1 = in ? to_f32(row[P + lane]) : -INFINITY;
+  return decode_row_u2_vals(l0, l1, P, k, renorm, sizeof(IO) == 2, sc, sel_i, sel_w);
+}
+
 }  // namespace
 
 // Decodes one product row (U * P logits) with the calling wave: the K
 // selected flat slots and their probabilities exp(sum_u (l_u[a_u] - lse_u))
 // (renormalised if asked) to sel_i / sel_w (lanes < k), and the per-digit
 // maxima and logsumexps to sc.dmax / sc.dlse.  Visible to the wave on return.
+// try_u2: rows of two digits of at most 64 first take the register search
+// (callers that already tried it pass false).
 template <typename IO>
 __device__ void decode_row_product(const IO* __restrict__ row, int U, int P, int k, int renorm,
-                                   ProdScratch& sc, int* sel_i, float* sel_w) {
-  if (U == 2 && P <= WAVE) {
+                                   ProdScratch& sc, int* sel_i, float* sel_w, bool try_u2 = true) {
+  if (try_u2 && U == 2 && P <= WAVE) {
     if (decode_row_u2<IO>(row, P, k, renorm, sc, sel_i, sel_w)) return;
     wave_sync();
   }
