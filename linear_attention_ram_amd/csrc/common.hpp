@@ -73,6 +73,19 @@ __device__ __forceinline__ void st_nt16(void* p, uint4 v) {
   __builtin_nontemporal_store(t, reinterpret_cast<u32x4_nt*>(p));
 }
 
+// Loads and stores through a pointer the compiler can no longer trace to a
+// kernel argument (it then emits flat accesses, which also count on the LDS
+// counter, so every LDS wait would wait for them too): the access is made in
+// the global address space explicitly.
+template <typename T>
+__device__ __forceinline__ T ld_global(const T* p) {
+  return *(const T __attribute__((address_space(1)))*)p;
+}
+template <typename T>
+__device__ __forceinline__ void st_global(T* p, T v) {
+  *(T __attribute__((address_space(1)))*)p = v;
+}
+
 // 16-byte vector of -inf in the io type (pads a row past its end).
 template <typename IO> __device__ __forceinline__ uint4 neg_inf16();
 template <> __device__ __forceinline__ uint4 neg_inf16<float>() {

@@ -221,7 +221,9 @@ struct Ev {
 __device__ __forceinline__ float4 load_rec(const EventRec* events, int cs, int n, int beg, int end) {
   (void)n;
   const int at = min(max(cs + (lane_id() & (CHUNK - 1)), beg), end - 1);
-  return *reinterpret_cast<const float4*>(events + at);
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 r = ld_global(reinterpret_cast<const f32x4*>(events + at));
+  return make_float4(r[0], r[1], r[2], r[3]);
 }
 
 __device__ __forceinline__ Ev decode_rec(float4 raw, int n, int h, int H) {
@@ -817,6 +819,43 @@ __device__ __forceinline__ void bwd_replay(BwdChunk<IO, CPL, SO>& ck, float (&s)
   });
 }
 
+// The same replay, which also forms the chunk's content adjoint map from a
+// zero adjoint at its end: walking back, a read adds r_i x_i and a write
+// scales by (1 - eta_j), so the adjoint at the chunk's start is
+//   q = sum over reads i of c_i x_i,  c_i = r_i * prod over writes j < i of (1 - eta_j)
+// (cq holds c_i in lane i) and the map is s_hat -> Q s_hat + q with Q the
+// product of all (1 - eta).
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ void bwd_replay_map(BwdChunk<IO, CPL, SO>& ck, float (&s)[CPL],
+                                               float (&pr)[CHUNK], float cq, float (&q)[CPL]) {
+  using LN = Lanes<IO, CPL>;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) q[k] = 0.f;
+  for_up<0, CHUNK>([&](auto I) {
+    pr[I] = 0.f;
+    if ((ck.wm >> I) & 1u) {
+      float xf[CPL];
+      LN::get(ck.x[I], xf);
+      const float e = bc<I>(ck.M.eta), om = bc<I>(ck.M.keep);
+      ck.template put_so<I>(s);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) s[k] = fmaf(om, s[k], e * xf[k]);
+    } else if ((ck.rm >> I) & 1u) {
+      float xf[CPL];
+      LN::get(ck.x[I], xf);
+      const float ci = bc<I>(cq);
+      float d = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        d = fmaf(xf[k], s[k], d);
+        q[k] = fmaf(ci, xf[k], q[k]);
+      }
+      pr[I] = d;
+    }
+    sched_fence<I>();
+  });
+}
+
 // Reverse walk of the content adjoint from sh (after the chunk) to sh (before
 // it): stores the dv contributions e * s_hat of the writes and leaves in pw
 // the lane-local partials of each event's scalar gradient: <s_hat_after,
@@ -862,36 +901,55 @@ __device__ __forceinline__ void bwd_walk(const BwdChunk<IO, CPL, SO>& ck, const 
   });
 }
 
-// Lane-parallel scalar part of a chunk's reverse step.  red (lane i) holds
-// dr_i for a read and deta_i for a write.  Stores dr, dw and the gamma parts;
-// mh goes from the mass adjoint after the chunk to the one before it.
+// Lane-parallel scalar part of a chunk's reverse step, in two halves.  red
+// (lane i) holds dr_i for a read and deta_i for a write.  The mass adjoint
+// m_hat_before = lambda * (m_hat_after - g * deta) of a write is affine in
+// m_hat; bwd_mass_maps composes these maps over the later events of the chunk
+// (lane i: F_i o ... o F_15, so lane 0 holds the whole chunk's map), and
+// bwd_mass_store, given the mass adjoint after the chunk, stores dr, dw and
+// the gamma parts and returns the adjoint before the chunk.
+struct MassAdj {
+  float A, B, deta;
+};
 template <typename IO, int CPL, bool SO>
-__device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
-                                            const BwdChunk<IO, CPL, SO>& ck, float red, float& mh) {
+__device__ __forceinline__ MassAdj bwd_mass_maps(const BwdChunk<IO, CPL, SO>& ck, float red) {
+  const Ev& ev = ck.ev;
+  const bool wr = ev.valid && ev.side == 0;
+  MassAdj ma;
+  ma.deta = wr ? red : 0.f;
+  ma.A = wr ? ev.lam : 1.f;
+  ma.B = wr ? -ev.lam * ck.gq * ma.deta : 0.f;
+  affine_suffix_scan(ma.A, ma.B);
+  return ma;
+}
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ float bwd_mass_store(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                                const BwdChunk<IO, CPL, SO>& ck,
+                                                const MassAdj& ma, float red, float mh) {
   const int lane = lane_id();
   const Ev& ev = ck.ev;
   const bool wr = ev.valid && ev.side == 0;
-  const float g = ck.gq;
-  const float deta = wr ? red : 0.f;
-  float A = wr ? ev.lam : 1.f;
-  float B = wr ? -ev.lam * g * deta : 0.f;
-  affine_suffix_scan(A, B);
-  const float before = fmaf(A, mh, B);
+  const float before = fmaf(ma.A, mh, ma.B);
   const float after = dpp_or<DPP_SHL1>(mh, before);   // lane 15: the chunk's m_hat
   const int64_t row = c.row0 + ev.rb;
   if (lane < CHUNK) {
     if (wr) {
-      const float M = after - g * deta;
-      const float dwi = ((ev.wt > 0.f) ? deta * ck.rden : 0.f) + M + M * ck.M.mo * ev.dl;
+      const float M = after - ck.gq * ma.deta;
+      const float dwi = ((ev.wt > 0.f) ? ma.deta * ck.rden : 0.f) + M + M * ck.M.mo * ev.dl;
       const float dgi = M * ck.M.mo * (-ev.lam * (1.f - ev.lam));
       const int64_t o = row * a.k_w + ev.j;
-      a.dw[o] = dwi;
-      a.dgam[o] = dgi;
+      st_global(a.dw + o, dwi);
+      st_global(a.dgam + o, dgi);
     } else if (ev.valid) {
-      a.dr[row * a.k_r + ev.j] = red;
+      st_global(a.dr + row * a.k_r + ev.j, red);
     }
   }
-  mh = readlane_f(before, 0);
+  return readlane_f(before, 0);
+}
+template <typename IO, int CPL, bool SO>
+__device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                            const BwdChunk<IO, CPL, SO>& ck, float red, float& mh) {
+  mh = bwd_mass_store(a, c, ck, bwd_mass_maps(ck, red), red, mh);
 }
 
 // State at the start of chunk cs of segment g: the initial state for the
@@ -919,8 +977,8 @@ __device__ __forceinline__ void chunk_state_load(const ScanBwdArgs& a, const Seg
   const float* mp = first ? (a.mass0 ? a.mass0 + g : a.ckpt_m) : a.ckpt_m + cs / CHUNK;
   const int cc = min(c.c0, a.d_v - CPL);
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) st.t[k] = sp[cc + k];
-  st.tm = *mp;
+  for (int k = 0; k < CPL; ++k) st.t[k] = ld_global(sp + cc + k);
+  st.tm = ld_global(mp);
 }
 template <typename IO, int CPL>
 __device__ __forceinline__ void chunk_state_take(const SegCtx<IO, CPL>& c, const ChunkStart<CPL>& st,
@@ -987,17 +1045,16 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
 
 // Long segments: a workgroup of NWL waves takes NWL consecutive chunks at a
 // time, from the end of the segment.  Each wave replays its chunk from its
-// checkpoint and forms the chunk's adjoint map from a symbolic zero at its
-// end
-//   s_hat_in = Q * s_hat_out + q
-//   m_hat_in = L * m_hat_out + <s_hat_out, U> + K
-// (Q = prod (1-eta), L = prod lambda over the writes; U and K collect the
-// mass terms).  Folding the content maps of the later chunks gives each wave
-// its true s_hat after its chunk; each wave then contributes
-// <s_hat_out, U> of its own map, which makes the mass maps scalar, and the
-// folded mass maps give each wave its true m_hat.  Each wave then runs the
-// exact reverse step; wave 0's result is the carry into the previous NWL
-// chunks.
+// checkpoint and, in the same pass, forms the chunk's content adjoint map
+// from a zero adjoint at its end, s_hat_in = Q * s_hat_out + q (Q = prod
+// (1 - eta); q a weighted sum of the chunk's read rows).  Folding the later
+// chunks' maps onto the carry gives each wave its true s_hat after its chunk,
+// and it runs the exact reverse walk from there, which fixes every deta of
+// the chunk.  The mass adjoint is then affine in m_hat with known
+// coefficients: each wave composes its chunk's scalar map, the maps are
+// folded the same way, and each wave finishes its own chunk's gradients.
+// Two workgroup barriers per NWL chunks; wave 0's walk gives the content
+// carry into the previous NWL chunks, the folded mass maps the mass carry.
 template <typename IO, int CPL>
 __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
   ScanBwdArgs a = args;
@@ -1007,10 +1064,9 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
   fresh(a.seg_offset);
   constexpr int NW = NWL;
   using LN = Lanes<IO, CPL>;
-  __shared__ float mQ[NW], mL[NW], mK[NW], mD[NW];
+  __shared__ float mQ[NW], mA[NW], mB[NW];
   __shared__ float mq[NW][MAX_DV];
   __shared__ float carry_s[MAX_DV];
-  __shared__ float carry_m;
   const SegCtx<IO, CPL> c = seg_ctx<IO, CPL>(g, a.S, a.H, a.T, a.d_v);
   const int lane = lane_id();
   const int w = wave_index();
@@ -1019,19 +1075,19 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
   const rsrc_t ro = make_rsrc(reinterpret_cast<const IO*>(a.d_o) + c.row0 * a.d_v, nrow * c.pitch);
   const rsrc_t rs = make_rsrc(reinterpret_cast<IO*>(a.stash) + c.row0 * a.k_w * a.d_v,
                               nrow * a.k_w * c.pitch);
-  const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
+  const int beg = ld_global(a.seg_offset + g), end = ld_global(a.seg_offset + g + 1);
   const int nchunks = (end - 1) / CHUNK - beg / CHUNK + 1;
 
   float sh_carry[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k)
-    sh_carry[k] = (c.active && a.d_slot1) ? a.d_slot1[g * a.d_v + c.c0 + k] : 0.f;
-  float mh_carry = a.d_mass1 ? a.d_mass1[g] : 0.f;
+    sh_carry[k] = (c.active && a.d_slot1) ? ld_global(a.d_slot1 + g * a.d_v + c.c0 + k) : 0.f;
+  float mh_carry = a.d_mass1 ? ld_global(a.d_mass1 + g) : 0.f;
 
   __shared__ float so_lds[NW][CHUNK][MAX_DV];   // pre-write contents, per wave
   BwdChunk<IO, CPL, true> ck;
   ck.so_lds = &so_lds[w][0][0] + c.c0;
-  float pr[CHUNK], pw[CHUNK], pm[CHUNK];
+  float pr[CHUNK], pw[CHUNK];
   auto chunk_of = [&](int k, int& cs, int& n) {
     cs = end;
     n = 0;
@@ -1079,68 +1135,22 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
     }
     chunk_state_load<IO, CPL>(a, c, g, beg, csn, st);
     bwd_gather_rows<IO, CPL>(a, c, rv, ro, xn, rec_n, nn);
-    bwd_replay(ck, s, pr);
-    const Ev& ev = ck.ev;
-    // adjoint map of the chunk: a reverse walk from zero.  coef_i is the
-    // factor of u_i = x_i - s_old_i in U: -(prefix product of lambda) *
-    // g_i * (product of (1 - eta) over the later events).  The prefix
-    // product of lambda over the writes is the A part of the mass scan.
-    const bool wr = ev.valid && ev.side == 0;
-    const float Lp = ck.M.A;
-    const float Qs = suffix_prod(ck.M.keep);
-    const float Qx = dpp_or<DPP_SHL1>(1.f, Qs);
-    const float gq = ck.gq;
-    const float coef = -Lp * gq * Qx;
-    // only earlier waves fold a chunk's map, so wave 0 forms none
-    float U[CPL];
+    // content adjoint map of the chunk from a zero adjoint at its end,
+    // formed during the replay (the weights of its reads are prefix
+    // products of 1 - eta over the chunk's earlier writes)
+    const float Pk = prefix_prod(ck.M.keep);
+    const float cq = ck.rr * dpp_or<DPP_SHR1>(1.f, Pk);
+    const float Qw = bc<15>(Pk);   // every lane: the broadcast reads lane 15
+    float q[CPL];
+    bwd_replay_map(ck, s, pr, cq, q);
+    if (c.active) {
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) U[k] = 0.f;
-    if (w != 0) {
-      float q[CPL];
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) q[k] = 0.f;
-      float so_n[CPL];
-      ck.template get_so<CHUNK - 1>(so_n);
-      for_down<CHUNK>([&](auto I) {
-        float so[CPL];
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) so[k] = so_n[k];
-        if constexpr (I > 0) ck.template get_so<I - 1>(so_n);
-        pm[I] = 0.f;
-        if ((ck.wm >> I) & 1u) {
-          float xf[CPL];
-          LN::get(ck.x[I], xf);
-          const float e = bc<I>(ck.M.eta), cf = bc<I>(coef);
-          float d = 0.f;
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) {
-            const float u = xf[k] - so[k];
-            d = fmaf(q[k], u, d);
-            U[k] = fmaf(cf, u, U[k]);
-            q[k] = fmaf(-e, q[k], q[k]);
-          }
-          pm[I] = d;
-        } else if ((ck.rm >> I) & 1u) {
-          float xf[CPL];
-          LN::get(ck.x[I], xf);
-          const float r = bc<I>(ck.rr);
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) q[k] = fmaf(r, xf[k], q[k]);
-        }
-        sched_fence<I>();
-      });
-      const float red1 = batched_sum(pm);    // <q_after, u> of the writes
-      const float K = row_sum(wr ? -Lp * gq * red1 : 0.f);
-      const float L = bc<15>(Lp);
-      const float Q = bc<0>(Qs);
-      if (c.active) {
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) mq[w][c.c0 + k] = q[k];
-      }
-      if (lane == 0) { mQ[w] = Q; mL[w] = L; mK[w] = K; }
+      for (int k = 0; k < CPL; ++k) mq[w][c.c0 + k] = q[k];
     }
+    if (lane == 0) mQ[w] = Qw;
     __syncthreads();
-    // content adjoint after this wave's chunk: fold the later content maps
+    // content adjoint after this wave's chunk: the later chunks' maps
+    // folded onto the carry; then the exact reverse walk from it
     float sh[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) sh[k] = sh_carry[k];
@@ -1149,31 +1159,24 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
 #pragma unroll
       for (int k = 0; k < CPL; ++k) sh[k] = fmaf(Qk, sh[k], c.active ? mq[kk][c.c0 + k] : 0.f);
     }
-    if (w != 0) {
-      float d = 0.f;
+    bwd_walk(ck, c, rs, sh, pr, pw);
+    if (w == 0 && c.active) {
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) d = fmaf(sh[k], U[k], d);
-      d = wave_sum(d);
-      if (lane == 0) mD[w] = d;
+      for (int k = 0; k < CPL; ++k) carry_s[c.c0 + k] = sh[k];
     }
+    // the mass adjoint, now that every deta is known: each chunk's map,
+    // folded the same way
+    const float red = batched_sum(pw);   // deta of the writes, dr of the reads
+    const MassAdj ma = bwd_mass_maps(ck, red);
+    if (lane == 0) { mA[w] = ma.A; mB[w] = ma.B; }
     __syncthreads();
     float mh = mh_carry;
-    for (int kk = NW - 1; kk > w; --kk) mh = fmaf(mL[kk], mh, mD[kk] + mK[kk]);
-    // exact reverse step of this wave's chunk
-    bwd_walk(ck, c, rs, sh, pr, pw);
-    bwd_scalars(a, c, ck, batched_sum(pw), mh);   // deta of the writes, dr of the reads
-    if (w == 0) {
-      if (c.active) {
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) carry_s[c.c0 + k] = sh[k];
-      }
-      if (lane == 0) carry_m = mh;
-    }
-    __syncthreads();
+    for (int kk = NW - 1; kk > w; --kk) mh = fmaf(mA[kk], mh, mB[kk]);
+    bwd_mass_store(a, c, ck, ma, red, mh);
+    for (int kk = w; kk >= 0; --kk) mh = fmaf(mA[kk], mh, mB[kk]);
+    mh_carry = mh;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) sh_carry[k] = c.active ? carry_s[c.c0 + k] : 0.f;
-    mh_carry = carry_m;
-    __syncthreads();
     rec = rec_n;
     cs = csn;
     n = nn;
@@ -1181,9 +1184,9 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
   if (w == 0) {
     if (a.d_slot0 && c.active) {
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) a.d_slot0[g * a.d_v + c.c0 + k] = sh_carry[k];
+      for (int k = 0; k < CPL; ++k) st_global(a.d_slot0 + g * a.d_v + c.c0 + k, sh_carry[k]);
     }
-    if (a.d_mass0 && lane == 0) a.d_mass0[g] = mh_carry;
+    if (a.d_mass0 && lane == 0) st_global(a.d_mass0 + g, mh_carry);
   }
 }
 
