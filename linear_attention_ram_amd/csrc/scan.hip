@@ -512,7 +512,6 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
   using LN = Lanes<IO, CPL>;
   __shared__ float mapA[NW], mapB[NW], mapP[NW];
   __shared__ float mapb[NW][MAX_DV];
-  __shared__ float carry_s[MAX_DV];
   const SegCtx<IO, CPL> c = seg_ctx<IO, CPL>(g, a.S, a.H, a.T, a.d_v);
   const int lane = lane_id();
   const int w = wave_index();
@@ -587,13 +586,11 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
     });
     const float Pi = prefix_prod(M.keep);   // lane i: product of (1 - eta) over events 0..i
     const float P = bc<15>(Pi);
-    if (w != NW - 1) {
-      if (c.active) {
+    if (c.active) {
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) mapb[w][c.c0 + k] = sz[k];
-      }
-      if (lane == 0) mapP[w] = P;
+      for (int k = 0; k < CPL; ++k) mapb[w][c.c0 + k] = sz[k];
     }
+    if (lane == 0) mapP[w] = P;
     __syncthreads();
     // the rows and records requested before the barriers have arrived by now
     wait_vmem();
@@ -632,16 +629,18 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
       const uint32_t xo_n = (ev_n.valid && ev_n.live && ev_n.side == 0) ? (uint32_t)ev_n.rb * c.pitch : OOB;
       for_up<0, CHUNK>([&](auto I) { x[I] = LN::load(rv, bcu<I>(xo_n) + c.lb); });
     }
-    // the last wave's state after its chunk is the carry into the next chunks
-    if (w == NW - 1 && c.active) {
+    // the carry into the next chunks: this wave's own map, then the later
+    // waves' maps (every wave computes it, in the same order of operations)
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) carry_s[c.c0 + k] = fmaf(P, s[k], sz[k]);
+    for (int k = 0; k < CPL; ++k) s_carry[k] = fmaf(P, s[k], sz[k]);
+    for (int kk = w + 1; kk < NW; ++kk) {
+      const float Pk = mapP[kk];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+        s_carry[k] = fmaf(Pk, s_carry[k], c.active ? mapb[kk][c.c0 + k] : 0.f);
     }
     m_carry = m_next;
     p = pn;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) s_carry[k] = c.active ? carry_s[c.c0 + k] : 0.f;
   }
   if (w == 0) {
     if (c.active) {
