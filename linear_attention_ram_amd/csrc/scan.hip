@@ -860,10 +860,14 @@ __device__ __forceinline__ void bwd_replay_map(BwdChunk<IO, CPL, SO>& ck, float 
 // the lane-local partials of each event's scalar gradient: <s_hat_after,
 // x - s_old> (the deta of a write), or the replay's partial pr of a read (its
 // dr), so that one batched reduction serves both kinds.
-template <typename IO, int CPL, bool SO>
-__device__ __forceinline__ void bwd_walk(const BwdChunk<IO, CPL, SO>& ck, const SegCtx<IO, CPL>& c,
+// DEFER (contents in LDS only): each write's contribution is left in its
+// event's LDS slot, whose pre-write content the walk no longer needs, and
+// stored later by flush_dv.
+template <typename IO, int CPL, bool SO, bool DEFER = false>
+__device__ __forceinline__ void bwd_walk(BwdChunk<IO, CPL, SO>& ck, const SegCtx<IO, CPL>& c,
                                          rsrc_t rs, float (&sh)[CPL], const float (&pr)[CHUNK],
                                          float (&pw)[CHUNK]) {
+  static_assert(!DEFER || SO, "deferred stores keep the contributions in LDS");
   using LN = Lanes<IO, CPL>;
   // each event's pre-write content is read from LDS one event ahead, outside
   // the per-kind branches, so the read has an event's work to complete in
@@ -886,7 +890,8 @@ __device__ __forceinline__ void bwd_walk(const BwdChunk<IO, CPL, SO>& ck, const 
         d = fmaf(sh[k], xf[k] - so[k], d);
         sh[k] = fmaf(-e, sh[k], sh[k]);
       }
-      LN::store(rs, bcu<I>(ck.sw) + c.lb, ctr);
+      if constexpr (DEFER) ck.template put_so<I>(ctr);
+      else LN::store(rs, bcu<I>(ck.sw) + c.lb, ctr);
       pw[I] = d;
     } else if ((ck.rm >> I) & 1u) {
       float xf[CPL];
@@ -900,13 +905,27 @@ __device__ __forceinline__ void bwd_walk(const BwdChunk<IO, CPL, SO>& ck, const 
   });
 }
 
+// Stores the dv contributions a deferred walk left in LDS (sw: the chunk's
+// per-event stash offsets, OOB for all but writes, so those stores drop).
+template <typename IO, int CPL>
+__device__ __forceinline__ void flush_dv(const BwdChunk<IO, CPL, true>& ck, rsrc_t rs, uint32_t sw,
+                                         uint32_t lb) {
+  using LN = Lanes<IO, CPL>;
+  for_up<0, CHUNK>([&](auto I) {
+    float v[CPL];
+    ck.template get_so<I>(v);
+    LN::store(rs, bcu<I>(sw) + lb, v);
+  });
+}
+
 // Lane-parallel scalar part of a chunk's reverse step, in two halves.  red
 // (lane i) holds dr_i for a read and deta_i for a write.  The mass adjoint
 // m_hat_before = lambda * (m_hat_after - g * deta) of a write is affine in
 // m_hat; bwd_mass_maps composes these maps over the later events of the chunk
 // (lane i: F_i o ... o F_15, so lane 0 holds the whole chunk's map), and
-// bwd_mass_store, given the mass adjoint after the chunk, stores dr, dw and
-// the gamma parts and returns the adjoint before the chunk.
+// bwd_mass_grads, given the mass adjoint after the chunk, forms dr, dw and
+// the gamma parts (ChunkGrads, stored by store_grads) and returns the adjoint
+// before the chunk.
 struct MassAdj {
   float A, B, deta;
 };
@@ -921,34 +940,48 @@ __device__ __forceinline__ MassAdj bwd_mass_maps(const BwdChunk<IO, CPL, SO>& ck
   affine_suffix_scan(ma.A, ma.B);
   return ma;
 }
+// Lane i < 16: the gradients of event i, at byte offsets inside its batch's
+// rows of dw and dgam (a write) or dr (a read); OOB where there is none.
+struct ChunkGrads {
+  float dw, dg, dr;
+  uint32_t ow, orr;
+};
 template <typename IO, int CPL, bool SO>
-__device__ __forceinline__ float bwd_mass_store(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
-                                                const BwdChunk<IO, CPL, SO>& ck,
-                                                const MassAdj& ma, float red, float mh) {
-  const int lane = lane_id();
+__device__ __forceinline__ float bwd_mass_grads(const ScanBwdArgs& a, const BwdChunk<IO, CPL, SO>& ck,
+                                                const MassAdj& ma, float red, float mh,
+                                                ChunkGrads& gr) {
   const Ev& ev = ck.ev;
   const bool wr = ev.valid && ev.side == 0;
   const float before = fmaf(ma.A, mh, ma.B);
   const float after = dpp_or<DPP_SHL1>(mh, before);   // lane 15: the chunk's m_hat
-  const int64_t row = c.row0 + ev.rb;
-  if (lane < CHUNK) {
-    if (wr) {
-      const float M = after - ck.gq * ma.deta;
-      const float dwi = ((ev.wt > 0.f) ? ma.deta * ck.rden : 0.f) + M + M * ck.M.mo * ev.dl;
-      const float dgi = M * ck.M.mo * (-ev.lam * (1.f - ev.lam));
-      const int64_t o = row * a.k_w + ev.j;
-      st_global(a.dw + o, dwi);
-      st_global(a.dgam + o, dgi);
-    } else if (ev.valid) {
-      st_global(a.dr + row * a.k_r + ev.j, red);
-    }
-  }
+  const float M = after - ck.gq * ma.deta;
+  gr.dw = ((ev.wt > 0.f) ? ma.deta * ck.rden : 0.f) + M + M * ck.M.mo * ev.dl;
+  gr.dg = M * ck.M.mo * (-ev.lam * (1.f - ev.lam));
+  gr.dr = red;
+  const bool mine = lane_id() < CHUNK;
+  gr.ow = (mine && wr) ? ((uint32_t)ev.rb * a.k_w + ev.j) * 4u : OOB;
+  gr.orr = (mine && !wr && ev.valid) ? ((uint32_t)ev.rb * a.k_r + ev.j) * 4u : OOB;
   return readlane_f(before, 0);
+}
+// Stores a chunk's gradients (three stores, each dropped where its offset is
+// OOB).
+template <typename IO, int CPL>
+__device__ __forceinline__ void store_grads(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
+                                            const ChunkGrads& gr) {
+  const uint32_t nrow = (uint32_t)a.T * a.H;
+  const rsrc_t rdw = make_rsrc(a.dw + c.row0 * a.k_w, nrow * a.k_w * 4u);
+  const rsrc_t rdg = make_rsrc(a.dgam + c.row0 * a.k_w, nrow * a.k_w * 4u);
+  const rsrc_t rdr = make_rsrc(a.dr + c.row0 * a.k_r, nrow * a.k_r * 4u);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gr.dw), rdw, gr.ow, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gr.dg), rdg, gr.ow, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gr.dr), rdr, gr.orr, 0, 0);
 }
 template <typename IO, int CPL, bool SO>
 __device__ __forceinline__ void bwd_scalars(const ScanBwdArgs& a, const SegCtx<IO, CPL>& c,
                                             const BwdChunk<IO, CPL, SO>& ck, float red, float& mh) {
-  mh = bwd_mass_store(a, c, ck, bwd_mass_maps(ck, red), red, mh);
+  ChunkGrads gr;
+  mh = bwd_mass_grads(a, ck, bwd_mass_maps(ck, red), red, mh, gr);
+  store_grads(a, c, gr);
 }
 
 // State at the start of chunk cs of segment g: the initial state for the
@@ -1099,6 +1132,14 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
   // start of the current chunk's work, into a second set of registers, so
   // that the loads are in flight during the whole iteration.
   typename LN::Raw xn[CHUNK];
+  // a chunk's stores are issued at the start of the next iteration, a whole
+  // iteration before the wait for that iteration's loads, so no wait ever
+  // covers a store just issued: its dv contributions stay in the wave's LDS
+  // slots, its gradients in gr, its stash offsets in sw_prev
+  uint32_t sw_prev = OOB;
+  ChunkGrads gr;
+  gr.dw = gr.dg = gr.dr = 0.f;
+  gr.ow = gr.orr = OOB;
   float4 rec, rec_next;
   ChunkStart<CPL> st;
   int cs, n;
@@ -1120,7 +1161,10 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
     for_up<0, CHUNK>([&](auto I) { ck.x[I] = xn[I]; });
     float s[CPL], m;
     chunk_state_take(c, st, s, m);
+    flush_dv(ck, rs, sw_prev, c.lb);
+    store_grads(a, c, gr);
     bwd_prepare(a, c, ck, rec, n, m);
+    sw_prev = ck.sw;
     // next chunk of this wave: rows, start state and the record after it
     // (unconditional: past the segment's start the chunk is empty)
     int csn, nn;
@@ -1158,7 +1202,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
 #pragma unroll
       for (int k = 0; k < CPL; ++k) sh[k] = fmaf(Qk, sh[k], c.active ? mq[kk][c.c0 + k] : 0.f);
     }
-    bwd_walk(ck, c, rs, sh, pr, pw);
+    bwd_walk<IO, CPL, true, true>(ck, c, rs, sh, pr, pw);
     if (w == 0 && c.active) {
 #pragma unroll
       for (int k = 0; k < CPL; ++k) carry_s[c.c0 + k] = sh[k];
@@ -1171,7 +1215,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
     __syncthreads();
     float mh = mh_carry;
     for (int kk = NW - 1; kk > w; --kk) mh = fmaf(mA[kk], mh, mB[kk]);
-    bwd_mass_store(a, c, ck, ma, red, mh);
+    bwd_mass_grads(a, ck, ma, red, mh, gr);
     for (int kk = w; kk >= 0; --kk) mh = fmaf(mA[kk], mh, mB[kk]);
     mh_carry = mh;
 #pragma unroll
@@ -1180,6 +1224,8 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
     cs = csn;
     n = nn;
   }
+  flush_dv(ck, rs, sw_prev, c.lb);
+  store_grads(a, c, gr);
   if (w == 0) {
     if (a.d_slot0 && c.active) {
 #pragma unroll
