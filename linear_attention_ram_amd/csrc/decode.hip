@@ -18,6 +18,8 @@
 //           cache), the elements >= tau are compacted into LDS, and each
 //           candidate's rank is counted exactly.  Rows with more than
 //           CAND_CAP candidates (massive ties) take an exact K-pass fallback.
+#include <type_traits>
+
 #include "decode.hpp"
 #include "decode_prod.hpp"
 
@@ -264,6 +266,120 @@ __global__ __launch_bounds__(256) void decode_fwd_u2_kernel(DecodeFwdArgs a) {
   }
 }
 
+// Decode backward of U = 2 rows of P <= 64 (P a multiple of 4) with k <= 16,
+// four rows per wave: DPP row r (lanes 16r .. 16r + 15) takes logits row r,
+// lane p of it holds entries 4p .. 4p + 3 of each digit (one 8- or 16-byte
+// vector per digit), and lane j < k of it holds selection j, broadcast to its
+// row with row_newbcast.  The same terms in the same order as the one-row
+// kernel below: dl_u[i] = -p_u[i] sum_j gw_j, then gw_j added in ascending j
+// to the entry holding digit u of a_j.
+constexpr int U2_BWD_K = 16;
+template <int J>
+__device__ __forceinline__ int row_bcast_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, 0x150 + J, 0xF, 0xF, true);
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<DPP_XOR1>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_HALF_MIRROR>(x);
+  return x + dpp<DPP_MIRROR>(x);
+}
+template <typename IO> struct Vec4;
+template <> struct Vec4<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float (&x)[4]) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    x[0] = __uint_as_float(q.x << 16);
+    x[1] = __uint_as_float(q.x & 0xffff0000u);
+    x[2] = __uint_as_float(q.y << 16);
+    x[3] = __uint_as_float(q.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float (&x)[4]) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(cvt2bf(x[0], x[1]), cvt2bf(x[2], x[3]));
+  }
+};
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&x)[4]) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    x[0] = q.x; x[1] = q.y; x[2] = q.z; x[3] = q.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&x)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+template <typename IO>
+__global__ __launch_bounds__(256) void decode_bwd_u2_kernel(DecodeBwdArgs a) {
+  const int lane = lane_id();
+  const int p = lane & 15;
+  const int64_t grow = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  const bool live = grow < (int64_t)a.nsides * a.N;
+  const int side = (live && grow >= a.N) ? 1 : 0;   // nsides <= 2
+  const int64_t row = live ? grow - (int64_t)side * a.N : 0;
+  const int k = a.k[side];
+  const int P = a.P;
+  const bool own = live && 4 * p < P;
+  const bool masked = live && a.mask && !a.mask[token_of(row, a.H)];
+  float gj = 0.f, wj = 0.f;
+  int aj0 = -1, aj1 = -1;
+  if (live && p < k) {
+    gj = a.g[side][row * k + p];
+    wj = a.w[side][row * k + p];
+    int aj = a.idx[side][row * k + p];
+    const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
+    if (shift >= 0) aj = (aj - shift + a.S) % a.S;
+    aj0 = aj / P;
+    aj1 = aj - aj0 * P;
+  }
+  // the row sums run with every lane active (lanes past k hold zeros)
+  const float gwr = a.renorm[side] ? (gj - row16_sum(gj * wj)) * wj : gj * wj;
+  const float gw = masked ? 0.f : gwr;
+  const float ntot = -row16_sum(gw);
+  float x0[4] = {0.f, 0.f, 0.f, 0.f}, x1[4] = {0.f, 0.f, 0.f, 0.f};
+  float nl0 = 0.f, nl1 = 0.f;
+  const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)(2 * P);
+  IO* dst = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)(2 * P);
+  if (own) {
+    Vec4<IO>::load(src + 4 * p, x0);
+    Vec4<IO>::load(src + P + 4 * p, x1);
+    nl0 = -a.lse[side][row * 2] * LOG2E;
+    nl1 = -a.lse[side][row * 2 + 1] * LOG2E;
+  }
+  float acc0[4], acc1[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc0[e] = ntot * fast_exp2(fmaf(x0[e], LOG2E, nl0));
+    acc1[e] = ntot * fast_exp2(fmaf(x1[e], LOG2E, nl1));
+  }
+  const int base = 4 * p;
+  auto add = [&](auto J) {
+    constexpr int j = decltype(J)::value;
+    const float g = dpp<0x150 + j>(gw);
+    const int d0 = row_bcast_i<j>(aj0) - base, d1 = row_bcast_i<j>(aj1) - base;
+    if (j < k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc0[e] = (d0 == e) ? acc0[e] + g : acc0[e];
+        acc1[e] = (d1 == e) ? acc1[e] + g : acc1[e];
+      }
+    }
+  };
+  add(std::integral_constant<int, 0>{});  add(std::integral_constant<int, 1>{});
+  add(std::integral_constant<int, 2>{});  add(std::integral_constant<int, 3>{});
+  add(std::integral_constant<int, 4>{});  add(std::integral_constant<int, 5>{});
+  add(std::integral_constant<int, 6>{});  add(std::integral_constant<int, 7>{});
+  add(std::integral_constant<int, 8>{});  add(std::integral_constant<int, 9>{});
+  add(std::integral_constant<int, 10>{}); add(std::integral_constant<int, 11>{});
+  add(std::integral_constant<int, 12>{}); add(std::integral_constant<int, 13>{});
+  add(std::integral_constant<int, 14>{}); add(std::integral_constant<int, 15>{});
+  if (own) {
+    if (masked) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc0[e] = acc1[e] = 0.f;
+    }
+    Vec4<IO>::store(dst + 4 * p, acc0);
+    Vec4<IO>::store(dst + P + 4 * p, acc1);
+  }
+}
+
 // Decode backward of product rows (one wave per row): with gw_j as for one
 // digit, dl_u[i] = sum_j gw_j [digit u of a_j = i] - p_u[i] sum_j gw_j,
 // p_u = exp(l_u - lse_u) the digit softmax (paper App. B.1: the slot
@@ -381,6 +497,13 @@ hipError_t launch_decode_bwd(const DecodeBwdArgs& a, bool bf16, hipStream_t st) 
   const int64_t rows = (int64_t)a.nsides * a.N;
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (a.U == 2 && a.P <= WAVE && a.P % 4 == 0 && a.k[0] <= U2_BWD_K &&
+      (a.nsides < 2 || a.k[1] <= U2_BWD_K)) {
+    const dim3 grid2((unsigned)((rows + 15) / 16));
+    if (bf16) hipLaunchKernelGGL(decode_bwd_u2_kernel<bf16_t>, grid2, block, 0, st, a);
+    else hipLaunchKernelGGL(decode_bwd_u2_kernel<float>, grid2, block, 0, st, a);
+    return hipGetLastError();
+  }
   if (a.U > 1) {
     if (bf16) hipLaunchKernelGGL(decode_bwd_prod_kernel<bf16_t>, grid, block, 0, st, a);
     else hipLaunchKernelGGL(decode_bwd_prod_kernel<float>, grid, block, 0, st, a);
