@@ -380,6 +380,254 @@ __global__ __launch_bounds__(256) void decode_bwd_u2_kernel(DecodeBwdArgs a) {
   }
 }
 
+// U = 2 rows of P <= 64 (P a multiple of 4, at least 4K entries) with K <= 16,
+// four rows per wave in the layout of decode_bwd_u2_kernel (DPP row r takes
+// logits row r, lane p entries 4p .. 4p + 3 of each digit).  The selection is
+// that of decode_row_u2_vals, made with row-local steps:
+//   tau = fl(M0 + v), v a lower bound of the K-th largest digit-1 logit (the
+//   largest 16-bit prefix of the ordered bits that K of its values reach;
+//   for bf16 logits that value itself), so K distinct slots (argmax l0, b)
+//   have keys >= tau and tau is at most the K-th best key;
+//   every slot with key fl(l0[a] + l1[b]) >= tau is listed (only digit-1
+//   values with fl(M0 + l1[b]) >= tau can give one) as a 64-bit word: its
+//   ordered key, then its index complemented in 16 bits, then its list
+//   position, so that the larger word is the earlier slot in (key
+//   descending, index ascending) and names its log-probability in the list;
+//   K rounds of a row maximum over the listed words give the K best in order.
+// Rows whose list would overflow or hold fewer than K slots (NaN logits, a
+// bound that is no number) take the whole-wave path afterwards, one by one.
+constexpr int U2X_CAP = 96;    // listed slots per row
+constexpr int U2X_QCAP = 32;   // listed digit-1 values per row
+constexpr int U2X_K = 16;
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<DPP_XOR1>(x));
+  x = fmaxf(x, dpp<DPP_XOR2>(x));
+  x = fmaxf(x, dpp<DPP_HALF_MIRROR>(x));
+  return fmaxf(x, dpp<DPP_MIRROR>(x));
+}
+// Inclusive sum of x over the lanes of the DPP row up to this one.
+__device__ __forceinline__ int row16_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  return x;
+}
+__device__ __forceinline__ int row16_last(int x) {   // lane 15 of the row
+  return __builtin_amdgcn_mov_dpp(x, 0x15F, 0xF, 0xF, true);
+}
+// Larger of two 64-bit words over the lanes of the DPP row (every lane gets it).
+template <int CTRL>
+__device__ __forceinline__ uint64_t max64_step(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xF, 0xF, true);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, true);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > x ? o : x;
+}
+__device__ __forceinline__ uint64_t row16_max64(uint64_t x) {
+  x = max64_step<DPP_XOR1>(x);
+  x = max64_step<DPP_XOR2>(x);
+  x = max64_step<DPP_HALF_MIRROR>(x);
+  return max64_step<DPP_MIRROR>(x);
+}
+
+template <typename IO>
+__global__ __launch_bounds__(256) void decode_fwd_u2x_kernel(DecodeFwdArgs a) {
+  // per wave: the lists of its four rows, or (afterwards) the scratch of the
+  // whole-wave path, in the same LDS
+  struct Lists {
+    uint64_t c_word[4][U2X_CAP];   // [row][slot]: ordered key, ~index
+    float c_lp[4][U2X_CAP];        // log-probability of the slot
+    float q_v[4][U2X_QCAP];        // qualifying digit-1 values
+    int q_b[4][U2X_QCAP];          //            and their indices
+  };
+  union WaveLds {
+    Lists l;
+    ProdScratch sc;
+  };
+  __shared__ WaveLds lds[4];
+  __shared__ int s_idx[4][MAX_K];
+  __shared__ float s_w[4][MAX_K];
+  const int wv = threadIdx.x >> 6;
+  Lists& L = lds[wv].l;
+  const int lane = lane_id();
+  const int r = lane >> 4, p = lane & 15;
+  const int64_t total = (int64_t)a.nsides * a.N;
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + wv) * 4;
+  const int64_t grow = g0 + r;
+  const bool live = grow < total;
+  const int side = (live && grow >= a.N) ? 1 : 0;   // nsides <= 2
+  const int64_t row = live ? grow - (int64_t)side * a.N : 0;
+  const int k = a.k[side];
+  const int P = a.P;
+  const bool own = live && 4 * p < P;
+  float x0[4], x1[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x0[e] = x1[e] = -INFINITY;
+  if (own) {
+    const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)(2 * P);
+    Vec4<IO>::load(src + 4 * p, x0);
+    Vec4<IO>::load(src + P + 4 * p, x1);
+  }
+  // digit maxima and logsumexps over the row
+  const float m0 = fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3]));
+  const float m1 = fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3]));
+  const float M0 = row16_max(m0), M1 = row16_max(m1);
+  float s0 = 0.f, s1 = 0.f;
+  if (M0 != -INFINITY) {
+    const float n = -M0 * LOG2E;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s0 += fast_exp2(fmaf(x0[e], LOG2E, n));
+  }
+  if (M1 != -INFINITY) {
+    const float n = -M1 * LOG2E;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s1 += fast_exp2(fmaf(x1[e], LOG2E, n));
+  }
+  const float lse0 = M0 + logf(row16_sum(s0));
+  const float lse1 = M1 + logf(row16_sum(s1));
+  // v: the largest 16-bit ordered prefix that K digit-1 values reach (for
+  // bf16 logits the K-th largest value itself)
+  uint32_t ob[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ob[e] = ordered_bits(x1[e]) >> 16;
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    float n = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) n += (ob[e] >= c) ? 1.f : 0.f;
+    t = (row16_sum(n) >= (float)k) ? c : t;
+  }
+  const float tau = M0 + from_ordered(t << 16);
+  // the row's digit-1 values that can reach tau, listed in LDS
+  int nq;
+  {
+    bool qf[4];
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[e] = own && M0 + x1[e] >= tau;
+      n += qf[e] ? 1 : 0;
+    }
+    const int incl = row16_incl(n);
+    int pos = incl - n;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (qf[e]) {
+        if (pos < U2X_QCAP) {
+          L.q_v[r][pos] = x1[e];
+          L.q_b[r][pos] = 4 * p + e;
+        }
+        ++pos;
+      }
+    }
+    nq = row16_last(incl);
+  }
+  const bool q_over = nq > U2X_QCAP;   // such a row takes the whole-wave path
+  if (q_over) nq = 0;
+  wave_sync();
+  // every slot reaching tau: each listed digit-1 value against the lane's
+  // four digit-0 values
+  const int nq_max = __builtin_amdgcn_readfirstlane((int)wave_max((float)nq));
+  int count = 0;
+  for (int i = 0; i < nq_max; ++i) {
+    const bool ok = i < nq;
+    const float l1b = ok ? L.q_v[r][i] : -INFINITY;
+    const int b = ok ? L.q_b[r][i] : 0;
+    bool cf[4];
+    int nc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cf[e] = ok && own && x0[e] + l1b >= tau;
+      nc += cf[e] ? 1 : 0;
+    }
+    const int incl = row16_incl(nc);
+    int pos = count + incl - nc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (cf[e]) {
+        if (pos < U2X_CAP) {
+          const float key = x0[e] + l1b;
+          const uint32_t id = (uint32_t)((4 * p + e) * P + b);   // < 2^12
+          L.c_word[r][pos] = ((uint64_t)sel_key(key) << 32) |
+                             ((uint32_t)(0xFFFFu - id) << 16) | (uint32_t)pos;
+          L.c_lp[r][pos] = (x0[e] - lse0) + (l1b - lse1);
+        }
+        ++pos;
+      }
+    }
+    count += row16_last(incl);
+  }
+  const bool failed = live && (q_over || count > U2X_CAP || count < k);
+  wave_sync();
+  // K rounds of the row maximum over the listed words (lane p holds the
+  // listed slots p, p + 16, ...; a taken or missing slot is 0)
+  constexpr int PER_LANE = U2X_CAP / 16;
+  static_assert(U2X_CAP % 16 == 0, "lanes hold whole shares of the list");
+  uint64_t wd[PER_LANE];
+#pragma unroll
+  for (int j = 0; j < PER_LANE; ++j) {
+    const int c = p + 16 * j;
+    wd[j] = (live && !failed && c < count) ? L.c_word[r][c] : 0ull;
+  }
+  const int k_max = __builtin_amdgcn_readfirstlane((int)wave_max((float)(live ? k : 0)));
+  uint64_t best = wd[0];
+#pragma unroll
+  for (int j = 1; j < PER_LANE; ++j) best = wd[j] > best ? wd[j] : best;
+  uint32_t my_word = 0;   // lane p: low half of the p-th best word
+  for (int rnd = 0; rnd < k_max; ++rnd) {
+    const uint64_t win = row16_max64(best);
+    if (p == rnd) my_word = (uint32_t)win;
+    if (win != 0ull && best == win) {   // this lane held it: take it out
+#pragma unroll
+      for (int j = 0; j < PER_LANE; ++j) wd[j] = (wd[j] == win) ? 0ull : wd[j];
+      best = wd[0];
+#pragma unroll
+      for (int j = 1; j < PER_LANE; ++j) best = wd[j] > best ? wd[j] : best;
+    }
+  }
+  if (live && !failed) {
+    float w = 0.f;
+    if (p < k) w = expf(L.c_lp[r][my_word & 0xFFFFu]);
+    const float tot = row16_sum(w);
+    if (a.renorm[side]) w = w / tot;
+    if (p < k) {
+      const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
+      const int id = (int)(0xFFFFu - (my_word >> 16));
+      a.idx[side][row * k + p] = (shift < 0) ? id : (id + shift) % a.S;
+      a.w[side][row * k + p] = w;
+    }
+    if (p == 0) a.lse[side][row * 2] = lse0;
+    if (p == 1) a.lse[side][row * 2 + 1] = lse1;
+  }
+  // rows that need the whole-wave path, one at a time (its scratch takes the
+  // lists' LDS, which every lane has finished reading)
+  uint64_t fm = __ballot(failed && p == 0);
+  wave_sync();
+  while (fm) {
+    const int rr = (int)__builtin_ctzll(fm) >> 4;
+    fm &= fm - 1;
+    const int64_t fg = g0 + rr;
+    const int fside = fg >= a.N ? 1 : 0;
+    const int64_t frow = fg - (int64_t)fside * a.N;
+    const int fk = a.k[fside];
+    const IO* fsrc = reinterpret_cast<const IO*>(a.logits[fside]) + frow * (int64_t)(2 * P);
+    wave_sync();
+    decode_row_product<IO>(fsrc, 2, P, fk, a.renorm[fside], lds[wv].sc, s_idx[wv], s_w[wv]);
+    wave_sync();
+    if (lane < fk) {
+      const int shift = cape_shift_of(frow, a.H, a.T, a.S, a.cape_heads, a.t0);
+      const int id = s_idx[wv][lane];
+      a.idx[fside][frow * fk + lane] = (shift < 0) ? id : (id + shift) % a.S;
+      a.w[fside][frow * fk + lane] = s_w[wv][lane];
+    }
+    if (lane < 2) a.lse[fside][frow * 2 + lane] = lds[wv].sc.dlse[lane];
+  }
+}
+
 // Decode backward of product rows (one wave per row): with gw_j as for one
 // digit, dl_u[i] = sum_j gw_j [digit u of a_j = i] - p_u[i] sum_j gw_j,
 // p_u = exp(l_u - lse_u) the digit softmax (paper App. B.1: the slot
@@ -459,6 +707,13 @@ __global__ __launch_bounds__(256) void decode_bwd_prod_kernel(DecodeBwdArgs a) {
 hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st) {
   const int64_t rows = (int64_t)a.nsides * a.N;
   if (rows == 0) return hipSuccess;
+  if (a.U == 2 && a.P <= WAVE && a.P % 4 == 0 && a.k[0] <= U2X_K && 4 * a.k[0] <= a.P &&
+      (a.nsides < 2 || (a.k[1] <= U2X_K && 4 * a.k[1] <= a.P))) {
+    const dim3 grid((unsigned)((rows + 15) / 16)), block(256);
+    if (bf16) hipLaunchKernelGGL(decode_fwd_u2x_kernel<bf16_t>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(decode_fwd_u2x_kernel<float>, grid, block, 0, st, a);
+    return hipGetLastError();
+  }
   if (a.U == 2 && a.P <= WAVE) {
     const dim3 grid((unsigned)((rows + 4 * U2_ROWS - 1) / (4 * U2_ROWS))), block(256);
     if (bf16) hipLaunchKernelGGL((decode_fwd_u2_kernel<bf16_t, U2_ROWS>), grid, block, 0, st, a);
