@@ -384,10 +384,10 @@ __global__ __launch_bounds__(256) void decode_bwd_u2_kernel(DecodeBwdArgs a) {
 // four rows per wave in the layout of decode_bwd_u2_kernel (DPP row r takes
 // logits row r, lane p entries 4p .. 4p + 3 of each digit).  The selection is
 // that of decode_row_u2_vals, made with row-local steps:
-//   tau = fl(M0 + v), v a lower bound of the K-th largest digit-1 logit (the
-//   largest 16-bit prefix of the ordered bits that K of its values reach;
-//   for bf16 logits that value itself), so K distinct slots (argmax l0, b)
-//   have keys >= tau and tau is at most the K-th best key;
+//   tau = max(fl(M0 + v1), fl(v0 + M1)), v_u a lower bound of the K-th
+//   largest logit of digit u (the largest 16-bit prefix of the ordered bits
+//   that K of its values reach; for bf16 logits that value itself), so K
+//   distinct slots reach tau and tau is at most the K-th best key;
 //   every slot with key fl(l0[a] + l1[b]) >= tau is listed (only digit-1
 //   values with fl(M0 + l1[b]) >= tau can give one) as a 64-bit word: its
 //   ordered key, then its index complemented in 16 bits, then its list
@@ -395,8 +395,9 @@ __global__ __launch_bounds__(256) void decode_bwd_u2_kernel(DecodeBwdArgs a) {
 //   descending, index ascending) and names its log-probability in the list;
 //   K rounds of a row maximum over the listed words give the K best in order.
 // Rows whose list would overflow or hold fewer than K slots (NaN logits, a
-// bound that is no number) take the whole-wave path afterwards, one by one.
-constexpr int U2X_CAP = 96;    // listed slots per row
+// bound that is no number) are marked and redone by the whole-wave path in a
+// second kernel, whose registers then do not limit this one's occupancy.
+constexpr int U2X_CAP = 64;    // listed slots per row
 constexpr int U2X_QCAP = 32;   // listed digit-1 values per row
 constexpr int U2X_K = 16;
 __device__ __forceinline__ float row16_max(float x) {
@@ -434,23 +435,16 @@ __device__ __forceinline__ uint64_t row16_max64(uint64_t x) {
 
 template <typename IO>
 __global__ __launch_bounds__(256) void decode_fwd_u2x_kernel(DecodeFwdArgs a) {
-  // per wave: the lists of its four rows, or (afterwards) the scratch of the
-  // whole-wave path, in the same LDS
+  // per wave: the lists of its four rows
   struct Lists {
-    uint64_t c_word[4][U2X_CAP];   // [row][slot]: ordered key, ~index
+    uint64_t c_word[4][U2X_CAP];   // [row][slot]: ordered key, complemented index, position
     float c_lp[4][U2X_CAP];        // log-probability of the slot
     float q_v[4][U2X_QCAP];        // qualifying digit-1 values
     int q_b[4][U2X_QCAP];          //            and their indices
   };
-  union WaveLds {
-    Lists l;
-    ProdScratch sc;
-  };
-  __shared__ WaveLds lds[4];
-  __shared__ int s_idx[4][MAX_K];
-  __shared__ float s_w[4][MAX_K];
+  __shared__ Lists lds[4];
   const int wv = threadIdx.x >> 6;
-  Lists& L = lds[wv].l;
+  Lists& L = lds[wv];
   const int lane = lane_id();
   const int r = lane >> 4, p = lane & 15;
   const int64_t total = (int64_t)a.nsides * a.N;
@@ -487,21 +481,31 @@ __global__ __launch_bounds__(256) void decode_fwd_u2x_kernel(DecodeFwdArgs a) {
   }
   const float lse0 = M0 + logf(row16_sum(s0));
   const float lse1 = M1 + logf(row16_sum(s1));
-  // v: the largest 16-bit ordered prefix that K digit-1 values reach (for
-  // bf16 logits the K-th largest value itself)
-  uint32_t ob[4];
+  // v0, v1: the largest 16-bit ordered prefixes that K values of digit 0 and
+  // of digit 1 reach (for bf16 logits the K-th largest values themselves);
+  // the two searches share one loop, their counts one row sum
+  uint32_t ob0[4], ob1[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ob[e] = ordered_bits(x1[e]) >> 16;
-  uint32_t t = 0;
+  for (int e = 0; e < 4; ++e) {
+    ob0[e] = ordered_bits(x0[e]) >> 16;
+    ob1[e] = ordered_bits(x1[e]) >> 16;
+  }
+  uint32_t t0 = 0, t1 = 0;
 #pragma unroll
   for (int b = 15; b >= 0; --b) {
-    const uint32_t c = t | (1u << b);
+    const uint32_t c0 = t0 | (1u << b), c1 = t1 | (1u << b);
     float n = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) n += (ob[e] >= c) ? 1.f : 0.f;
-    t = (row16_sum(n) >= (float)k) ? c : t;
+    for (int e = 0; e < 4; ++e) n += ((ob0[e] >= c0) ? 1.f : 0.f) + ((ob1[e] >= c1) ? 128.f : 0.f);
+    const float tot = row16_sum(n);          // count0 + 128 count1, both <= 64
+    const float n1 = floorf(tot * (1.f / 128.f));
+    t0 = (tot - 128.f * n1 >= (float)k) ? c0 : t0;
+    t1 = (n1 >= (float)k) ? c1 : t1;
   }
-  const float tau = M0 + from_ordered(t << 16);
+  // K distinct slots (argmax l0, b) reach fl(M0 + v1) and K distinct slots
+  // (a, argmax l1) reach fl(v0 + M1): either is at most the K-th best key
+  // (fmaxf keeps the number when one bound is NaN)
+  const float tau = fmaxf(M0 + from_ordered(t1 << 16), from_ordered(t0 << 16) + M1);
   // the row's digit-1 values that can reach tau, listed in LDS
   int nq;
   {
@@ -603,28 +607,48 @@ __global__ __launch_bounds__(256) void decode_fwd_u2x_kernel(DecodeFwdArgs a) {
     if (p == 0) a.lse[side][row * 2] = lse0;
     if (p == 1) a.lse[side][row * 2 + 1] = lse1;
   }
-  // rows that need the whole-wave path, one at a time (its scratch takes the
-  // lists' LDS, which every lane has finished reading)
-  uint64_t fm = __ballot(failed && p == 0);
-  wave_sync();
+  // a row that needs the whole-wave path is marked by index -1 in its first
+  // entry; decode_fwd_u2_fix redoes it
+  if (failed && p == 0) a.idx[side][row * k] = -1;
+}
+
+// The rows decode_fwd_u2x_kernel marked, by the whole-wave path, one at a
+// time: a wave looks at 64 consecutive rows.
+template <typename IO>
+__global__ __launch_bounds__(256) void decode_fwd_u2_fix_kernel(DecodeFwdArgs a) {
+  __shared__ ProdScratch scratch[4];
+  __shared__ int s_idx[4][MAX_K];
+  __shared__ float s_w[4][MAX_K];
+  const int wv = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int64_t total = (int64_t)a.nsides * a.N;
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + wv) * WAVE;
+  const int64_t grow = g0 + lane;
+  bool marked = false;
+  if (grow < total) {
+    const int side = grow >= a.N ? 1 : 0;
+    const int64_t row = grow - (int64_t)side * a.N;
+    marked = a.idx[side][row * a.k[side]] == -1;
+  }
+  uint64_t fm = __ballot(marked);
   while (fm) {
-    const int rr = (int)__builtin_ctzll(fm) >> 4;
+    const int l = (int)__builtin_ctzll(fm);
     fm &= fm - 1;
-    const int64_t fg = g0 + rr;
-    const int fside = fg >= a.N ? 1 : 0;
-    const int64_t frow = fg - (int64_t)fside * a.N;
-    const int fk = a.k[fside];
-    const IO* fsrc = reinterpret_cast<const IO*>(a.logits[fside]) + frow * (int64_t)(2 * P);
+    const int64_t fg = g0 + l;
+    const int side = fg >= a.N ? 1 : 0;
+    const int64_t row = fg - (int64_t)side * a.N;
+    const int k = a.k[side];
+    const IO* src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)(2 * a.P);
+    decode_row_product<IO>(src, 2, a.P, k, a.renorm[side], scratch[wv], s_idx[wv], s_w[wv]);
     wave_sync();
-    decode_row_product<IO>(fsrc, 2, P, fk, a.renorm[fside], lds[wv].sc, s_idx[wv], s_w[wv]);
-    wave_sync();
-    if (lane < fk) {
-      const int shift = cape_shift_of(frow, a.H, a.T, a.S, a.cape_heads, a.t0);
+    if (lane < k) {
+      const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
       const int id = s_idx[wv][lane];
-      a.idx[fside][frow * fk + lane] = (shift < 0) ? id : (id + shift) % a.S;
-      a.w[fside][frow * fk + lane] = s_w[wv][lane];
+      a.idx[side][row * k + lane] = (shift < 0) ? id : (id + shift) % a.S;
+      a.w[side][row * k + lane] = s_w[wv][lane];
     }
-    if (lane < 2) a.lse[fside][frow * 2 + lane] = lds[wv].sc.dlse[lane];
+    if (lane < 2) a.lse[side][row * 2 + lane] = scratch[wv].dlse[lane];
+    wave_sync();   // the next row rewrites the scratch
   }
 }
 
@@ -710,8 +734,14 @@ hipError_t launch_decode_fwd(const DecodeFwdArgs& a, bool bf16, hipStream_t st) 
   if (a.U == 2 && a.P <= WAVE && a.P % 4 == 0 && a.k[0] <= U2X_K && 4 * a.k[0] <= a.P &&
       (a.nsides < 2 || (a.k[1] <= U2X_K && 4 * a.k[1] <= a.P))) {
     const dim3 grid((unsigned)((rows + 15) / 16)), block(256);
-    if (bf16) hipLaunchKernelGGL(decode_fwd_u2x_kernel<bf16_t>, grid, block, 0, st, a);
-    else hipLaunchKernelGGL(decode_fwd_u2x_kernel<float>, grid, block, 0, st, a);
+    const dim3 fgrid((unsigned)((rows + 4 * WAVE - 1) / (4 * WAVE)));
+    if (bf16) {
+      hipLaunchKernelGGL(decode_fwd_u2x_kernel<bf16_t>, grid, block, 0, st, a);
+      hipLaunchKernelGGL(decode_fwd_u2_fix_kernel<bf16_t>, fgrid, block, 0, st, a);
+    } else {
+      hipLaunchKernelGGL(decode_fwd_u2x_kernel<float>, grid, block, 0, st, a);
+      hipLaunchKernelGGL(decode_fwd_u2_fix_kernel<float>, fgrid, block, 0, st, a);
+    }
     return hipGetLastError();
   }
   if (a.U == 2 && a.P <= WAVE) {

@@ -43,6 +43,10 @@ DECODE_CASES = [
     (5, 4, 8, "bf16", False, "normal"),
     (5, 4, 8, "f32", False, "int"),
     (2, 64, 8, "bf16", False, "normal"),
+    (2, 64, 8, "f32", True, "int"),          # four rows per wave; ties overflow the row list
+    (2, 32, 8, "bf16", False, "int"),        # P = 4K: K lanes of a row hold values
+    (2, 48, 12, "bf16", False, "normal"),    # P not a power of two
+    (2, 64, 16, "f32", True, "normal"),      # the largest K of the four-row kernel
     (2, 64, 33, "f32", True, "int"),
     (2, 128, 64, "bf16", False, "normal"),   # S = 16384, k = 64
     (2, 5, 25, "f32", False, "int"),         # k = S
