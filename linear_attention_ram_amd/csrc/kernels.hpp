@@ -5,7 +5,7 @@
 
 namespace ramk {
 
-constexpr int CHUNK = 16;        // scan chunk: checkpoints at 16-aligned events
+constexpr int CHUNK = 16;        // scan chunk: 16 events from the segment start
 constexpr int NWL = 4;           // waves per long-segment scan workgroup
 constexpr int SHORT_WAVES = 4;   // waves (one short segment each) per short-segment workgroup
 constexpr int LONG_EVENTS = 128; // segments with more events take the cooperative path

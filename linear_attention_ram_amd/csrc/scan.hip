@@ -4,10 +4,12 @@
 // accumulated back to its token).
 //
 // A segment (b, h, slot) keeps its content in registers: lane l holds channels
-// [l*CPL, l*CPL + CPL).  Events are taken in chunks of up to CHUNK = 16 that
-// are aligned to multiples of 16 in the global event list; the state before
-// every aligned event inside a segment is saved as a checkpoint for the
-// reverse pass.
+// [l*CPL, l*CPL + CPL).  Events are taken in chunks of CHUNK = 16 from the
+// segment's start (the last chunk may be shorter); the state before every
+// chunk but the first is saved as a checkpoint for the reverse pass, at index
+// (chunk start) / 16 of the checkpoint array: chunk starts of one segment are
+// 16 apart and those of later segments lie more than 16 beyond, so no two
+// share an index.
 //
 // Lane layout of a chunk.  Lane l also holds the scalars of event (l & 15):
 // the four 16-lane rows of the wave carry identical copies, so the DPP
@@ -342,11 +344,10 @@ __device__ __forceinline__ float batched_sum(const float (&x)[CHUNK]) {
   return __shfl(y, (lane & (CHUNK - 1)) * 4, WAVE);
 }
 
-// Start of chunk k of the chunk sequence that begins at position p (p is the
-// segment start or a multiple of CHUNK), clamped to end.
+// Start of chunk k of the chunk sequence that begins at position p (a chunk
+// start), clamped to end.
 __device__ __forceinline__ int chunk_start(int p, int k, int end) {
-  if (k == 0) return min(p, end);
-  return min(end, (p / CHUNK + k) * CHUNK);
+  return min(end, p + k * CHUNK);
 }
 
 // Entry counts of the long-segment list's length classes, read once per
@@ -469,9 +470,9 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
   float m = a.mass0 ? a.mass0[g] : 0.f;
 
   float4 rec = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (beg < end) rec = load_rec(a.events, beg, min(end, (beg / CHUNK + 1) * CHUNK) - beg, beg, end);
+  if (beg < end) rec = load_rec(a.events, beg, min(end, beg + CHUNK) - beg, beg, end);
   for (int p0 = beg; p0 < end;) {
-    const int p1 = min(end, (p0 / CHUNK + 1) * CHUNK);
+    const int p1 = min(end, p0 + CHUNK);
     const int n = p1 - p0;
     if (p0 != beg) {
       float* ck = a.ckpt_s + (int64_t)(p0 / CHUNK) * a.d_v;
@@ -488,7 +489,7 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
     const float rr = (ev.side == 1) ? ev.wt : 0.f;
     const uint32_t xo = (ev.valid && ev.live && ev.side == 0) ? (uint32_t)ev.rb * c.pitch : OOB;
     const uint32_t so = (ev.valid && ev.side == 1) ? ((uint32_t)ev.rb * a.k_r + ev.j) * c.pitch : OOB;
-    rec = load_rec(a.events, p1, min(end, (p1 / CHUNK + 1) * CHUNK) - p1, beg, end);   // next chunk
+    rec = load_rec(a.events, p1, min(end, p1 + CHUNK) - p1, beg, end);   // next chunk
 
     const uint32_t wm = (uint32_t)__ballot(ev.valid && ev.side == 0) & 0xFFFFu;
     const uint32_t rm = (uint32_t)__ballot(ev.valid && ev.side == 1) & 0xFFFFu;
@@ -1048,10 +1049,10 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
   if (beg < end) {
     BwdChunk<IO, CPL, false> ck;
     float pr[CHUNK], pw[CHUNK];
-    int cs = max(beg, ((end - 1) / CHUNK) * CHUNK);
+    int cs = beg + ((end - 1 - beg) / CHUNK) * CHUNK;
     float4 rec = load_rec(a.events, cs, end - cs, beg, end);
     while (true) {
-      const int n = min(end, (cs / CHUNK + 1) * CHUNK) - cs;
+      const int n = min(end, cs + CHUNK) - cs;
       const int cp = max(beg, cs - CHUNK);
       float s[CPL], m;
       chunk_state<IO, CPL>(a, c, g, beg, cs, s, m);
@@ -1108,7 +1109,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
   const rsrc_t rs = make_rsrc(reinterpret_cast<IO*>(a.stash) + c.row0 * a.k_w * a.d_v,
                               nrow * a.k_w * c.pitch);
   const int beg = ld_global(a.seg_offset + g), end = ld_global(a.seg_offset + g + 1);
-  const int nchunks = (end - 1) / CHUNK - beg / CHUNK + 1;
+  const int nchunks = (end - beg + CHUNK - 1) / CHUNK;
 
   float sh_carry[CPL];
 #pragma unroll
