@@ -235,7 +235,7 @@ __device__ __forceinline__ void finish_weights(const DecodeScratch& sc, int k, f
 // one read of the row from memory, then every pass works on registers.
 // FULL: the row has exactly NV * 64 vectors.
 template <typename IO, int NV, bool FULL>
-__device__ float decode_row_resident(const IO* __restrict__ row, int S, int k, int renorm,
+__device__ __forceinline__ float decode_row_resident(const IO* __restrict__ row, int S, int k, int renorm,
                                      DecodeScratch& sc, int* sel_i, float* sel_w) {
   constexpr int E = vec16<IO>::E;
   const int lane = lane_id();
