@@ -121,12 +121,17 @@ typedef struct ram_ws_layout {
                          d lambda/d w}; code = (t << 7) | (side << 6) | j, bit 31 set for
                          the (weight 0, no-op) events of masked tokens; segment-major, time
                          order inside a segment, a token's write before its read            */
-  size_t ckpt_s;      /* float (E/16 + 1, d_v): slot content at every 16-aligned event        */
+  size_t ckpt_s;      /* float (E/16 + 1, d_v): slot content before every 16-event chunk of a
+                         segment but its first (chunks counted from the segment's first
+                         event), at index (chunk's first event) / 16                         */
   size_t ckpt_m;      /* float (E/16 + 1): slot mass at the same points                      */
   size_t stash;       /* io (N, k_r, d_v): read contributions r_j * s_t[a_j] of each (token, j) */
   size_t tile_hist;   /* int32: bucketing scratch                                              */
   size_t long_list;   /* int32: segments that take the cooperative scan path                   */
-  size_t long_count;  /* int32: their number per length class, and the scans' work counters     */
+  size_t long_count;  /* int32: their number per length class, the scans' work counters, and
+                         the length of short_list                                              */
+  size_t short_list;  /* int32: segments with 1 to 128 events (slots without events need no
+                         scan)                                                                 */
   size_t stash_b;     /* io (N, k_w, d_v): backward scratch, d_v contributions of each write     */
   size_t dw;          /* float (N, k_w): gradient of each write weight                          */
   size_t dr;          /* float (N, k_r): gradient of each read weight                           */

@@ -65,7 +65,7 @@ class Problem(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "idx_w", "w_w", "lse_w", "idx_r", "w_r", "lse_r", "seg_offset", "events", "ckpt_s",
-        "ckpt_m", "stash", "tile_hist", "long_list", "long_count", "stash_b", "dw", "dr",
+        "ckpt_m", "stash", "tile_hist", "long_list", "long_count", "short_list", "stash_b", "dw", "dr",
         "dgam", "epi_d_o", "epi_part", "fwd_bytes", "total_bytes")]
 
 

@@ -87,6 +87,7 @@ int long_cap(const Dims& d) {
   return (int)(c < d.nseg ? c : d.nseg);
 }
 
+
 void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
@@ -106,6 +107,7 @@ void make_layout(const ram_problem* p, const Dims& d, ram_ws_layout* L) {
                       ((size_t)d.ntiles * d.S + scan_blocks(d.S)));
   L->long_list = take(sizeof(int32_t) * NBIN * long_cap(d));
   L->long_count = take(sizeof(int32_t) * LONG_WORDS);
+  L->short_list = take(sizeof(int32_t) * (d.E < d.nseg ? d.E : d.nseg));
   L->fwd_bytes = off;
   L->stash_b = take(d.io_bytes * d.N * p->k_w * p->d_v);
   L->dw = take(sizeof(float) * d.N * p->k_w);
@@ -401,6 +403,7 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
   ba.long_list = (int32_t*)(w + L.long_list);
   ba.long_count = (int32_t*)(w + L.long_count);
   ba.long_cap = cap;
+  ba.short_list = (int32_t*)(w + L.short_list);
   e = launch_bucket(ba, bf, s, before, after);
   if (e != hipSuccess) return RAM_EHIP;
 
@@ -419,6 +422,8 @@ int forward_impl(const ram_problem* p, const ram_epilogue* ep, const void* wlogi
   sa.queue = ba.long_count + NBIN;
   sa.long_cap = cap;
   sa.use_long = d.ntiles > 0;
+  sa.short_list = ba.short_list;
+  sa.short_count = ba.long_count + SHORT_WORD;
   sa.seg_offset = ba.seg_offset;
   sa.events = ba.events;
   sa.v = v;
@@ -548,6 +553,8 @@ int backward_impl(const ram_problem* p, const ram_epilogue* ep, void* ws, size_t
   sb.queue = (int32_t*)(w + L.long_count) + NBIN + 2;
   sb.long_cap = cap;
   sb.use_long = d.ntiles > 0;
+  sb.short_list = (const int32_t*)(w + L.short_list);
+  sb.short_count = (const int32_t*)(w + L.long_count) + SHORT_WORD;
   sb.seg_offset = (const int32_t*)(w + L.seg_offset);
   sb.events = (const EventRec*)(w + L.events);
   sb.v = v;

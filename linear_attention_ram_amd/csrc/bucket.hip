@@ -11,7 +11,9 @@
 //            entry (always 0); the block's event count goes to blk_tot.
 //            Segments with more than LONG_EVENTS events are listed for the
 //            cooperative scan path, in NBIN classes of doubling length (any
-//            order inside a class).  Every (b, h) holds exactly
+//            order inside a class), and segments with 1 to LONG_EVENTS
+//            events in the short list (slot order inside a block, blocks
+//            in any order).  Every (b, h) holds exactly
 //            T*(k_w+k_r) events, so segment offsets need no scan across
 //            (b, h);
 //   scatter  one workgroup per (b, h, tile): its waves set up the tile's
@@ -61,8 +63,9 @@ __global__ __launch_bounds__(256) void bucket_hist_kernel(BucketArgs a) {
 
 __global__ __launch_bounds__(SCAN_SLOTS) void bucket_scan_kernel(BucketArgs a) {
   static_assert(SCAN_SLOTS == 16 * WAVE, "one slot per thread, 16 waves");
-  __shared__ int wave_tot[16];
+  __shared__ int wave_tot[16], wave_short[16];
   __shared__ int cls_n[NBIN], cls_at[NBIN];   // long segments of the block per class
+  __shared__ int short_at;                    // the block's place in the short list
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x;
   if (tid < NBIN) cls_n[tid] = 0;
@@ -87,13 +90,25 @@ __global__ __launch_bounds__(SCAN_SLOTS) void bucket_scan_kernel(BucketArgs a) {
     }
   }
   const int incl = wave_incl_scan(cnt);
-  if (lane_id() == WAVE - 1) wave_tot[tid / WAVE] = incl;
+  // segments with 1 to LONG_EVENTS events: listed for the short-segment
+  // scans (slots without events need no scan), in slot order inside the
+  // block, the block's share reserved with one global counter update
+  const bool shrt = s < S && cnt > 0 && cnt <= LONG_EVENTS;
+  const uint64_t sbal = __ballot(shrt);
+  if (lane_id() == WAVE - 1) {
+    wave_tot[tid / WAVE] = incl;
+    wave_short[tid / WAVE] = __popcll(sbal);
+  }
   __syncthreads();
-  int before = 0, all = 0;
+  int before = 0, all = 0, s_before = 0, s_all = 0;
   for (int w = 0; w < 16; ++w) {
-    const int wt = wave_tot[w];
-    if (w < tid / WAVE) before += wt;
+    const int wt = wave_tot[w], ws = wave_short[w];
+    if (w < tid / WAVE) {
+      before += wt;
+      s_before += ws;
+    }
     all += wt;
+    s_all += ws;
   }
   // long segments: a place in the block's share of their class, then one
   // global counter update per class and block (hot slots make the global
@@ -107,8 +122,11 @@ __global__ __launch_bounds__(SCAN_SLOTS) void bucket_scan_kernel(BucketArgs a) {
   }
   __syncthreads();
   if (tid < NBIN && cls_n[tid] > 0) cls_at[tid] = atomicAdd(&a.long_count[tid], cls_n[tid]);
+  if (tid == NBIN && s_all > 0) short_at = atomicAdd(&a.long_count[SHORT_WORD], s_all);
   __syncthreads();
   if (lng) a.long_list[(int64_t)cls * a.long_cap + cls_at[cls] + rank] = (int32_t)((int64_t)bh * S + s);
+  if (shrt)
+    a.short_list[short_at + s_before + __popcll(sbal & lanemask_lt())] = (int32_t)((int64_t)bh * S + s);
   if (tid == 0) a.blk_tot[(int64_t)bh * a.nblk + blk] = all;
   if (blk == 0 && bh == a.B * a.H - 1 && tid == 0)
     a.seg_offset[(int64_t)a.B * a.H * S] =

@@ -12,10 +12,13 @@ constexpr int LONG_EVENTS = 128; // segments with more events take the cooperati
 constexpr int NBIN = 8;          // length classes of the long-segment list: class c holds
                                  // segments of [129 * 2^c, 129 * 2^(c+1)) events (the last
                                  // class is open-ended); scans take the longest first
-constexpr int LONG_WORDS = NBIN + 4;  // int32 words per long-segment list header:
+constexpr int SHORT_WORD = 32;        // a 128-byte line of its own: the work queues' atomics
+                                      // would hold up its many reads
+constexpr int LONG_WORDS = SHORT_WORD + 1;  // int32 words per long-segment list header:
                                       //   [0, NBIN)  entries per class
                                       //   NBIN, +1   forward scan: next ticket, finished workgroups
                                       //   NBIN+2, +3 reverse scan: the same
+                                      //   SHORT_WORD entries of the short-segment list
 constexpr int SCAN_SLOTS = 1024; // slots per workgroup of the bucketing scan
 constexpr int MAX_DV = 128;      // widest slot
 constexpr uint32_t MAX_BUF_BYTES = 0x7FE00000u;  // one batch's v, dO or stash rows (scans)
@@ -47,8 +50,10 @@ struct BucketArgs {
                           // of this call's piece; events is the whole list)
   EventRec* events;       // (all events of the call)
   int32_t* long_list;     // (NBIN, long_cap): segments with more than LONG_EVENTS events
-  int32_t* long_count;    // (LONG_WORDS): entries per class, then the scans' work queues
+  int32_t* long_count;    // (LONG_WORDS): entries per class, the scans' work queues, the
+                          // short-list length
   int long_cap;
+  int32_t* short_list;    // (B*H*S at most): segments with 1 to LONG_EVENTS events
 };
 
 struct ScanFwdArgs {
@@ -59,7 +64,9 @@ struct ScanFwdArgs {
   const int32_t* long_count;  // (NBIN)
   int32_t* queue;             // (2): next ticket, finished workgroups; zero at launch
   int long_cap;
-  int use_long;           // long_list / long_count are valid
+  int use_long;           // long_list / long_count / short_list are valid
+  const int32_t* short_list;  // segments with 1 to LONG_EVENTS events
+  const int32_t* short_count; // its length
   const int32_t* seg_offset;
   const EventRec* events;
   const void* v;          // (N, d_v) io
@@ -81,6 +88,8 @@ struct ScanBwdArgs {
   int32_t* queue;         // (2), as in the forward
   int long_cap;
   int use_long;
+  const int32_t* short_list;
+  const int32_t* short_count;
   const int32_t* seg_offset;
   const EventRec* events;
   const void* v;          // io

@@ -34,7 +34,9 @@
 //     stores its contribution r*s, in the io dtype, to its own (token, j) row
 //     of a stash.  A token-major pass later sums the K rows of each token.
 //     No atomics: the read-out scatter is plain stores.
-// Short segments (<= LONG_EVENTS events) take one wave each.  Long segments
+// Short segments (1 to LONG_EVENTS events) take one wave each, found through
+// the bucketing's list of them where most segments have no events (a hot
+// slot layout leaves most slots untouched).  Long segments
 // (hot slots) take a workgroup of NWL waves that advance NWL chunks at a
 // time: each wave forms its chunk's mass map and, once its incoming mass is
 // known, its content map s -> P*s + b (computed from s = 0); the maps are
@@ -454,7 +456,7 @@ __device__ __forceinline__ void fwd_replay(const typename Lanes<IO, CPL>::Raw (&
 // ---------------------------------------------------------------------------
 
 template <typename IO, int CPL>
-__device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
+__device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g, int beg, int end) {
   using LN = Lanes<IO, CPL>;
   const SegCtx<IO, CPL> c = seg_ctx<IO, CPL>(g, a.S, a.H, a.T, a.d_v);
   const int lane = lane_id();
@@ -462,7 +464,6 @@ __device__ void scan_fwd_short(const ScanFwdArgs& a, int64_t g) {
   const rsrc_t rv = make_rsrc(reinterpret_cast<const IO*>(a.v) + c.row0 * a.d_v, nrow * c.pitch);
   const rsrc_t rs = make_rsrc(reinterpret_cast<IO*>(a.stash) + c.row0 * a.k_r * a.d_v,
                               nrow * a.k_r * c.pitch);
-  const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
 
   float s[CPL];
 #pragma unroll
@@ -652,14 +653,62 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
   }
 }
 
-// Short segments: one wave each, SHORT_WAVES waves per workgroup, one
-// workgroup per SHORT_WAVES consecutive segments (long ones are skipped).
+// Segment i without events keeps its state: dst = src (or 0), lane l
+// holding channels [l * CPL, l * CPL + CPL).
+template <int CPL>
+__device__ __forceinline__ void keep_state(int64_t i, int d_v, const float* src_s,
+                                           const float* src_m, float* dst_s, float* dst_m) {
+  const int c0 = lane_id() * CPL;
+  if (dst_s && dst_s != src_s && c0 < d_v) {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) dst_s[i * d_v + c0 + k] = src_s ? src_s[i * d_v + c0 + k] : 0.f;
+  }
+  if (dst_m && dst_m != src_m && lane_id() == 0) dst_m[i] = src_m ? src_m[i] : 0.f;
+}
+
+// The segment wave i of a short-segment kernel scans (-1: none) and its
+// event range.  When at most half of the segments are in the bucketing's
+// short list (hot slots take most events, most slots none), wave i takes
+// list entry i, so the waves with work are the grid's first and the rest
+// end at once; otherwise it takes segment i itself when that one is short,
+// which saves the list's extra dependent load where nearly every segment
+// has a few events.  pb / pe: the event range of segment i, loaded when
+// the caller keeps the state of empty segments (keep) or segment i is the
+// one to scan; a wave without work then ends after the list length alone.
+template <typename Args>
+__device__ __forceinline__ int64_t short_segment(const Args& a, int64_t i, bool keep, int& pb,
+                                                 int& pe, int& beg, int& end) {
+  const int64_t n = a.use_long ? *a.short_count : 0;
+  if (keep || 2 * n > a.nseg) {
+    pb = a.seg_offset[i];
+    pe = a.seg_offset[i + 1];
+  }
+  if (2 * n <= a.nseg) {
+    if (i >= n) return -1;
+    const int64_t g = a.short_list[i];
+    beg = a.seg_offset[g];
+    end = a.seg_offset[g + 1];
+    return g;
+  }
+  beg = pb;
+  end = pe;
+  return (pe > pb && pe - pb <= LONG_EVENTS) ? i : -1;
+}
+
+// Segments of 1 to LONG_EVENTS events: one wave each (short_segment).  In
+// the forward wave i also keeps the state of segment i if that one has no
+// events; in the reverse it does so only when d_slot0 / d_mass0 are asked
+// for.
 template <typename IO, int CPL>
 __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_fwd_short_kernel(ScanFwdArgs a) {
-  const int64_t g = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
-  if (g >= a.nseg) return;
-  if (a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS) return;
-  scan_fwd_short<IO, CPL>(a, g);
+  // the grid's last waves past the segments load for the last one and end
+  const int64_t w = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
+  const int64_t i = w < a.nseg ? w : a.nseg - 1;
+  int pb = 0, pe = 0, beg, end;
+  const int64_t g = short_segment(a, i, true, pb, pe, beg, end);
+  if (w >= a.nseg) return;
+  if (pe == pb) keep_state<CPL>(i, a.d_v, a.slot0, a.mass0, a.slot1, a.mass1);
+  if (g >= 0) scan_fwd_short<IO, CPL>(a, g, beg, end);
 }
 
 // Long segments: a resident grid of NWL-wave workgroups takes the list's
@@ -1030,7 +1079,7 @@ __device__ __forceinline__ void chunk_state(const ScanBwdArgs& a, const SegCtx<I
 }
 
 template <typename IO, int CPL>
-__device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
+__device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g, int beg, int end) {
   const SegCtx<IO, CPL> c = seg_ctx<IO, CPL>(g, a.S, a.H, a.T, a.d_v);
   const int lane = lane_id();
   const uint32_t nrow = (uint32_t)a.T * a.H;
@@ -1038,7 +1087,6 @@ __device__ void scan_bwd_short(const ScanBwdArgs& a, int64_t g) {
   const rsrc_t ro = make_rsrc(reinterpret_cast<const IO*>(a.d_o) + c.row0 * a.d_v, nrow * c.pitch);
   const rsrc_t rs = make_rsrc(reinterpret_cast<IO*>(a.stash) + c.row0 * a.k_w * a.d_v,
                               nrow * a.k_w * c.pitch);
-  const int beg = a.seg_offset[g], end = a.seg_offset[g + 1];
 
   float sh[CPL];
 #pragma unroll
@@ -1236,13 +1284,19 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
   }
 }
 
-// Same split as the forward.
+// Same split as the forward (an empty segment passes d_slot1 / d_mass1 on
+// to d_slot0 / d_mass0).
 template <typename IO, int CPL>
 __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_bwd_short_kernel(ScanBwdArgs a) {
-  const int64_t g = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
-  if (g >= a.nseg) return;
-  if (a.use_long && a.seg_offset[g + 1] - a.seg_offset[g] > LONG_EVENTS) return;
-  scan_bwd_short<IO, CPL>(a, g);
+  // the grid's last waves past the segments load for the last one and end
+  const int64_t w = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
+  const int64_t i = w < a.nseg ? w : a.nseg - 1;
+  const bool keep = a.d_slot0 || a.d_mass0;
+  int pb = 0, pe = 1, beg, end;
+  const int64_t g = short_segment(a, i, keep, pb, pe, beg, end);
+  if (w >= a.nseg) return;
+  if (keep && pe == pb) keep_state<CPL>(i, a.d_v, a.d_slot1, a.d_mass1, a.d_slot0, a.d_mass0);
+  if (g >= 0) scan_bwd_short<IO, CPL>(a, g, beg, end);
 }
 
 // At most 128 registers, so that 4 workgroups fit on a CU (the rows of the
@@ -1327,7 +1381,8 @@ int resident_blocks(void (*kern)(Args), int threads, int cap) {
 // streams).  The long grid is the resident count above, capped by the list
 // capacity: the work queue needs no more.  The long kernel is enqueued
 // first so that its workgroups, which hold the critical path, are resident
-// before the short kernel's many small ones fill the device.
+// before the short kernel's many small ones fill the device.  The short
+// kernel has a wave per segment.
 template <typename Args>
 hipError_t launch_pair(void (*shortk)(Args), void (*longk)(Args), int& resident, int per_cu,
                        const Args& a, hipStream_t st, hipStream_t side) {

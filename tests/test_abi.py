@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def test_problem_struct_matches_header_size():
     assert ctypes.sizeof(ram.Problem) == 64
-    assert ctypes.sizeof(ram.WsLayout) == 22 * ctypes.sizeof(ctypes.c_size_t)
+    assert ctypes.sizeof(ram.WsLayout) == 23 * ctypes.sizeof(ctypes.c_size_t)
     assert ctypes.sizeof(ram.Epilogue) == 24
 
 

@@ -2,6 +2,7 @@
 gradients of both logit sides, v, gamma and the initial state within the
 tolerance of the io dtype; the decoded-weight gradients (float32 internals)
 within 1e-4."""
+import numpy as np
 import pytest
 import torch
 
@@ -132,6 +133,22 @@ def test_hot_slots_over_ragged_slot_blocks():
     cfg = synth.Config("hot-ragged", 2, 2, 1024, 2504, 8, 8, 64, "bf16", zipf=1.1)
     x = synth.layer_inputs(cfg, device=DEV, seed=41, with_state=True, with_state_grads=True)
     full_check(cfg, x, gpu_problem(cfg), True, True, TOL["bf16"])
+
+
+@pytest.mark.parametrize("nhot,bias,listed", [(512, 2.0, True), (1024, 1.0, False)])
+def test_short_segments_listed_or_direct(nhot, bias, listed):
+    # as the forward case: both ways of the short-segment reverse scan, and
+    # d_slot1 / d_mass1 passed on through the slots without events
+    from test_gpu_forward import raised_slots, short_list_mode
+    cfg = synth.Config("raised", 1, 2, 512, 2048, 4, 4, 64, "bf16")
+    x = raised_slots(cfg, 51, nhot, bias, with_state=True, with_state_grads=True)
+    p = gpu_problem(cfg)
+    r, g = full_check(cfg, x, p, True, True, TOL["bf16"])
+    seg = ram.ws_views(p, r["ws"])["seg_offset"].cpu().numpy()
+    assert short_list_mode(seg) == listed
+    empty = torch.from_numpy(np.diff(seg.astype(np.int64)) == 0).to(DEV).reshape(cfg.B, cfg.H, cfg.S)
+    assert torch.equal(g["d_slot0"][empty], x["d_slot1"][empty])
+    assert torch.equal(g["d_mass0"][empty], x["d_mass1"][empty])
 
 
 def test_widest_address_space():

@@ -207,6 +207,44 @@ def test_hot_slots_over_ragged_slot_blocks(S):
     assert (seg[1:] - seg[:-1]).max() > 1000
 
 
+def raised_slots(cfg, seed, nhot, bias, **kw):
+    """Inputs whose first nhot slots have their logits raised by bias, so
+    that they take most selections."""
+    x = synth.layer_inputs(cfg, device=DEV, seed=seed, **kw)
+    for side in ("wl", "rl"):
+        x[side][..., :nhot] += bias
+    return x
+
+
+def short_list_mode(seg):
+    """Whether the short-segment scans take the bucketing's short list (at
+    most half of all segments have 1 to 128 events) or map waves to
+    segments directly."""
+    n = np.diff(seg.astype(np.int64))
+    return 2 * int(((n > 0) & (n <= 128)).sum()) <= n.size
+
+
+# 512 tokens, S = 2048, k = 4: 512 raised slots give about 500 short
+# segments per head (the list), 1024 slots raised by 1 about 1100 (direct)
+RAISED = [(512, 2.0, True), (1024, 1.0, False)]
+
+
+@pytest.mark.parametrize("nhot,bias,listed", RAISED)
+def test_short_segments_listed_or_direct(nhot, bias, listed):
+    # both ways the short-segment scans find their segments, with the state
+    # of the slots without events kept bit for bit
+    cfg = synth.Config("raised", 1, 2, 512, 2048, 4, 4, 64, "bf16")
+    x = raised_slots(cfg, 50, nhot, bias, with_state=True, with_d_o=False)
+    p = gpu_problem(cfg)
+    r = full_check(cfg, x, p, True, TOL["bf16"])
+    seg = ram.ws_views(p, r["ws"])["seg_offset"].cpu().numpy()
+    assert short_list_mode(seg) == listed
+    empty = torch.from_numpy(np.diff(seg.astype(np.int64)) == 0).to(DEV).reshape(cfg.B, cfg.H, cfg.S)
+    assert empty.any()
+    assert torch.equal(r["slot1"][empty], x["slot0"][empty])
+    assert torch.equal(r["mass1"][empty], x["mass0"][empty])
+
+
 def test_widest_address_space():
     # S = 16384, the largest flat address space: 16 blocks in the bucketing
     # scan and the largest LDS tables of the bucketing scatter
