@@ -653,36 +653,17 @@ __device__ void scan_fwd_long(const ScanFwdArgs& a, int64_t g) {
   }
 }
 
-// Segment i without events keeps its state: dst = src (or 0), lane l
-// holding channels [l * CPL, l * CPL + CPL).
-template <int CPL>
-__device__ __forceinline__ void keep_state(int64_t i, int d_v, const float* src_s,
-                                           const float* src_m, float* dst_s, float* dst_m) {
-  const int c0 = lane_id() * CPL;
-  if (dst_s && dst_s != src_s && c0 < d_v) {
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) dst_s[i * d_v + c0 + k] = src_s ? src_s[i * d_v + c0 + k] : 0.f;
-  }
-  if (dst_m && dst_m != src_m && lane_id() == 0) dst_m[i] = src_m ? src_m[i] : 0.f;
-}
-
 // The segment wave i of a short-segment kernel scans (-1: none) and its
 // event range.  When at most half of the segments are in the bucketing's
 // short list (hot slots take most events, most slots none), wave i takes
 // list entry i, so the waves with work are the grid's first and the rest
 // end at once; otherwise it takes segment i itself when that one is short,
 // which saves the list's extra dependent load where nearly every segment
-// has a few events.  pb / pe: the event range of segment i, loaded when
-// the caller keeps the state of empty segments (keep) or segment i is the
-// one to scan; a wave without work then ends after the list length alone.
+// has a few events; a wave without work then ends after reading the list
+// length alone.  Segments without events are left to fill_empty_kernel.
 template <typename Args>
-__device__ __forceinline__ int64_t short_segment(const Args& a, int64_t i, bool keep, int& pb,
-                                                 int& pe, int& beg, int& end) {
+__device__ __forceinline__ int64_t short_segment(const Args& a, int64_t i, int& beg, int& end) {
   const int64_t n = a.use_long ? *a.short_count : 0;
-  if (keep || 2 * n > a.nseg) {
-    pb = a.seg_offset[i];
-    pe = a.seg_offset[i + 1];
-  }
   if (2 * n <= a.nseg) {
     if (i >= n) return -1;
     const int64_t g = a.short_list[i];
@@ -690,24 +671,18 @@ __device__ __forceinline__ int64_t short_segment(const Args& a, int64_t i, bool 
     end = a.seg_offset[g + 1];
     return g;
   }
-  beg = pb;
-  end = pe;
-  return (pe > pb && pe - pb <= LONG_EVENTS) ? i : -1;
+  beg = a.seg_offset[i];
+  end = a.seg_offset[i + 1];
+  return (end > beg && end - beg <= LONG_EVENTS) ? i : -1;
 }
 
-// Segments of 1 to LONG_EVENTS events: one wave each (short_segment).  In
-// the forward wave i also keeps the state of segment i if that one has no
-// events; in the reverse it does so only when d_slot0 / d_mass0 are asked
-// for.
+// Segments of 1 to LONG_EVENTS events: one wave each (short_segment).
 template <typename IO, int CPL>
 __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_fwd_short_kernel(ScanFwdArgs a) {
-  // the grid's last waves past the segments load for the last one and end
-  const int64_t w = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
-  const int64_t i = w < a.nseg ? w : a.nseg - 1;
-  int pb = 0, pe = 0, beg, end;
-  const int64_t g = short_segment(a, i, true, pb, pe, beg, end);
-  if (w >= a.nseg) return;
-  if (pe == pb) keep_state<CPL>(i, a.d_v, a.slot0, a.mass0, a.slot1, a.mass1);
+  const int64_t i = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
+  if (i >= a.nseg) return;
+  int beg, end;
+  const int64_t g = short_segment(a, i, beg, end);
   if (g >= 0) scan_fwd_short<IO, CPL>(a, g, beg, end);
 }
 
@@ -716,6 +691,7 @@ __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_fwd_short_kernel(Scan
 template <typename IO, int CPL>
 __global__ __launch_bounds__(NWL * WAVE) void scan_fwd_long_kernel(ScanFwdArgs a) {
   const LongCounts L = long_counts(a.long_count);
+  if (L.total == 0) return;   // the queue stays at zero
   for (int i = take_ticket(a.queue); i < L.total; i = take_ticket(a.queue))
     scan_fwd_long<IO, CPL>(a, long_entry(a.long_list, L, a.long_cap, i));
   release_queue(a.queue);
@@ -1284,19 +1260,65 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
   }
 }
 
-// Same split as the forward (an empty segment passes d_slot1 / d_mass1 on
-// to d_slot0 / d_mass0).
+// Same split as the forward.
 template <typename IO, int CPL>
 __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_bwd_short_kernel(ScanBwdArgs a) {
-  // the grid's last waves past the segments load for the last one and end
-  const int64_t w = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
-  const int64_t i = w < a.nseg ? w : a.nseg - 1;
-  const bool keep = a.d_slot0 || a.d_mass0;
-  int pb = 0, pe = 1, beg, end;
-  const int64_t g = short_segment(a, i, keep, pb, pe, beg, end);
-  if (w >= a.nseg) return;
-  if (keep && pe == pb) keep_state<CPL>(i, a.d_v, a.d_slot1, a.d_mass1, a.d_slot0, a.d_mass0);
+  const int64_t i = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
+  if (i >= a.nseg) return;
+  int beg, end;
+  const int64_t g = short_segment(a, i, beg, end);
   if (g >= 0) scan_bwd_short<IO, CPL>(a, g, beg, end);
+}
+
+// Segments without events keep their state: dst = src bit for bit, or 0
+// where src is null (forward: slot1 / mass1 from slot0 / mass0; reverse:
+// d_slot0 / d_mass0 from d_slot1 / d_mass1).  One wave per 64 consecutive
+// segments: lane l checks segment g0 + l, then the wave writes the rows of
+// the empty ones item by item (16-byte vectors when VEC, else floats), four
+// items per lane at a time, every load before any store.
+struct FillArgs {
+  int64_t nseg;
+  int d_v;
+  const int32_t* seg_offset;
+  const float* src_s;     // (nseg, d_v) or null
+  const float* src_m;     // (nseg) or null
+  float* dst_s;           // (nseg, d_v) or null: nothing to write
+  float* dst_m;           // (nseg) or null
+};
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void fill_empty_kernel(FillArgs f) {
+  using T = typename std::conditional<VEC, float4, float>::type;
+  const int lane = lane_id();
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + wave_index()) * WAVE;
+  if (g0 >= f.nseg) return;
+  const int64_t g = g0 + lane;
+  const bool empty = g < f.nseg && f.seg_offset[g + 1] == f.seg_offset[g];
+  const uint64_t em = __ballot(empty);
+  if (em == 0) return;
+  if (empty && f.dst_m) f.dst_m[g] = f.src_m ? f.src_m[g] : 0.f;
+  if (!f.dst_s) return;
+  const uint32_t per = VEC ? f.d_v / 4 : f.d_v;   // items per row
+  const uint32_t items = WAVE * per;
+  const T* src = reinterpret_cast<const T*>(f.src_s);
+  T* dst = reinterpret_cast<T*>(f.dst_s);
+  for (uint32_t it0 = 0; it0 < items; it0 += 4 * WAVE) {
+    T x[4];
+    int64_t at[4];
+    bool ok[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t it = it0 + u * WAVE + lane;
+      const uint32_t r = it / per;
+      ok[u] = it < items && ((em >> r) & 1);
+      at[u] = (g0 + r) * per + (it - r * per);
+      if (src && ok[u]) x[u] = src[at[u]];
+      else x[u] = T{};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (ok[u]) dst[at[u]] = x[u];
+  }
 }
 
 // At most 128 registers, so that 4 workgroups fit on a CU (the rows of the
@@ -1304,6 +1326,7 @@ __global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_bwd_short_kernel(Scan
 template <typename IO, int CPL>
 __global__ __launch_bounds__(NWL * WAVE, 4) void scan_bwd_long_kernel(ScanBwdArgs a) {
   const LongCounts L = long_counts(a.long_count);
+  if (L.total == 0) return;   // the queue stays at zero
   for (int i = take_ticket(a.queue); i < L.total; i = take_ticket(a.queue))
     scan_bwd_long<IO, CPL>(a, long_entry(a.long_list, L, a.long_cap, i));
   release_queue(a.queue);
@@ -1358,10 +1381,10 @@ namespace {
 // Long-kernel workgroups per CU at most.  The long kernel pulls work until
 // its queue is empty, so the wave slots and registers it leaves free are the
 // ones the short-segment kernel beside it runs in.  Measured on the
-// 1.3B-layer shape: 3 for the forward (2, 4 and 6 are slower), 4 for the
+// 1.3B-layer shape: 4 for the forward (3, 5 and 6 are slower), 4 for the
 // reverse (its LDS allows no more; at 128 registers its 4 workgroups then
 // hold all of a CU's registers until their queue runs dry, and 3 is slower).
-constexpr int LONG_GROUPS_FWD = 3;
+constexpr int LONG_GROUPS_FWD = 4;
 constexpr int LONG_GROUPS_BWD = 4;
 
 // Workgroups of the long kernel that run at once: as many as fit, at most
@@ -1397,32 +1420,54 @@ hipError_t launch_pair(void (*shortk)(Args), void (*longk)(Args), int& resident,
   hipLaunchKernelGGL(shortk, dim3(sgrid), dim3(SHORT_WAVES * WAVE), 0, side, a);
   return hipGetLastError();
 }
+
+// The state of the segments without events, on `st` after the long kernel
+// (beside the short kernel it held that one up): nothing to do when dst is
+// null or the same arrays as src.
+hipError_t launch_fill(const FillArgs& f, hipStream_t st) {
+  if (!f.dst_s && !f.dst_m) return hipSuccess;
+  if (f.dst_s == f.src_s && f.dst_m == f.src_m) return hipSuccess;
+  const bool vec = f.d_v % 4 == 0 && (((uintptr_t)f.src_s | (uintptr_t)f.dst_s) & 15u) == 0;
+  const unsigned groups = (unsigned)((f.nseg + 4 * WAVE - 1) / (4 * WAVE));
+  if (vec) hipLaunchKernelGGL(fill_empty_kernel<true>, dim3(groups), dim3(256), 0, st, f);
+  else hipLaunchKernelGGL(fill_empty_kernel<false>, dim3(groups), dim3(256), 0, st, f);
+  return hipGetLastError();
+}
+
+template <typename Args>
+hipError_t launch_scan(void (*shortk)(Args), void (*longk)(Args), int& resident, int per_cu,
+                       const Args& a, const FillArgs& f, hipStream_t st, hipStream_t side) {
+  const hipError_t e = launch_pair(shortk, longk, resident, per_cu, a, st, side);
+  return e != hipSuccess ? e : launch_fill(f, st);
+}
 }  // namespace
 
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st, hipStream_t side) {
   if (a.nseg == 0) return hipSuccess;
   static int res[4] = {0, 0, 0, 0};
+  const FillArgs f{a.nseg, a.d_v, a.seg_offset, a.slot0, a.mass0, a.slot1, a.mass1};
   if (bf16) {
     if (a.d_v > 64)
-      return launch_pair(scan_fwd_short_kernel<bf16_t, 2>, scan_fwd_long_kernel<bf16_t, 2>, res[0], LONG_GROUPS_FWD, a, st, side);
-    return launch_pair(scan_fwd_short_kernel<bf16_t, 1>, scan_fwd_long_kernel<bf16_t, 1>, res[1], LONG_GROUPS_FWD, a, st, side);
+      return launch_scan(scan_fwd_short_kernel<bf16_t, 2>, scan_fwd_long_kernel<bf16_t, 2>, res[0], LONG_GROUPS_FWD, a, f, st, side);
+    return launch_scan(scan_fwd_short_kernel<bf16_t, 1>, scan_fwd_long_kernel<bf16_t, 1>, res[1], LONG_GROUPS_FWD, a, f, st, side);
   }
   if (a.d_v > 64)
-    return launch_pair(scan_fwd_short_kernel<float, 2>, scan_fwd_long_kernel<float, 2>, res[2], LONG_GROUPS_FWD, a, st, side);
-  return launch_pair(scan_fwd_short_kernel<float, 1>, scan_fwd_long_kernel<float, 1>, res[3], LONG_GROUPS_FWD, a, st, side);
+    return launch_scan(scan_fwd_short_kernel<float, 2>, scan_fwd_long_kernel<float, 2>, res[2], LONG_GROUPS_FWD, a, f, st, side);
+  return launch_scan(scan_fwd_short_kernel<float, 1>, scan_fwd_long_kernel<float, 1>, res[3], LONG_GROUPS_FWD, a, f, st, side);
 }
 
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st, hipStream_t side) {
   if (a.nseg == 0) return hipSuccess;
   static int res[4] = {0, 0, 0, 0};
+  const FillArgs f{a.nseg, a.d_v, a.seg_offset, a.d_slot1, a.d_mass1, a.d_slot0, a.d_mass0};
   if (bf16) {
     if (a.d_v > 64)
-      return launch_pair(scan_bwd_short_kernel<bf16_t, 2>, scan_bwd_long_kernel<bf16_t, 2>, res[0], LONG_GROUPS_BWD, a, st, side);
-    return launch_pair(scan_bwd_short_kernel<bf16_t, 1>, scan_bwd_long_kernel<bf16_t, 1>, res[1], LONG_GROUPS_BWD, a, st, side);
+      return launch_scan(scan_bwd_short_kernel<bf16_t, 2>, scan_bwd_long_kernel<bf16_t, 2>, res[0], LONG_GROUPS_BWD, a, f, st, side);
+    return launch_scan(scan_bwd_short_kernel<bf16_t, 1>, scan_bwd_long_kernel<bf16_t, 1>, res[1], LONG_GROUPS_BWD, a, f, st, side);
   }
   if (a.d_v > 64)
-    return launch_pair(scan_bwd_short_kernel<float, 2>, scan_bwd_long_kernel<float, 2>, res[2], LONG_GROUPS_BWD, a, st, side);
-  return launch_pair(scan_bwd_short_kernel<float, 1>, scan_bwd_long_kernel<float, 1>, res[3], LONG_GROUPS_BWD, a, st, side);
+    return launch_scan(scan_bwd_short_kernel<float, 2>, scan_bwd_long_kernel<float, 2>, res[2], LONG_GROUPS_BWD, a, f, st, side);
+  return launch_scan(scan_bwd_short_kernel<float, 1>, scan_bwd_long_kernel<float, 1>, res[3], LONG_GROUPS_BWD, a, f, st, side);
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st) {
