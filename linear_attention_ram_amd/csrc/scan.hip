@@ -824,7 +824,6 @@ __device__ __forceinline__ void bwd_replay(BwdChunk<IO, CPL, SO>& ck, float (&s)
                                            float (&pr)[CHUNK]) {
   using LN = Lanes<IO, CPL>;
   for_up<0, CHUNK>([&](auto I) {
-    pr[I] = 0.f;
     if ((ck.wm >> I) & 1u) {
       float xf[CPL];
       LN::get(ck.x[I], xf);
@@ -857,7 +856,6 @@ __device__ __forceinline__ void bwd_replay_map(BwdChunk<IO, CPL, SO>& ck, float 
 #pragma unroll
   for (int k = 0; k < CPL; ++k) q[k] = 0.f;
   for_up<0, CHUNK>([&](auto I) {
-    pr[I] = 0.f;
     if ((ck.wm >> I) & 1u) {
       float xf[CPL];
       LN::get(ck.x[I], xf);
