@@ -730,9 +730,28 @@ struct BwdChunk {
   float rden;                      // 1 / (m' + eps): mass after the event plus eps
   float gq;                        // w / (m' + eps)^2 of a write, else 0
   typename Lanes<IO, CPL>::Raw x[CHUNK];
+  // rows in float, unpacked once for both passes where registers allow
+  // (the LDS variant: its workgroups are held to four per CU by LDS)
+  static constexpr bool UNPACKED = SO_LDS && sizeof(IO) == 2;
+  float xf[UNPACKED ? CHUNK : 1][CPL];
   float so_reg[SO_LDS ? 1 : CHUNK][CPL];
   float* so_lds;                   // [CHUNK][MAX_DV] floats at the lane's channel c0
 
+  __device__ __forceinline__ void unpack_rows() {
+    if constexpr (UNPACKED) {
+#pragma unroll
+      for (int i = 0; i < CHUNK; ++i) Lanes<IO, CPL>::get(x[i], xf[i]);
+    }
+  }
+  template <int I>
+  __device__ __forceinline__ void get_x(float (&f)[CPL]) const {
+    if constexpr (UNPACKED) {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) f[k] = xf[I][k];
+    } else {
+      Lanes<IO, CPL>::get(x[I], f);
+    }
+  }
   template <int I>
   __device__ __forceinline__ void put_so(const float (&s)[CPL]) {
     if constexpr (SO_LDS) {
@@ -826,14 +845,14 @@ __device__ __forceinline__ void bwd_replay(BwdChunk<IO, CPL, SO>& ck, float (&s)
   for_up<0, CHUNK>([&](auto I) {
     if ((ck.wm >> I) & 1u) {
       float xf[CPL];
-      LN::get(ck.x[I], xf);
+      ck.template get_x<I>(xf);
       const float e = bc<I>(ck.M.eta), om = bc<I>(ck.M.keep);
       ck.template put_so<I>(s);
 #pragma unroll
       for (int k = 0; k < CPL; ++k) s[k] = fmaf(om, s[k], e * xf[k]);
     } else if ((ck.rm >> I) & 1u) {
       float xf[CPL];
-      LN::get(ck.x[I], xf);
+      ck.template get_x<I>(xf);
       float d = 0.f;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) d = fmaf(xf[k], s[k], d);
@@ -858,14 +877,14 @@ __device__ __forceinline__ void bwd_replay_map(BwdChunk<IO, CPL, SO>& ck, float 
   for_up<0, CHUNK>([&](auto I) {
     if ((ck.wm >> I) & 1u) {
       float xf[CPL];
-      LN::get(ck.x[I], xf);
+      ck.template get_x<I>(xf);
       const float e = bc<I>(ck.M.eta), om = bc<I>(ck.M.keep);
       ck.template put_so<I>(s);
 #pragma unroll
       for (int k = 0; k < CPL; ++k) s[k] = fmaf(om, s[k], e * xf[k]);
     } else if ((ck.rm >> I) & 1u) {
       float xf[CPL];
-      LN::get(ck.x[I], xf);
+      ck.template get_x<I>(xf);
       const float ci = bc<I>(cq);
       float d = 0.f;
 #pragma unroll
@@ -905,7 +924,7 @@ __device__ __forceinline__ void bwd_walk(BwdChunk<IO, CPL, SO>& ck, const SegCtx
     pw[I] = 0.f;
     if ((ck.wm >> I) & 1u) {
       float xf[CPL], ctr[CPL];
-      LN::get(ck.x[I], xf);
+      ck.template get_x<I>(xf);
       const float e = bc<I>(ck.M.eta);
       float d = 0.f;
 #pragma unroll
@@ -919,7 +938,7 @@ __device__ __forceinline__ void bwd_walk(BwdChunk<IO, CPL, SO>& ck, const SegCtx
       pw[I] = d;
     } else if ((ck.rm >> I) & 1u) {
       float xf[CPL];
-      LN::get(ck.x[I], xf);
+      ck.template get_x<I>(xf);
       const float r = bc<I>(ck.rr);
 #pragma unroll
       for (int k = 0; k < CPL; ++k) sh[k] = fmaf(r, xf[k], sh[k]);
@@ -1182,6 +1201,7 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
     // event loops' stores never wait
     wait_vmem();
     for_up<0, CHUNK>([&](auto I) { ck.x[I] = xn[I]; });
+    ck.unpack_rows();
     float s[CPL], m;
     chunk_state_take(c, st, s, m);
     flush_dv(ck, rs, sw_prev, c.lb);
