@@ -998,7 +998,14 @@ __device__ __forceinline__ float bwd_mass_grads(const ScanBwdArgs& a, const BwdC
   const float before = fmaf(ma.A, mh, ma.B);
   const float after = dpp_or<DPP_SHL1>(mh, before);   // lane 15: the chunk's m_hat
   const float M = after - ck.gq * ma.deta;
-  gr.dw = ((ev.wt > 0.f) ? ma.deta * ck.rden : 0.f) + M + M * ck.M.mo * ev.dl;
+  // dw = deta * d eta/dw + M * dm'/dw with dm'/dw = 1 + m * dlambda/dw.  The
+  // part of deta * d eta/dw that goes through m' is taken together with the
+  // direct one: 1/(m'+eps) - w/(m'+eps)^2 = (lambda m + eps)/(m'+eps)^2,
+  // which keeps the small eps of a first write to an empty slot exact where
+  // the difference of the two terms (both about 1/w) would lose it.
+  const float dm = fmaf(ck.M.mo, ev.dl, 1.f);
+  const float deta_dw = (ev.wt > 0.f) ? fmaf(ev.lam, ck.M.mo, a.eps) * ck.rden * ck.rden : 0.f;
+  gr.dw = ma.deta * (deta_dw - ck.gq * ck.M.mo * ev.dl) + after * dm;
   gr.dg = M * ck.M.mo * (-ev.lam * (1.f - ev.lam));
   gr.dr = red;
   const bool mine = lane_id() < CHUNK;

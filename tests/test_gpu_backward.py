@@ -90,6 +90,10 @@ EDGE = [
     (2, 2, 600, 8, 8, 8, 16, "f32", (False, False), 1e-6),  # long segments: many chunks
     (1, 2, 2000, 16, 4, 4, 16, "f32", (False, False), 1e-6),  # ~1000-event segments
     (1, 1, 3000, 8, 3, 2, 128, "f32", (True, True), 1e-6),    # long segments, wide slots
+    # most slots without events, rows not of whole 16-byte vectors (the
+    # second case passes d_slot1 / d_mass1 on through the empty slots)
+    (1, 2, 5, 256, 2, 2, 66, "f32", (False, False), 1e-6),
+    (1, 2, 5, 256, 2, 2, 7, "bf16", (False, False), 1e-6),
 ]
 
 

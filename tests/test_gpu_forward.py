@@ -143,6 +143,10 @@ EDGE = [
     (2, 2, 600, 8, 8, 8, 16, "bf16", (True, True), 0.0),   # 8 slots, every token writes all
     (1, 2, 2000, 16, 4, 4, 16, "f32", (False, False), 1e-6),  # ~1000-event segments
     (1, 1, 3000, 8, 3, 2, 128, "f32", (False, False), 1e-6),  # long segments, wide slots
+    # most slots without events (the short list), rows not of whole 16-byte
+    # vectors: the empty slots' state element by element, zero then copied
+    (1, 2, 5, 256, 2, 2, 66, "f32", (False, False), 1e-6),
+    (1, 2, 5, 256, 2, 2, 7, "bf16", (False, False), 1e-6),
 ]
 
 
