@@ -1006,7 +1006,11 @@ __device__ __forceinline__ float bwd_mass_grads(const ScanBwdArgs& a, const BwdC
   const float dm = fmaf(ck.M.mo, ev.dl, 1.f);
   const float deta_dw = (ev.wt > 0.f) ? fmaf(ev.lam, ck.M.mo, a.eps) * ck.rden * ck.rden : 0.f;
   gr.dw = ma.deta * (deta_dw - ck.gq * ck.M.mo * ev.dl) + after * dm;
-  gr.dg = M * ck.M.mo * (-ev.lam * (1.f - ev.lam));
+  // d lambda / d gamma = -lambda (1 - lambda) = (d lambda / d w) w (1 - w):
+  // the first form where lambda < 1/2, the second (1 - w close to 1) where
+  // 1 - lambda would be the difference of two numbers close to 1
+  const float lam1 = (ev.lam < 0.5f) ? -ev.lam * (1.f - ev.lam) : ev.dl * ev.wt * (1.f - ev.wt);
+  gr.dg = M * ck.M.mo * lam1;
   gr.dr = red;
   const bool mine = lane_id() < CHUNK;
   gr.ow = (mine && wr) ? ((uint32_t)ev.rb * a.k_w + ev.j) * 4u : OOB;
