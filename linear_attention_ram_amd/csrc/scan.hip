@@ -1012,6 +1012,12 @@ __device__ __forceinline__ float bwd_mass_grads(const ScanBwdArgs& a, const BwdC
   const float lam1 = (ev.lam < 0.5f) ? -ev.lam * (1.f - ev.lam) : ev.dl * ev.wt * (1.f - ev.wt);
   gr.dg = M * ck.M.mo * lam1;
   gr.dr = red;
+  if (!ev.live) {
+    // a masked token's no-op event stands for no event at all: no gradients
+    gr.dw = 0.f;
+    gr.dg = 0.f;
+    gr.dr = 0.f;
+  }
   const bool mine = lane_id() < CHUNK;
   gr.ow = (mine && wr) ? ((uint32_t)ev.rb * a.k_w + ev.j) * 4u : OOB;
   gr.orr = (mine && !wr && ev.valid) ? ((uint32_t)ev.rb * a.k_r + ev.j) * 4u : OOB;
