@@ -19,6 +19,7 @@
 //           candidate's rank is counted exactly.  Rows with more than
 //           CAND_CAP candidates (massive ties) take an exact K-pass fallback.
 #include <type_traits>
+#include <utility>
 
 #include "decode.hpp"
 #include "decode_prod.hpp"
@@ -393,7 +394,9 @@ __global__ __launch_bounds__(256) void decode_bwd_u2_kernel(DecodeBwdArgs a) {
 //   ordered key, then its index complemented in 16 bits, then its list
 //   position, so that the larger word is the earlier slot in (key
 //   descending, index ascending) and names its log-probability in the list;
-//   K rounds of a row maximum over the listed words give the K best in order.
+//   the K best in order: where every row of the wave lists at most 32 slots,
+//   by each word's rank (the number of larger words of its row, the words
+//   being distinct); otherwise by K rounds of a row maximum over the words.
 // Rows whose list would overflow or hold fewer than K slots (NaN logits, a
 // bound that is no number) are marked and redone by the whole-wave path in a
 // second kernel, whose registers then do not limit this one's occupancy.
@@ -432,6 +435,33 @@ __device__ __forceinline__ uint64_t row16_max64(uint64_t x) {
   x = max64_step<DPP_HALF_MIRROR>(x);
   return max64_step<DPP_MIRROR>(x);
 }
+// A 64-bit word of the lane S places further along the DPP row (rotating).
+template <int S>
+__device__ __forceinline__ uint64_t row_ror64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, 0x120 + S, 0xF, 0xF, true);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), 0x120 + S, 0xF, 0xF, true);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Ranks of two words per lane among the 32 words of the lane's DPP row: the
+// number of words of the row larger than each (distinct words get distinct
+// ranks; a zero word is larger than none).
+template <int... S>
+__device__ __forceinline__ void row32_ranks(uint64_t w0, uint64_t w1, int& n0, int& n1,
+                                            std::integer_sequence<int, S...>) {
+  n0 = (w1 > w0) ? 1 : 0;
+  n1 = (w0 > w1) ? 1 : 0;
+  auto step = [&](auto R) {
+    constexpr int s = decltype(R)::value + 1;
+    const uint64_t o0 = row_ror64<s>(w0), o1 = row_ror64<s>(w1);
+    n0 += ((o0 > w0) ? 1 : 0) + ((o1 > w0) ? 1 : 0);
+    n1 += ((o0 > w1) ? 1 : 0) + ((o1 > w1) ? 1 : 0);
+    // one rotation at a time (the counts are taken after each, so the
+    // compiler keeps no more than one rotation's words live)
+    asm volatile("" : "+v"(n0), "+v"(n1));
+  };
+  (step(std::integral_constant<int, S>{}), ...);
+}
 
 template <typename IO>
 __global__ __launch_bounds__(256) void decode_fwd_u2x_kernel(DecodeFwdArgs a) {
@@ -441,6 +471,7 @@ __global__ __launch_bounds__(256) void decode_fwd_u2x_kernel(DecodeFwdArgs a) {
     float c_lp[4][U2X_CAP];        // log-probability of the slot
     float q_v[4][U2X_QCAP];        // qualifying digit-1 values
     int q_b[4][U2X_QCAP];          //            and their indices
+    uint32_t top[4][U2X_K];        // low halves of the K best words, in order
   };
   __shared__ Lists lds[4];
   const int wv = threadIdx.x >> 6;
@@ -567,30 +598,45 @@ __global__ __launch_bounds__(256) void decode_fwd_u2x_kernel(DecodeFwdArgs a) {
   }
   const bool failed = live && (q_over || count > U2X_CAP || count < k);
   wave_sync();
-  // K rounds of the row maximum over the listed words (lane p holds the
-  // listed slots p, p + 16, ...; a taken or missing slot is 0)
-  constexpr int PER_LANE = U2X_CAP / 16;
-  static_assert(U2X_CAP % 16 == 0, "lanes hold whole shares of the list");
-  uint64_t wd[PER_LANE];
-#pragma unroll
-  for (int j = 0; j < PER_LANE; ++j) {
-    const int c = p + 16 * j;
-    wd[j] = (live && !failed && c < count) ? L.c_word[r][c] : 0ull;
-  }
-  const int k_max = __builtin_amdgcn_readfirstlane((int)wave_max((float)(live ? k : 0)));
-  uint64_t best = wd[0];
-#pragma unroll
-  for (int j = 1; j < PER_LANE; ++j) best = wd[j] > best ? wd[j] : best;
   uint32_t my_word = 0;   // lane p: low half of the p-th best word
-  for (int rnd = 0; rnd < k_max; ++rnd) {
-    const uint64_t win = row16_max64(best);
-    if (p == rnd) my_word = (uint32_t)win;
-    if (win != 0ull && best == win) {   // this lane held it: take it out
+  const int listed = (live && !failed) ? count : 0;
+  const int n_max = __builtin_amdgcn_readfirstlane((int)wave_max((float)listed));
+  if (n_max <= 32) {
+    // lane p holds listed words p and p + 16 (a missing one is 0); the word
+    // of rank n < K goes to entry n of the row's top list
+    const uint64_t w0 = (p < listed) ? L.c_word[r][p] : 0ull;
+    const uint64_t w1 = (p + 16 < listed) ? L.c_word[r][p + 16] : 0ull;
+    int n0, n1;
+    row32_ranks(w0, w1, n0, n1, std::make_integer_sequence<int, 15>{});
+    if (w0 != 0ull && n0 < k) L.top[r][n0] = (uint32_t)w0;
+    if (w1 != 0ull && n1 < k) L.top[r][n1] = (uint32_t)w1;
+    wave_sync();
+    if (listed > 0 && p < k) my_word = L.top[r][p];
+  } else {
+    // K rounds of the row maximum over the listed words (lane p holds the
+    // listed slots p, p + 16, ...; a taken or missing slot is 0)
+    constexpr int PER_LANE = U2X_CAP / 16;
+    static_assert(U2X_CAP % 16 == 0, "lanes hold whole shares of the list");
+    uint64_t wd[PER_LANE];
 #pragma unroll
-      for (int j = 0; j < PER_LANE; ++j) wd[j] = (wd[j] == win) ? 0ull : wd[j];
-      best = wd[0];
+    for (int j = 0; j < PER_LANE; ++j) {
+      const int c = p + 16 * j;
+      wd[j] = (c < listed) ? L.c_word[r][c] : 0ull;
+    }
+    const int k_max = __builtin_amdgcn_readfirstlane((int)wave_max((float)(live ? k : 0)));
+    uint64_t best = wd[0];
 #pragma unroll
-      for (int j = 1; j < PER_LANE; ++j) best = wd[j] > best ? wd[j] : best;
+    for (int j = 1; j < PER_LANE; ++j) best = wd[j] > best ? wd[j] : best;
+    for (int rnd = 0; rnd < k_max; ++rnd) {
+      const uint64_t win = row16_max64(best);
+      if (p == rnd) my_word = (uint32_t)win;
+      if (win != 0ull && best == win) {   // this lane held it: take it out
+#pragma unroll
+        for (int j = 0; j < PER_LANE; ++j) wd[j] = (wd[j] == win) ? 0ull : wd[j];
+        best = wd[0];
+#pragma unroll
+        for (int j = 1; j < PER_LANE; ++j) best = wd[j] > best ? wd[j] : best;
+      }
     }
   }
   if (live && !failed) {

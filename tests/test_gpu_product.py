@@ -88,6 +88,29 @@ def test_rounding_limited_keys():
     check_decode(p, 0, lg.contiguous(), w_tol)
 
 
+def test_two_digit_rows_by_listed_count():
+    # U = 2 rows whose top c digit-0 values and top 8 digit-1 values are all
+    # 1 and the rest near -3: exactly 8c slots tie at the best key 2, ranked
+    # by index.  Rows of four (one wave) list 32 slots (ranked by count), 40
+    # or 64 (ranked by rounds of the row maximum), or mix those; c = 9 lists
+    # 72, more than a row holds, and is redone by the whole-wave kernel.
+    B, T, H, U, P, k = 1, 48, 2, 2, 64, 8
+    pattern = [4, 4, 4, 4, 4, 5, 2, 1, 8, 8, 8, 8, 9, 1, 4, 3]
+    g = torch.Generator(device="cpu").manual_seed(11)
+    lg = -3.0 + 0.1 * torch.randn((B, T, H, U, P), generator=g)
+    for i in range(T * H):
+        t, h = divmod(i, H)
+        c = pattern[i % len(pattern)]
+        d0 = torch.randperm(P, generator=g)[:c]
+        d1 = torch.randperm(P, generator=g)[:8]
+        lg[0, t, h, 0, d0] = 1.0
+        lg[0, t, h, 1, d1] = 1.0
+    lg = lg.to(torch.bfloat16).to(DEV)
+    p = ram.problem(B, H, T, None, k, k, 16, io="bf16", U=U, P=P)
+    for side in (0, 1):
+        check_decode(p, side, lg)
+
+
 @pytest.mark.parametrize("U,P", [(2, 64), (5, 4), (2, 128)])
 def test_all_equal_rows_take_the_exhaustive_fallback(U, P):
     # every slot ties: more kept prefixes than the list holds
