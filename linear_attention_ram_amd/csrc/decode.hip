@@ -285,6 +285,16 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += dpp<DPP_HALF_MIRROR>(x);
   return x + dpp<DPP_MIRROR>(x);
 }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t row16_sum_u(uint32_t x) {
+  x += dpp_u<DPP_XOR1>(x);
+  x += dpp_u<DPP_XOR2>(x);
+  x += dpp_u<DPP_HALF_MIRROR>(x);
+  return x + dpp_u<DPP_MIRROR>(x);
+}
 template <typename IO> struct Vec4;
 template <> struct Vec4<bf16_t> {
   static __device__ __forceinline__ void load(const bf16_t* p, float (&x)[4]) {
@@ -389,8 +399,10 @@ __global__ __launch_bounds__(256) void decode_bwd_u2_kernel(DecodeBwdArgs a) {
 //   largest logit of digit u (the largest 16-bit prefix of the ordered bits
 //   that K of its values reach; for bf16 logits that value itself), so K
 //   distinct slots reach tau and tau is at most the K-th best key;
-//   every slot with key fl(l0[a] + l1[b]) >= tau is listed (only digit-1
-//   values with fl(M0 + l1[b]) >= tau can give one) as a 64-bit word: its
+//   every slot with key fl(l0[a] + l1[b]) >= tau is listed (only a digit-0
+//   value with fl(l0[a] + M1) >= tau and a digit-1 value with
+//   fl(M0 + l1[b]) >= tau can give one, so those pairs are tried) as a
+//   64-bit word: its
 //   ordered key, then its index complemented in 16 bits, then its list
 //   position, so that the larger word is the earlier slot in (key
 //   descending, index ascending) and names its log-probability in the list;
@@ -401,7 +413,7 @@ __global__ __launch_bounds__(256) void decode_bwd_u2_kernel(DecodeBwdArgs a) {
 // bound that is no number) are marked and redone by the whole-wave path in a
 // second kernel, whose registers then do not limit this one's occupancy.
 constexpr int U2X_CAP = 64;    // listed slots per row
-constexpr int U2X_QCAP = 32;   // listed digit-1 values per row
+constexpr int U2X_QCAP = 24;   // listed values of each digit per row (at most 32)
 constexpr int U2X_K = 16;
 __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, dpp<DPP_XOR1>(x));
@@ -469,8 +481,10 @@ __global__ __launch_bounds__(256) void decode_fwd_u2x_kernel(DecodeFwdArgs a) {
   struct Lists {
     uint64_t c_word[4][U2X_CAP];   // [row][slot]: ordered key, complemented index, position
     float c_lp[4][U2X_CAP];        // log-probability of the slot
-    float q_v[4][U2X_QCAP];        // qualifying digit-1 values
-    int q_b[4][U2X_QCAP];          //            and their indices
+    float a_v[4][U2X_QCAP];        // A: qualifying digit-0 values
+    int a_i[4][U2X_QCAP];          //    and their indices
+    float b_v[4][U2X_QCAP];        // B: qualifying digit-1 values
+    int b_i[4][U2X_QCAP];          //    and their indices
     uint32_t top[4][U2X_K];        // low halves of the K best words, in order
   };
   __shared__ Lists lds[4];
@@ -525,75 +539,79 @@ __global__ __launch_bounds__(256) void decode_fwd_u2x_kernel(DecodeFwdArgs a) {
 #pragma unroll
   for (int b = 15; b >= 0; --b) {
     const uint32_t c0 = t0 | (1u << b), c1 = t1 | (1u << b);
-    float n = 0.f;
+    uint32_t n0 = 0, n1 = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) n += ((ob0[e] >= c0) ? 1.f : 0.f) + ((ob1[e] >= c1) ? 128.f : 0.f);
-    const float tot = row16_sum(n);          // count0 + 128 count1, both <= 64
-    const float n1 = floorf(tot * (1.f / 128.f));
-    t0 = (tot - 128.f * n1 >= (float)k) ? c0 : t0;
-    t1 = (n1 >= (float)k) ? c1 : t1;
+    for (int e = 0; e < 4; ++e) {
+      n0 += (ob0[e] >= c0) ? 1u : 0u;
+      n1 += (ob1[e] >= c1) ? 1u : 0u;
+    }
+    const uint32_t tot = row16_sum_u(n0 | (n1 << 8));   // count0 + 256 count1, both <= 64
+    t0 = ((tot & 0xFFu) >= (uint32_t)k) ? c0 : t0;
+    t1 = ((tot >> 8) >= (uint32_t)k) ? c1 : t1;
   }
   // K distinct slots (argmax l0, b) reach fl(M0 + v1) and K distinct slots
   // (a, argmax l1) reach fl(v0 + M1): either is at most the K-th best key
   // (fmaxf keeps the number when one bound is NaN)
   const float tau = fmaxf(M0 + from_ordered(t1 << 16), from_ordered(t0 << 16) + M1);
-  // the row's digit-1 values that can reach tau, listed in LDS
-  int nq;
-  {
-    bool qf[4];
+  // A: the row's digit-0 values that reach tau together with the largest
+  // digit-1 value; B: its digit-1 values that reach tau together with the
+  // largest digit-0 value.  Float addition is monotone, so every slot whose
+  // key reaches tau pairs an entry of A with one of B.  Both are listed in LDS.
+  auto list_reaching = [&](const float (&x)[4], float best_other, float* vals, int* ids) {
+    bool f[4];
     int n = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      qf[e] = own && M0 + x1[e] >= tau;
-      n += qf[e] ? 1 : 0;
+      f[e] = own && x[e] + best_other >= tau;
+      n += f[e] ? 1 : 0;
     }
     const int incl = row16_incl(n);
     int pos = incl - n;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (qf[e]) {
+      if (f[e]) {
         if (pos < U2X_QCAP) {
-          L.q_v[r][pos] = x1[e];
-          L.q_b[r][pos] = 4 * p + e;
+          vals[pos] = x[e];
+          ids[pos] = 4 * p + e;
         }
         ++pos;
       }
     }
-    nq = row16_last(incl);
-  }
-  const bool q_over = nq > U2X_QCAP;   // such a row takes the whole-wave path
-  if (q_over) nq = 0;
+    return row16_last(incl);
+  };
+  int na = list_reaching(x0, M1, L.a_v[r], L.a_i[r]);
+  int nb = list_reaching(x1, M0, L.b_v[r], L.b_i[r]);
+  const bool q_over = na > U2X_QCAP || nb > U2X_QCAP;   // such a row takes the whole-wave path
+  if (q_over) na = nb = 0;
   wave_sync();
-  // every slot reaching tau: each listed digit-1 value against the lane's
-  // four digit-0 values
-  const int nq_max = __builtin_amdgcn_readfirstlane((int)wave_max((float)nq));
+  // every slot reaching tau: lane p holds entries p and p + 16 of B and
+  // meets the entries of A one after another
+  const bool has0 = p < nb, has1 = p + 16 < nb;
+  const float bv0 = has0 ? L.b_v[r][p] : 0.f, bv1 = has1 ? L.b_v[r][p + 16] : 0.f;
+  const int bi0 = has0 ? L.b_i[r][p] : 0, bi1 = has1 ? L.b_i[r][p + 16] : 0;
+  const int na_max = __builtin_amdgcn_readfirstlane((int)wave_max((float)na));
   int count = 0;
-  for (int i = 0; i < nq_max; ++i) {
-    const bool ok = i < nq;
-    const float l1b = ok ? L.q_v[r][i] : -INFINITY;
-    const int b = ok ? L.q_b[r][i] : 0;
-    bool cf[4];
-    int nc = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      cf[e] = ok && own && x0[e] + l1b >= tau;
-      nc += cf[e] ? 1 : 0;
-    }
+  auto put = [&](float av, int ai, float bv, int bi, int pos) {
+    const float key = av + bv;
+    const uint32_t id = (uint32_t)(ai * P + bi);   // < 2^12
+    L.c_word[r][pos] = ((uint64_t)sel_key(key) << 32) | ((uint32_t)(0xFFFFu - id) << 16) |
+                       (uint32_t)pos;
+    L.c_lp[r][pos] = (av - lse0) + (bv - lse1);
+  };
+  for (int i = 0; i < na_max; ++i) {
+    const bool ok = i < na;
+    const float av = ok ? L.a_v[r][i] : 0.f;
+    const int ai = ok ? L.a_i[r][i] : 0;
+    const bool f0 = ok && has0 && av + bv0 >= tau;
+    const bool f1 = ok && has1 && av + bv1 >= tau;
+    const int nc = (f0 ? 1 : 0) + (f1 ? 1 : 0);
     const int incl = row16_incl(nc);
     int pos = count + incl - nc;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (cf[e]) {
-        if (pos < U2X_CAP) {
-          const float key = x0[e] + l1b;
-          const uint32_t id = (uint32_t)((4 * p + e) * P + b);   // < 2^12
-          L.c_word[r][pos] = ((uint64_t)sel_key(key) << 32) |
-                             ((uint32_t)(0xFFFFu - id) << 16) | (uint32_t)pos;
-          L.c_lp[r][pos] = (x0[e] - lse0) + (l1b - lse1);
-        }
-        ++pos;
-      }
+    if (f0) {
+      if (pos < U2X_CAP) put(av, ai, bv0, bi0, pos);
+      ++pos;
     }
+    if (f1 && pos < U2X_CAP) put(av, ai, bv1, bi1, pos);
     count += row16_last(incl);
   }
   const bool failed = live && (q_over || count > U2X_CAP || count < k);
