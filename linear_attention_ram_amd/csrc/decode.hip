@@ -189,6 +189,90 @@ __global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
   }
 }
 
+// Rows of one or two 1 KiB vector rows (S * io = 1 or 2 KiB): RPW
+// consecutive rows per wave, so that a wave keeps 4 KiB of loads in flight as
+// the larger rows' waves do (a wave of one 2 KiB row is bound by latency).
+// Each row is computed as in decode_bwd_kernel: its scalars from lanes j < k,
+// then its vectors, the selected entries put in before the stores.
+template <typename IO, int RPW>
+__global__ __launch_bounds__(256) void decode_bwd_small_kernel(DecodeBwdArgs a) {
+  constexpr int E = vec16<IO>::E;
+  constexpr int VPL = 4 / RPW;   // 16-byte vectors per lane and row: nvec = VPL * WAVE
+  const int lane = lane_id();
+  const int wv = threadIdx.x >> 6;
+  const int64_t total = (int64_t)a.nsides * a.N;
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + wv) * RPW;
+  if (g0 >= total) return;
+  const IO* src[RPW];
+  IO* dst[RPW];
+  bool live[RPW], zero[RPW];
+  int k[RPW], aj[RPW], renorm[RPW];
+  float gj[RPW], wj[RPW], lj[RPW], nl[RPW];
+  // every row's scalars are requested before any is used
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const int64_t grow = g0 + q;
+    live[q] = grow < total;
+    const int side = (live[q] && grow >= a.N) ? 1 : 0;   // nsides <= 2
+    const int64_t row = live[q] ? grow - (int64_t)side * a.N : 0;
+    k[q] = a.k[side];
+    renorm[q] = a.renorm[side];
+    src[q] = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
+    dst[q] = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)a.S;
+    zero[q] = !live[q] || (a.mask && !a.mask[token_of(row, a.H)]);
+    gj[q] = wj[q] = lj[q] = 0.f;
+    aj[q] = 0;
+    nl[q] = zero[q] ? 0.f : -a.lse[side][row] * LOG2E;
+    if (!zero[q] && lane < k[q]) {
+      gj[q] = a.g[side][row * k[q] + lane];
+      wj[q] = a.w[side][row * k[q] + lane];
+      int j = a.idx[side][row * k[q] + lane];
+      // the logit behind a CAPE slot is the content index (slot - shift)
+      const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
+      if (shift >= 0) j = (j - shift + a.S) % a.S;
+      aj[q] = j;
+      lj[q] = to_f32(src[q][j]);
+    }
+  }
+  uint4 v[RPW][VPL];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q)
+#pragma unroll
+    for (int u = 0; u < VPL; ++u)
+      v[q][u] = zero[q] ? make_uint4(0, 0, 0, 0) : ld_nt16(src[q] + (int64_t)(u * WAVE + lane) * E);
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    if (zero[q]) continue;   // wave-uniform: a masked token's row stays zero
+    const float gw = decode_gw(gj[q], wj[q], renorm[q]);
+    const float ntot = -wave_sum(gw);
+    const float fix = gw + ntot * fast_exp2(fmaf(lj[q], LOG2E, nl[q]));
+    const int fix_row = (lane < k[q]) ? aj[q] / (E * WAVE) : -1;   // vector row holding a_j
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      float x[E];
+      unpack16(v[q][u], x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = ntot * fast_exp2(fmaf(x[e], LOG2E, nl[q]));
+      uint64_t fixes = __ballot(fix_row == u);
+      while (fixes) {
+        const int j = (int)__builtin_ctzll(fixes);
+        fixes &= fixes - 1;
+        const int id = readlane_i(aj[q], j);
+        const float val = readlane_f(fix, j);
+        const bool mine = lane == (id / E) % WAVE;
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = (mine && id % E == e) ? val : x[e];
+      }
+      v[q][u] = pack16(x);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < RPW; ++q)
+#pragma unroll
+    for (int u = 0; u < VPL; ++u)
+      if (live[q]) st_nt16(dst[q] + (int64_t)(u * WAVE + lane) * E, v[q][u]);
+}
+
 // Product rows (U >= 2 digits, see decode_prod.hpp): one wave per row, rows
 // of side 0 first.  lse holds the U per-digit logsumexps of each row.
 template <typename IO>
@@ -862,7 +946,16 @@ hipError_t launch_decode_bwd(const DecodeBwdArgs& a, bool bf16, hipStream_t st) 
   // 1.3B-layer shape (S = 4096 bf16), 2.978 -> 2.913 ms (5.77 -> 5.90 TB/s);
   // 4 waves of 2 KiB take 3.55 ms.  A copy in the same layout shows the same
   // (4 KiB per wave 5.94 TB/s, 8 KiB per wave 5.15 TB/s).
-  if (bf16 && a.S == 4096) {
+  // Rows of 1 or 2 KiB take 4 or 2 rows per wave (4 KiB in flight).
+  const int nvec = a.S / (bf16 ? vec16<bf16_t>::E : vec16<float>::E);
+  if (nvec == WAVE || nvec == 2 * WAVE) {
+    const int rpw = nvec == WAVE ? 4 : 2;
+    const dim3 gs((unsigned)((rows + 4 * rpw - 1) / (4 * rpw)));
+    if (bf16 && rpw == 4) hipLaunchKernelGGL((decode_bwd_small_kernel<bf16_t, 4>), gs, block, 0, st, a);
+    else if (bf16) hipLaunchKernelGGL((decode_bwd_small_kernel<bf16_t, 2>), gs, block, 0, st, a);
+    else if (rpw == 4) hipLaunchKernelGGL((decode_bwd_small_kernel<float, 4>), gs, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_bwd_small_kernel<float, 2>), gs, block, 0, st, a);
+  } else if (bf16 && a.S == 4096) {
     const dim3 g2((unsigned)((rows + 1) / 2));
     hipLaunchKernelGGL((decode_bwd_kernel<bf16_t, 2>), g2, block, 0, st, a);
   } else if (bf16) {
