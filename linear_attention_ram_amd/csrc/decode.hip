@@ -104,173 +104,65 @@ __device__ __forceinline__ float decode_gw(float gj, float wj, int renorm) {
 // Decode backward: with g_j the gradient of the j-th output weight,
 // gw_j = g_j w_j (renormalised: gw_j = (g_j - sum_i g_i w_i) w_j),
 // dl_i = [i = a_j] gw_j - p_i sum_j gw_j, p = softmax(l) = exp(l - lse).
-// RW waves share a row: each takes a contiguous share of its 1 KiB vector
-// rows (64 lanes x 16 bytes) and streams it in tiles of TILE 16-byte vectors
-// per lane (all loads of a tile in flight before the first store).  Every
-// wave of the row gathers the k selected logits (lane j < k) and forms the
-// full value of entry a_j; the lane that owns that entry's vector puts it
-// into the vector before the vector is stored (scattered 2-byte stores
-// after the stream cost more than the stream's own writes would suggest).
-template <typename IO, int RW>
-__global__ __launch_bounds__(256) void decode_bwd_kernel(DecodeBwdArgs a) {
+// One wave per 1 KiB vector row (64 lanes x 16 bytes) of a logits row, and
+// one wave per workgroup: the row's scalars (lse and lanes j < k: g_j, w_j,
+// a_j) are requested together with the wave's one vector, so every load of
+// the wave is in flight at once.  A selected entry a_j inside the wave's
+// vector row takes gw_j added to its streamed value -p_i sum_j gw_j (the
+// same sum, in the same order, as gw_j + (-sum) p_{a_j}).
+template <typename IO>
+__global__ __launch_bounds__(WAVE) void decode_bwd_vec_kernel(DecodeBwdArgs a) {
   constexpr int E = vec16<IO>::E;
-  constexpr int TILE = 8 / RW;
-  constexpr int ROWS = 4 / RW;   // rows per workgroup of 4 waves
   const int lane = lane_id();
-  const int wv = threadIdx.x >> 6;
-  const int part = wv % RW;
-  const int64_t grow = (int64_t)blockIdx.x * ROWS + wv / RW;
+  const int nvec = a.S / E;
+  const int vrows = (nvec + WAVE - 1) / WAVE;
+  const int64_t grow = (int64_t)blockIdx.x / vrows;
+  const int part = (int)((int64_t)blockIdx.x - grow * vrows);
   if (grow >= (int64_t)a.nsides * a.N) return;
   const int side = grow >= a.N ? 1 : 0;   // nsides <= 2
   const int64_t row = grow - (int64_t)side * a.N;
   const int k = a.k[side];
   const IO* __restrict__ src = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
   IO* __restrict__ dst = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)a.S;
-  const int nvec = a.S / E;
-  const int vrows = (nvec + WAVE - 1) / WAVE;            // 1 KiB vector rows of the row
-  const int lo = (part * vrows / RW) * WAVE;             // this wave's vectors [lo, hi)
-  const int hi = min(nvec, ((part + 1) * vrows / RW) * WAVE);
+  const int c = part * WAVE + lane;
+  const bool has = c < nvec;
   if (a.mask && !a.mask[token_of(row, a.H)]) {
     // a masked token takes no part in the computation: zero gradient
-    for (int c = lo + lane; c < hi; c += WAVE) st_nt16(dst + (int64_t)c * E, make_uint4(0, 0, 0, 0));
+    if (has) st_nt16(dst + (int64_t)c * E, make_uint4(0, 0, 0, 0));
     return;
   }
-  float gw = 0.f, wj = 0.f, gj = 0.f, lj = 0.f;
-  int aj = 0;
+  uint4 q = ld_nt16(src + (int64_t)min(c, nvec - 1) * E);   // clamped: in bounds
+  float gj = 0.f, wj = 0.f;
+  int aj = -1;
   if (lane < k) {
     gj = a.g[side][row * k + lane];
     wj = a.w[side][row * k + lane];
     aj = a.idx[side][row * k + lane];
+  }
+  const float nl = -a.lse[side][row] * LOG2E;
+  if (lane < k) {
     // the logit behind a CAPE slot is the content index (slot - shift)
     const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
     if (shift >= 0) aj = (aj - shift + a.S) % a.S;
-    lj = to_f32(src[aj]);
   }
-  gw = decode_gw(gj, wj, a.renorm[side]);
-  const float tot = wave_sum(gw);
-  const float nl = -a.lse[side][row] * LOG2E;
-  const float ntot = -tot;
-  const float fix = gw + ntot * fast_exp2(fmaf(lj, LOG2E, nl));
-  const int fix_row = (lane < k) ? aj / (E * WAVE) : -1;   // vector row holding a_j
-  for (int c0 = lo; c0 < hi; c0 += WAVE * TILE) {
-    uint4 q[TILE];
+  const float gw = decode_gw(gj, wj, a.renorm[side]);
+  const float ntot = -wave_sum(gw);
+  float x[E];
+  unpack16(q, x);
 #pragma unroll
-    for (int u = 0; u < TILE; ++u) {
-      const int c = c0 + u * WAVE + lane;
-      if (c < hi) q[u] = ld_nt16(src + (int64_t)c * E);
-    }
-    // every vector of the tile is finished before the first store: loads and
-    // stores share one completion counter, so a store between two vectors
-    // would make the next vector wait for it
+  for (int e = 0; e < E; ++e) x[e] = ntot * fast_exp2(fmaf(x[e], LOG2E, nl));
+  // selected entries inside this vector row (usually none)
+  uint64_t fixes = __ballot(lane < k && aj / (E * WAVE) == part);
+  while (fixes) {
+    const int j = (int)__builtin_ctzll(fixes);
+    fixes &= fixes - 1;
+    const int id = readlane_i(aj, j);
+    const float gwj = readlane_f(gw, j);
+    const bool mine = lane == (id / E) % WAVE;
 #pragma unroll
-    for (int u = 0; u < TILE; ++u) {
-      float x[E];
-      unpack16(q[u], x);
-#pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = ntot * fast_exp2(fmaf(x[e], LOG2E, nl));
-      // selected entries inside this vector row (usually none)
-      uint64_t fixes = __ballot(fix_row == c0 / WAVE + u);
-      while (fixes) {
-        const int j = (int)__builtin_ctzll(fixes);
-        fixes &= fixes - 1;
-        const int id = readlane_i(aj, j);
-        const float v = readlane_f(fix, j);
-        const bool mine = lane == (id / E) % WAVE;
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = (mine && id % E == e) ? v : x[e];
-      }
-      q[u] = pack16(x);
-    }
-#pragma unroll
-    for (int u = 0; u < TILE; ++u) {
-      const int c = c0 + u * WAVE + lane;
-      if (c < hi) st_nt16(dst + (int64_t)c * E, q[u]);
-    }
+    for (int e = 0; e < E; ++e) x[e] = (mine && id % E == e) ? gwj + x[e] : x[e];
   }
-}
-
-// Rows of one or two 1 KiB vector rows (S * io = 1 or 2 KiB): RPW
-// consecutive rows per wave, so that a wave keeps 4 KiB of loads in flight as
-// the larger rows' waves do (a wave of one 2 KiB row is bound by latency).
-// Each row is computed as in decode_bwd_kernel: its scalars from lanes j < k,
-// then its vectors, the selected entries put in before the stores.
-template <typename IO, int RPW>
-__global__ __launch_bounds__(256) void decode_bwd_small_kernel(DecodeBwdArgs a) {
-  constexpr int E = vec16<IO>::E;
-  constexpr int VPL = 4 / RPW;   // 16-byte vectors per lane and row: nvec = VPL * WAVE
-  const int lane = lane_id();
-  const int wv = threadIdx.x >> 6;
-  const int64_t total = (int64_t)a.nsides * a.N;
-  const int64_t g0 = ((int64_t)blockIdx.x * 4 + wv) * RPW;
-  if (g0 >= total) return;
-  const IO* src[RPW];
-  IO* dst[RPW];
-  bool live[RPW], zero[RPW];
-  int k[RPW], aj[RPW], renorm[RPW];
-  float gj[RPW], wj[RPW], lj[RPW], nl[RPW];
-  // every row's scalars are requested before any is used
-#pragma unroll
-  for (int q = 0; q < RPW; ++q) {
-    const int64_t grow = g0 + q;
-    live[q] = grow < total;
-    const int side = (live[q] && grow >= a.N) ? 1 : 0;   // nsides <= 2
-    const int64_t row = live[q] ? grow - (int64_t)side * a.N : 0;
-    k[q] = a.k[side];
-    renorm[q] = a.renorm[side];
-    src[q] = reinterpret_cast<const IO*>(a.logits[side]) + row * (int64_t)a.S;
-    dst[q] = reinterpret_cast<IO*>(a.dlogits[side]) + row * (int64_t)a.S;
-    zero[q] = !live[q] || (a.mask && !a.mask[token_of(row, a.H)]);
-    gj[q] = wj[q] = lj[q] = 0.f;
-    aj[q] = 0;
-    nl[q] = zero[q] ? 0.f : -a.lse[side][row] * LOG2E;
-    if (!zero[q] && lane < k[q]) {
-      gj[q] = a.g[side][row * k[q] + lane];
-      wj[q] = a.w[side][row * k[q] + lane];
-      int j = a.idx[side][row * k[q] + lane];
-      // the logit behind a CAPE slot is the content index (slot - shift)
-      const int shift = cape_shift_of(row, a.H, a.T, a.S, a.cape_heads, a.t0);
-      if (shift >= 0) j = (j - shift + a.S) % a.S;
-      aj[q] = j;
-      lj[q] = to_f32(src[q][j]);
-    }
-  }
-  uint4 v[RPW][VPL];
-#pragma unroll
-  for (int q = 0; q < RPW; ++q)
-#pragma unroll
-    for (int u = 0; u < VPL; ++u)
-      v[q][u] = zero[q] ? make_uint4(0, 0, 0, 0) : ld_nt16(src[q] + (int64_t)(u * WAVE + lane) * E);
-#pragma unroll
-  for (int q = 0; q < RPW; ++q) {
-    if (zero[q]) continue;   // wave-uniform: a masked token's row stays zero
-    const float gw = decode_gw(gj[q], wj[q], renorm[q]);
-    const float ntot = -wave_sum(gw);
-    const float fix = gw + ntot * fast_exp2(fmaf(lj[q], LOG2E, nl[q]));
-    const int fix_row = (lane < k[q]) ? aj[q] / (E * WAVE) : -1;   // vector row holding a_j
-#pragma unroll
-    for (int u = 0; u < VPL; ++u) {
-      float x[E];
-      unpack16(v[q][u], x);
-#pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = ntot * fast_exp2(fmaf(x[e], LOG2E, nl[q]));
-      uint64_t fixes = __ballot(fix_row == u);
-      while (fixes) {
-        const int j = (int)__builtin_ctzll(fixes);
-        fixes &= fixes - 1;
-        const int id = readlane_i(aj[q], j);
-        const float val = readlane_f(fix, j);
-        const bool mine = lane == (id / E) % WAVE;
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = (mine && id % E == e) ? val : x[e];
-      }
-      v[q][u] = pack16(x);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < RPW; ++q)
-#pragma unroll
-    for (int u = 0; u < VPL; ++u)
-      if (live[q]) st_nt16(dst[q] + (int64_t)(u * WAVE + lane) * E, v[q][u]);
+  if (has) st_nt16(dst + (int64_t)c * E, pack16(x));
 }
 
 // Product rows (U >= 2 digits, see decode_prod.hpp): one wave per row, rows
@@ -942,27 +834,14 @@ hipError_t launch_decode_bwd(const DecodeBwdArgs& a, bool bf16, hipStream_t st) 
     else hipLaunchKernelGGL(decode_bwd_prod_kernel<float>, grid, block, 0, st, a);
     return hipGetLastError();
   }
-  // Rows of 8 KiB are split over 2 waves of 4 KiB each: measured at the
-  // 1.3B-layer shape (S = 4096 bf16), 2.978 -> 2.913 ms (5.77 -> 5.90 TB/s);
-  // 4 waves of 2 KiB take 3.55 ms.  A copy in the same layout shows the same
-  // (4 KiB per wave 5.94 TB/s, 8 KiB per wave 5.15 TB/s).
-  // Rows of 1 or 2 KiB take 4 or 2 rows per wave (4 KiB in flight).
+  // One wave per 1 KiB of a row, one wave per workgroup (the fastest copy
+  // layout measured on this device).
   const int nvec = a.S / (bf16 ? vec16<bf16_t>::E : vec16<float>::E);
-  if (nvec == WAVE || nvec == 2 * WAVE) {
-    const int rpw = nvec == WAVE ? 4 : 2;
-    const dim3 gs((unsigned)((rows + 4 * rpw - 1) / (4 * rpw)));
-    if (bf16 && rpw == 4) hipLaunchKernelGGL((decode_bwd_small_kernel<bf16_t, 4>), gs, block, 0, st, a);
-    else if (bf16) hipLaunchKernelGGL((decode_bwd_small_kernel<bf16_t, 2>), gs, block, 0, st, a);
-    else if (rpw == 4) hipLaunchKernelGGL((decode_bwd_small_kernel<float, 4>), gs, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_bwd_small_kernel<float, 2>), gs, block, 0, st, a);
-  } else if (bf16 && a.S == 4096) {
-    const dim3 g2((unsigned)((rows + 1) / 2));
-    hipLaunchKernelGGL((decode_bwd_kernel<bf16_t, 2>), g2, block, 0, st, a);
-  } else if (bf16) {
-    hipLaunchKernelGGL((decode_bwd_kernel<bf16_t, 1>), grid, block, 0, st, a);
-  } else {
-    hipLaunchKernelGGL((decode_bwd_kernel<float, 1>), grid, block, 0, st, a);
-  }
+  const int64_t waves = rows * ((nvec + WAVE - 1) / WAVE);
+  if (waves > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  const dim3 gv((unsigned)waves), bv(WAVE);
+  if (bf16) hipLaunchKernelGGL(decode_bwd_vec_kernel<bf16_t>, gv, bv, 0, st, a);
+  else hipLaunchKernelGGL(decode_bwd_vec_kernel<float>, gv, bv, 0, st, a);
   return hipGetLastError();
 }
 

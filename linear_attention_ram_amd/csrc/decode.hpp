@@ -1,6 +1,8 @@
 // Row decoder of the RAM-Net attention core, shared by the decode kernels and
 // the autoregressive step kernel.  See decode.hip for the algorithm.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace ramk {
@@ -144,6 +146,31 @@ __device__ __forceinline__ float kth_lane_max(float m, int k) {
   return from_ordered(t);
 }
 
+// K-th largest lane value with multiplicity, for values that are bf16
+// numbers (their ordered bit patterns end in 16 zero bits, or 16 one bits
+// for negative values): the same search as kth_lane_max over the upper 16
+// bits only.
+__device__ __forceinline__ float kth_lane_max_bf16(float m, int k) {
+  const uint32_t mb = ordered_bits(m) >> 16;
+  const int ku = __builtin_amdgcn_readfirstlane(k);
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    t = (__popcll(__ballot(mb >= c)) >= ku) ? c : t;
+    t = __builtin_amdgcn_readfirstlane(t);
+  }
+  return from_ordered((t << 16) | ((t & 0x8000u) ? 0u : 0xFFFFu));
+}
+
+// tau of a row of io values: for bf16 rows the lane maxima are bf16 numbers
+// and the 16-bit search finds the same value in half the rounds.
+template <typename IO>
+__device__ __forceinline__ float kth_lane_max_io(float m, int k) {
+  if constexpr (std::is_same<IO, bf16_t>::value) return kth_lane_max_bf16(m, k);
+  else return kth_lane_max(m, k);
+}
+
 // Exact rank of every one of the `count` candidates in sc among the
 // candidates; the K best go to sc.sv / sc.si in order.
 __device__ __forceinline__ void rank_candidates(DecodeScratch& sc, int count, int k) {
@@ -272,7 +299,7 @@ __device__ __forceinline__ float decode_row_resident(const IO* __restrict__ row,
     }
   }
   const float lse = M + logf(wave_sum(s));
-  const float tau = kth_lane_max(m, k);
+  const float tau = kth_lane_max_io<IO>(m, k);
 
   // stage the vectors whose maximum reaches tau (they hold every top-K
   // element), then compact their elements >= tau into the candidate list
@@ -366,7 +393,7 @@ __device__ float decode_row_wave(const IO* __restrict__ row, int S, int k, int r
   const float part = (m == -INFINITY) ? 0.f : s * fast_exp2((m - M) * LOG2E);
   const float lse = M + logf(wave_sum(part));
 
-  const float tau = kth_lane_max(m, k);
+  const float tau = kth_lane_max_io<IO>(m, k);
 
   // lanes that may hold top-K elements
   const bool winner = (m >= tau);

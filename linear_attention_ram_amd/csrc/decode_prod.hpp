@@ -100,23 +100,6 @@ __device__ __noinline__ void product_k_passes(ProdScratch& sc, int U, int P, int
   }
 }
 
-// K-th largest lane value with multiplicity, for values that are bf16
-// numbers (their ordered bit patterns end in 16 zero bits, or 16 one bits
-// for negative values): the same search as kth_lane_max over the upper 16
-// bits only.
-__device__ __forceinline__ float kth_lane_max_bf16(float m, int k) {
-  const uint32_t mb = ordered_bits(m) >> 16;
-  const int ku = __builtin_amdgcn_readfirstlane(k);
-  uint32_t t = 0;
-#pragma unroll
-  for (int b = 15; b >= 0; --b) {
-    const uint32_t c = t | (1u << b);
-    t = (__popcll(__ballot(mb >= c)) >= ku) ? c : t;
-    t = __builtin_amdgcn_readfirstlane(t);
-  }
-  return from_ordered((t << 16) | ((t & 0x8000u) ? 0u : 0xFFFFu));
-}
-
 // Two digits of at most 64 values, in registers (lane L holds l0[L] and
 // l1[L], -inf past P).  The best key with digit-1 value L is fl(M0 + l1[L])
 // (M0 the largest digit-0 logit); tau = the K-th largest of these over the
