@@ -179,14 +179,18 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, WAVE);
   return x;
 }
-// Inclusive prefix sum over the lanes of a wave.
+// Inclusive prefix sum over the lanes of a wave, without LDS: row shifts
+// by 1, 2, 4 and 8 sum inside each row of 16 lanes (a lane with no source
+// in its row adds 0), then row_bcast:15 adds row 0's total to row 1 and
+// row 2's to row 3, and row_bcast:31 adds the total of rows 0-1 to rows 2-3.
+// Every lane must be active.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    int y = __shfl_up(x, o, WAVE);
-    if (lane >= o) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
   return x;
 }
 

@@ -14,8 +14,7 @@ constexpr int MAX_K = 64;       // largest top-K per side
 constexpr int STAGE_CAP = 64;   // 16-byte vectors staged per row by the resident decoder
 
 struct DecodeScratch {
-  float cv[CAND_CAP];
-  int ci[CAND_CAP];
+  uint64_t ck[CAND_CAP];   // candidate words: cand_word(value, index)
   uint4 stage[STAGE_CAP];
   int stage_c[STAGE_CAP];
   float sv[MAX_K];
@@ -172,14 +171,20 @@ __device__ __forceinline__ float kth_lane_max_io(float m, int k) {
 }
 
 // Exact rank of every one of the `count` candidates in sc among the
-// candidates; the K best go to sc.sv / sc.si in order.
+// candidates; the K best go to sc.sv / sc.si in order.  A candidate is
+// ranked by its word (cand_word): the larger word is the earlier entry in
+// (value descending, index ascending) order, and the words of distinct
+// indices are distinct, so the rank is the number of larger words.
 __device__ __forceinline__ void rank_candidates(DecodeScratch& sc, int count, int k) {
   for (int ci = lane_id(); ci < count; ci += WAVE) {
-    const float v = sc.cv[ci];
-    const int id = sc.ci[ci];
+    const uint64_t mine = sc.ck[ci];
     int rank = 0;
-    for (int o = 0; o < count; ++o) rank += before(sc.cv[o], sc.ci[o], v, id) ? 1 : 0;
-    if (rank < k) { sc.sv[rank] = v; sc.si[rank] = id; }
+#pragma unroll 4
+    for (int o = 0; o < count; ++o) rank += (sc.ck[o] > mine) ? 1 : 0;
+    if (rank < k) {
+      sc.sv[rank] = from_ordered((uint32_t)(mine >> 32));
+      sc.si[rank] = (int)(0xFFFFFFFFu - (uint32_t)mine);
+    }
   }
 }
 
@@ -189,6 +194,11 @@ __device__ __forceinline__ void rank_candidates(DecodeScratch& sc, int count, in
 __device__ __forceinline__ uint32_t sel_key(float x) {
   if (x != x) return 0u;
   return ordered_bits(x == 0.f ? 0.f : x);
+}
+// Word of a candidate (value x, not NaN, at index i): the ordered bits of x
+// (+0 for -0) above the complemented index.
+__device__ __forceinline__ uint64_t cand_word(float x, int i) {
+  return ((uint64_t)ordered_bits(x == 0.f ? 0.f : x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
 }
 __device__ __forceinline__ bool key_before(uint32_t v, int i, uint32_t v2, int i2) {
   return (v > v2) || (v == v2 && i < i2);
@@ -336,7 +346,7 @@ __device__ __forceinline__ float decode_row_resident(const IO* __restrict__ row,
       int pos = incl - mine;
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (x[e] >= tau) { sc.cv[pos] = x[e]; sc.ci[pos] = base + e; ++pos; }
+        if (x[e] >= tau) { sc.ck[pos] = cand_word(x[e], base + e); ++pos; }
     }
   }
   // fewer than K candidates: NaN logits (they compare false with tau)
@@ -427,7 +437,7 @@ __device__ float decode_row_wave(const IO* __restrict__ row, int S, int k, int r
     if (base >= 0) {
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (x[e] >= tau) { sc.cv[pos] = x[e]; sc.ci[pos] = base + e; ++pos; }
+        if (x[e] >= tau) { sc.ck[pos] = cand_word(x[e], base + e); ++pos; }
     }
     count += total;
   }
