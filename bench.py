@@ -302,7 +302,7 @@ def bench_stream(args, torch, ram, dev):
         read[name] = n / timed(lambda: ram.ram_stream_probe(0, v, src, dst)) / 1e9
         copy[name] = 2 * n / timed(lambda: ram.ram_stream_probe(1, v, src, dst)) / 1e9
     torch_copy = 2 * n / timed(lambda: dst.copy_(src)) / 1e9
-    own = ram.STREAM_PROBE_VARIANTS[0]
+    own = ram.STREAM_PROBE_VARIANTS[5]   # the decode backward's pattern
     return {
         "metric": "HBM streaming roofs of the decoders' access pattern on 1 MI355X",
         "value": copy[own], "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,

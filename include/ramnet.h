@@ -268,8 +268,10 @@ const char* ram_status_string(int status);
  * its loads in flight at once) and, with mode 1, writes it to dst (a copy,
  * the pattern of a decode backward row: read a row, write a row); mode 0
  * only reads.  variant: 0 = 8 KiB rows, 4 waves per workgroup, nontemporal
- * loads and stores (the decoders' own); 1 = the same with plain loads and
- * stores; 2 = 16 KiB rows; 3 = 4 KiB rows; 4 = 8 waves per workgroup.  src
+ * loads and stores (the forward decoder's own); 1 = the same with plain
+ * loads and stores; 2 = 16 KiB rows; 3 = 4 KiB rows; 4 = 8 waves per
+ * workgroup; 5 = 1 KiB rows, one wave per workgroup (the decode backward's
+ * own); 6 = 2 KiB rows, one wave per workgroup.  src
  * and dst are device buffers of `bytes` each, 16-byte aligned; bytes must be a
  * multiple of the variant's workgroup tile (128 KiB covers every variant),
  * else RAM_EINVAL.  Asynchronous on the given stream. */

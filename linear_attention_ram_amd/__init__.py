@@ -343,7 +343,8 @@ def ram_decode_step(p: Problem, wlogits, rlogits, v, gamma, slot, mass, o, strea
 
 STREAM_PROBE_VARIANTS = ("8 KiB rows, 4 waves, nontemporal", "8 KiB rows, 4 waves, plain",
                          "16 KiB rows, 4 waves, nontemporal", "4 KiB rows, 4 waves, nontemporal",
-                         "8 KiB rows, 8 waves, nontemporal")
+                         "8 KiB rows, 8 waves, nontemporal", "1 KiB rows, 1 wave, nontemporal",
+                         "2 KiB rows, 1 wave, nontemporal")
 
 
 def ram_stream_probe(mode: int, variant: int, src, dst, stream=None):

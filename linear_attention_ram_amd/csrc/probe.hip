@@ -42,10 +42,12 @@ struct Variant {
   int row_vecs, waves;
   bool nt;
 };
-// 0: the decoders' pattern (8 KiB rows, 4 waves, nontemporal); 1: the same
-// with plain loads and stores; 2: 16 KiB rows; 3: 4 KiB rows; 4: 8 waves
+// 0: the forward decoder's pattern (8 KiB rows, 4 waves, nontemporal); 1: the
+// same with plain loads and stores; 2: 16 KiB rows; 3: 4 KiB rows; 4: 8 waves;
+// 5: 1 KiB rows, one wave per workgroup (the decode backward's pattern);
+// 6: 2 KiB rows, one wave per workgroup
 constexpr Variant VARIANTS[] = {{8, 4, true}, {8, 4, false}, {16, 4, true}, {4, 4, true},
-                                {8, 8, true}};
+                                {8, 8, true}, {1, 1, true},  {2, 1, true}};
 constexpr int NVARIANTS = (int)(sizeof(VARIANTS) / sizeof(VARIANTS[0]));
 
 template <int RV, int W, bool NT>
@@ -83,7 +85,9 @@ extern "C" int ram_stream_probe(int mode, int variant, const void* src, void* ds
     case 1: e = launch_v<8, 4, false>(copy, src, dst, bytes, st); break;
     case 2: e = launch_v<16, 4, true>(copy, src, dst, bytes, st); break;
     case 3: e = launch_v<4, 4, true>(copy, src, dst, bytes, st); break;
-    default: e = launch_v<8, 8, true>(copy, src, dst, bytes, st); break;
+    case 4: e = launch_v<8, 8, true>(copy, src, dst, bytes, st); break;
+    case 5: e = launch_v<1, 1, true>(copy, src, dst, bytes, st); break;
+    default: e = launch_v<2, 1, true>(copy, src, dst, bytes, st); break;
   }
   return e == hipSuccess ? RAM_OK : RAM_EHIP;
 }
