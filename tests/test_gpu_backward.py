@@ -63,6 +63,17 @@ def test_340m_full(with_state):
     full_check(cfg, x, gpu_problem(cfg), with_state, with_state, TOL["bf16"])
 
 
+@pytest.mark.parametrize("S,io,k", [(640, "bf16", 12), (1000, "f32", 9), (2056, "bf16", 16)])
+def test_partial_last_kilobyte(S, io, k):
+    # the decode backward streams each logits row in 1 KiB pieces, one wave
+    # each: rows whose length is not a multiple of 1 KiB (here 1280, 4000 and
+    # 4112 bytes) end in a partial piece, and with k up to 16 several selected
+    # entries can share a piece
+    cfg = synth.Config(f"partial-{S}-{io}", 2, 3, 96, S, k, k, 64 if io == "bf16" else 40, io)
+    x = synth.layer_inputs(cfg, device=DEV, seed=11, with_state=True, with_state_grads=True)
+    full_check(cfg, x, gpu_problem(cfg), True, True, TOL[io])
+
+
 def test_1_3b_sampled_slices():
     cfg = synth.CONFIGS["1.3b"]
     x = synth.layer_inputs(cfg, device=DEV, seed=0)
