@@ -1403,10 +1403,16 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
     for (int j = 0; j < a.k; ++j) acc += to_f32(st[(row * a.k + j) * a.d_v + c]);
     out[row * a.d_v + c] = from_f32<IO>(acc);
   }
-  if (a.dgam && tid < a.N) {
-    float sum = 0.f;
-    for (int j = 0; j < a.k; ++j) sum += a.dgam[tid * a.k + j];
-    reinterpret_cast<IO*>(a.d_gamma)[tid] = from_f32<IO>(sum);
+  if (a.dgam) {
+    // the thread of a row's first column also sums the row's dgam, so that
+    // the sums spread over the grid with the rows
+    const int per_row = (a.d_v % E == 0) ? a.d_v / E : a.d_v;
+    const int64_t row = tid / per_row;
+    if (tid - row * per_row == 0 && row < a.N) {
+      float sum = 0.f;
+      for (int j = 0; j < a.k; ++j) sum += a.dgam[row * a.k + j];
+      reinterpret_cast<IO*>(a.d_gamma)[row] = from_f32<IO>(sum);
+    }
   }
 }
 
@@ -1508,9 +1514,10 @@ hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st, hipS
 hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
   const int E = bf16 ? 8 : 4;
-  int64_t threads = (a.d_v % E == 0) ? a.N * (a.d_v / E) : a.N * a.d_v;
-  if (threads < a.N) threads = a.N;
-  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  const int64_t threads = (a.d_v % E == 0) ? a.N * (a.d_v / E) : a.N * a.d_v;
+  // one-wave workgroups: a read-heavy stream runs faster in them on this
+  // device than in four-wave ones
+  const dim3 grid((unsigned)((threads + WAVE - 1) / WAVE)), block(WAVE);
   if (bf16) hipLaunchKernelGGL(finalize_kernel<bf16_t>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(finalize_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
