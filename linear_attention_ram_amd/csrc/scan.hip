@@ -1295,9 +1295,15 @@ __device__ void scan_bwd_long(const ScanBwdArgs& args, int64_t g) {
   }
 }
 
-// Same split as the forward.
+// Same split as the forward.  Held to five waves per SIMD (96 registers,
+// three of them spilled): its waves are bound by dependent memory round
+// trips, and the fifth wave measured 3-4% faster where short segments carry
+// the pass (1.3B shape without bias: 1.108 -> 1.074 ms; as U = 2 x 64:
+// 1.056 -> 1.016 ms); six or eight waves spill 18 or 34 registers and are
+// 20-50% slower.
 template <typename IO, int CPL>
-__global__ __launch_bounds__(SHORT_WAVES * WAVE) void scan_bwd_short_kernel(ScanBwdArgs a) {
+__global__ __launch_bounds__(SHORT_WAVES * WAVE) __attribute__((amdgpu_waves_per_eu(5, 8)))
+void scan_bwd_short_kernel(ScanBwdArgs a) {
   const int64_t i = (int64_t)blockIdx.x * SHORT_WAVES + wave_index();
   if (i >= a.nseg) return;
   int beg, end;
